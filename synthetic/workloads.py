@@ -1,0 +1,169 @@
+"""The five synthetic workloads of PLaMo 3's attention hot path, with their sizes.
+
+Shapes follow the PLaMo 3 31B configuration (64 query heads, 8 KV heads, head
+dimension 128, window 2048, local RoPE base 1e4, global base 1e6) as given in
+「PLaMo 3アーキテクチャ徹底解析」 §2.1. Values are synthetic N(0, 1) draws; the
+norm gains are the stored-weight part only, drawn N(0, 0.02), with the offset
+passed separately.
+
+Draw order within a workload's stream: q, k, v, q-norm weight, k-norm weight.
+Large decode caches are drawn separately (``cache_seed``), on the device that
+holds them, by ``synthetic.device_normal_bf16``.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import BASE_SEED, Draw
+
+
+@dataclass(frozen=True)
+class Rope:
+    theta: float
+    yarn_factor: float = 0.0  # <= 1 disables YaRN
+    orig_ctx: float = 4096.0
+    beta_fast: float = 32.0
+    beta_slow: float = 1.0
+
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    B: int
+    T: int
+    Hq: int
+    Hkv: int
+    d: int
+    window: int  # 0 = global causal layer
+    rope: Rope
+    norm_offset: float | None  # None = no Q/K norm
+    bf16: bool
+    seed: int
+    norm_std: float = 0.02
+    eps: float = 1e-6
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def draw(self):
+        """Return dict of float32 arrays (bf16-exact when ``bf16``):
+        q [B,T,Hq,d], k [B,T,Hkv,d], v [B,T,Hkv,d], wq [d], wk [d] (None without norm)."""
+        dr = Draw(self.seed, self.bf16)
+        q = dr.normal((self.B, self.T, self.Hq, self.d))
+        k = dr.normal((self.B, self.T, self.Hkv, self.d))
+        v = dr.normal((self.B, self.T, self.Hkv, self.d))
+        wq = wk = None
+        if self.norm_offset is not None:
+            wq = dr.normal((self.d,), self.norm_std)
+            wk = dr.normal((self.d,), self.norm_std)
+        return dict(q=q, k=k, v=v, wq=wq, wk=wk)
+
+    def attended_pairs_per_head(self) -> int:
+        """Number of unmasked (query, key) pairs of one head, prefill from an empty cache."""
+        T, W = self.T, self.window
+        if W <= 0 or W >= T:
+            return T * (T + 1) // 2
+        return W * (W + 1) // 2 + (T - W) * W
+
+    def flops(self) -> float:
+        """Algorithmic FLOP: 2·d for the score and 2·d for the weighted sum per pair and head."""
+        return 4.0 * self.d * self.Hq * self.B * self.attended_pairs_per_head()
+
+
+TINY_SWA_FP32 = PrefillWorkload(
+    name="tiny_swa_prefill_fp32", B=1, T=512, Hq=8, Hkv=2, d=128, window=128,
+    rope=Rope(theta=1e4), norm_offset=None, bf16=False, seed=BASE_SEED + 1)
+
+LOCAL_PREFILL = PrefillWorkload(
+    name="local_prefill_T8192_W2048", B=1, T=8192, Hq=64, Hkv=8, d=128, window=2048,
+    rope=Rope(theta=1e4), norm_offset=0.2, bf16=True, seed=BASE_SEED + 2)
+
+GLOBAL_PREFILL = PrefillWorkload(
+    name="global_prefill_T32768_yarn64", B=1, T=32768, Hq=64, Hkv=8, d=128, window=0,
+    rope=Rope(theta=1e6, yarn_factor=64.0), norm_offset=5.0 ** -1.5, bf16=True,
+    seed=BASE_SEED + 3)
+
+
+@dataclass(frozen=True)
+class DecodeLayer:
+    window: int  # 0 = global
+    rope: Rope
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    pos_offset: int  # absolute position of the first decoded token
+    layers: tuple
+    steps: int
+    seed: int
+    norm_offset: float = 1.0
+    norm_std: float = 0.02
+    eps: float = 1e-6
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def keys_attended(self, layer: DecodeLayer, step: int = 0) -> int:
+        p = self.pos_offset + step
+        kept = p if layer.window == 0 else min(p, layer.window - 1)
+        return kept + 1
+
+    def cache_cap(self, layer: DecodeLayer) -> int:
+        if layer.window == 0:
+            return self.pos_offset + self.steps
+        return layer.window
+
+    def kv_bytes(self, layer: DecodeLayer, step: int = 0) -> int:
+        """Algorithmic KV bytes read by one decode of one layer: K and V rows (bf16) of every
+        attended key, once per sequence and KV head (shared by the query heads of a group)."""
+        return 2 * 2 * self.B * self.Hkv * self.d * self.keys_attended(layer, step)
+
+    def draw_new_tokens(self, step: int, layer_index: int):
+        """q [B,1,Hq,d], k, v [B,1,Hkv,d] and norm weights for one (step, layer), bf16-exact."""
+        dr = Draw(self.seed * 1000003 + step * 64 + layer_index, True)
+        q = dr.normal((self.B, 1, self.Hq, self.d))
+        k = dr.normal((self.B, 1, self.Hkv, self.d))
+        v = dr.normal((self.B, 1, self.Hkv, self.d))
+        wq = dr.normal((self.d,), self.norm_std)
+        wk = dr.normal((self.d,), self.norm_std)
+        return dict(q=q, k=k, v=v, wq=wq, wk=wk)
+
+    def cache_seed(self, layer_index: int) -> int:
+        return self.seed * 7919 + layer_index
+
+
+LOCAL_ROPE = Rope(theta=1e4)
+GLOBAL_ROPE = Rope(theta=1e6, yarn_factor=64.0)
+
+BATCHED_DECODE = DecodeWorkload(
+    name="batched_decode_B64", B=64, Hq=64, Hkv=8, d=128, pos_offset=32767,
+    layers=(DecodeLayer(2048, LOCAL_ROPE), DecodeLayer(0, GLOBAL_ROPE)), steps=1,
+    seed=BASE_SEED + 4)
+
+PERIOD_DECODE = DecodeWorkload(
+    name="period8_decode_B8_ctx131072", B=8, Hq=64, Hkv=8, d=128, pos_offset=131071,
+    layers=tuple([DecodeLayer(2048, LOCAL_ROPE)] * 7 + [DecodeLayer(0, GLOBAL_ROPE)]),
+    steps=128, seed=BASE_SEED + 5)
+
+
+def device_normal_bf16(shape, seed: int, device):
+    """N(0, 1) draws rounded to bfloat16, generated by torch on ``device`` (used for
+    decode caches of several GiB). The same (shape, seed, device type) gives the same
+    values; the CPU side copies whatever it needs from the returned tensor."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return x.to(torch.bfloat16)
