@@ -1,0 +1,304 @@
+"""Benchmark of the PLaMo 3 hybrid attention hot path on one MI355X.
+
+One JSON line on stdout. The headline step is one local-layer prefill at the PLaMo 3
+shape (B=1, T=8192, Hq=64, Hkv=8, d=128, W=2048): plamo_kv_append (QK norm, cache
+write, RoPE, prefill operands) + plamo_attn_prefill, inputs resident in HBM. ``value``
+is algorithmic prefill FLOP (4*d per attended (query, key) pair and query head) per
+second of that step. Also reported: the global-layer prefill (T=32768, YaRN), batched
+decode (B=64; ring W=2048 and global 32768) as KV-read GB/s, the 8-layer period decode
+at 131072 context, the roofline object of the prefill kernel, and the CPU oracle timed
+on a bounded sample of the headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn TFLOP/s (SWA W=2048 + global) & decode KV-read GB/s, 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# timing helpers: torch events on the stream the library launches on
+# ----------------------------------------------------------------------------
+
+class Timer:
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def span(self):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        self.pairs.append((a, b))
+        return a, b
+
+    def mean_ms(self):
+        self.torch.cuda.synchronize()
+        v = [a.elapsed_time(b) for a, b in self.pairs]
+        return sum(v) / len(v)
+
+
+def dev_bf16(torch, x):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda()
+
+
+def rope_params(swg, r):
+    return swg.RopeParams(r.theta, r.yarn_factor, r.orig_ctx, r.beta_fast, r.beta_slow)
+
+
+# ----------------------------------------------------------------------------
+# prefill
+# ----------------------------------------------------------------------------
+
+def bench_prefill(torch, swg, wl, steps, warmup, norm_offset):
+    from sliding_window_global_amd import layer
+    inp = wl.draw()
+    q, k, v = dev_bf16(torch, inp["q"]), dev_bf16(torch, inp["k"]), dev_bf16(torch, inp["v"])
+    wq, wk = dev_bf16(torch, inp["wq"]), dev_bf16(torch, inp["wk"])
+    tab = swg.make_rope_table(wl.T + 64, rope_params(swg, wl.rope))
+    cap = wl.window if wl.window else wl.T
+    kc = torch.empty((wl.B, wl.Hkv, cap, wl.d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    bufs = layer.PrefillBuffers(wl.B, wl.T, wl.Hq, wl.Hkv, wl.d, torch.bfloat16)
+
+    def step(t_step=None, t_attn=None):
+        if t_step:
+            t_step[0].record()
+        swg.plamo_kv_append(q, k, v, bufs.q_rot, window=wl.window, pos_offset=0, rope_table=tab,
+                            q_norm_w=wq, k_norm_w=wk, norm_offset=norm_offset, k_rot_out=bufs.k_rot,
+                            v_t_out=bufs.v_t, k_cache=kc, v_cache=vc)
+        if t_attn:
+            t_attn[0].record()
+        swg.plamo_attn_prefill(bufs.q_rot, bufs.k_rot, bufs.v_t, bufs.out, window=wl.window)
+        if t_attn:
+            t_attn[1].record()
+        if t_step:
+            t_step[1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ts, ta = Timer(torch), Timer(torch)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for _ in range(steps):
+        step(ts.span(), ta.span())
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step, ms_attn = ts.mean_ms(), ta.mean_ms()
+    flops = wl.flops()
+    return dict(workload=wl.name, flops=flops, ms_per_step=ms_step, ms_attn=ms_attn,
+                step_tflops=flops / ms_step / 1e9, attn_tflops=flops / ms_attn / 1e9,
+                wall_ms_per_step=wall / steps * 1e3)
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+
+def bench_decode_batched(torch, swg, wl, layer_idx, steps, warmup):
+    """attn_decode alone (the split kernel + combine) over a cache at its real size."""
+    from sliding_window_global_amd import layer
+    from synthetic.workloads import device_normal_bf16
+    ly = wl.layers[layer_idx]
+    p = wl.pos_offset
+    cap = wl.cache_cap(ly)
+    kc = device_normal_bf16((wl.B, wl.Hkv, cap, wl.d), wl.cache_seed(layer_idx), "cuda")
+    vc = device_normal_bf16((wl.B, wl.Hkv, cap, wl.d), wl.cache_seed(layer_idx) + 1, "cuda")
+    new = wl.draw_new_tokens(0, layer_idx)
+    tab = swg.make_rope_table(p + wl.steps + 64, rope_params(swg, ly.rope))
+    bufs = layer.DecodeBuffers(wl.B, wl.Hq, wl.Hkv, wl.d, ly.window, p)
+    swg.plamo_kv_append(dev_bf16(torch, new["q"]), dev_bf16(torch, new["k"]), dev_bf16(torch, new["v"]),
+                        bufs.q_rot, window=ly.window, pos_offset=p, rope_table=tab,
+                        q_norm_w=dev_bf16(torch, new["wq"]), k_norm_w=dev_bf16(torch, new["wk"]),
+                        norm_offset=wl.norm_offset, k_cache=kc, v_cache=vc)
+
+    def run():
+        swg.plamo_attn_decode(bufs.q_rot, kc, vc, bufs.out, bufs.workspace, window=ly.window,
+                              pos_offset=p, rope_table=tab)
+
+    for _ in range(warmup):
+        run()
+    t = Timer(torch)
+    for _ in range(steps):
+        a, b = t.span()
+        a.record()
+        run()
+        b.record()
+    ms = t.mean_ms()
+    nbytes = wl.kv_bytes(ly)
+    del kc, vc
+    torch.cuda.empty_cache()
+    return dict(workload=f"{wl.name}_{'global' if ly.window == 0 else 'local'}", kv_bytes=nbytes,
+                keys=wl.keys_attended(ly), ms=ms, gbs=nbytes / ms / 1e6, frac_hbm=nbytes / ms / 1e6 / PEAK_HBM_GBS)
+
+
+def bench_period(torch, swg, wl, n_steps):
+    """The 8-layer period (7 local W=2048 + 1 global), append + decode per layer per step,
+    at 131072+k global context, batch 8."""
+    from sliding_window_global_amd import layer
+    from synthetic.workloads import device_normal_bf16
+    caches, tabs, bufs, news = [], [], [], []
+    for li, ly in enumerate(wl.layers):
+        cap = wl.cache_cap(ly)
+        caches.append((device_normal_bf16((wl.B, wl.Hkv, cap, wl.d), wl.cache_seed(li), "cuda"),
+                       device_normal_bf16((wl.B, wl.Hkv, cap, wl.d), wl.cache_seed(li) + 1, "cuda")))
+        tabs.append(swg.make_rope_table(wl.pos_offset + wl.steps + 64, rope_params(swg, ly.rope)))
+        bufs.append(layer.DecodeBuffers(wl.B, wl.Hq, wl.Hkv, wl.d, ly.window, wl.pos_offset + wl.steps))
+    for s in range(min(n_steps, 4)):  # a few distinct token sets, reused cyclically
+        news.append([{k: (dev_bf16(torch, x) if x is not None else None) for k, x in wl.draw_new_tokens(s, li).items()}
+                     for li in range(len(wl.layers))])
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    total_bytes = 0
+    t0.record()
+    for s in range(n_steps):
+        p = wl.pos_offset + s
+        for li, ly in enumerate(wl.layers):
+            nt = news[s % len(news)][li]
+            kc, vc = caches[li]
+            layer.decode(nt["q"], nt["k"], nt["v"], kc, vc, window=ly.window, pos_offset=p,
+                         rope_table=tabs[li], q_norm_w=nt["wq"], k_norm_w=nt["wk"],
+                         norm_offset=wl.norm_offset, bufs=bufs[li])
+            total_bytes += wl.kv_bytes(ly, s)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    del caches
+    torch.cuda.empty_cache()
+    return dict(workload=wl.name, steps=n_steps, ms_total=ms, ms_per_step=ms / n_steps,
+                kv_bytes_total=total_bytes, gbs=total_bytes / ms / 1e6,
+                frac_hbm=total_bytes / ms / 1e6 / PEAK_HBM_GBS)
+
+
+# ----------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample of the headline workload)
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(wl, norm_offset, n_rows):
+    import numpy as np
+
+    from oracle import LayerKVCache, attention_layer_step
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    inp = wl.draw()
+    rows = np.linspace(0, wl.T - 1, n_rows).astype(np.int64)
+    t0 = time.perf_counter()
+    cache = LayerKVCache(wl.Hkv, wl.d, wl.window)
+    attention_layer_step(inp["q"][0], inp["k"][0], inp["v"][0], cache, theta=wl.rope.theta,
+                         yarn_factor=wl.rope.yarn_factor, q_norm_w=inp["wq"], k_norm_w=inp["wk"],
+                         norm_offset=norm_offset, scale=1.0 / math.sqrt(wl.d), rows=rows)
+    sec = time.perf_counter() - t0
+    pairs = int(np.sum(np.minimum(rows + 1, wl.window if wl.window else wl.T)))
+    flops = 4.0 * wl.d * wl.Hq * pairs
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{wl.name}: {n_rows} of {wl.T} query rows x {wl.Hq} heads (full norm, cache, "
+                      f"RoPE of all {wl.T} keys; fp64 NumPy), {sec:.1f} s"}
+
+
+# ----------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="", help="prefill_local|prefill_global|decode|period")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--period-steps", type=int, default=128)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import sliding_window_global_amd as swg
+    from synthetic.workloads import BATCHED_DECODE, GLOBAL_PREFILL, LOCAL_PREFILL, PERIOD_DECODE
+
+    torch.cuda.set_device(0)
+    swg._lib.load()
+    only = args.only
+    extra = {}
+    local = None
+    if only in ("", "prefill_local"):
+        log("[bench] local prefill T=8192 W=2048")
+        local = bench_prefill(torch, swg, LOCAL_PREFILL, args.steps, args.warmup, LOCAL_PREFILL.norm_offset)
+        log(f"[bench]   {local}")
+    if only in ("", "prefill_global"):
+        log("[bench] global prefill T=32768 YaRN")
+        g = bench_prefill(torch, swg, GLOBAL_PREFILL, max(3, args.steps // 4), max(1, args.warmup // 2),
+                          GLOBAL_PREFILL.norm_offset)
+        log(f"[bench]   {g}")
+        extra["prefill_global"] = {k: g[k] for k in ("workload", "ms_per_step", "ms_attn", "step_tflops", "attn_tflops")}
+        extra["prefill_global"]["frac_mfma"] = g["attn_tflops"] / PEAK_BF16_TFLOPS
+    if only in ("", "decode"):
+        for li in (0, 1):
+            log(f"[bench] batched decode layer {li}")
+            r = bench_decode_batched(torch, swg, BATCHED_DECODE, li, args.steps, args.warmup)
+            log(f"[bench]   {r}")
+            extra[r["workload"]] = r
+    if only in ("", "period"):
+        log("[bench] 8-layer period decode")
+        r = bench_period(torch, swg, PERIOD_DECODE, args.period_steps)
+        log(f"[bench]   {r}")
+        extra["period_decode"] = r
+
+    if local is None:
+        print(json.dumps({"metric": METRIC, "partial": only, "extra": extra}))
+        return
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu oracle baseline")
+        cpu = cpu_baseline(LOCAL_PREFILL, LOCAL_PREFILL.norm_offset, args.cpu_rows)
+        log(f"[bench]   {cpu}")
+    line = {
+        "metric": METRIC,
+        "value": round(local["step_tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(local["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": LOCAL_PREFILL.name, "B": 1, "T": 8192, "Hq": 64, "Hkv": 8, "d": 128,
+                   "window": 2048, "step": "kv_append + attn_prefill"},
+        "roofline": {"bound": "mfma", "achieved": round(local["attn_tflops"], 3),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(local["attn_tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_bf16_kernel", "flop_per_launch": LOCAL_PREFILL.flops()},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

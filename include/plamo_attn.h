@@ -1,0 +1,172 @@
+/*
+ * plamo_attn.h -- C ABI of the MI355X (gfx950) implementation of PLaMo 3's hybrid
+ * sliding-window / global grouped-query attention, prefill and KV-cached decode.
+ *
+ * Sources (page title, section):
+ *   [P3] 「PLaMo 3アーキテクチャ徹底解析」 (imoz.jp, 2026-10-26)
+ *
+ * What one attention layer computes, in this order [P3 §4.4]:
+ *   1. per-head RMSNorm of Q and K with gain (c + w) [P3 §3.2, §4.3]; V untouched;
+ *   2. KV-cache update: the cache stores normalised K *before* RoPE and raw V
+ *      [P3 §4.4]; a global layer keeps every token, a local layer keeps at most the
+ *      last W-1 tokens after the update [P3 §4.4];
+ *   3. split-half RoPE (pairs j, j+d/2) [P3 §6.1] on the current Q and on every K
+ *      the cache returns, with YaRN frequencies and amplitude on global layers
+ *      [P3 §6.3]; positions are renumbered: the S returned keys get 0..S-1 and the
+ *      T queries S-T..S-1 [P3 §4.4];
+ *   4. softmax(Q'K'^T * scale + M) V with the causal mask, plus i - j < W on local
+ *      layers [P3 §4.5, §5.1]; query head h reads KV head h / (Hq/Hkv) [P3 §4.2].
+ *
+ * Conventions for every entry point
+ *   - Pointers are device memory owned by the caller unless stated otherwise. The
+ *     library never allocates or frees device memory; decode scratch comes in as
+ *     a caller-provided workspace.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *     Nothing synchronises; buffers must stay alive until the stream has run it.
+ *   - Arguments are checked before anything is launched; on failure the call
+ *     returns a negative plamo_status and enqueues nothing. A launch error is
+ *     reported as PLAMO_ERR_HIP. No C++ exception crosses this boundary.
+ *   - dtype PLAMO_BF16: bf16 tensors, fp32 arithmetic inside. PLAMO_F32: fp32
+ *     tensors and arithmetic (prefill path only).
+ *   - Head dimension d must be 128 (PLaMo 3's head_dim [P3 §2.1]); Hq must be a
+ *     multiple of Hkv and Hq/Hkv <= 16.
+ *   - Positions are 64-bit; one pos_offset serves every sequence of the batch.
+ *   - Entry points hold no mutable global state and may be called from several
+ *     host threads on different streams.
+ */
+#ifndef PLAMO_ATTN_H
+#define PLAMO_ATTN_H
+
+#include <stddef.h>
+
+#if defined(__GNUC__)
+#define PLAMO_API __attribute__((visibility("default")))
+#else
+#define PLAMO_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PLAMO_OK = 0,
+  PLAMO_ERR_INVALID_ARG = -1, /* shape, pointer, alignment or size mismatch */
+  PLAMO_ERR_UNSUPPORTED = -2, /* valid per the method, not implemented here */
+  PLAMO_ERR_WORKSPACE = -3,   /* rope table or workspace too small */
+  PLAMO_ERR_HIP = -4          /* the HIP runtime reported an error at launch */
+} plamo_status;
+
+typedef enum { PLAMO_F32 = 0, PLAMO_BF16 = 1 } plamo_dtype;
+
+/* RoPE parameters of one layer type [P3 §2.1, §6.2, §6.3].
+ * Local layers: theta = 1e4, no YaRN. Global layers: theta = 1e6 with YaRN. */
+typedef struct {
+  double theta;       /* RoPE base */
+  double yarn_factor; /* YaRN factor s; <= 1 disables YaRN (amplitude 1) */
+  double orig_ctx;    /* YaRN original context L0 (4096) */
+  double beta_fast;   /* 32 */
+  double beta_slow;   /* 1 */
+} plamo_rope;
+
+/* ---------------------------------------------------------------------------
+ * RoPE table [P3 §6.1, §6.3]
+ *
+ * Opaque device table of rotation factors for positions 0 .. max_pos-1 and the
+ * d/2 pairs, built in fp64 and stored as fp32 (cos, sin) pairs, the YaRN
+ * amplitude included. One table serves one layer type; a table built for
+ * max_pos covers every position below it.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes needed for a table covering positions [0, max_pos). 0 on bad arguments. */
+PLAMO_API size_t plamo_rope_table_bytes(long long max_pos, int d);
+
+/* Fill `table` (device, `table_bytes` >= plamo_rope_table_bytes(max_pos, d)). */
+PLAMO_API int plamo_rope_table_init(void* table, size_t table_bytes, long long max_pos, int d,
+                          const plamo_rope* rope, void* stream);
+
+/* Padded token count used by the prefill operand layouts: T rounded up to 128. */
+PLAMO_API long long plamo_prefill_padded_len(long long T);
+
+/* ---------------------------------------------------------------------------
+ * plamo_kv_append -- steps 1-3 for T new tokens of B sequences [P3 §4.3, §4.4, §6]
+ *
+ * The new tokens have absolute positions pos_offset .. pos_offset+T-1. kept =
+ * pos_offset (global, window = 0) or min(pos_offset, window-1) (local); their
+ * renumbered positions are kept .. kept+T-1.
+ *
+ * q        [B, T, Hq,  d]  projected queries                     (dtype)
+ * k, v     [B, T, Hkv, d]  projected keys and values             (dtype)
+ * q_norm_w, k_norm_w [d]   stored norm weights w (gain c + w); both NULL = no norm
+ * norm_offset, norm_eps    c (1 for q_norm/k_norm [P3 §3.2]) and eps (1e-6)
+ * q_out    [B, T, Hq, d]   normalised and rotated Q                (dtype, required)
+ * k_rot_out [B, Hkv, Tp, d] normalised, cache-rounded and rotated K, Tp =
+ *                          plamo_prefill_padded_len(T); rows T..Tp-1 are zeroed.
+ *                          NULL = not written. (Prefill operand.)
+ * v_t_out  [B, Hkv, d, Tp] V transposed (token index fastest), pad zeroed. NULL =
+ *                          not written. (Prefill operand.)
+ * k_cache, v_cache [B, Hkv, cap, d]  normalised pre-RoPE K and raw V (dtype). NULL
+ *                          (both) = no cache. Global: token n goes to slot n,
+ *                          cap >= pos_offset + T. Local: slot n mod window (a ring of
+ *                          `window` slots, cap >= window); only the last `window`
+ *                          new tokens are written.
+ * window   0 = global layer, W > 0 = local layer with W keys including self.
+ * rope_table / rope_table_bytes  a table built for this layer type covering every
+ *                          renumbered position < kept + T.
+ * ------------------------------------------------------------------------- */
+PLAMO_API int plamo_kv_append(int dtype, const void* q, const void* k, const void* v,
+                    const void* q_norm_w, const void* k_norm_w, float norm_offset,
+                    float norm_eps, void* q_out, void* k_rot_out, void* v_t_out,
+                    void* k_cache, void* v_cache, long long cap, int B, int T, int Hq,
+                    int Hkv, int d, int window, long long pos_offset,
+                    const void* rope_table, size_t rope_table_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * plamo_attn_prefill -- step 4 for a prefill from an empty cache [P3 §4.5, §5.1]
+ *
+ * q_rot [B, T, Hq, d]; k_rot [B, Hkv, Tp, d]; v_t [B, Hkv, d, Tp] as written by
+ * plamo_kv_append (Tp = plamo_prefill_padded_len(T)); out [B, T, Hq, d] (token
+ * major, i.e. [B, T, Hq*d] ready for the output projection [P3 §4.5]).
+ * Query i (0..T-1) attends keys j <= i, and i - j < window when window > 0.
+ * softmax_scale is 1/sqrt(d) [P3 §4.5]; the YaRN amplitude is already in q_rot
+ * and k_rot. pos_offset must be 0 (a prefill on top of a populated cache is not
+ * implemented: PLAMO_ERR_UNSUPPORTED).
+ * ------------------------------------------------------------------------- */
+PLAMO_API int plamo_attn_prefill(int dtype, const void* q_rot, const void* k_rot, const void* v_t,
+                       void* out, int B, int T, int Hq, int Hkv, int d, int window,
+                       long long pos_offset, float softmax_scale, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * plamo_attn_decode -- step 4 for one new token per sequence, read from the cache
+ * [P3 §4.4, §4.5, §5.1]
+ *
+ * Call after plamo_kv_append(T = 1) at the same pos_offset p. The cache then holds
+ * the S = kept + 1 attended tokens p-kept .. p (kept as in plamo_kv_append);
+ * their renumbered positions 0 .. S-1 rotate the pre-RoPE K on the fly with
+ * `rope_table`; q_rot carries position S-1.
+ *
+ * q_rot [B, 1, Hq, d]; k_cache, v_cache [B, Hkv, cap, d] (bf16); out [B, 1, Hq, d].
+ * workspace: device scratch of at least plamo_attn_decode_workspace_bytes(...)
+ * bytes (split-K partial results); contents on entry do not matter.
+ * dtype must be PLAMO_BF16; T must be 1.
+ * ------------------------------------------------------------------------- */
+PLAMO_API size_t plamo_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int window,
+                                         long long pos_offset);
+
+PLAMO_API int plamo_attn_decode(int dtype, const void* q_rot, const void* k_cache,
+                      const void* v_cache, long long cap, void* out, void* workspace,
+                      size_t workspace_bytes, int B, int T, int Hq, int Hkv, int d,
+                      int window, long long pos_offset, const void* rope_table,
+                      size_t rope_table_bytes, float softmax_scale, void* stream);
+
+/* Human-readable text for a status code (static storage). */
+PLAMO_API const char* plamo_status_str(int status);
+
+/* Detail of the last failed check on the calling thread (static thread-local). */
+PLAMO_API const char* plamo_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PLAMO_ATTN_H */

@@ -1,0 +1,191 @@
+"""PLaMo 3 hybrid sliding-window / global GQA attention on MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libplamo_attn.so`` (include/plamo_attn.h).
+Each function takes torch tensors that already live on the GPU, checks their dtype,
+device, contiguity and shapes, reads the sizes off them, and forwards raw device
+pointers plus the current HIP stream to the C entry point of the same name. Every
+step of the computation runs in the library's HIP kernels; there is no CPU path.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import PlamoRope
+
+PLAMO_F32 = 0
+PLAMO_BF16 = 1
+HEAD_DIM = 128
+
+__all__ = [
+    "PlamoError", "RopeParams", "LOCAL_ROPE", "GLOBAL_ROPE",
+    "plamo_rope_table_bytes", "plamo_rope_table_init", "make_rope_table",
+    "plamo_prefill_padded_len", "plamo_kv_append", "plamo_attn_prefill",
+    "plamo_attn_decode_workspace_bytes", "plamo_attn_decode", "library_path",
+]
+
+
+class PlamoError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        lib = _lib.load()
+        self.status = status
+        detail = lib.plamo_last_error().decode()
+        super().__init__(f"{fn}: {lib.plamo_status_str(status).decode()} ({status}): {detail}")
+
+
+@dataclass(frozen=True)
+class RopeParams:
+    """RoPE of one layer type: base theta, YaRN factor (<= 1 = off), L0, beta_fast, beta_slow."""
+    theta: float
+    yarn_factor: float = 0.0
+    orig_ctx: float = 4096.0
+    beta_fast: float = 32.0
+    beta_slow: float = 1.0
+
+    def c_struct(self) -> PlamoRope:
+        return PlamoRope(self.theta, self.yarn_factor, self.orig_ctx, self.beta_fast, self.beta_slow)
+
+
+LOCAL_ROPE = RopeParams(theta=1e4)
+GLOBAL_ROPE = RopeParams(theta=1e6, yarn_factor=256.0)
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _check(status: int, fn: str) -> None:
+    if status != 0:
+        raise PlamoError(status, fn)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor | None, name: str, dtype=None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return PLAMO_BF16
+    if dt == torch.float32:
+        return PLAMO_F32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def plamo_rope_table_bytes(max_pos: int, d: int = HEAD_DIM) -> int:
+    return int(_lib.load().plamo_rope_table_bytes(int(max_pos), int(d)))
+
+
+def plamo_rope_table_init(table: torch.Tensor, max_pos: int, rope: RopeParams, d: int = HEAD_DIM,
+                          stream=None) -> None:
+    p = _dev(table, "table")
+    nbytes = table.numel() * table.element_size()
+    st = _lib.load().plamo_rope_table_init(p, nbytes, int(max_pos), int(d), rope.c_struct(), _stream(stream))
+    _check(st, "plamo_rope_table_init")
+
+
+def make_rope_table(max_pos: int, rope: RopeParams, device="cuda", stream=None) -> torch.Tensor:
+    """Allocate (torch) and fill a rope table covering positions [0, max_pos)."""
+    nbytes = plamo_rope_table_bytes(max_pos)
+    if nbytes == 0:
+        raise ValueError("bad max_pos")
+    table = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
+    plamo_rope_table_init(table, max_pos, rope, stream=stream)
+    return table
+
+
+def plamo_prefill_padded_len(T: int) -> int:
+    return int(_lib.load().plamo_prefill_padded_len(int(T)))
+
+
+def plamo_kv_append(q, k, v, q_out, *, window: int, pos_offset: int, rope_table,
+                    q_norm_w=None, k_norm_w=None, norm_offset: float = 1.0, norm_eps: float = 1e-6,
+                    k_rot_out=None, v_t_out=None, k_cache=None, v_cache=None, stream=None) -> None:
+    """q [B,T,Hq,d], k/v [B,T,Hkv,d]; outputs as documented in plamo_attn.h."""
+    dt = q.dtype
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, T, Hkv, d) or tuple(v.shape) != (B, T, Hkv, d):
+        raise ValueError("k and v must be [B, T, Hkv, d] matching q")
+    if tuple(q_out.shape) != (B, T, Hq, d):
+        raise ValueError("q_out must match q")
+    Tp = plamo_prefill_padded_len(T)
+    if k_rot_out is not None and tuple(k_rot_out.shape) != (B, Hkv, Tp, d):
+        raise ValueError(f"k_rot_out must be [B, Hkv, {Tp}, d]")
+    if v_t_out is not None and tuple(v_t_out.shape) != (B, Hkv, d, Tp):
+        raise ValueError(f"v_t_out must be [B, Hkv, d, {Tp}]")
+    cap = 0
+    if k_cache is not None:
+        cap = k_cache.shape[2]
+        if tuple(k_cache.shape) != (B, Hkv, cap, d) or v_cache is None or tuple(v_cache.shape) != tuple(k_cache.shape):
+            raise ValueError("caches must both be [B, Hkv, cap, d]")
+    st = _lib.load().plamo_kv_append(
+        _dtype_code(dt), _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt),
+        _dev(q_norm_w, "q_norm_w", dt), _dev(k_norm_w, "k_norm_w", dt), float(norm_offset), float(norm_eps),
+        _dev(q_out, "q_out", dt), _dev(k_rot_out, "k_rot_out", dt), _dev(v_t_out, "v_t_out", dt),
+        _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), int(cap), B, T, Hq, Hkv, d,
+        int(window), int(pos_offset), _dev(rope_table, "rope_table", torch.float32),
+        rope_table.numel() * 4, _stream(stream))
+    _check(st, "plamo_kv_append")
+
+
+def plamo_attn_prefill(q_rot, k_rot, v_t, out, *, window: int, pos_offset: int = 0,
+                       softmax_scale: float | None = None, stream=None) -> None:
+    """q_rot [B,T,Hq,d], k_rot [B,Hkv,Tp,d], v_t [B,Hkv,d,Tp] -> out [B,T,Hq,d]."""
+    dt = q_rot.dtype
+    B, T, Hq, d = q_rot.shape
+    Hkv = k_rot.shape[1]
+    Tp = plamo_prefill_padded_len(T)
+    if tuple(k_rot.shape) != (B, Hkv, Tp, d) or tuple(v_t.shape) != (B, Hkv, d, Tp):
+        raise ValueError(f"k_rot must be [B, Hkv, {Tp}, d] and v_t [B, Hkv, d, {Tp}]")
+    if tuple(out.shape) != (B, T, Hq, d):
+        raise ValueError("out must match q_rot")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    st = _lib.load().plamo_attn_prefill(
+        _dtype_code(dt), _dev(q_rot, "q_rot", dt), _dev(k_rot, "k_rot", dt), _dev(v_t, "v_t", dt),
+        _dev(out, "out", dt), B, T, Hq, Hkv, d, int(window), int(pos_offset), scale, _stream(stream))
+    _check(st, "plamo_attn_prefill")
+
+
+def plamo_attn_decode_workspace_bytes(B: int, Hq: int, Hkv: int, window: int, pos_offset: int,
+                                      d: int = HEAD_DIM) -> int:
+    return int(_lib.load().plamo_attn_decode_workspace_bytes(B, Hq, Hkv, d, int(window), int(pos_offset)))
+
+
+def plamo_attn_decode(q_rot, k_cache, v_cache, out, workspace, *, window: int, pos_offset: int,
+                      rope_table, softmax_scale: float | None = None, stream=None) -> None:
+    """q_rot [B,1,Hq,d]; caches [B,Hkv,cap,d] (bf16) -> out [B,1,Hq,d]."""
+    dt = q_rot.dtype
+    B, T, Hq, d = q_rot.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, cap, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches must both be [B, Hkv, cap, d]")
+    if tuple(out.shape) != (B, T, Hq, d):
+        raise ValueError("out must match q_rot")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.load().plamo_attn_decode(
+        _dtype_code(dt), _dev(q_rot, "q_rot", dt), _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        int(cap), _dev(out, "out", dt), _dev(workspace, "workspace"), ws_bytes, B, T, Hq, Hkv, d,
+        int(window), int(pos_offset), _dev(rope_table, "rope_table", torch.float32), rope_table.numel() * 4,
+        scale, _stream(stream))
+    _check(st, "plamo_attn_decode")

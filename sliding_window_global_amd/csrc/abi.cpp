@@ -1,0 +1,231 @@
+// C-ABI entry points: argument validation, position bookkeeping and kernel dispatch.
+// The declarations and their contracts live in include/plamo_attn.h.
+#include "plamo_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* what) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s", what);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return PLAMO_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kHeadDim = 128;
+constexpr long long kFine = 64;
+constexpr long long kPad = 128;
+constexpr size_t kRowBytes = (kHeadDim / 2) * 2 * sizeof(float);  // one table row
+
+// Positions [0, covered) that a table of `bytes` bytes can rotate.
+long long table_positions(size_t bytes) {
+  if (bytes % kRowBytes) return -1;
+  const long long rows = static_cast<long long>(bytes / kRowBytes);
+  if (rows <= kFine) return 0;
+  return (rows - kFine) * kFine;
+}
+
+// Checks shared by every attention entry point; returns PLAMO_OK or an error status.
+int check_heads(int B, int T, int Hq, int Hkv, int d, int window, long long pos_offset) {
+  if (B < 0 || T < 0) return fail(PLAMO_ERR_INVALID_ARG, "B and T must be >= 0");
+  if (d != kHeadDim) return fail(d > 0 ? PLAMO_ERR_UNSUPPORTED : PLAMO_ERR_INVALID_ARG, "head dim must be 128");
+  if (Hq < 1 || Hkv < 1) return fail(PLAMO_ERR_INVALID_ARG, "Hq and Hkv must be >= 1");
+  if (Hq % Hkv) return fail(PLAMO_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+  if (Hq / Hkv > 16) return fail(PLAMO_ERR_UNSUPPORTED, "Hq/Hkv must be <= 16");
+  if (window < 0) return fail(PLAMO_ERR_INVALID_ARG, "window must be >= 0");
+  if (pos_offset < 0) return fail(PLAMO_ERR_INVALID_ARG, "pos_offset must be >= 0");
+  if (B > 65535 || Hkv > 65535) return fail(PLAMO_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
+  if (T > (1LL << 30)) return fail(PLAMO_ERR_UNSUPPORTED, "T must be <= 2^30");
+  if (pos_offset > (1LL << 40)) return fail(PLAMO_ERR_UNSUPPORTED, "pos_offset must be <= 2^40");
+  return PLAMO_OK;
+}
+
+long long kept_tokens(int window, long long pos_offset) {
+  if (window == 0) return pos_offset;
+  return pos_offset < window - 1 ? pos_offset : static_cast<long long>(window - 1);
+}
+
+int launched(hipError_t e) {
+  if (e != hipSuccess) return fail(PLAMO_ERR_HIP, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* plamo_status_str(int status) {
+  switch (status) {
+    case PLAMO_OK: return "ok";
+    case PLAMO_ERR_INVALID_ARG: return "invalid argument";
+    case PLAMO_ERR_UNSUPPORTED: return "unsupported";
+    case PLAMO_ERR_WORKSPACE: return "rope table or workspace too small";
+    case PLAMO_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* plamo_last_error(void) { return g_last_error; }
+
+long long plamo_prefill_padded_len(long long T) {
+  if (T <= 0) return 0;
+  return (T + kPad - 1) / kPad * kPad;
+}
+
+size_t plamo_rope_table_bytes(long long max_pos, int d) {
+  if (max_pos < 1 || d != kHeadDim || max_pos > (1LL << 40)) return 0;
+  const long long coarse = (max_pos + kFine - 1) / kFine;
+  return static_cast<size_t>(kFine + coarse) * kRowBytes;
+}
+
+int plamo_rope_table_init(void* table, size_t table_bytes, long long max_pos, int d,
+                          const plamo_rope* rope, void* stream) {
+  if (d != kHeadDim) return fail(d > 0 ? PLAMO_ERR_UNSUPPORTED : PLAMO_ERR_INVALID_ARG, "head dim must be 128");
+  if (max_pos < 1 || max_pos > (1LL << 40)) return fail(PLAMO_ERR_INVALID_ARG, "max_pos must be in [1, 2^40]");
+  if (!table || !rope) return fail(PLAMO_ERR_INVALID_ARG, "table and rope must be non-NULL");
+  if (!aligned16(table)) return fail(PLAMO_ERR_INVALID_ARG, "table must be 16-byte aligned");
+  const size_t need = plamo_rope_table_bytes(max_pos, d);
+  if (table_bytes < need) return fail(PLAMO_ERR_WORKSPACE, "table_bytes < plamo_rope_table_bytes(max_pos, d)");
+  if (!(rope->theta > 1.0) || !std::isfinite(rope->theta)) return fail(PLAMO_ERR_INVALID_ARG, "theta must be > 1");
+  double j_low = 0, j_high = 1, amp = 1.0, s = rope->yarn_factor;
+  if (s > 1.0) {
+    if (!std::isfinite(s) || !(rope->orig_ctx > 0) || !(rope->beta_slow > 0) ||
+        !(rope->beta_fast > rope->beta_slow))
+      return fail(PLAMO_ERR_INVALID_ARG, "YaRN needs orig_ctx > 0 and beta_fast > beta_slow > 0");
+    // 「PLaMo 3アーキテクチャ徹底解析」 §6.3: unrounded ramp bounds, leading factor d/2
+    const double half = d / 2.0, lt = std::log(rope->theta);
+    j_low = half * std::log(rope->orig_ctx / (2.0 * M_PI * rope->beta_fast)) / lt;
+    j_high = half * std::log(rope->orig_ctx / (2.0 * M_PI * rope->beta_slow)) / lt;
+    amp = 1.0 + 0.1 * std::log(s);
+  } else {
+    s = 0.0;
+  }
+  const long long coarse = (max_pos + kFine - 1) / kFine;
+  return launched(plamo::launch_rope_table(static_cast<float2*>(table), coarse, d, rope->theta, s,
+                                           j_low, j_high, amp, static_cast<hipStream_t>(stream)));
+}
+
+int plamo_kv_append(int dtype, const void* q, const void* k, const void* v, const void* q_norm_w,
+                    const void* k_norm_w, float norm_offset, float norm_eps, void* q_out,
+                    void* k_rot_out, void* v_t_out, void* k_cache, void* v_cache, long long cap,
+                    int B, int T, int Hq, int Hkv, int d, int window, long long pos_offset,
+                    const void* rope_table, size_t rope_table_bytes, void* stream) {
+  if (dtype != PLAMO_F32 && dtype != PLAMO_BF16) return fail(PLAMO_ERR_INVALID_ARG, "unknown dtype");
+  if (int st = check_heads(B, T, Hq, Hkv, d, window, pos_offset)) return st;
+  if (B == 0 || T == 0) return ok();
+  if (!q || !k || !v || !q_out) return fail(PLAMO_ERR_INVALID_ARG, "q, k, v and q_out must be non-NULL");
+  if ((q_norm_w == nullptr) != (k_norm_w == nullptr))
+    return fail(PLAMO_ERR_INVALID_ARG, "give both norm weights or neither");
+  if ((k_cache == nullptr) != (v_cache == nullptr))
+    return fail(PLAMO_ERR_INVALID_ARG, "give both caches or neither");
+  const void* ptrs[] = {q, k, v, q_norm_w, k_norm_w, q_out, k_rot_out, v_t_out, k_cache, v_cache, rope_table};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if (!(norm_eps >= 0.f) || !std::isfinite(norm_offset)) return fail(PLAMO_ERR_INVALID_ARG, "bad norm offset/eps");
+  if (k_cache) {
+    if (window > 0 && cap < window) return fail(PLAMO_ERR_INVALID_ARG, "local cache needs cap >= window");
+    if (window == 0 && cap < pos_offset + T) return fail(PLAMO_ERR_INVALID_ARG, "global cache needs cap >= pos_offset + T");
+  }
+  const long long kept = kept_tokens(window, pos_offset);
+  if (!rope_table) return fail(PLAMO_ERR_INVALID_ARG, "rope_table must be non-NULL");
+  const long long covered = table_positions(rope_table_bytes);
+  if (covered < 0) return fail(PLAMO_ERR_INVALID_ARG, "rope_table_bytes is not a whole number of rows");
+  if (covered < kept + T) return fail(PLAMO_ERR_WORKSPACE, "rope table does not cover positions < kept + T");
+
+  plamo::AppendArgs a;
+  a.q = q; a.k = k; a.v = v; a.wq = q_norm_w; a.wk = k_norm_w;
+  a.norm_offset = norm_offset; a.eps = norm_eps;
+  a.q_out = q_out; a.k_rot_out = k_rot_out; a.v_t_out = v_t_out;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.cap = cap;
+  a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.window = window;
+  a.Tp = plamo_prefill_padded_len(T);
+  a.pos_offset = pos_offset; a.kept = kept;
+  a.rope = static_cast<const float2*>(rope_table);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launched(dtype == PLAMO_BF16 ? plamo::launch_kv_append_bf16(a, s) : plamo::launch_kv_append_f32(a, s));
+}
+
+int plamo_attn_prefill(int dtype, const void* q_rot, const void* k_rot, const void* v_t, void* out,
+                       int B, int T, int Hq, int Hkv, int d, int window, long long pos_offset,
+                       float softmax_scale, void* stream) {
+  if (dtype != PLAMO_F32 && dtype != PLAMO_BF16) return fail(PLAMO_ERR_INVALID_ARG, "unknown dtype");
+  if (int st = check_heads(B, T, Hq, Hkv, d, window, pos_offset)) return st;
+  if (pos_offset != 0) return fail(PLAMO_ERR_UNSUPPORTED, "prefill on a populated cache (pos_offset > 0)");
+  if (B == 0 || T == 0) return ok();
+  if (!q_rot || !k_rot || !v_t || !out) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be non-NULL");
+  const void* ptrs[] = {q_rot, k_rot, v_t, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return fail(PLAMO_ERR_INVALID_ARG, "softmax_scale must be > 0");
+  const long long blocks = (static_cast<long long>(T) + 127) / 128 * Hq * static_cast<long long>(B);
+  if (blocks > 0x7fffffffLL) return fail(PLAMO_ERR_UNSUPPORTED, "grid too large");
+
+  plamo::PrefillArgs a;
+  a.q_rot = q_rot; a.k_rot = k_rot; a.v_t = v_t; a.out = out;
+  a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.window = window;
+  a.Tp = plamo_prefill_padded_len(T);
+  a.scale = softmax_scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launched(dtype == PLAMO_BF16 ? plamo::launch_prefill_bf16(a, s) : plamo::launch_prefill_f32(a, s));
+}
+
+size_t plamo_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int window, long long pos_offset) {
+  if (check_heads(B, 1, Hq, Hkv, d, window, pos_offset) != PLAMO_OK) return 0;
+  if (B == 0) return 0;
+  const long long S = kept_tokens(window, pos_offset) + 1;
+  return plamo::decode_workspace_bytes(B, Hq, plamo::plan_decode(B, Hkv, S));
+}
+
+int plamo_attn_decode(int dtype, const void* q_rot, const void* k_cache, const void* v_cache,
+                      long long cap, void* out, void* workspace, size_t workspace_bytes, int B, int T,
+                      int Hq, int Hkv, int d, int window, long long pos_offset,
+                      const void* rope_table, size_t rope_table_bytes, float softmax_scale,
+                      void* stream) {
+  if (dtype != PLAMO_BF16) return fail(dtype == PLAMO_F32 ? PLAMO_ERR_UNSUPPORTED : PLAMO_ERR_INVALID_ARG,
+                                       "decode reads a bf16 cache");
+  if (T != 1) return fail(T < 0 ? PLAMO_ERR_INVALID_ARG : PLAMO_ERR_UNSUPPORTED, "decode takes T = 1");
+  if (int st = check_heads(B, T, Hq, Hkv, d, window, pos_offset)) return st;
+  if (B == 0) return ok();
+  if (!q_rot || !k_cache || !v_cache || !out || !rope_table)
+    return fail(PLAMO_ERR_INVALID_ARG, "q_rot, caches, out and rope_table must be non-NULL");
+  const void* ptrs[] = {q_rot, k_cache, v_cache, out, workspace, rope_table};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if (window > 0 && cap < window) return fail(PLAMO_ERR_INVALID_ARG, "local cache needs cap >= window");
+  if (window == 0 && cap < pos_offset + 1) return fail(PLAMO_ERR_INVALID_ARG, "global cache needs cap >= pos_offset + 1");
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return fail(PLAMO_ERR_INVALID_ARG, "softmax_scale must be > 0");
+  const long long kept = kept_tokens(window, pos_offset);
+  const long long S = kept + 1;
+  const long long covered = table_positions(rope_table_bytes);
+  if (covered < 0) return fail(PLAMO_ERR_INVALID_ARG, "rope_table_bytes is not a whole number of rows");
+  if (covered < S) return fail(PLAMO_ERR_WORKSPACE, "rope table does not cover positions < kept + 1");
+  const plamo::DecodePlan plan = plamo::plan_decode(B, Hkv, S);
+  const size_t need = plamo::decode_workspace_bytes(B, Hq, plan);
+  if (!workspace || workspace_bytes < need) return fail(PLAMO_ERR_WORKSPACE, "workspace too small");
+  if (static_cast<long long>(B) * Hq > 0x7fffffffLL) return fail(PLAMO_ERR_UNSUPPORTED, "grid too large");
+
+  plamo::DecodeArgs a;
+  a.q_rot = q_rot; a.k_cache = k_cache; a.v_cache = v_cache; a.cap = cap; a.out = out;
+  a.ws = static_cast<float*>(workspace);
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.window = window;
+  a.S = S; a.base = pos_offset - kept; a.plan = plan;
+  a.rope = static_cast<const float2*>(rope_table);
+  a.scale = softmax_scale;
+  return launched(plamo::launch_decode_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

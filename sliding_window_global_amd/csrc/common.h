@@ -1,0 +1,60 @@
+// Shared device helpers for the gfx950 attention kernels: storage types, bf16
+// conversion, the rope-table lookup and small wave-level reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace plamo {
+
+constexpr int kHeadDim = 128;      // PLaMo 3 head_dim (「PLaMo 3アーキテクチャ徹底解析」 §2.1)
+constexpr int kHalf = kHeadDim / 2;
+constexpr int kRopeFine = 64;      // positions per coarse rope-table row
+constexpr int kPadT = 128;         // prefill operand padding of the token axis
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits in memory
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ bf16_t f32_to_bf16(float x) {
+  __bf16 b = static_cast<__bf16>(x);
+  return __builtin_bit_cast(bf16_t, b);
+}
+
+// Pack two floats into one dword of two bf16 (lo in the low half).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Rotation factor amp * exp(i p w_j) from the two-level table: coarse row p >> 6 times
+// fine row p & 63 (complex product, fp32). Layout: fine [64][d/2] float2 first, then
+// coarse [n_coarse][d/2] float2.
+__device__ __forceinline__ float2 rope_factor(const float2* __restrict__ table, long long p, int j) {
+  const float2 f = table[(p & (kRopeFine - 1)) * kHalf + j];
+  const float2 c = table[(kRopeFine + (p >> 6)) * kHalf + j];
+  return make_float2(c.x * f.x - c.y * f.y, c.x * f.y + c.y * f.x);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace plamo

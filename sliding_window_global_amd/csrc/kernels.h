@@ -1,0 +1,71 @@
+// Host-side launchers of the gfx950 kernels. Arguments have been validated by the
+// C-ABI layer (abi.cpp) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace plamo {
+
+hipError_t launch_rope_table(float2* table, long long n_coarse, int d, double theta,
+                             double yarn_factor, double j_low, double j_high,
+                             double amplitude, hipStream_t stream);
+
+struct AppendArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* wq;  // NULL = no norm
+  const void* wk;
+  float norm_offset;
+  float eps;
+  void* q_out;
+  void* k_rot_out;  // may be NULL
+  void* v_t_out;    // may be NULL
+  void* k_cache;    // may be NULL (then v_cache is NULL too)
+  void* v_cache;
+  long long cap;
+  int B, T, Hq, Hkv, window;
+  long long Tp;          // padded token count of the prefill operands
+  long long pos_offset;  // absolute position of the first new token
+  long long kept;        // cached tokens returned before the new ones
+  const float2* rope;
+};
+hipError_t launch_kv_append_bf16(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_kv_append_f32(const AppendArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  const void* q_rot;  // [B, T, Hq, d]
+  const void* k_rot;  // [B, Hkv, Tp, d]
+  const void* v_t;    // [B, Hkv, d, Tp]
+  void* out;          // [B, T, Hq, d]
+  int B, T, Hq, Hkv, window;
+  long long Tp;
+  float scale;
+};
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+
+struct DecodePlan {
+  int n_split;         // key ranges per (sequence, KV head)
+  long long chunk;     // keys per range, a multiple of the key tile
+};
+DecodePlan plan_decode(int B, int Hkv, long long S);
+size_t decode_workspace_bytes(int B, int Hq, const DecodePlan& plan);
+
+struct DecodeArgs {
+  const void* q_rot;    // [B, 1, Hq, d]
+  const void* k_cache;  // [B, Hkv, cap, d]
+  const void* v_cache;
+  long long cap;
+  void* out;            // [B, 1, Hq, d]
+  float* ws;            // [B, Hq, n_split, d + 2]
+  int B, Hq, Hkv, window;
+  long long S;          // attended keys (renumbered 0 .. S-1)
+  long long base;       // absolute position of renumbered key 0
+  DecodePlan plan;
+  const float2* rope;
+  float scale;
+};
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace plamo

@@ -1,0 +1,69 @@
+"""One attention layer step on the GPU, composed from the C-ABI calls.
+
+Allocation of outputs and scratch uses torch (device memory only); every step of the
+computation is a kernel of the library: plamo_kv_append (norm, cache update, RoPE,
+prefill operands) followed by plamo_attn_prefill or plamo_attn_decode.
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import (plamo_attn_decode, plamo_attn_decode_workspace_bytes, plamo_attn_prefill,
+               plamo_kv_append, plamo_prefill_padded_len)
+
+
+class PrefillBuffers:
+    """Operands of one prefill: normalised/rotated Q, rotated K and transposed V."""
+
+    def __init__(self, B, T, Hq, Hkv, d, dtype, device="cuda"):
+        Tp = plamo_prefill_padded_len(T)
+        self.q_rot = torch.empty((B, T, Hq, d), dtype=dtype, device=device)
+        self.k_rot = torch.empty((B, Hkv, Tp, d), dtype=dtype, device=device)
+        self.v_t = torch.empty((B, Hkv, d, Tp), dtype=dtype, device=device)
+        self.out = torch.empty((B, T, Hq, d), dtype=dtype, device=device)
+
+
+def prefill(q, k, v, *, window, rope_table, q_norm_w=None, k_norm_w=None, norm_offset=1.0,
+            norm_eps=1e-6, k_cache=None, v_cache=None, bufs: PrefillBuffers | None = None,
+            softmax_scale=None, stream=None) -> PrefillBuffers:
+    """Prefill from an empty cache: q [B,T,Hq,d], k/v [B,T,Hkv,d] on the GPU."""
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if bufs is None:
+        bufs = PrefillBuffers(B, T, Hq, Hkv, d, q.dtype, q.device)
+    plamo_kv_append(q, k, v, bufs.q_rot, window=window, pos_offset=0, rope_table=rope_table,
+                    q_norm_w=q_norm_w, k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps,
+                    k_rot_out=bufs.k_rot, v_t_out=bufs.v_t, k_cache=k_cache, v_cache=v_cache,
+                    stream=stream)
+    plamo_attn_prefill(bufs.q_rot, bufs.k_rot, bufs.v_t, bufs.out, window=window, pos_offset=0,
+                       softmax_scale=softmax_scale, stream=stream)
+    return bufs
+
+
+class DecodeBuffers:
+    def __init__(self, B, Hq, Hkv, d, window, pos_offset, dtype=torch.bfloat16, device="cuda"):
+        self.q_rot = torch.empty((B, 1, Hq, d), dtype=dtype, device=device)
+        self.out = torch.empty((B, 1, Hq, d), dtype=dtype, device=device)
+        nbytes = plamo_attn_decode_workspace_bytes(B, Hq, Hkv, window, pos_offset, d)
+        self.workspace = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device=device)
+
+
+def decode(q, k, v, k_cache, v_cache, *, window, pos_offset, rope_table, q_norm_w=None,
+           k_norm_w=None, norm_offset=1.0, norm_eps=1e-6, bufs: DecodeBuffers | None = None,
+           softmax_scale=None, stream=None) -> DecodeBuffers:
+    """One decode step at absolute position pos_offset: q [B,1,Hq,d], k/v [B,1,Hkv,d]."""
+    B, _, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if bufs is None:
+        bufs = DecodeBuffers(B, Hq, Hkv, d, window, pos_offset, q.dtype, q.device)
+    plamo_kv_append(q, k, v, bufs.q_rot, window=window, pos_offset=pos_offset, rope_table=rope_table,
+                    q_norm_w=q_norm_w, k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps,
+                    k_cache=k_cache, v_cache=v_cache, stream=stream)
+    plamo_attn_decode(bufs.q_rot, k_cache, v_cache, bufs.out, bufs.workspace, window=window,
+                      pos_offset=pos_offset, rope_table=rope_table,
+                      softmax_scale=1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale,
+                      stream=stream)
+    return bufs

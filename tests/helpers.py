@@ -1,0 +1,84 @@
+"""Shared test helpers: oracle evaluation of the workloads and the parity check.
+
+The oracle side (fp64 NumPy) and the GPU side receive the same synthetic bytes; no
+expected value comes from the GPU path."""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from oracle import LayerKVCache, attention_layer_step
+
+# Parity bar: every element satisfies |gpu - ref| <= atol + rtol * |ref|.
+TOL_BF16 = (2e-2, 2e-2)
+TOL_F32 = (1e-4, 1e-4)
+
+
+def parity(gpu, ref, tol):
+    """Return (ok, max_abs, max_rel, worst_index) for the elementwise bar."""
+    atol, rtol = tol
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    err = np.abs(gpu - ref)
+    bound = atol + rtol * np.abs(ref)
+    ok = bool(np.all(err <= bound)) and bool(np.all(np.isfinite(gpu)))
+    max_abs = float(err.max()) if err.size else 0.0
+    max_rel = float((err / np.maximum(np.abs(ref), atol)).max()) if err.size else 0.0
+    worst = np.unravel_index(int(np.argmax(err - bound)), err.shape) if err.size else None
+    return ok, max_abs, max_rel, worst
+
+
+def assert_parity(gpu, ref, tol, what=""):
+    ok, ma, mr, worst = parity(gpu, ref, tol)
+    assert ok, f"{what}: max_abs={ma:.3e} max_rel={mr:.3e} worst={worst}"
+    return ma, mr
+
+
+def oracle_prefill(q, k, v, *, window, rope, wq=None, wk=None, norm_offset=1.0, eps=1e-6,
+                   scale=None, rows=None):
+    """Oracle of a prefill from an empty cache for every sequence: q [B,T,Hq,d] etc.
+    Returns [B, T or len(rows), Hq, d] float64."""
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    outs = []
+    for b in range(B):
+        cache = LayerKVCache(Hkv, d, window)
+        outs.append(attention_layer_step(
+            q[b], k[b], v[b], cache, theta=rope.theta, yarn_factor=rope.yarn_factor,
+            orig_ctx=rope.orig_ctx, beta_fast=rope.beta_fast, beta_slow=rope.beta_slow,
+            q_norm_w=wq, k_norm_w=wk, norm_offset=norm_offset, eps=eps,
+            scale=scale if scale is not None else 1.0 / math.sqrt(d), rows=rows))
+    return np.stack(outs)
+
+
+def oracle_decode_one(q, k, v, prior_k, prior_v, pos_offset, *, window, rope, wq, wk,
+                      norm_offset=1.0, eps=1e-6):
+    """Oracle of one decode step of one sequence: q [1,Hq,d], k/v [1,Hkv,d]; prior_k/v are
+    the kept tokens (normalised pre-RoPE K, raw V) in token order. Returns [1, Hq, d]."""
+    cache = LayerKVCache.with_prior(prior_k, prior_v, pos_offset, window)
+    return attention_layer_step(
+        q, k, v, cache, theta=rope.theta, yarn_factor=rope.yarn_factor, orig_ctx=rope.orig_ctx,
+        beta_fast=rope.beta_fast, beta_slow=rope.beta_slow, q_norm_w=wq, k_norm_w=wk,
+        norm_offset=norm_offset, eps=eps, scale=1.0 / math.sqrt(q.shape[-1]))
+
+
+def kept_slots(pos_offset, window):
+    """Cache slots of the tokens a layer keeps before appending token pos_offset, in
+    token order (ring slot n mod W on local layers)."""
+    kept = pos_offset if window == 0 else min(pos_offset, window - 1)
+    toks = np.arange(pos_offset - kept, pos_offset)
+    return toks if window == 0 else toks % window
+
+
+def window_mean_closed_form(v, window):
+    """Uniform attention over the visible keys: O[t] = mean of V over the window
+    ending at t (prefix sums in fp64). v [T, Hkv, d] -> [T, Hkv, d]."""
+    v = np.asarray(v, dtype=np.float64)
+    T = v.shape[0]
+    csum = np.concatenate([np.zeros((1,) + v.shape[1:]), np.cumsum(v, axis=0)])
+    t = np.arange(T)
+    lo = np.zeros(T, dtype=np.int64) if window == 0 else np.maximum(0, t - window + 1)
+    return (csum[t + 1] - csum[lo]) / (t + 1 - lo)[:, None, None]

@@ -1,0 +1,164 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+entry point the header declares, and rejects bad arguments with the documented status
+before launching anything. Only calls that fail validation are made here."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sliding_window_global_amd import _lib
+from sliding_window_global_amd.build import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "plamo_attn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+BF16, F32 = 1, 0
+FAKE = ctypes.c_void_p(0x7F0000000000)      # never dereferenced: every call below fails validation
+MISALIGNED = ctypes.c_void_p(0x7F0000000008)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        pytest.fail(f"{LIB_PATH} not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def declared_functions():
+    src = open(HEADER, encoding="utf-8").read()
+    return re.findall(r"PLAMO_API[^;(]*?\b(plamo_\w+)\s*\(", src)
+
+
+def test_header_declares_the_abi():
+    names = set(declared_functions())
+    assert {"plamo_kv_append", "plamo_attn_prefill", "plamo_attn_decode"} <= names
+    assert names == set(_lib.SIGNATURES), "binding signatures must mirror the header"
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for st in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR):
+        assert lib.plamo_status_str(st)
+    assert lib.plamo_status_str(12345) == b"unknown status"
+
+
+def test_pure_host_helpers(lib):
+    assert lib.plamo_prefill_padded_len(0) == 0
+    assert lib.plamo_prefill_padded_len(1) == 128
+    assert lib.plamo_prefill_padded_len(128) == 128
+    assert lib.plamo_prefill_padded_len(8193) == 8320
+    # rope table: 64 fine rows + ceil(max_pos / 64) coarse rows of 64 (cos, sin) fp32 pairs
+    assert lib.plamo_rope_table_bytes(1, 128) == (64 + 1) * 512
+    assert lib.plamo_rope_table_bytes(131200, 128) == (64 + 2050) * 512
+    assert lib.plamo_rope_table_bytes(0, 128) == 0
+    assert lib.plamo_rope_table_bytes(100, 64) == 0
+
+
+def test_decode_workspace_sizes(lib):
+    # a workspace holds (acc[128], m, l) fp32 per (sequence, query head, split)
+    n = lib.plamo_attn_decode_workspace_bytes(64, 64, 8, 128, 0, 32767)
+    assert n > 0 and n % (130 * 4 * 64 * 64) == 0
+    assert lib.plamo_attn_decode_workspace_bytes(64, 64, 8, 96, 0, 10) == 0  # d != 128
+    assert lib.plamo_attn_decode_workspace_bytes(0, 64, 8, 128, 0, 10) == 0
+
+
+def _append(lib, **over):
+    a = dict(dtype=BF16, q=FAKE, k=FAKE, v=FAKE, wq=None, wk=None, c=1.0, eps=1e-6, q_out=FAKE,
+             k_rot=None, v_t=None, kc=None, vc=None, cap=0, B=1, T=4, Hq=8, Hkv=2, d=128, window=16,
+             pos=0, table=FAKE, table_bytes=(64 + 1) * 512, stream=None)
+    a.update(over)
+    return lib.plamo_kv_append(a["dtype"], a["q"], a["k"], a["v"], a["wq"], a["wk"], a["c"], a["eps"],
+                               a["q_out"], a["k_rot"], a["v_t"], a["kc"], a["vc"], a["cap"], a["B"], a["T"],
+                               a["Hq"], a["Hkv"], a["d"], a["window"], a["pos"], a["table"],
+                               a["table_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=7), INVALID),
+    (dict(d=96), UNSUPPORTED),
+    (dict(d=0), INVALID),
+    (dict(Hq=6, Hkv=4), INVALID),
+    (dict(Hq=34, Hkv=2), UNSUPPORTED),
+    (dict(window=-1), INVALID),
+    (dict(pos=-5), INVALID),
+    (dict(B=-1), INVALID),
+    (dict(q=None), INVALID),
+    (dict(q_out=None), INVALID),
+    (dict(wq=FAKE), INVALID),                       # one norm weight without the other
+    (dict(kc=FAKE), INVALID),                       # one cache without the other
+    (dict(kc=FAKE, vc=FAKE, cap=8), INVALID),       # local ring smaller than the window
+    (dict(kc=FAKE, vc=FAKE, cap=3, window=0), INVALID),  # global cap < pos + T
+    (dict(q=MISALIGNED), INVALID),
+    (dict(table=None), INVALID),
+    (dict(table_bytes=100), INVALID),               # not whole rows
+    (dict(pos=64, window=0, table_bytes=(64 + 1) * 512), WORKSPACE),  # table too short
+    (dict(eps=-1.0), INVALID),
+])
+def test_kv_append_validation(lib, over, status):
+    assert _append(lib, **over) == status
+    assert lib.plamo_last_error()
+
+
+def test_kv_append_empty_is_ok(lib):
+    assert _append(lib, T=0, q=None, k=None, v=None, q_out=None) == OK
+    assert _append(lib, B=0, q=None, k=None, v=None, q_out=None) == OK
+
+
+def _prefill(lib, **over):
+    a = dict(dtype=BF16, q=FAKE, k=FAKE, v=FAKE, out=FAKE, B=1, T=100, Hq=8, Hkv=2, d=128, window=0,
+             pos=0, scale=0.0884, stream=None)
+    a.update(over)
+    return lib.plamo_attn_prefill(a["dtype"], a["q"], a["k"], a["v"], a["out"], a["B"], a["T"], a["Hq"],
+                                  a["Hkv"], a["d"], a["window"], a["pos"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=3), INVALID), (dict(d=64), UNSUPPORTED), (dict(Hq=9, Hkv=2), INVALID),
+    (dict(pos=10), UNSUPPORTED), (dict(out=None), INVALID), (dict(k=MISALIGNED), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID), (dict(T=-3), INVALID),
+])
+def test_prefill_validation(lib, over, status):
+    assert _prefill(lib, **over) == status
+
+
+def _decode(lib, **over):
+    a = dict(dtype=BF16, q=FAKE, kc=FAKE, vc=FAKE, cap=2048, out=FAKE, ws=FAKE, ws_bytes=1 << 30, B=4, T=1,
+             Hq=64, Hkv=8, d=128, window=2048, pos=5000, table=FAKE, table_bytes=(64 + 32) * 512,
+             scale=0.0884, stream=None)
+    a.update(over)
+    return lib.plamo_attn_decode(a["dtype"], a["q"], a["kc"], a["vc"], a["cap"], a["out"], a["ws"],
+                                 a["ws_bytes"], a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], a["window"],
+                                 a["pos"], a["table"], a["table_bytes"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=F32), UNSUPPORTED), (dict(dtype=9), INVALID), (dict(T=2), UNSUPPORTED),
+    (dict(T=-1), INVALID), (dict(Hq=64, Hkv=2), UNSUPPORTED), (dict(cap=100), INVALID),
+    (dict(window=0, cap=4000), INVALID), (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
+    (dict(table_bytes=(64 + 31) * 512), WORKSPACE), (dict(kc=None), INVALID),
+    (dict(out=MISALIGNED), INVALID), (dict(scale=-1.0), INVALID),
+])
+def test_decode_validation(lib, over, status):
+    assert _decode(lib, **over) == status
+
+
+def test_rope_init_validation(lib):
+    r = _lib.PlamoRope(1e6, 256.0, 4096.0, 32.0, 1.0)
+    bad_beta = _lib.PlamoRope(1e6, 256.0, 4096.0, 1.0, 32.0)
+    bad_theta = _lib.PlamoRope(0.5, 0.0, 4096.0, 32.0, 1.0)
+    need = lib.plamo_rope_table_bytes(1000, 128)
+    assert lib.plamo_rope_table_init(None, need, 1000, 128, ctypes.byref(r), None) == INVALID
+    assert lib.plamo_rope_table_init(FAKE, need - 512, 1000, 128, ctypes.byref(r), None) == WORKSPACE
+    assert lib.plamo_rope_table_init(FAKE, need, 1000, 64, ctypes.byref(r), None) == UNSUPPORTED
+    assert lib.plamo_rope_table_init(FAKE, need, 1000, 128, ctypes.byref(bad_beta), None) == INVALID
+    assert lib.plamo_rope_table_init(FAKE, need, 1000, 128, ctypes.byref(bad_theta), None) == INVALID
+    assert lib.plamo_rope_table_init(FAKE, need, 0, 128, ctypes.byref(r), None) == INVALID

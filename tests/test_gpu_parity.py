@@ -1,0 +1,335 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar (written here, applied elementwise): |gpu - oracle| <= atol + rtol*|oracle| with
+atol = rtol = 2e-2 for bf16 and 1e-4 for fp32 (helpers.TOL_*). Inputs are the seeded
+synthetic workloads; full-size workloads are checked on sampled rows the oracle
+computes one by one, and everywhere through size-independent closed forms."""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import (TOL_BF16, TOL_F32, assert_parity, kept_slots, oracle_decode_one,
+                     oracle_prefill, window_mean_closed_form)
+from oracle import apply_rope, offset_rms_norm, rope_frequencies
+from synthetic import Draw
+from synthetic.workloads import (BATCHED_DECODE, GLOBAL_PREFILL, LOCAL_PREFILL, PERIOD_DECODE,
+                                 TINY_SWA_FP32, Rope, device_normal_bf16)
+
+pytestmark = pytest.mark.gpu
+
+swg = pytest.importorskip("sliding_window_global_amd")
+from sliding_window_global_amd import layer  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    swg._lib.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(x, bf16=True):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return (t.to(torch.bfloat16) if bf16 else t).cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+_TABLES = {}
+
+
+def rope_table(rope: Rope, max_pos: int):
+    key = (rope, max_pos)
+    if key not in _TABLES:
+        _TABLES[key] = swg.make_rope_table(max_pos, swg.RopeParams(rope.theta, rope.yarn_factor,
+                                                                    rope.orig_ctx, rope.beta_fast,
+                                                                    rope.beta_slow))
+    return _TABLES[key]
+
+
+# ----------------------------------------------------------------------------
+# rope table and the fused append
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rope", [Rope(1e4), Rope(1e6, 64.0), Rope(1e6, 256.0)], ids=["local", "yarn64", "yarn256"])
+def test_rope_table_factors(rope):
+    """Coarse x fine product equals amp * exp(i p w_j) from the oracle's frequencies."""
+    max_pos = 131200
+    tab = host(rope_table(rope, max_pos)).reshape(-1, 64, 2)
+    omega, amp = rope_frequencies(128, rope.theta, rope.yarn_factor)
+    pos = np.array([0, 1, 63, 64, 65, 2047, 2048, 4095, 32767, 65536 + 17, 131071, 131199])
+    f = tab[pos & 63]
+    c = tab[64 + (pos >> 6)]
+    zr = c[..., 0] * f[..., 0] - c[..., 1] * f[..., 1]
+    zi = c[..., 0] * f[..., 1] + c[..., 1] * f[..., 0]
+    ang = pos[:, None] * omega[None, :]
+    assert np.max(np.abs(zr - amp * np.cos(ang))) < 2e-6 * amp
+    assert np.max(np.abs(zi - amp * np.sin(ang))) < 2e-6 * amp
+
+
+@pytest.mark.parametrize("window,pos_offset,T", [(0, 0, 200), (2048, 0, 300), (2048, 2046, 1),
+                                                 (2048, 2047, 1), (2048, 2048, 1), (0, 32767, 1),
+                                                 (16, 5, 40), (16, 100, 3)])
+def test_kv_append_intermediates(window, pos_offset, T):
+    """Q' (normalised, rotated at kept + t), the cache contents (pre-RoPE K, raw V, ring slot
+    n mod W, only the last W of a chunk) and the prefill operands K' and V^T."""
+    B, Hq, Hkv, d = 2, 8, 2, 128
+    dr = Draw(1234 + pos_offset + T, True)
+    q, k, v = dr.normal((B, T, Hq, d)), dr.normal((B, T, Hkv, d)), dr.normal((B, T, Hkv, d))
+    wq, wk = dr.normal((d,), 0.02), dr.normal((d,), 0.02)
+    rope = Rope(1e6, 64.0) if window == 0 else Rope(1e4)
+    c = 1.0
+    cap = window if window else pos_offset + T
+    kc = torch.full((B, Hkv, cap, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    Tp = swg.plamo_prefill_padded_len(T)
+    q_out = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device="cuda")
+    k_rot = torch.full((B, Hkv, Tp, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    v_t = torch.full((B, Hkv, d, Tp), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kept = pos_offset if window == 0 else min(pos_offset, window - 1)
+    swg.plamo_kv_append(dev(q), dev(k), dev(v), q_out, window=window, pos_offset=pos_offset,
+                        rope_table=rope_table(rope, 40000), q_norm_w=dev(wq), k_norm_w=dev(wk),
+                        norm_offset=c, k_rot_out=k_rot, v_t_out=v_t, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    omega, amp = rope_frequencies(d, rope.theta, rope.yarn_factor)
+    pos = kept + np.arange(T)
+    qn = offset_rms_norm(q, wq, c)
+    kn = offset_rms_norm(k, wk, c)
+    q_ref = np.stack([apply_rope(qn[b], pos, omega, amp) for b in range(B)])
+    assert_parity(host(q_out), q_ref, TOL_BF16, "q_out")
+    k_ref = np.stack([apply_rope(kn[b], pos, omega, amp) for b in range(B)])
+    kr = host(k_rot)
+    assert_parity(kr[:, :, :T].transpose(0, 2, 1, 3), k_ref, TOL_BF16, "k_rot")
+    assert np.all(kr[:, :, T:] == 0)
+    vt = host(v_t)
+    assert np.array_equal(vt[..., :T].transpose(0, 3, 1, 2), v)  # exact copy
+    assert np.all(vt[..., T:] == 0)
+    kch, vch = host(kc), host(vc)
+    written = np.arange(T) if window == 0 else np.arange(max(0, T - window), T)
+    for t in written:
+        n = pos_offset + t
+        slot = n if window == 0 else n % window
+        assert_parity(kch[:, :, slot], kn[:, t], TOL_BF16, f"k_cache slot {slot}")
+        assert np.array_equal(vch[:, :, slot], v[:, t])
+    touched = {(pos_offset + t) if window == 0 else (pos_offset + t) % window for t in written}
+    untouched = [s for s in range(cap) if s not in touched]
+    assert np.all(np.isnan(kch[:, :, untouched])) and np.all(np.isnan(vch[:, :, untouched]))
+
+
+# ----------------------------------------------------------------------------
+# prefill
+# ----------------------------------------------------------------------------
+
+def _run_prefill(inp, window, rope, norm_offset, bf16):
+    B, T, Hq, d = inp["q"].shape
+    tab = rope_table(rope, max(T, 64))
+    kw = {}
+    if inp.get("wq") is not None:
+        kw = dict(q_norm_w=dev(inp["wq"], bf16), k_norm_w=dev(inp["wk"], bf16), norm_offset=norm_offset)
+    bufs = layer.prefill(dev(inp["q"], bf16), dev(inp["k"], bf16), dev(inp["v"], bf16), window=window,
+                         rope_table=tab, **kw)
+    torch.cuda.synchronize()
+    return bufs
+
+
+def test_prefill_tiny_fp32():
+    """The tiny fp32 sliding-window workload (T=512, Hq=8, Hkv=2, W=128), full oracle, 1e-4."""
+    wl = TINY_SWA_FP32
+    inp = wl.draw()
+    bufs = _run_prefill(inp, wl.window, wl.rope, None, bf16=False)
+    ref = oracle_prefill(inp["q"], inp["k"], inp["v"], window=wl.window, rope=wl.rope)
+    assert_parity(host(bufs.out), ref, TOL_F32, wl.name)
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,W", [
+    (1, 1, 8, 2, 0), (1, 5, 8, 2, 3), (2, 64, 4, 4, 0), (1, 130, 16, 1, 7), (2, 300, 8, 2, 128),
+    (1, 1000, 8, 1, 200), (1, 777, 4, 2, 4096), (1, 513, 8, 8, 1), (1, 640, 16, 2, 64),
+    (3, 257, 2, 1, 129)])
+def test_prefill_bf16_small(B, T, Hq, Hkv, W):
+    """Several tiles, ragged tails, window 1 (self only), W > T, G = 1..16; full oracle."""
+    d = 128
+    dr = Draw(777 + 31 * T + W, True)
+    inp = dict(q=dr.normal((B, T, Hq, d)), k=dr.normal((B, T, Hkv, d)), v=dr.normal((B, T, Hkv, d)),
+               wq=dr.normal((d,), 0.02), wk=dr.normal((d,), 0.02))
+    rope = Rope(1e4) if W else Rope(1e6, 256.0)
+    bufs = _run_prefill(inp, W, rope, 1.0, bf16=True)
+    ref = oracle_prefill(inp["q"], inp["k"], inp["v"], window=W, rope=rope, wq=inp["wq"], wk=inp["wk"],
+                         norm_offset=1.0)
+    assert_parity(host(bufs.out), ref, TOL_BF16, f"B{B} T{T} Hq{Hq} Hkv{Hkv} W{W}")
+
+
+def _sample_rows(T, n_mid, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 63, 64, 127, 128, 2047, 2048, 2049, T // 2, T - 129, T - 128, T - 2, T - 1]
+    rows = set(r for r in fixed if 0 <= r < T)
+    rows.update(rng.integers(0, T, n_mid).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("norm_offset", [0.2, 1.0], ids=["c0.2", "c1"])
+def test_prefill_local_full_size(norm_offset):
+    """Local layer at its real shape (T=8192, Hq=64, Hkv=8, W=2048): sampled rows vs the
+    oracle, with the workload's offset 0.2 and the pages' q/k-norm offset 1."""
+    wl = LOCAL_PREFILL
+    inp = wl.draw()
+    bufs = _run_prefill(inp, wl.window, wl.rope, norm_offset, bf16=True)
+    rows = _sample_rows(wl.T, 10, 5)
+    ref = oracle_prefill(inp["q"], inp["k"], inp["v"], window=wl.window, rope=wl.rope, wq=inp["wq"],
+                         wk=inp["wk"], norm_offset=norm_offset, rows=rows)
+    assert_parity(host(bufs.out[:, rows]), ref, TOL_BF16, f"{wl.name} c={norm_offset}")
+
+
+@pytest.mark.parametrize("window,T", [(2048, 8192), (0, 32768)], ids=["local8192", "global32768"])
+def test_prefill_uniform_closed_form_full_size(window, T):
+    """Every row at full size: gain c + w = 0 zeroes Q, so each output is the mean of V over
+    the window (prefix sums). Exercises every tile, the window edge and the tile skipping."""
+    wl = LOCAL_PREFILL if window else GLOBAL_PREFILL
+    dr = Draw(4242 + T, True)
+    B, Hq, Hkv, d = 1, 64, 8, 128
+    q = dr.normal((B, T, Hq, d))
+    k = dr.normal((B, T, Hkv, d))
+    v = dr.normal((B, T, Hkv, d))
+    c = 1.0
+    inp = dict(q=q, k=k, v=v, wq=np.full(d, -c, np.float32), wk=dr.normal((d,), 0.02))
+    bufs = _run_prefill(inp, window, wl.rope, c, bf16=True)
+    out = host(bufs.out)[0]
+    mean = window_mean_closed_form(v[0], window)  # [T, Hkv, d]
+    ref = np.repeat(mean, Hq // Hkv, axis=1)
+    assert_parity(out, ref, TOL_BF16, f"closed form W={window}")
+
+
+@pytest.mark.parametrize("yarn", [64.0, 256.0])
+def test_prefill_global_full_size(yarn):
+    """Global layer at its real shape (T=32768, causal, YaRN, theta 1e6): sampled rows."""
+    wl = GLOBAL_PREFILL
+    inp = wl.draw()
+    rope = Rope(1e6, yarn)
+    bufs = _run_prefill(inp, 0, rope, wl.norm_offset, bf16=True)
+    rows = _sample_rows(wl.T, 4, 9)
+    ref = oracle_prefill(inp["q"], inp["k"], inp["v"], window=0, rope=rope, wq=inp["wq"], wk=inp["wk"],
+                         norm_offset=wl.norm_offset, rows=rows)
+    assert_parity(host(bufs.out[:, rows]), ref, TOL_BF16, f"global s={yarn}")
+
+
+def test_prefill_deterministic():
+    wl = LOCAL_PREFILL
+    inp = wl.draw()
+    a = _run_prefill(inp, wl.window, wl.rope, 0.2, True).out.clone()
+    b = _run_prefill(inp, wl.window, wl.rope, 0.2, True).out.clone()
+    assert torch.equal(a, b)
+
+
+def test_prefill_empty_is_noop():
+    q = torch.empty((1, 0, 8, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((1, 0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    tab = rope_table(Rope(1e4), 64)
+    swg.plamo_kv_append(q, k, k, q.clone(), window=16, pos_offset=0, rope_table=tab)
+    lib = swg._lib.load()
+    assert lib.plamo_attn_prefill(1, None, None, None, None, 1, 0, 8, 2, 128, 16, 0, 0.1, None) == 0
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+
+def _decode_case(B, Hq, Hkv, window, pos_offset, rope, seed, check_b, poison_future=True):
+    d = 128
+    cap = window if window else pos_offset + 1
+    kc = device_normal_bf16((B, Hkv, cap, d), seed, "cuda")
+    vc = device_normal_bf16((B, Hkv, cap, d), seed + 1, "cuda")
+    slots = kept_slots(pos_offset, window)
+    if poison_future:  # slots that hold no kept token must never be read
+        live = np.zeros(cap, dtype=bool)
+        live[slots] = True
+        dead = torch.from_numpy(np.nonzero(~live)[0]).cuda()
+        kc[:, :, dead] = float("nan")
+        vc[:, :, dead] = float("nan")
+    prior_k = {b: host(kc[b][:, torch.from_numpy(slots).cuda()]).transpose(1, 0, 2) for b in check_b}
+    prior_v = {b: host(vc[b][:, torch.from_numpy(slots).cuda()]).transpose(1, 0, 2) for b in check_b}
+    dr = Draw(seed + 7, True)
+    q, k, v = dr.normal((B, 1, Hq, d)), dr.normal((B, 1, Hkv, d)), dr.normal((B, 1, Hkv, d))
+    wq, wk = dr.normal((d,), 0.02), dr.normal((d,), 0.02)
+    tab = rope_table(rope, max(pos_offset + 2, 64))
+    bufs = layer.decode(dev(q), dev(k), dev(v), kc, vc, window=window, pos_offset=pos_offset,
+                        rope_table=tab, q_norm_w=dev(wq), k_norm_w=dev(wk), norm_offset=1.0)
+    torch.cuda.synchronize()
+    out = host(bufs.out)
+    for b in check_b:
+        ref = oracle_decode_one(q[b], k[b], v[b], prior_k[b], prior_v[b], pos_offset, window=window,
+                                rope=rope, wq=wq, wk=wk)
+        assert_parity(out[b], ref, TOL_BF16, f"decode b={b} W={window} p={pos_offset}")
+    return bufs
+
+
+@pytest.mark.parametrize("window,pos_offset", [(2048, 0), (2048, 1), (2048, 100), (2048, 2046),
+                                               (2048, 2047), (2048, 2048), (2048, 32767),
+                                               (2048, 32767 + 1000), (0, 0), (0, 63), (0, 64),
+                                               (0, 5000), (16, 3), (16, 40)])
+def test_decode_small_batch(window, pos_offset):
+    """Ring fill-up and wrap, contiguous growth, tile edges; dead slots hold NaN."""
+    rope = Rope(1e4) if window else Rope(1e6, 64.0)
+    _decode_case(3, 16, 2, window, pos_offset, rope, 100 + pos_offset + window, check_b=[0, 1, 2])
+
+
+@pytest.mark.parametrize("G", [1, 4, 16])
+def test_decode_group_sizes(G):
+    _decode_case(2, 2 * G, 2, 2048, 3000, Rope(1e4), 900 + G, check_b=[0, 1])
+
+
+@pytest.mark.parametrize("layer_idx", [0, 1], ids=["local_ring2048", "global32768"])
+def test_decode_batched_full_size(layer_idx):
+    """Batched decode at its real shape: B=64, Hq=64, Hkv=8, local ring (2047 kept + 1) and
+    global cache (32767 kept + 1); sampled sequences vs the oracle."""
+    wl = BATCHED_DECODE
+    ly = wl.layers[layer_idx]
+    _decode_case(wl.B, wl.Hq, wl.Hkv, ly.window, wl.pos_offset, ly.rope, wl.cache_seed(layer_idx),
+                 check_b=[0, 31, 63], poison_future=False)
+
+
+def test_decode_period_long_context_step():
+    """One step of the 8-layer period at B=8 with 131071 kept global tokens: the global
+    layer and one local layer, sampled sequences."""
+    wl = PERIOD_DECODE
+    for li in (0, 7):
+        ly = wl.layers[li]
+        _decode_case(wl.B, wl.Hq, wl.Hkv, ly.window, wl.pos_offset, ly.rope, wl.cache_seed(li),
+                     check_b=[0, 7], poison_future=False)
+
+
+@pytest.mark.parametrize("window", [0, 16, 2048])
+def test_prefill_then_decode_matches_oracle(window):
+    """Prefill T tokens into the cache, then decode k more one by one: each step equals the
+    oracle run on the same token stream (「PLaMo 3アーキテクチャ徹底解析」 §10 method)."""
+    B, Hq, Hkv, d, T, steps = 2, 8, 2, 128, 2100, 4
+    rope = Rope(1e4) if window else Rope(1e6, 256.0)
+    dr = Draw(555 + window, True)
+    n = T + steps
+    q, k, v = dr.normal((B, n, Hq, d)), dr.normal((B, n, Hkv, d)), dr.normal((B, n, Hkv, d))
+    wq, wk = dr.normal((d,), 0.02), dr.normal((d,), 0.02)
+    cap = window if window else n
+    kc = torch.zeros((B, Hkv, cap, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    tab = rope_table(rope, n + 64)
+    pre = layer.prefill(dev(q[:, :T]), dev(k[:, :T]), dev(v[:, :T]), window=window, rope_table=tab,
+                        q_norm_w=dev(wq), k_norm_w=dev(wk), norm_offset=1.0, k_cache=kc, v_cache=vc)
+    outs = [host(pre.out)]
+    for s in range(steps):
+        p = T + s
+        bufs = layer.decode(dev(q[:, p:p + 1]), dev(k[:, p:p + 1]), dev(v[:, p:p + 1]), kc, vc,
+                            window=window, pos_offset=p, rope_table=tab, q_norm_w=dev(wq),
+                            k_norm_w=dev(wk), norm_offset=1.0)
+        torch.cuda.synchronize()
+        outs.append(host(bufs.out))
+    got = np.concatenate(outs, axis=1)
+    rows = np.concatenate([np.array([0, 1, T // 2, T - 1]), T + np.arange(steps)])
+    ref = oracle_prefill(q, k, v, window=window, rope=rope, wq=wq, wk=wk, norm_offset=1.0, rows=rows)
+    assert_parity(got[:, rows], ref, TOL_BF16, f"prefill+decode W={window}")
