@@ -225,7 +225,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="", help="prefill_local|prefill_global|decode|period")
+    ap.add_argument("--only", default="", help="prefill_local|prefill_global|decode|period|copy_calibration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--period-steps", type=int, default=128)
@@ -267,6 +267,15 @@ def main():
         log(f"[bench]   {r}")
         extra["period_decode"] = r
 
+    if only == "copy_calibration":
+        # a plain device-to-device copy of known size: the reference for HBM byte counters
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        extra["copy_calibration"] = {"bytes_read": n, "bytes_written": n, "launches": args.steps}
     if local is None:
         print(json.dumps({"metric": METRIC, "partial": only, "extra": extra}))
         return

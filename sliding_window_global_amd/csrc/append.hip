@@ -9,9 +9,12 @@
 //   §6.1/§6.3  split-half pairs (j, j + 64); rotation factors from the two-level table.
 //
 // One block = 64 tokens of one sequence and one KV head: its G = Hq/Hkv query heads,
-// the K head and the V head. Lane j of a wave owns pair j of the row it works on, so the
-// rotation is lane-local and the norm is one wave reduction. V is staged through LDS to
-// write the transposed prefill operand with 128-byte rows.
+// the K head and the V head. The block first forms the rotation factors of its 64
+// positions in LDS. A row (one token of one head) is handled by a group of lanes, each
+// holding one 16-byte chunk of the first half and the matching chunk of the second
+// half, so every rotation pair is lane-local and the norm is a reduction over the
+// group. V is staged through LDS to write the transposed prefill operand with
+// full rows.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,6 +24,7 @@ namespace {
 
 constexpr int kTokBlock = 64;
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 
 template <typename E>
 struct Io;
@@ -28,21 +32,45 @@ struct Io;
 template <>
 struct Io<float> {
   static __device__ __forceinline__ float ld(const float* p) { return *p; }
-  static __device__ __forceinline__ void st(float* p, float x) { *p = x; }
   static __device__ __forceinline__ float rnd(float x) { return x; }
+  static __device__ __forceinline__ void unpack(const u32x4& w, float* x) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e]);
+  }
+  static __device__ __forceinline__ u32x4 pack(const float* x) {
+    return u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+  }
 };
 
 template <>
 struct Io<bf16_t> {
   static __device__ __forceinline__ float ld(const bf16_t* p) { return bf16_to_f32(*p); }
-  static __device__ __forceinline__ void st(bf16_t* p, float x) { *p = f32_to_bf16(x); }
   static __device__ __forceinline__ float rnd(float x) { return bf16_to_f32(f32_to_bf16(x)); }
+  static __device__ __forceinline__ void unpack(const u32x4& w, float* x) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = lo_bf16(w[e]);
+      x[2 * e + 1] = hi_bf16(w[e]);
+    }
+  }
+  static __device__ __forceinline__ u32x4 pack(const float* x) {
+    return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                 pack_bf16x2(x[6], x[7])};
+  }
 };
 
 template <typename E>
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
+  constexpr int kVec = 16 / sizeof(E);          // elements per 16-byte chunk
+  constexpr int kLanesPerRow = kHalf / kVec;    // 8 (bf16) or 16 (fp32)
+  constexpr int kRowsPerPass = 64 / kLanesPerRow;
+  constexpr int kUnroll = 2;
+  __shared__ __attribute__((aligned(16))) float2 zs[kTokBlock][kHalf];
+
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int c = lane % kLanesPerRow;  // chunk index within a half row: pairs c*kVec ..
+  const int slot = lane / kLanesPerRow;
   const int t0 = blockIdx.x * kTokBlock;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
@@ -58,97 +86,144 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   E* __restrict__ k_cache = static_cast<E*>(a.k_cache);
   E* __restrict__ v_cache = static_cast<E*>(a.v_cache);
   const bool norm = wq != nullptr;
-  const float gq0 = norm ? a.norm_offset + Io<E>::ld(wq + lane) : 1.f;
-  const float gq1 = norm ? a.norm_offset + Io<E>::ld(wq + lane + kHalf) : 1.f;
-  const float gk0 = norm ? a.norm_offset + Io<E>::ld(wk + lane) : 1.f;
-  const float gk1 = norm ? a.norm_offset + Io<E>::ld(wk + lane + kHalf) : 1.f;
   const int n_tok = min(kTokBlock, a.T - t0);  // may be <= 0 in the padding blocks
 
-  // --- queries: norm, rotate at renumbered position kept + t ---------------------------
-  for (int r = wave; r < n_tok * G; r += kThreads / 64) {
-    const int t = t0 + r / G;
-    const int hq = kvh * G + r % G;
-    const long long row = ((static_cast<long long>(b) * a.T + t) * a.Hq + hq) * kHeadDim;
-    float x0 = Io<E>::ld(q + row + lane);
-    float x1 = Io<E>::ld(q + row + lane + kHalf);
-    if (norm) {
-      const float inv = rsqrtf(wave_sum(x0 * x0 + x1 * x1) * (1.f / kHeadDim) + a.eps);
-      x0 *= inv * gq0;
-      x1 *= inv * gq1;
+  // rotation factors of this block's renumbered positions kept + t
+  for (int i = threadIdx.x; i < kTokBlock * kHalf; i += kThreads) {
+    const int r = i / kHalf, j = i % kHalf;
+    if (r < n_tok) zs[r][j] = rope_factor(a.rope, a.kept + t0 + r, j);
+  }
+  float gq[2 * kVec], gk[2 * kVec];  // gains c + w of this lane's dims (both halves)
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+      const int dim = h * kHalf + c * kVec + e;
+      gq[h * kVec + e] = norm ? a.norm_offset + Io<E>::ld(wq + dim) : 1.f;
+      gk[h * kVec + e] = norm ? a.norm_offset + Io<E>::ld(wk + dim) : 1.f;
     }
-    const float2 z = rope_factor(a.rope, a.kept + t, lane);
-    Io<E>::st(q_out + row + lane, x0 * z.x - x1 * z.y);
-    Io<E>::st(q_out + row + lane + kHalf, x0 * z.y + x1 * z.x);
+  __syncthreads();
+
+  // One pass normalises and rotates kRowsPerPass rows per wave (kUnroll passes in flight).
+  // is_k: row r is token t0 + r of the K head; else row r is (token r / G, head r % G).
+  auto rows = [&](const E* __restrict__ src, int n_rows, bool is_k) {
+    const float* g = is_k ? gk : gq;
+    for (int base = wave * kRowsPerPass * kUnroll; base < n_rows; base += kWaves * kRowsPerPass * kUnroll) {
+      float x[kUnroll][2 * kVec];
+      float ss[kUnroll];
+      long long off[kUnroll];
+      int tt[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int r = min(base + u * kRowsPerPass + slot, n_rows - 1);
+        tt[u] = is_k ? r : r / G;
+        const int head = is_k ? kvh : kvh * G + r % G;
+        const int H = is_k ? a.Hkv : a.Hq;
+        off[u] = ((static_cast<long long>(b) * a.T + t0 + tt[u]) * H + head) * kHeadDim + c * kVec;
+        const u32x4 w0 = *reinterpret_cast<const u32x4*>(src + off[u]);
+        const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + off[u] + kHalf);
+        Io<E>::unpack(w0, x[u]);
+        Io<E>::unpack(w1, x[u] + kVec);
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 2 * kVec; ++e) s += x[u][e] * x[u][e];
+        ss[u] = s;
+      }
+      if (norm) {
+#pragma unroll
+        for (int m = 1; m < kLanesPerRow; m <<= 1)
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) ss[u] += __shfl_xor(ss[u], m, 64);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int r = base + u * kRowsPerPass + slot;
+        if (r >= n_rows) continue;
+        const int t = t0 + tt[u];
+        if (norm) {
+          const float inv = rsqrtf(ss[u] * (1.f / kHeadDim) + a.eps);
+#pragma unroll
+          for (int e = 0; e < 2 * kVec; ++e) x[u][e] *= inv * g[e];
+        }
+        if (is_k) {
+#pragma unroll
+          for (int e = 0; e < 2 * kVec; ++e) x[u][e] = Io<E>::rnd(x[u][e]);  // the cached value
+          if (k_cache && (a.window == 0 || t >= a.T - a.window)) {
+            const long long n = a.pos_offset + t;
+            const long long s = a.window == 0 ? n : n % a.window;
+            E* dst = k_cache + ((static_cast<long long>(b) * a.Hkv + kvh) * a.cap + s) * kHeadDim + c * kVec;
+            *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(x[u]);
+            *reinterpret_cast<u32x4*>(dst + kHalf) = Io<E>::pack(x[u] + kVec);
+          }
+          if (!k_rot) continue;
+        }
+        float y[2 * kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+          const float2 z = zs[tt[u]][c * kVec + e];
+          const float x0 = x[u][e], x1 = x[u][kVec + e];
+          y[e] = x0 * z.x - x1 * z.y;
+          y[kVec + e] = x0 * z.y + x1 * z.x;
+        }
+        E* dst = is_k ? k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t) * kHeadDim + c * kVec
+                      : q_out + off[u];
+        *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(y);
+        *reinterpret_cast<u32x4*>(dst + kHalf) = Io<E>::pack(y + kVec);
+      }
+    }
+  };
+  rows(q, n_tok * G, false);
+  rows(k, n_tok, true);
+
+  if (k_rot) {  // zero the padding rows T .. Tp-1 of this block
+    for (int i = threadIdx.x; i < kTokBlock * (kHeadDim / kVec); i += kThreads) {
+      const long long t = t0 + i / (kHeadDim / kVec);
+      if (t >= a.T && t < a.Tp)
+        reinterpret_cast<u32x4*>(k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t) * kHeadDim)
+            [i % (kHeadDim / kVec)] = u32x4{0, 0, 0, 0};
+    }
   }
 
-  // --- keys: norm, round to the cache type, cache write, rotate -----------------------
-  const int k_rows = k_rot ? kTokBlock : n_tok;  // padding rows only feed k_rot zeros
-  for (int r = wave; r < k_rows; r += kThreads / 64) {
-    const int t = t0 + r;
-    if (t >= a.T) {
-      if (t < a.Tp) {
-        const long long orow = ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t) * kHeadDim;
-        Io<E>::st(k_rot + orow + lane, 0.f);
-        Io<E>::st(k_rot + orow + lane + kHalf, 0.f);
-      }
-      continue;
-    }
-    const long long row = ((static_cast<long long>(b) * a.T + t) * a.Hkv + kvh) * kHeadDim;
-    float x0 = Io<E>::ld(k + row + lane);
-    float x1 = Io<E>::ld(k + row + lane + kHalf);
-    if (norm) {
-      const float inv = rsqrtf(wave_sum(x0 * x0 + x1 * x1) * (1.f / kHeadDim) + a.eps);
-      x0 = Io<E>::rnd(x0 * inv * gk0);
-      x1 = Io<E>::rnd(x1 * inv * gk1);
-    }
-    if (k_cache) {
-      const long long n = a.pos_offset + t;
-      const bool write = a.window == 0 || t >= a.T - a.window;
-      if (write) {
-        const long long slot = a.window == 0 ? n : n % a.window;
-        const long long crow = ((static_cast<long long>(b) * a.Hkv + kvh) * a.cap + slot) * kHeadDim;
-        Io<E>::st(k_cache + crow + lane, x0);
-        Io<E>::st(k_cache + crow + lane + kHalf, x1);
-      }
-    }
-    if (k_rot) {
-      const float2 z = rope_factor(a.rope, a.kept + t, lane);
-      const long long orow = ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t) * kHeadDim;
-      Io<E>::st(k_rot + orow + lane, x0 * z.x - x1 * z.y);
-      Io<E>::st(k_rot + orow + lane + kHalf, x0 * z.y + x1 * z.x);
-    }
-  }
-
-  // --- values: raw copy into the cache, transposed prefill operand --------------------
+  // --- values: raw copy into the cache (16-byte chunks), transposed prefill operand ----
+  constexpr int kChunks = kHeadDim / kVec;  // 16-byte chunks per row
   if (v_cache) {
-    for (int r = wave; r < n_tok; r += kThreads / 64) {
-      const int t = t0 + r;
+    for (int i = threadIdx.x; i < n_tok * kChunks; i += kThreads) {
+      const int t = t0 + i / kChunks;
       if (!(a.window == 0 || t >= a.T - a.window)) continue;
       const long long n = a.pos_offset + t;
-      const long long slot = a.window == 0 ? n : n % a.window;
+      const long long s = a.window == 0 ? n : n % a.window;
+      const int cidx = i % kChunks;
       const long long row = ((static_cast<long long>(b) * a.T + t) * a.Hkv + kvh) * kHeadDim;
-      const long long crow = ((static_cast<long long>(b) * a.Hkv + kvh) * a.cap + slot) * kHeadDim;
-      v_cache[crow + lane] = v[row + lane];
-      v_cache[crow + lane + kHalf] = v[row + lane + kHalf];
+      const long long crow = ((static_cast<long long>(b) * a.Hkv + kvh) * a.cap + s) * kHeadDim;
+      reinterpret_cast<u32x4*>(v_cache + crow)[cidx] = reinterpret_cast<const u32x4*>(v + row)[cidx];
     }
   }
   if (v_t) {
-    __shared__ E tile[kHeadDim][kTokBlock + 1];
-    for (int i = threadIdx.x; i < kTokBlock * kHeadDim; i += kThreads) {
-      const int r = i / kHeadDim;
-      const int c = i % kHeadDim;
+    constexpr int kTS = kTokBlock + kVec;  // LDS row stride (tokens), keeps rows 16-byte aligned
+    __shared__ __attribute__((aligned(16))) E tile[kHeadDim * kTS];
+    for (int i = threadIdx.x; i < kTokBlock * kChunks; i += kThreads) {
+      const int r = i / kChunks, cidx = i % kChunks;
       const int t = t0 + r;
-      E x = E(0);
-      if (t < a.T) x = v[((static_cast<long long>(b) * a.T + t) * a.Hkv + kvh) * kHeadDim + c];
-      tile[c][r] = x;
+      E x[kVec];
+      if (t < a.T) {
+        const u32x4 w = reinterpret_cast<const u32x4*>(v + ((static_cast<long long>(b) * a.T + t) * a.Hkv + kvh) * kHeadDim)[cidx];
+        __builtin_memcpy(x, &w, 16);
+      } else {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) x[e] = E(0);
+      }
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) tile[(cidx * kVec + e) * kTS + r] = x[e];
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < kTokBlock * kHeadDim; i += kThreads) {
-      const int c = i / kTokBlock;
-      const int r = i % kTokBlock;
-      const long long t = t0 + r;
-      if (t < a.Tp)
-        v_t[((static_cast<long long>(b) * a.Hkv + kvh) * kHeadDim + c) * a.Tp + t] = tile[c][r];
+    constexpr int kTokChunks = kTokBlock / kVec;
+    for (int i = threadIdx.x; i < kHeadDim * kTokChunks; i += kThreads) {
+      const int cc = i / kTokChunks, tc = i % kTokChunks;
+      const long long t = t0 + tc * kVec;
+      if (t < a.Tp) {  // Tp is a multiple of 128, so a chunk is wholly inside or outside
+        const u32x4 w = *reinterpret_cast<const u32x4*>(&tile[cc * kTS + tc * kVec]);
+        *reinterpret_cast<u32x4*>(v_t + ((static_cast<long long>(b) * a.Hkv + kvh) * kHeadDim + cc) * a.Tp + t) = w;
+      }
     }
   }
 }

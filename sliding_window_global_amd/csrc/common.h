@@ -32,9 +32,20 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float x) {
   return __builtin_bit_cast(bf16_t, b);
 }
 
-// Pack two floats into one dword of two bf16 (lo in the low half).
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Pack two floats into one dword of two bf16 (lo in the low half), round to nearest
+// even: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const f32x2v f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
+}
+
+// acc + lo(w) + hi(w) for a dword of two bf16 (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+  const bf16x2v one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w), one, acc, false);
 }
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }

@@ -29,6 +29,8 @@ constexpr int kTile = 64;
 constexpr int KS = kHeadDim + 8;  // LDS row stride (elements): 272 B
 constexpr int kMaxGroup = 16;
 constexpr int kPartial = kHeadDim + 2;  // acc[128], m, l
+constexpr int kMaxSplit = 256;         // key ranges per (sequence, KV head)
+constexpr long long kMinChunk = 256;   // keys per range, at least
 
 struct DecTile {
   u32x4 k[4];
@@ -118,17 +120,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
     if (tid < 32) reinterpret_cast<float4*>(cs[buf])[tid] = r.cr;
   };
 
-  DecTile regs;
-  load(regs, s_begin);
-  store(regs, 0);
-  __syncthreads();
-
-  const int n_tiles = static_cast<int>((s_end - s_begin + kTile - 1) / kTile);
-  for (int it = 0; it < n_tiles; ++it) {
-    const int buf = it & 1;
-    const long long tb = s_begin + static_cast<long long>(it) * kTile;
-    if (it + 1 < n_tiles) load(regs, tb + kTile);
-
+  // Software pipeline: two register sets alternate so that two tiles are in flight
+  // while the LDS copy of the current one is consumed.
+  auto compute = [&](int buf, long long tb) {
     const long long wave_key0 = tb + wave * 16;
     if (wave_key0 < s_end) {  // wave-uniform
       // K' rows: lane reads its key's 4 x 8 dims, rotates its 16 pairs, packs to bf16
@@ -206,8 +200,24 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
         oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[dt], 0, 0, 0);
       }
     }
+  };
 
-    if (it + 1 < n_tiles) store(regs, buf ^ 1);
+  const int n_tiles = static_cast<int>((s_end - s_begin + kTile - 1) / kTile);
+  DecTile ra, rb;
+  load(ra, s_begin);
+  if (n_tiles > 1) load(rb, s_begin + kTile);
+  store(ra, 0);
+  __syncthreads();
+  for (int it = 0; it < n_tiles; it += 2) {
+    const long long tb = s_begin + static_cast<long long>(it) * kTile;
+    if (it + 2 < n_tiles) load(ra, tb + 2 * kTile);
+    compute(0, tb);
+    if (it + 1 < n_tiles) store(rb, 1);
+    __syncthreads();
+    if (it + 1 >= n_tiles) break;
+    if (it + 3 < n_tiles) load(rb, tb + 3 * kTile);
+    compute(1, tb + kTile);
+    if (it + 2 < n_tiles) store(ra, 0);
     __syncthreads();
   }
 
@@ -249,33 +259,52 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   }
 }
 
-// One block per (sequence, query head); thread d merges the split partials in order.
+// One block per (sequence, query head): the split states are merged in a fixed order
+// (deterministic); thread d owns output component d.
 __global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(const float* __restrict__ ws,
                                                                   bf16_t* __restrict__ out,
                                                                   int n_split) {
+  __shared__ float wsc[kMaxSplit];
+  __shared__ float red[2][kHeadDim / 64];
   const int bh = blockIdx.x;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6;
   const float* p = ws + static_cast<long long>(bh) * n_split * kPartial;
   float M = -INFINITY;
-  for (int i = 0; i < n_split; ++i) M = fmaxf(M, p[i * kPartial + kHeadDim]);
-  float acc = 0.f, l = 0.f;
-  for (int i = 0; i < n_split; ++i) {
-    const float sc = fast_exp2(p[i * kPartial + kHeadDim] - M);
-    acc += sc * p[i * kPartial + d];
-    l += sc * p[i * kPartial + kHeadDim + 1];
+  for (int i = tid; i < n_split; i += kHeadDim) M = fmaxf(M, p[i * kPartial + kHeadDim]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+  if ((tid & 63) == 0) red[0][wv] = M;
+  __syncthreads();
+  M = fmaxf(red[0][0], red[0][1]);
+  float L = 0.f;
+  for (int i = tid; i < n_split; i += kHeadDim) {
+    const float w = fast_exp2(p[i * kPartial + kHeadDim] - M);
+    wsc[i] = w;
+    L += w * p[i * kPartial + kHeadDim + 1];
   }
-  out[static_cast<long long>(bh) * kHeadDim + d] = f32_to_bf16(acc / l);
+  L = wave_sum(L);
+  if ((tid & 63) == 0) red[1][wv] = L;
+  __syncthreads();
+  L = red[1][0] + red[1][1];
+  float acc = 0.f;
+#pragma unroll 8
+  for (int i = 0; i < n_split; ++i) acc += wsc[i] * p[i * kPartial + tid];
+  out[static_cast<long long>(bh) * kHeadDim + tid] = f32_to_bf16(acc / L);
 }
 
 }  // namespace
 
 DecodePlan plan_decode(int B, int Hkv, long long S) {
+  // Aim for ~2048 blocks (8 per CU) with at least kMinChunk keys each and at most
+  // kMaxSplit ranges per (sequence, KV head).
   const long long pairs = static_cast<long long>(B) * Hkv;
   const long long target_blocks = 2048;
-  const long long max_split = (S + kTile - 1) / kTile;
   long long n = (target_blocks + pairs - 1) / pairs;
+  const long long by_min_chunk = (S + kMinChunk - 1) / kMinChunk;
+  if (n > by_min_chunk) n = by_min_chunk;
+  if (n > kMaxSplit) n = kMaxSplit;
   if (n < 1) n = 1;
-  if (n > max_split) n = max_split;
   long long chunk = (S + n - 1) / n;
   chunk = (chunk + kTile - 1) / kTile * kTile;
   DecodePlan p;

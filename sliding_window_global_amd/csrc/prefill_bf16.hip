@@ -34,6 +34,7 @@ constexpr int KS = kHeadDim + 8;  // K tile row stride (elements): 272 B
 constexpr int VS = BN + 8;        // V^T tile row stride (elements): 144 B
 constexpr int kKTile = BN * KS;
 constexpr int kVTile = kHeadDim * VS;
+constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -83,6 +84,8 @@ __device__ __forceinline__ void store_tile(const TileRegs& r, bf16_t* ks, bf16_t
   }
 }
 
+// kLocal: sliding-window layer (window > 0); otherwise the global causal layer.
+template <bool kLocal>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (kKTile + kVTile)];
 
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   const int b = rest / a.Hkv;
   const int hq = kvh * G + g_in;
   // causal work grows with the query block: longest first (local work is flat)
-  const int qb = a.window == 0 ? nqb - 1 - qb_order : qb_order;
+  const int qb = kLocal ? qb_order : nqb - 1 - qb_order;
   const int i0 = qb * BM;
 
   const bf16_t* __restrict__ q = static_cast<const bf16_t*>(a.q_rot);
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 
   // ---- key tiles this block touches ------------------------------------------------
   const int last_row = min(i0 + BM, a.T) - 1;
-  const int lo = a.window > 0 ? max(0, i0 - a.window + 1) : 0;
+  const int lo = kLocal ? max(0, i0 - a.window + 1) : 0;
   const int kt_lo = lo / BN;
   const int kt_hi = last_row / BN;
 
@@ -158,9 +161,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 
     const int j0 = kt * BN;
     // wave-uniform visibility of this tile for rows r0 .. r0+31
-    const bool any = (j0 <= r0 + 31) && (a.window == 0 || j0 + BN - 1 > r0 - a.window);
+    const bool any = (j0 <= r0 + 31) && (!kLocal || j0 + BN - 1 > r0 - a.window);
     if (any) {
-      const bool need_mask = (j0 + BN - 1 > r0) || (a.window > 0 && r0 + 31 - j0 >= a.window);
+      const bool need_mask = (j0 + BN - 1 > r0) || (kLocal && r0 + 31 - j0 >= a.window);
       f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = j0 + kb * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
-            const bool ok = key <= qrow && (a.window == 0 || qrow - key < a.window);
+            const bool ok = key <= qrow && (!kLocal || qrow - key < a.window);
             if (!ok) sacc[kb][e] = -INFINITY;
           }
       }
@@ -190,37 +193,42 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx * c);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float psum = 0.f;
+      // Lazy rescaling: the running reference max only moves (and O, l are only rescaled)
+      // when some row of the wave gains more than 2^8 over it, so p stays <= 256.
+      const float mx_c = mx * c;
+      if (__builtin_amdgcn_ballot_w64(mx_c > m_run + kRescaleLog2) != 0) {  // wave-uniform
+        const float m_new = fmaxf(m_run, mx_c);
+        const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+        m_run = m_new;
+      }
+      // a row whose keys so far are all masked has m_run = -inf and only -inf scores here
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(sacc[kb][e] * c - m_use);
-          sacc[kb][e] = p;
-          psum += p;
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+        for (int e = 0; e < 16; ++e) sacc[kb][e] = fast_exp2(fmaf(sacc[kb][e], c, -m_use));
 
-      // P^T as MFMA B operand: k-step u covers keys 16u..16u+15 = sacc[u/2][(u%2)*8 ..+7]
+      // P^T as MFMA B operand: k-step u covers keys 16u..16u+15 = sacc[u/2][(u%2)*8 ..+7].
+      // The row sum adds the same bf16-rounded p that enter the P V product.
       bf16x8 pb[4];
+      float psum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int kb = u >> 1, e0 = (u & 1) * 8;
         u32x4 w;
-        w[0] = pack_bf16x2(sacc[kb][e0 + 0], sacc[kb][e0 + 1]);
-        w[1] = pack_bf16x2(sacc[kb][e0 + 2], sacc[kb][e0 + 3]);
-        w[2] = pack_bf16x2(sacc[kb][e0 + 4], sacc[kb][e0 + 5]);
-        w[3] = pack_bf16x2(sacc[kb][e0 + 6], sacc[kb][e0 + 7]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          w[i] = pack_bf16x2(sacc[kb][e0 + 2 * i], sacc[kb][e0 + 2 * i + 1]);
+          psum[i] = add_bf16x2(w[i], psum[i]);
+        }
         pb[u] = __builtin_bit_cast(bf16x8, w);
       }
+      l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
@@ -260,8 +268,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   const long long nqb = (a.T + BM - 1) / BM;
   const long long blocks = nqb * a.Hq * a.B;
-  hipLaunchKernelGGL(prefill_bf16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                     stream, a);
+  if (a.window > 0)
+    hipLaunchKernelGGL(prefill_bf16_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(prefill_bf16_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
