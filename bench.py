@@ -227,7 +227,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="", help="prefill_local|prefill_global|decode|period|copy_calibration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--period-steps", type=int, default=128)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -237,6 +237,7 @@ def main():
     import torch
 
     import sliding_window_global_amd as swg
+    from sliding_window_global_amd.profiling import read_traffic
     from synthetic.workloads import BATCHED_DECODE, GLOBAL_PREFILL, LOCAL_PREFILL, PERIOD_DECODE
 
     torch.cuda.set_device(0)
@@ -301,7 +302,8 @@ def main():
                    "window": 2048, "step": "kv_append + attn_prefill"},
         "roofline": {"bound": "mfma", "achieved": round(local["attn_tflops"], 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(local["attn_tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(local["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": read_traffic(os.path.join(ROOT, "profiles", "prefill_local_T8192_hbm_traffic.txt")),
                      "kernel": "prefill_bf16_kernel", "flop_per_launch": LOCAL_PREFILL.flops()},
         "cpu_baseline": cpu,
         "extra": extra,

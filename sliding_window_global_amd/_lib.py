@@ -43,7 +43,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     global _LIB
     if _LIB is not None:
         return _LIB
-    path = path or LIB_PATH
+    path = path or os.environ.get("PLAMO_ATTN_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
     lib = ctypes.CDLL(path)
