@@ -100,11 +100,18 @@ PLAMO_API long long plamo_prefill_padded_len(long long T);
  * q_norm_w, k_norm_w [d]   stored norm weights w (gain c + w); both NULL = no norm
  * norm_offset, norm_eps    c (1 for q_norm/k_norm [P3 §3.2]) and eps (1e-6)
  * q_out    [B, T, Hq, d]   normalised and rotated Q                (dtype, required)
- * k_rot_out [B, Hkv, Tp, d] normalised, cache-rounded and rotated K, Tp =
- *                          plamo_prefill_padded_len(T); rows T..Tp-1 are zeroed.
- *                          NULL = not written. (Prefill operand.)
- * v_t_out  [B, Hkv, d, Tp] V transposed (token index fastest), pad zeroed. NULL =
- *                          not written. (Prefill operand.)
+ * k_rot_out normalised, cache-rounded and rotated K, Tp = plamo_prefill_padded_len(T)
+ *                          tokens per (b, KV head), tokens T..Tp-1 zeroed. NULL = not
+ *                          written. (Prefill operand.) Layout per (b, KV head):
+ *                            fp32: [Tp][d];
+ *                            bf16: Tp/64 tiles of 64 tokens, tile = [16][64][8]
+ *                                  (dim / 8, token in tile, dim % 8), 16 KiB.
+ * v_t_out  V transposed, pad zeroed. NULL = not written. (Prefill operand.) Layout
+ *                          per (b, KV head):
+ *                            fp32: [d][Tp] (token index fastest);
+ *                            bf16: Tp/64 tiles, tile = [8][128][8]
+ *                                  (token in tile / 8, dim, token % 8), 16 KiB.
+ *                          Either operand occupies B*Hkv*Tp*d elements.
  * k_cache, v_cache [B, Hkv, cap, d]  normalised pre-RoPE K and raw V (dtype). NULL
  *                          (both) = no cache. Global: token n goes to slot n,
  *                          cap >= pos_offset + T. Local: slot n mod window (a ring of
@@ -124,7 +131,7 @@ PLAMO_API int plamo_kv_append(int dtype, const void* q, const void* k, const voi
 /* ---------------------------------------------------------------------------
  * plamo_attn_prefill -- step 4 for a prefill from an empty cache [P3 §4.5, §5.1]
  *
- * q_rot [B, T, Hq, d]; k_rot [B, Hkv, Tp, d]; v_t [B, Hkv, d, Tp] as written by
+ * q_rot [B, T, Hq, d]; k_rot and v_t in the dtype's layout written by
  * plamo_kv_append (Tp = plamo_prefill_padded_len(T)); out [B, T, Hq, d] (token
  * major, i.e. [B, T, Hq*d] ready for the output projection [P3 §4.5]).
  * Query i (0..T-1) attends keys j <= i, and i - j < window when window > 0.

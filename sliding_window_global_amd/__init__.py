@@ -117,6 +117,22 @@ def plamo_prefill_padded_len(T: int) -> int:
     return int(_lib.load().plamo_prefill_padded_len(int(T)))
 
 
+PREFILL_KEY_TILE = 64
+
+
+def prefill_operand_shapes(B: int, T: int, Hkv: int, d: int, dtype) -> tuple[tuple, tuple]:
+    """Shapes of (k_rot, v_t) as plamo_kv_append writes them (include/plamo_attn.h).
+
+    fp32: [B, Hkv, Tp, d] and [B, Hkv, d, Tp]. bf16: tiled by 64 tokens,
+    [B, Hkv, Tp/64, d/8, 64, 8] and [B, Hkv, Tp/64, 8, d, 8].
+    """
+    Tp = plamo_prefill_padded_len(T)
+    if dtype == torch.bfloat16:
+        nt = Tp // PREFILL_KEY_TILE
+        return (B, Hkv, nt, d // 8, PREFILL_KEY_TILE, 8), (B, Hkv, nt, PREFILL_KEY_TILE // 8, d, 8)
+    return (B, Hkv, Tp, d), (B, Hkv, d, Tp)
+
+
 def plamo_kv_append(q, k, v, q_out, *, window: int, pos_offset: int, rope_table,
                     q_norm_w=None, k_norm_w=None, norm_offset: float = 1.0, norm_eps: float = 1e-6,
                     k_rot_out=None, v_t_out=None, k_cache=None, v_cache=None, stream=None) -> None:
@@ -128,11 +144,11 @@ def plamo_kv_append(q, k, v, q_out, *, window: int, pos_offset: int, rope_table,
         raise ValueError("k and v must be [B, T, Hkv, d] matching q")
     if tuple(q_out.shape) != (B, T, Hq, d):
         raise ValueError("q_out must match q")
-    Tp = plamo_prefill_padded_len(T)
-    if k_rot_out is not None and tuple(k_rot_out.shape) != (B, Hkv, Tp, d):
-        raise ValueError(f"k_rot_out must be [B, Hkv, {Tp}, d]")
-    if v_t_out is not None and tuple(v_t_out.shape) != (B, Hkv, d, Tp):
-        raise ValueError(f"v_t_out must be [B, Hkv, d, {Tp}]")
+    k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dt)
+    if k_rot_out is not None and tuple(k_rot_out.shape) != k_shape:
+        raise ValueError(f"k_rot_out must be {list(k_shape)}")
+    if v_t_out is not None and tuple(v_t_out.shape) != v_shape:
+        raise ValueError(f"v_t_out must be {list(v_shape)}")
     cap = 0
     if k_cache is not None:
         cap = k_cache.shape[2]
@@ -150,13 +166,13 @@ def plamo_kv_append(q, k, v, q_out, *, window: int, pos_offset: int, rope_table,
 
 def plamo_attn_prefill(q_rot, k_rot, v_t, out, *, window: int, pos_offset: int = 0,
                        softmax_scale: float | None = None, stream=None) -> None:
-    """q_rot [B,T,Hq,d], k_rot [B,Hkv,Tp,d], v_t [B,Hkv,d,Tp] -> out [B,T,Hq,d]."""
+    """q_rot [B,T,Hq,d], k_rot / v_t as prefill_operand_shapes -> out [B,T,Hq,d]."""
     dt = q_rot.dtype
     B, T, Hq, d = q_rot.shape
     Hkv = k_rot.shape[1]
-    Tp = plamo_prefill_padded_len(T)
-    if tuple(k_rot.shape) != (B, Hkv, Tp, d) or tuple(v_t.shape) != (B, Hkv, d, Tp):
-        raise ValueError(f"k_rot must be [B, Hkv, {Tp}, d] and v_t [B, Hkv, d, {Tp}]")
+    k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dt)
+    if tuple(k_rot.shape) != k_shape or tuple(v_t.shape) != v_shape:
+        raise ValueError(f"k_rot must be {list(k_shape)} and v_t {list(v_shape)}")
     if tuple(out.shape) != (B, T, Hq, d):
         raise ValueError("out must match q_rot")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)

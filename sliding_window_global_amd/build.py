@@ -21,6 +21,9 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["rope_table.hip", "append.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "abi.cpp"]
+# The bf16 prefill's softmax only ever sees finite or -inf scores: without NaN semantics
+# its running-max chain compiles to bare v_max3 (no input canonicalisation).
+EXTRA_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"]}
 
 ARCH = "gfx950"
 COMMON_FLAGS = [
@@ -45,7 +48,7 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
     res = subprocess.run(cmd, capture_output=True, text=True)

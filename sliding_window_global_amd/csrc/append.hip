@@ -15,6 +15,10 @@
 // half, so every rotation pair is lane-local and the norm is a reduction over the
 // group. V is staged through LDS to write the transposed prefill operand with
 // full rows.
+//
+// bf16 prefill operands are tiled by 64 keys, each tile 16 KiB in the order the prefill
+// kernel copies straight into LDS: K' tile = [16 dim chunks][64 keys][8 dims], V^T tile =
+// [8 key chunks][128 dims][8 keys]. fp32 operands are plain [Tp][d] and [d][Tp].
 #include "common.h"
 #include "kernels.h"
 
@@ -65,6 +69,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   constexpr int kLanesPerRow = kHalf / kVec;    // 8 (bf16) or 16 (fp32)
   constexpr int kRowsPerPass = 64 / kLanesPerRow;
   constexpr int kUnroll = 2;
+  constexpr bool kTiled = sizeof(E) == 2;      // bf16 prefill operands are tiled
   __shared__ __attribute__((aligned(16))) float2 zs[kTokBlock][kHalf];
 
   const int lane = threadIdx.x & 63;
@@ -165,10 +170,17 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
           y[e] = x0 * z.x - x1 * z.y;
           y[kVec + e] = x0 * z.y + x1 * z.x;
         }
-        E* dst = is_k ? k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t) * kHeadDim + c * kVec
-                      : q_out + off[u];
-        *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(y);
-        *reinterpret_cast<u32x4*>(dst + kHalf) = Io<E>::pack(y + kVec);
+        if (kTiled && is_k) {  // chunks c and c + 8 of key t within its tile
+          E* dst = k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t0) * kHeadDim +
+                   (c * kTokBlock + tt[u]) * kVec;
+          *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(y);
+          *reinterpret_cast<u32x4*>(dst + 8 * kTokBlock * kVec) = Io<E>::pack(y + kVec);
+        } else {
+          E* dst = is_k ? k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t) * kHeadDim + c * kVec
+                        : q_out + off[u];
+          *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(y);
+          *reinterpret_cast<u32x4*>(dst + kHalf) = Io<E>::pack(y + kVec);
+        }
       }
     }
   };
@@ -177,10 +189,17 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
 
   if (k_rot) {  // zero the padding rows T .. Tp-1 of this block
     for (int i = threadIdx.x; i < kTokBlock * (kHeadDim / kVec); i += kThreads) {
-      const long long t = t0 + i / (kHeadDim / kVec);
-      if (t >= a.T && t < a.Tp)
-        reinterpret_cast<u32x4*>(k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t) * kHeadDim)
-            [i % (kHeadDim / kVec)] = u32x4{0, 0, 0, 0};
+      if (kTiled) {  // i = chunk * 64 + key in tile
+        const long long t = t0 + i % kTokBlock;
+        if (t >= a.T && t < a.Tp)
+          reinterpret_cast<u32x4*>(k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t0) * kHeadDim)[i] =
+              u32x4{0, 0, 0, 0};
+      } else {
+        const long long t = t0 + i / (kHeadDim / kVec);
+        if (t >= a.T && t < a.Tp)
+          reinterpret_cast<u32x4*>(k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t) * kHeadDim)
+              [i % (kHeadDim / kVec)] = u32x4{0, 0, 0, 0};
+      }
     }
   }
 
@@ -217,12 +236,22 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
     }
     __syncthreads();
     constexpr int kTokChunks = kTokBlock / kVec;
-    for (int i = threadIdx.x; i < kHeadDim * kTokChunks; i += kThreads) {
-      const int cc = i / kTokChunks, tc = i % kTokChunks;
-      const long long t = t0 + tc * kVec;
-      if (t < a.Tp) {  // Tp is a multiple of 128, so a chunk is wholly inside or outside
-        const u32x4 w = *reinterpret_cast<const u32x4*>(&tile[cc * kTS + tc * kVec]);
-        *reinterpret_cast<u32x4*>(v_t + ((static_cast<long long>(b) * a.Hkv + kvh) * kHeadDim + cc) * a.Tp + t) = w;
+    if (kTiled) {
+      if (t0 < a.Tp) {  // Tp is a multiple of 128, so a tile is wholly inside or outside
+        u32x4* dst = reinterpret_cast<u32x4*>(v_t + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t0) * kHeadDim);
+        for (int i = threadIdx.x; i < kHeadDim * kTokChunks; i += kThreads) {  // i = key chunk * 128 + dim
+          const int cc = i % kHeadDim, tc = i / kHeadDim;
+          dst[i] = *reinterpret_cast<const u32x4*>(&tile[cc * kTS + tc * kVec]);
+        }
+      }
+    } else {
+      for (int i = threadIdx.x; i < kHeadDim * kTokChunks; i += kThreads) {
+        const int cc = i / kTokChunks, tc = i % kTokChunks;
+        const long long t = t0 + tc * kVec;
+        if (t < a.Tp) {  // Tp is a multiple of 128, so a chunk is wholly inside or outside
+          const u32x4 w = *reinterpret_cast<const u32x4*>(&tile[cc * kTS + tc * kVec]);
+          *reinterpret_cast<u32x4*>(v_t + ((static_cast<long long>(b) * a.Hkv + kvh) * kHeadDim + cc) * a.Tp + t) = w;
+        }
       }
     }
   }

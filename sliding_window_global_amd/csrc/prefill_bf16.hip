@@ -53,10 +53,12 @@ __device__ __forceinline__ int key_of_row(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-// LDS element offset of 16-byte chunk c of K' row r (16 chunks per row).
-__device__ __forceinline__ int k_chunk(int r, int c) { return (r * 16 + (c ^ (r & 15))) * 8; }
-// LDS element offset of 16-byte chunk c of V^T row d (8 chunks per row).
-__device__ __forceinline__ int v_chunk(int d, int c) { return (d * 8 + (c ^ ((d >> 1) & 7))) * 8; }
+// LDS element offset of 16-byte chunk c of K' row r (16 chunks per row): chunk-major, so
+// the operand reads of one MFMA cover consecutive 16-byte slots and the reads of the
+// different chunks differ by compile-time offsets.
+__device__ __forceinline__ int k_chunk(int r, int c) { return (c * BN + r) * 8; }
+// LDS element offset of 16-byte chunk c of V^T row d (8 chunks per row), chunk-major.
+__device__ __forceinline__ int v_chunk(int d, int c) { return (c * kHeadDim + d) * 8; }
 
 // kLocal: sliding-window layer (window > 0); otherwise the global causal layer.
 template <bool kLocal>
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int n = lane & 31;   // MFMA column = query row within the wave
   const int hl = lane >> 5;  // lane half
 
@@ -104,33 +106,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   const int kt_hi = last_row / BN;
   const int n_tiles = kt_hi - lo / BN + 1;
 
-  // Each wave moves 4 x 1 KiB of a tile: LDS chunk p = (wave*4 + i)*64 + lane receives
-  // the global chunk that the swizzle assigns to p.
-  // Per-lane 32-bit element offsets of the 4 chunks each lane moves per tile (a wave-
-  // uniform base plus these offsets lets the loads use a scalar base address).
-  int k_off[4], v_off[4];
+  // K' and V^T arrive tiled by 64 keys, each tile 16 KiB in exactly the LDS order below, so
+  // a tile is one contiguous copy: direct load g = wave*4 + i moves bytes 1024g .. +1023
+  // (lane l: 16 bytes at 1024g + 16l), a wave-uniform base plus a per-lane offset.
+  const uint32_t lane_off = static_cast<uint32_t>(lane) * 16;
+  auto issue = [&](const bf16_t* base, int step, bf16_t* buf) __attribute__((always_inline)) {
+    const char* src = reinterpret_cast<const char*>(base + static_cast<long long>(kt_hi - step) * kTileElems);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = (wave * 4 + i) * 64 + lane;
-    const int r = p >> 4, kc = (p & 15) ^ (r & 15);
-    k_off[i] = r * kHeadDim + kc * 8;
-    const int d = p >> 3, vc = (p & 7) ^ ((d >> 1) & 7);
-    v_off[i] = d * static_cast<int>(a.Tp) + vc * 8;
-  }
-  auto issue_k = [&](int step, bf16_t* buf) {
-    const bf16_t* src = kbase + static_cast<long long>(kt_hi - step) * BN * kHeadDim;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(src + k_off[i], buf + (wave * 4 + i) * 512, 16, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int g = wave * 4 + i;
+      __builtin_amdgcn_global_load_lds(src + g * 1024 + lane_off, buf + g * 512, 16, 0, 0);
+    }
   };
-  auto issue_v = [&](int step, bf16_t* buf) {
-    const bf16_t* src = vbase + (kt_hi - step) * BN;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(src + v_off[i], buf + (wave * 4 + i) * 512, 16, 0, 0);
-  };
+  auto issue_k = [&](int step, bf16_t* buf) __attribute__((always_inline)) { issue(kbase, step, buf); };
+  auto issue_v = [&](int step, bf16_t* buf) __attribute__((always_inline)) { issue(vbase, step, buf); };
 
   // ---- Q' fragment (MFMA B operand): lane holds dims s*16 + hl*8 .. +7 of its row ----
+  // Pre-multiplied by scale * log2(e), so that S comes out of the MFMA in exp2 units.
+  const float c = a.scale * 1.4426950408889634f;
   const int r0 = i0 + wave * 32;
   const int qrow = r0 + n;
   bf16x8 qf[8];
@@ -141,30 +134,30 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       u32x4 w = ok ? *reinterpret_cast<const u32x4*>(src + s * 16) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = pack_bf16x2(lo_bf16(w[i]) * c, hi_bf16(w[i]) * c);
       qf[s] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
-  // wave-uniform: does tile `step` hold any visible (row, key) pair for rows r0..r0+31?
-  auto visible = [&](int step) {
+  // wave-uniform: does tile `step` hold a masked pair for some row r0..r0+31? (A tile that
+  // lies wholly outside the wave's rows' windows is computed fully masked: the four waves
+  // of a block move through the tiles in step, so skipping it would not end the step
+  // sooner.)
+  auto needs_mask = [&](int step) __attribute__((always_inline)) {
     const int j0 = (kt_hi - step) * BN;
-    return (j0 <= r0 + 31) && (!kLocal || j0 + BN - 1 > r0 - a.window);
+    return (j0 + BN - 1 > r0) || (kLocal && r0 + 31 - j0 >= a.window);
   };
-  // S^T of one tile from K' buffer `buf` (MFMA rows in key_of_row order)
-  auto scores = [&](const bf16_t* kbuf, f32x16* sacc) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int r = kb * 32 + key_of_row(n);
-        const u32x4 w = *reinterpret_cast<const u32x4*>(kbuf + k_chunk(r, 2 * s + hl));
-        sacc[kb] = mfma32(__builtin_bit_cast(bf16x8, w), qf[s], sacc[kb]);
-      }
-    }
+
+  // MFMA operand i of one step: i < 16 is K' chunk (s = i/2, key block i%2) of the next
+  // tile's S^T = K' Q'^T; i >= 16 is V^T chunk (k-step (i-16)/4, d block (i-16)%4) of
+  // this tile's O^T += V^T P^T.
+  auto frag = [&](int i, const bf16_t* kbuf, const bf16_t* vbuf) __attribute__((always_inline)) {
+    if (i < 16)
+      return *reinterpret_cast<const u32x4*>(kbuf + k_chunk((i & 1) * 32 + key_of_row(n), i + hl - (i & 1)));
+    const int j = i - 16;
+    return *reinterpret_cast<const u32x4*>(vbuf + v_chunk((j & 3) * 32 + n, 2 * (j >> 2) + hl));
   };
 
   f32x16 oacc[4];
@@ -172,103 +165,157 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
+  // Running reference max of the lane's row in exp2 units (-inf until its first tile);
+  // S^T of a tile is produced already shifted by it (the MFMA accumulator starts at
+  // -m_run), so the softmax numerator is a bare exp2.
   float m_run = -INFINITY;
   float l_run = 0.f;
-  const float c = a.scale * 1.4426950408889634f;  // scores in the exp2 domain
+  constexpr int kDepth = 4;  // MFMA operands read ahead from LDS
 
-  // ---- prologue: K'(0), V^T(0), K'(1) in LDS; S(0) -----------------------------------
-  issue_k(0, ks0);
-  issue_v(0, vs0);
-  if (n_tiles > 1) issue_k(1, ks1);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
-  f32x16 s_a[2], s_b[2];  // S of the current and of the next tile, roles alternating
-  if (visible(0)) scores(ks0, s_a);
-  __syncthreads();  // step 0 refills ks0: every wave must be done reading K'(0)
-
-  // One step; `k_next`, `v_cur` are read, `k_fill`, `v_fill` receive direct loads.
-  auto run_step = [&](int step, const bf16_t* k_next, const bf16_t* v_cur, bf16_t* k_fill,
-                      bf16_t* v_fill, f32x16* s_cur, f32x16* s_next) {
-      // LDS holds K'(step+1) in ks[(step+1)&1] and V^T(step) in vs[step&1]; the buffers
-      // refilled here were last read before the previous barrier.
-      if (step + 2 < n_tiles) issue_k(step + 2, k_fill);
-      if (step + 1 < n_tiles) issue_v(step + 1, v_fill);
-      if (step + 1 < n_tiles && visible(step + 1)) scores(k_next, s_next);
-
-      if (visible(step)) {
-        const int j0 = (kt_hi - step) * BN;
-        const bool need_mask = (j0 + BN - 1 > r0) || (kLocal && r0 + 31 - j0 >= a.window);
-        if (need_mask) {
+  // One pipeline step: S^T(step+1) = K'(step+1) Q'^T (if kQK) on the matrix cores while
+  // the vector ALUs turn S^T(step) into P^T (if kPV); then O^T += V^T(step) P^T (if kPV)
+  // while the row maxima of S^T(step+1) are taken. `s_cur` holds S^T(step) shifted and
+  // masked; `s_next` receives S^T(step+1).
+  auto step_body = [&](auto QK, auto PV, int step, const bf16_t* kbuf, const bf16_t* vbuf,
+                       f32x16* s_cur, f32x16* s_next) __attribute__((always_inline)) {
+    constexpr bool kQK = decltype(QK)::value, kPV = decltype(PV)::value;
+    constexpr int i_first = kQK ? 0 : 16, i_last = kPV ? 32 : 16;
+    const float m_base = m_run == -INFINITY ? 0.f : m_run;
+    f32x16 init;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+    for (int e = 0; e < 16; ++e) init[e] = -m_base;
+
+    u32x4 fr[kDepth];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int key = j0 + kb * 32 + (e >> 3) * 16 + hl * 8 + (e & 7);
-              const bool ok = key <= qrow && (!kLocal || qrow - key < a.window);
-              if (!ok) s_cur[kb][e] = -INFINITY;
-            }
+    for (int i = i_first; i < i_first + kDepth; ++i) fr[i % kDepth] = frag(i, kbuf, vbuf);
+
+    // part A: 16 QK MFMAs; P^T words: pair j = keys 2j, 2j+1 of the lane's 32 (flat index
+    // f = kb*16 + e), word j of the B operand for k-step j/4
+    u32x4 pw[4];
+    float psum[4] = {0.f, 0.f, 0.f, 0.f};
+    float* sc = reinterpret_cast<float*>(s_cur);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (kQK) {
+        const int kb = i & 1, s = i >> 1;
+        s_next[kb] = mfma32(__builtin_bit_cast(bf16x8, fr[i % kDepth]), qf[s], s == 0 ? init : s_next[kb]);
+        if (i + kDepth < i_last) fr[i % kDepth] = frag(i + kDepth, kbuf, vbuf);
+      }
+      if (kPV) {
+        sc[2 * i] = fast_exp2(sc[2 * i]);
+        sc[2 * i + 1] = fast_exp2(sc[2 * i + 1]);
+        if (i >= 1) pw[(i - 1) >> 2][(i - 1) & 3] = pack_bf16x2(sc[2 * i - 2], sc[2 * i - 1]);
+        if (i >= 2) psum[(i - 2) & 3] = add_bf16x2(pw[(i - 2) >> 2][(i - 2) & 3], psum[(i - 2) & 3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (kPV) {
+      pw[3][3] = pack_bf16x2(sc[30], sc[31]);
+      psum[2] = add_bf16x2(pw[3][2], psum[2]);
+      psum[3] = add_bf16x2(pw[3][3], psum[3]);
+      l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+      // keep the P^T words computed here, under the QK MFMAs, rather than sunk past the
+      // mask branch below
+#pragma unroll
+      for (int u = 0; u < 4; ++u) asm volatile("" : "+v"(pw[u]));
+      asm volatile("" : "+v"(l_run));
+    }
+
+    // the last step has no next tile: its S^T is never used
+    const bool real_next = step + 1 < n_tiles;
+    if (kQK && real_next && needs_mask(step + 1)) {
+      // key k of the tile is visible to row qrow iff k <= qrow - j0 and, on local layers,
+      // k > qrow - j0 - window
+      const int dq = qrow - (kt_hi - step - 1) * BN - hl * 8;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int ko = kb * 32 + (e >> 3) * 16 + (e & 7);
+          const bool ok = ko <= dq && (!kLocal || ko > dq - a.window);
+          if (!ok) s_next[kb][e] = -INFINITY;
         }
-        float mx = s_cur[0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s_cur[kb][e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // Lazy rescaling: the running reference max only moves (and O, l are only rescaled)
-        // when some row of the wave gains more than 2^8 over it, so p stays <= 256.
-        const float mx_c = mx * c;
-        if (__builtin_amdgcn_ballot_w64(mx_c > m_run + kRescaleLog2) != 0) {  // wave-uniform
-          const float m_new = fmaxf(m_run, mx_c);
-          const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
-          l_run *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
-          m_run = m_new;
-        }
-        // a row whose keys so far are all masked has m_run = -inf and only -inf scores here
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) s_cur[kb][e] = fast_exp2(fmaf(s_cur[kb][e], c, -m_use));
+    }
 
-        // P^T as MFMA B operand: k-step u covers keys 16u..16u+15 = s_cur[u/2][(u%2)*8 ..+7].
-        // The row sum adds the same bf16-rounded p that enter the P V product.
-        bf16x8 pb[4];
-        float psum[4] = {0.f, 0.f, 0.f, 0.f};
+    // part B: 16 PV MFMAs; row max of S^T(step+1) over the second half
+    float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int kb = u >> 1, e0 = (u & 1) * 8;
-          u32x4 w;
+    for (int i = 16; i < 32; ++i) {
+      if (kPV) {
+        const int j = i - 16;
+        oacc[j & 3] = mfma32(__builtin_bit_cast(bf16x8, fr[i % kDepth]),
+                             __builtin_bit_cast(bf16x8, pw[j >> 2]), oacc[j & 3]);
+        if (i + kDepth < 32) fr[i % kDepth] = frag(i + kDepth, kbuf, vbuf);
+      }
+      if (kQK && (!kPV || i >= 24)) {
+        const int f = kPV ? (i - 24) * 4 : (i - 16) * 2;
+        const int cnt = kPV ? 4 : 2;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            w[i] = pack_bf16x2(s_cur[kb][e0 + 2 * i], s_cur[kb][e0 + 2 * i + 1]);
-            psum[i] = add_bf16x2(w[i], psum[i]);
-          }
-          pb[u] = __builtin_bit_cast(bf16x8, w);
-        }
-        l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(v_cur + v_chunk(dt * 32 + n, 2 * u + hl));
-            oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, w), pb[u], oacc[dt]);
-          }
+        for (int u = 0; u < cnt; u += 2) {
+          const float x = s_next[(f + u) >> 4][(f + u) & 15], y = s_next[(f + u + 1) >> 4][(f + u + 1) & 15];
+          if (((f + u) >> 1) & 1) mx1 = fmaxf(mx1, fmaxf(x, y));
+          else mx0 = fmaxf(mx0, fmaxf(x, y));
         }
       }
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    if (kQK) {
+      float mx = fmaxf(mx0, mx1);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      // Lazy rescaling: the reference max only moves (and O, l are only rescaled) when some
+      // row of the wave gains more than 2^8 over it, or on a row's first tile.
+      const bool first = m_run == -INFINITY;
+      if (real_next && __builtin_amdgcn_ballot_w64(mx > kRescaleLog2 || first) != 0) {  // wave-uniform
+        // first tile: the reference becomes the row max (a row with no visible key yet
+        // keeps -inf); later: it moves up by the gain, if any
+        const float bump = first ? (mx == -INFINITY ? 0.f : mx) : fmaxf(mx, 0.f);
+        const float alpha = first ? 0.f : fast_exp2(-bump);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s_next[kb][e] -= bump;
+        m_run = (first && mx == -INFINITY) ? -INFINITY : m_base + bump;
+      }
+    }
   };
+  using T1 = std::integral_constant<bool, true>;
+  using T0 = std::integral_constant<bool, false>;
+  // `k_fill`, `v_fill` receive K'(step+2) and V^T(step+1); `kbuf` holds K'(step+1) and
+  // `vbuf` V^T(step). The buffers refilled here were last read before the previous barrier.
+  auto run_step = [&](int step, const bf16_t* kbuf, const bf16_t* vbuf, bf16_t* k_fill, bf16_t* v_fill,
+                      f32x16* s_cur, f32x16* s_next) __attribute__((always_inline)) {
+    if (step + 2 < n_tiles) issue_k(step + 2, k_fill);
+    if (step + 1 < n_tiles) issue_v(step + 1, v_fill);
+    step_body(T1{}, T1{}, step, kbuf, vbuf, s_cur, s_next);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  };
+
+  // ---- K'(0) in LDS; S^T(0) while K'(1) and V^T(0) arrive; then steps 0 .. n_tiles-1 ----
+  issue_k(0, ks0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  f32x16 s_a[2], s_b[2];  // S^T of the current and of the next tile, roles alternating
+  if (n_tiles > 1) issue_k(1, ks1);
+  issue_v(0, vs0);
+  step_body(T1{}, T0{}, -1, ks0, vs1, s_b, s_a);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
   for (int step = 0; step < n_tiles; step += 2) {
     run_step(step, ks1, vs0, ks0, vs1, s_a, s_b);
     if (step + 1 < n_tiles) run_step(step + 1, ks0, vs1, ks1, vs0, s_b, s_a);
   }
 
   // ---- normalise and store: lane writes d = dt*32 + i*8 + hl*4 + 0..3 of its row ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+  const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
   if (qrow < a.T) {
     const float inv = 1.f / l_tot;
     bf16_t* dst = static_cast<bf16_t*>(a.out) +

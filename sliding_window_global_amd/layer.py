@@ -12,17 +12,17 @@ import math
 import torch
 
 from . import (plamo_attn_decode, plamo_attn_decode_workspace_bytes, plamo_attn_prefill,
-               plamo_kv_append, plamo_prefill_padded_len)
+               plamo_kv_append, prefill_operand_shapes)
 
 
 class PrefillBuffers:
     """Operands of one prefill: normalised/rotated Q, rotated K and transposed V."""
 
     def __init__(self, B, T, Hq, Hkv, d, dtype, device="cuda"):
-        Tp = plamo_prefill_padded_len(T)
+        k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dtype)
         self.q_rot = torch.empty((B, T, Hq, d), dtype=dtype, device=device)
-        self.k_rot = torch.empty((B, Hkv, Tp, d), dtype=dtype, device=device)
-        self.v_t = torch.empty((B, Hkv, d, Tp), dtype=dtype, device=device)
+        self.k_rot = torch.empty(k_shape, dtype=dtype, device=device)
+        self.v_t = torch.empty(v_shape, dtype=dtype, device=device)
         self.out = torch.empty((B, T, Hq, d), dtype=dtype, device=device)
 
 

@@ -82,3 +82,15 @@ def window_mean_closed_form(v, window):
     t = np.arange(T)
     lo = np.zeros(T, dtype=np.int64) if window == 0 else np.maximum(0, t - window + 1)
     return (csum[t + 1] - csum[lo]) / (t + 1 - lo)[:, None, None]
+
+
+def untile_k_rot(kr):
+    """bf16 K' operand [B, Hkv, Tp/64, d/8, 64, 8] (include/plamo_attn.h) -> [B, Hkv, Tp, d]."""
+    B, H, nt, nc, kt, w = kr.shape
+    return kr.transpose(0, 1, 2, 4, 3, 5).reshape(B, H, nt * kt, nc * w)
+
+
+def untile_v_t(vt):
+    """bf16 V^T operand [B, Hkv, Tp/64, 8, d, 8] (include/plamo_attn.h) -> [B, Hkv, d, Tp]."""
+    B, H, nt, nc, d, w = vt.shape
+    return vt.transpose(0, 1, 4, 2, 3, 5).reshape(B, H, d, nt * nc * w)

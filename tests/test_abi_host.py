@@ -8,6 +8,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from sliding_window_global_amd import _lib
@@ -162,3 +163,22 @@ def test_rope_init_validation(lib):
     assert lib.plamo_rope_table_init(FAKE, need, 1000, 128, ctypes.byref(bad_beta), None) == INVALID
     assert lib.plamo_rope_table_init(FAKE, need, 1000, 128, ctypes.byref(bad_theta), None) == INVALID
     assert lib.plamo_rope_table_init(FAKE, need, 0, 128, ctypes.byref(r), None) == INVALID
+
+
+def test_tiled_operand_helpers_invert_documented_layout():
+    """The test-side untiling of the bf16 prefill operands follows the element order stated in
+    include/plamo_attn.h, written out index by index here."""
+    from helpers import untile_k_rot, untile_v_t
+    rng = np.random.default_rng(5)
+    B, H, Tp, d = 2, 3, 128, 16
+    k = rng.standard_normal((B, H, Tp, d))
+    vt = rng.standard_normal((B, H, d, Tp))
+    nt = Tp // 64
+    k_tiled = np.empty((B, H, nt, d // 8, 64, 8))
+    v_tiled = np.empty((B, H, nt, 8, d, 8))
+    for t in range(Tp):
+        for j in range(d):
+            k_tiled[:, :, t // 64, j // 8, t % 64, j % 8] = k[:, :, t, j]
+            v_tiled[:, :, t // 64, (t % 64) // 8, j, t % 8] = vt[:, :, j, t]
+    assert np.array_equal(untile_k_rot(k_tiled), k)
+    assert np.array_equal(untile_v_t(v_tiled), vt)

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from helpers import (TOL_BF16, TOL_F32, assert_parity, kept_slots, oracle_decode_one,
-                     oracle_prefill, window_mean_closed_form)
+                     oracle_prefill, window_mean_closed_form, untile_k_rot, untile_v_t)
 from oracle import apply_rope, offset_rms_norm, rope_frequencies
 from synthetic import Draw
 from synthetic.workloads import (BATCHED_DECODE, GLOBAL_PREFILL, LOCAL_PREFILL, PERIOD_DECODE,
@@ -91,10 +91,10 @@ def test_kv_append_intermediates(window, pos_offset, T):
     cap = window if window else pos_offset + T
     kc = torch.full((B, Hkv, cap, d), float("nan"), dtype=torch.bfloat16, device="cuda")
     vc = torch.full_like(kc, float("nan"))
-    Tp = swg.plamo_prefill_padded_len(T)
     q_out = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device="cuda")
-    k_rot = torch.full((B, Hkv, Tp, d), float("nan"), dtype=torch.bfloat16, device="cuda")
-    v_t = torch.full((B, Hkv, d, Tp), float("nan"), dtype=torch.bfloat16, device="cuda")
+    k_shape, v_shape = swg.prefill_operand_shapes(B, T, Hkv, d, torch.bfloat16)
+    k_rot = torch.full(k_shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    v_t = torch.full(v_shape, float("nan"), dtype=torch.bfloat16, device="cuda")
     kept = pos_offset if window == 0 else min(pos_offset, window - 1)
     swg.plamo_kv_append(dev(q), dev(k), dev(v), q_out, window=window, pos_offset=pos_offset,
                         rope_table=rope_table(rope, 40000), q_norm_w=dev(wq), k_norm_w=dev(wk),
@@ -107,10 +107,10 @@ def test_kv_append_intermediates(window, pos_offset, T):
     q_ref = np.stack([apply_rope(qn[b], pos, omega, amp) for b in range(B)])
     assert_parity(host(q_out), q_ref, TOL_BF16, "q_out")
     k_ref = np.stack([apply_rope(kn[b], pos, omega, amp) for b in range(B)])
-    kr = host(k_rot)
+    kr = untile_k_rot(host(k_rot))
     assert_parity(kr[:, :, :T].transpose(0, 2, 1, 3), k_ref, TOL_BF16, "k_rot")
     assert np.all(kr[:, :, T:] == 0)
-    vt = host(v_t)
+    vt = untile_v_t(host(v_t))
     assert np.array_equal(vt[..., :T].transpose(0, 3, 1, 2), v)  # exact copy
     assert np.all(vt[..., T:] == 0)
     kch, vch = host(kc), host(vc)
