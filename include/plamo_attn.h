@@ -154,7 +154,8 @@ PLAMO_API int plamo_attn_prefill(int dtype, const void* q_rot, const void* k_rot
  *
  * q_rot [B, 1, Hq, d]; k_cache, v_cache [B, Hkv, cap, d] (bf16); out [B, 1, Hq, d].
  * workspace: device scratch of at least plamo_attn_decode_workspace_bytes(...)
- * bytes (split-K partial results); contents on entry do not matter.
+ * bytes (split-K partial results); contents on entry do not matter. When that
+ * size is 0 (one key range per sequence and KV head) workspace may be NULL.
  * dtype must be PLAMO_BF16; T must be 1.
  * ------------------------------------------------------------------------- */
 PLAMO_API size_t plamo_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int window,

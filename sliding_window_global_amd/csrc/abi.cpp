@@ -215,7 +215,7 @@ int plamo_attn_decode(int dtype, const void* q_rot, const void* k_cache, const v
   if (covered < S) return fail(PLAMO_ERR_WORKSPACE, "rope table does not cover positions < kept + 1");
   const plamo::DecodePlan plan = plamo::plan_decode(B, Hkv, S);
   const size_t need = plamo::decode_workspace_bytes(B, Hq, plan);
-  if (!workspace || workspace_bytes < need) return fail(PLAMO_ERR_WORKSPACE, "workspace too small");
+  if (need > 0 && (!workspace || workspace_bytes < need)) return fail(PLAMO_ERR_WORKSPACE, "workspace too small");
   if (static_cast<long long>(B) * Hq > 0x7fffffffLL) return fail(PLAMO_ERR_UNSUPPORTED, "grid too large");
 
   plamo::DecodeArgs a;

@@ -8,15 +8,21 @@
 // once for the whole group (the read volume of §2.3: 4 B Hkv d A bytes).
 //
 // Decomposition: block = (split, KV head, sequence), 4 waves; a split is a contiguous
-// range of renumbered keys, a multiple of 64. Per 64-key tile, K and V rows are loaded
-// with 16-byte coalesced loads (prefetched one tile ahead), staged in LDS, and each wave
-// takes 16 keys:
+// range of renumbered keys, a multiple of 64 long, cut into 64-key tiles. Wave w owns
+// keys 16w .. 16w+15 of every tile and streams them on its own, without block barriers:
+//   K rows   global -> registers, already in the MFMA operand layout (4 x 16 B per lane),
+//   V rows   global -> LDS by direct loads (rows padded to 272 B: the transposed operand
+//            reads below are free of bank conflicts),
+//   rope     the tile's coarse factor row global -> LDS by one direct load,
+// three sub-tiles per wave in flight or in use (a ring unrolled by three).
 //   S^T[16 keys][16 heads] = K'[16][128] Q'^T  (v_mfma_f32_16x16x32_bf16; heads padded to 16)
 //   O^T[128 d][16 heads]  += V^T[128][16] P^T   (v_mfma_f32_16x16x16_bf16)
 // Each lane rotates its key's 16 pairs in registers: the fine rope factor of its key is
 // fixed for the whole loop (tile starts are multiples of 64), the coarse row comes with
-// the tile. The 4 waves' partial softmax states merge in LDS; a second kernel merges the
-// splits in a fixed order (deterministic, no atomics).
+// the tile. The softmax reference max moves lazily (only when a head's score exceeds it
+// by 2^8). The 4 waves' partial states merge in LDS; with one split the block writes the
+// output, otherwise a second kernel merges the splits in a fixed order (deterministic,
+// no atomics).
 #include "common.h"
 #include "kernels.h"
 
@@ -25,31 +31,40 @@ namespace plamo {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 64;
-constexpr int KS = kHeadDim + 8;  // LDS row stride (elements): 272 B
+constexpr int kWaves = kThreads / 64;
+constexpr int kTile = 64;                  // keys per tile = kWaves x kSub
+constexpr int kSub = 16;                   // keys per wave per tile
 constexpr int kMaxGroup = 16;
-constexpr int kPartial = kHeadDim + 2;  // acc[128], m, l
-constexpr int kMaxSplit = 256;         // key ranges per (sequence, KV head)
-constexpr long long kMinChunk = 256;   // keys per range, at least
+constexpr int kPartial = kHeadDim + 2;     // acc[128], m, l
+constexpr int kMaxSplit = 256;             // key ranges per (sequence, KV head)
+constexpr long long kMinChunk = 256;       // keys per range, at least
+constexpr int kVRow = kHeadDim + 8;        // padded V row in LDS (elements): 272 B
+constexpr int kVChunks = kSub * kVRow / 8; // 16-byte slots of one V sub-tile: 272
+constexpr int kVLoads = (kVChunks + 63) / 64;  // direct loads per V sub-tile: 5
+constexpr int kVSlot = kVLoads * 64 * 8;   // elements reserved per V sub-tile
+constexpr float kRescaleLog2 = 8.f;        // lazy-rescale threshold (log2 units)
+constexpr int kLoadsPerIssue = 4 + kVLoads + 1;  // K rows, V rows, coarse row
 
-struct DecTile {
-  u32x4 k[4];
-  u32x4 v[4];
-  float4 cr;  // 16 B of the coarse rope row (threads 0..31)
-};
+// s_waitcnt vmcnt(n), expcnt / lgkmcnt left alone (gfx9 encoding: vmcnt bits 3:0, 15:14)
+constexpr unsigned wait_vmcnt(int n) { return 0x0F70u | (n & 15) | ((n >> 4) << 14); }
 
-__device__ __forceinline__ long long slot_of(long long n, int window) {
-  return window == 0 ? n : n % window;
-}
+// Cache addressing: contiguous (global layer), ring of W >= 64 slots (at most one wrap per
+// 64-key tile), ring of W < 64 slots.
+enum CacheMode { kContiguous = 0, kRing = 1, kSmallRing = 2 };
 
+template <int kMode>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t ks[2][kTile * KS];
-  __shared__ __attribute__((aligned(16))) bf16_t vs[2][kTile * KS];
-  __shared__ __attribute__((aligned(16))) float2 cs[2][kHalf];
+  // three ring slots, separate LDS objects so that reads of one slot never wait for the
+  // direct loads in flight into the others
+  __shared__ __attribute__((aligned(16))) bf16_t vs0[kWaves][kVSlot];
+  __shared__ __attribute__((aligned(16))) bf16_t vs1[kWaves][kVSlot];
+  __shared__ __attribute__((aligned(16))) bf16_t vs2[kWaves][kVSlot];
+  __shared__ __attribute__((aligned(16))) float2 cs0[kWaves][2 * kHalf];
+  __shared__ __attribute__((aligned(16))) float2 cs1[kWaves][2 * kHalf];
+  __shared__ __attribute__((aligned(16))) float2 cs2[kWaves][2 * kHalf];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m16 = lane & 15;  // MFMA row/col index within 16
   const int g = lane >> 4;    // lane group 0..3
   const int split = blockIdx.x;
@@ -59,6 +74,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
 
   const long long s_begin = static_cast<long long>(split) * a.plan.chunk;
   const long long s_end = min(a.S, s_begin + a.plan.chunk);
+  const int n_tiles = static_cast<int>((s_end - s_begin + kTile - 1) / kTile);
   const bf16_t* __restrict__ kc =
       static_cast<const bf16_t*>(a.k_cache) + (static_cast<long long>(b) * a.Hkv + kvh) * a.cap * kHeadDim;
   const bf16_t* __restrict__ vc =
@@ -74,187 +90,238 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int d0 = (s >> 1) * kHalf + g * 16 + (s & 1) * 8;
-      u32x4 w = ok ? *reinterpret_cast<const u32x4*>(src + d0) : u32x4{0, 0, 0, 0};
+      u32x4 w = *reinterpret_cast<const u32x4*>(src + d0);
+      if (!ok) w = u32x4{0, 0, 0, 0};
       qf[s] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
-  // ---- fine rope factors of this lane's key (position & 63 is fixed) -----------------
-  const int key_in_tile = wave * 16 + m16;
+  // ---- fine rope factors of this lane's key (its position & 63 is fixed) -------------
+  const int key_in_tile = wave * kSub + m16;
   float2 fine[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) fine[e] = a.rope[key_in_tile * kHalf + g * 16 + e];
+  // Wait for Q' and the fine factors here, once: the stream below keeps direct loads in
+  // flight, and a use of these inside the loop would otherwise wait for all of them.
+#pragma unroll
+  for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(qf[s]));
+#pragma unroll
+  for (int e = 0; e < 16; ++e) asm volatile("" : "+v"(fine[e].x), "+v"(fine[e].y));
+
+  // ---- per-lane pieces of the loads ---------------------------------------------------
+  // V direct load i, lane l fills padded slot p = 64 i + l: row p / 17, chunk p % 17 (the
+  // pad chunk 16 and the slots past 16 rows copy a chunk of the last row, never read).
+  int v_row[kVLoads], v_col[kVLoads];
+#pragma unroll
+  for (int i = 0; i < kVLoads; ++i) {
+    const int p = 64 * i + lane;
+    v_row[i] = min(p / 17, kSub - 1);
+    v_col[i] = min(p % 17, 15);
+  }
+  // Issue the loads of this wave's keys of the next tile into a K register set, a V slot
+  // and a coarse-row slot. Tiles are issued in order 0, 1, 2, ...; past the end the last
+  // tile is issued again (the same count of loads stays in flight at every step), and keys
+  // past s_end read the last key (their p is zero). The cache slot of renumbered key
+  // tb + j is s0 + j with s0 = (base + tb) mod W kept per tile (one wrap at most when
+  // W >= 64), or base + tb + j on global layers.
+  int t_issue = 0;
+  long long tb_issue = s_begin;
+  int s0 = kMode != kContiguous ? static_cast<int>((a.base + s_begin) % a.window) : 0;
+  auto cache_row = [&](int j) __attribute__((always_inline)) {
+    j = min(j, static_cast<int>(s_end - 1 - tb_issue));
+    if (kMode == kContiguous) return a.base + tb_issue + j;
+    int sl = s0 + j;
+    if (kMode == kRing) sl -= sl >= a.window ? a.window : 0;
+    else sl %= a.window;
+    return static_cast<long long>(sl);
+  };
+  auto issue = [&](u32x4* kw, bf16_t* vslot, float2* cslot) __attribute__((always_inline)) {
+    {
+      const bf16_t* row = kc + cache_row(key_in_tile) * kHeadDim;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kw[s] = *reinterpret_cast<const u32x4*>(row + (s >> 1) * kHalf + g * 16 + (s & 1) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < kVLoads; ++i) {
+      // (the address goes through a named pointer: passing the lambda call straight into
+      // the builtin drops this kernel's host-side launch stub)
+      const bf16_t* src = vc + cache_row(wave * kSub + v_row[i]) * kHeadDim + v_col[i] * 8;
+      __builtin_amdgcn_global_load_lds(src, vslot + i * 512, 16, 0, 0);
+    }
+    // coarse row of the tile (64 pairs, 512 B), copied twice over the 64 lanes
+    const float2* crow = a.rope + (kRopeFine + (tb_issue >> 6)) * kHalf + (lane & 31) * 2;
+    __builtin_amdgcn_global_load_lds(crow, cslot, 16, 0, 0);
+    if (t_issue + 1 < n_tiles) {
+      ++t_issue;
+      tb_issue += kTile;
+      if (kMode == kRing) {
+        s0 += kTile;
+        s0 -= s0 >= a.window ? a.window : 0;
+      } else if (kMode == kSmallRing) {
+        s0 = (s0 + kTile) % a.window;
+      }
+    }
+  };
 
   f32x4 oacc[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;  // reference max (log2 units) and row sum of head m16
   const float c = a.scale * 1.4426950408889634f;
 
-  auto load = [&](DecTile& r, long long tb) {
+  auto compute = [&](int t, const u32x4* kw, const bf16_t* vslot, const float2* cslot)
+      __attribute__((always_inline)) {
+    const long long key0 = s_begin + static_cast<long long>(t) * kTile + wave * kSub;
+    if (key0 >= s_end) return;  // wave-uniform: no key of this wave in the tile
+    // K': rotate the lane's 16 pairs, pack to bf16 in the A-operand layout
+    bf16x8 kf[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ch = tid + kThreads * i;
-      const int row = ch >> 4, col = ch & 15;
-      const long long s = tb + row;
-      if (s < s_end) {
-        const long long off = slot_of(a.base + s, a.window) * kHeadDim + col * 8;
-        r.k[i] = *reinterpret_cast<const u32x4*>(kc + off);
-        r.v[i] = *reinterpret_cast<const u32x4*>(vc + off);
-      } else {
-        r.k[i] = u32x4{0, 0, 0, 0};
-        r.v[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-    if (tid < 32)
-      r.cr = reinterpret_cast<const float4*>(a.rope + (kRopeFine + (tb >> 6)) * kHalf)[tid];
-  };
-  auto store = [&](const DecTile& r, int buf) {
+    for (int hs = 0; hs < 2; ++hs) {  // hs: slices (hs, hs+2) hold pairs 16g + 8hs + e
+      u32x4 lo_w, hi_w;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ch = tid + kThreads * i;
-      const int row = ch >> 4, col = ch & 15;
-      *reinterpret_cast<u32x4*>(&ks[buf][row * KS + col * 8]) = r.k[i];
-      *reinterpret_cast<u32x4*>(&vs[buf][row * KS + col * 8]) = r.v[i];
-    }
-    if (tid < 32) reinterpret_cast<float4*>(cs[buf])[tid] = r.cr;
-  };
-
-  // Software pipeline: two register sets alternate so that two tiles are in flight
-  // while the LDS copy of the current one is consumed.
-  auto compute = [&](int buf, long long tb) {
-    const long long wave_key0 = tb + wave * 16;
-    if (wave_key0 < s_end) {  // wave-uniform
-      // K' rows: lane reads its key's 4 x 8 dims, rotates its 16 pairs, packs to bf16
-      const bf16_t* krow = &ks[buf][key_in_tile * KS];
-      u32x4 kw[4];
+      for (int e2 = 0; e2 < 4; ++e2) {
+        float ra[2], rb[2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int d0 = (s >> 1) * kHalf + g * 16 + (s & 1) * 8;
-        kw[s] = *reinterpret_cast<const u32x4*>(krow + d0);
-      }
-      bf16x8 kf[4];
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {  // hs: slices (hs, hs+2) hold pairs 16g + 8hs + e
-        u32x4 lo_w, hi_w;
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          float ra[2], rb[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int e = e2 * 2 + u;
-            const float x0 = u ? hi_bf16(kw[hs][e2]) : lo_bf16(kw[hs][e2]);
-            const float x1 = u ? hi_bf16(kw[hs + 2][e2]) : lo_bf16(kw[hs + 2][e2]);
-            const float2 cr = cs[buf][g * 16 + hs * 8 + e];
-            const float2 f = fine[hs * 8 + e];
-            const float zx = cr.x * f.x - cr.y * f.y;
-            const float zy = cr.x * f.y + cr.y * f.x;
-            ra[u] = x0 * zx - x1 * zy;
-            rb[u] = x0 * zy + x1 * zx;
-          }
-          lo_w[e2] = pack_bf16x2(ra[0], ra[1]);
-          hi_w[e2] = pack_bf16x2(rb[0], rb[1]);
+        for (int u = 0; u < 2; ++u) {
+          const int e = e2 * 2 + u;
+          const float x0 = u ? hi_bf16(kw[hs][e2]) : lo_bf16(kw[hs][e2]);
+          const float x1 = u ? hi_bf16(kw[hs + 2][e2]) : lo_bf16(kw[hs + 2][e2]);
+          const float2 cr = cslot[g * 16 + hs * 8 + e];
+          const float2 f = fine[hs * 8 + e];
+          const float zx = cr.x * f.x - cr.y * f.y;
+          const float zy = cr.x * f.y + cr.y * f.x;
+          ra[u] = x0 * zx - x1 * zy;
+          rb[u] = x0 * zy + x1 * zx;
         }
-        kf[hs] = __builtin_bit_cast(bf16x8, lo_w);
-        kf[hs + 2] = __builtin_bit_cast(bf16x8, hi_w);
+        lo_w[e2] = pack_bf16x2(ra[0], ra[1]);
+        hi_w[e2] = pack_bf16x2(rb[0], rb[1]);
       }
-      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+      kf[hs] = __builtin_bit_cast(bf16x8, lo_w);
+      kf[hs + 2] = __builtin_bit_cast(bf16x8, hi_w);
+    }
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], sacc, 0, 0, 0);
+    for (int s = 0; s < 4; ++s) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], sacc, 0, 0, 0);
 
-      // S^T layout: lane holds head m16, keys wave_key0 + 4g + i
-      float mx = -INFINITY;
+    // S^T layout: lane holds head m16, keys key0 + 4g + i
+    float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const long long key = wave_key0 + 4 * g + i;
-        if (key >= s_end) sacc[i] = -INFINITY;
-        mx = fmaxf(mx, sacc[i]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx * c);  // finite: key wave_key0 is valid
-      const float alpha = fast_exp2(m_run - m_new);
-      float p[4];
-      float psum = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      sacc[i] *= c;
+      if (key0 + 4 * g + i >= s_end) sacc[i] = -INFINITY;
+      mx = fmaxf(mx, sacc[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // finite: key key0 is valid
+    // Lazy rescaling: the reference only moves when a head gains more than 2^8 over it.
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2) != 0) {  // wave-uniform
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile
+      l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = fast_exp2(sacc[i] * c - m_new);
-        psum += p[i];
-      }
-      l_run = l_run * alpha + psum;
+      for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
       m_run = m_new;
-      const u32x2 pw = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-      const s16x4 pb = __builtin_bit_cast(s16x4, pw);
+    }
+    u32x2 pw;
+    pw[0] = pack_bf16x2(fast_exp2(sacc[0] - m_run), fast_exp2(sacc[1] - m_run));
+    pw[1] = pack_bf16x2(fast_exp2(sacc[2] - m_run), fast_exp2(sacc[3] - m_run));
+    l_run = add_bf16x2(pw[1], add_bf16x2(pw[0], l_run));  // the same bf16 p as P V
+    const s16x4 pb = __builtin_bit_cast(s16x4, pw);
 
-      // V^T fragments: d = 16dt + m16, keys wave_key0 + 4g + i (row-major V in LDS)
-      const bf16_t* vrow = &vs[buf][(wave * 16 + 4 * g) * KS + m16];
+    // V^T fragments: d = 16dt + m16, keys 4g + i of the sub-tile (padded rows in LDS)
+    const bf16_t* vrow = vslot + (4 * g) * kVRow + m16;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        oacc[dt] *= alpha;
-        const uint32_t v01 = static_cast<uint32_t>(vrow[dt * 16]) |
-                             (static_cast<uint32_t>(vrow[KS + dt * 16]) << 16);
-        const uint32_t v23 = static_cast<uint32_t>(vrow[2 * KS + dt * 16]) |
-                             (static_cast<uint32_t>(vrow[3 * KS + dt * 16]) << 16);
-        const s16x4 va = __builtin_bit_cast(s16x4, u32x2{v01, v23});
-        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[dt], 0, 0, 0);
-      }
+    for (int dt = 0; dt < 8; ++dt) {
+      s16x4 va;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) va[i] = static_cast<short>(vrow[i * kVRow + dt * 16]);
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[dt], 0, 0, 0);
     }
   };
 
-  const int n_tiles = static_cast<int>((s_end - s_begin + kTile - 1) / kTile);
-  DecTile ra, rb;
-  load(ra, s_begin);
-  if (n_tiles > 1) load(rb, s_begin + kTile);
-  store(ra, 0);
-  __syncthreads();
-  for (int it = 0; it < n_tiles; it += 2) {
-    const long long tb = s_begin + static_cast<long long>(it) * kTile;
-    if (it + 2 < n_tiles) load(ra, tb + 2 * kTile);
-    compute(0, tb);
-    if (it + 1 < n_tiles) store(rb, 1);
-    __syncthreads();
-    if (it + 1 >= n_tiles) break;
-    if (it + 3 < n_tiles) load(rb, tb + 3 * kTile);
-    compute(1, tb + kTile);
-    if (it + 2 < n_tiles) store(ra, 0);
-    __syncthreads();
+  // ---- three sub-tiles per wave: compute t while t+1, t+2 land ------------------------
+  u32x4 k0[4], k1[4], k2[4];
+  bf16_t* const v0 = vs0[wave];
+  bf16_t* const v1 = vs1[wave];
+  bf16_t* const v2 = vs2[wave];
+  float2* const c0 = cs0[wave];
+  float2* const c1 = cs1[wave];
+  float2* const c2 = cs2[wave];
+  issue(k0, v0, c0);  // tile 0
+  issue(k1, v1, c1);  // tile 1
+  // Before computing tile t, an explicit wait leaves the loads of the tiles issued after it
+  // in flight (the compiler's own waits cannot follow the ring across loop iterations).
+  constexpr unsigned kTwoBehind = wait_vmcnt(2 * kLoadsPerIssue);
+  constexpr unsigned kOneBehind = wait_vmcnt(kLoadsPerIssue);
+  int t = 0;
+  for (; t + 3 <= n_tiles; t += 3) {
+    issue(k2, v2, c2);  // tile t + 2
+    __builtin_amdgcn_s_waitcnt(kTwoBehind);
+    compute(t, k0, v0, c0);
+    issue(k0, v0, c0);  // tile t + 3
+    __builtin_amdgcn_s_waitcnt(kTwoBehind);
+    compute(t + 1, k1, v1, c1);
+    issue(k1, v1, c1);  // tile t + 4
+    __builtin_amdgcn_s_waitcnt(kTwoBehind);
+    compute(t + 2, k2, v2, c2);
   }
+  if (t < n_tiles) {
+    __builtin_amdgcn_s_waitcnt(kOneBehind);
+    compute(t, k0, v0, c0);
+  }
+  if (t + 1 < n_tiles) {
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    compute(t + 1, k1, v1, c1);
+  }
+  // the repeated tiles past the end may still be landing in LDS
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
 
-  // ---- merge the 4 waves' states in LDS (reusing the K tile buffers) ----------------
+  // ---- merge the 4 waves' states in LDS (reusing the V slots) -------------------------
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  float* red = reinterpret_cast<float*>(&ks[0][0]);  // [4][16][128] acc, then m, l
-  float* red_m = red + 4 * kMaxGroup * kHeadDim;
-  float* red_l = red_m + 4 * kMaxGroup;
+  // [16 heads][128] accumulators of waves 0, 1 in vs0 and of waves 2, 3 in vs1; m, l in cs0, cs1
+  static_assert(sizeof(vs0) >= 2 * kMaxGroup * kHeadDim * sizeof(float), "merge buffer");
+  auto red_of = [&](int w) __attribute__((always_inline)) {
+    return reinterpret_cast<float*>(w < 2 ? &vs0[0][0] : &vs1[0][0]) + (w & 1) * kMaxGroup * kHeadDim;
+  };
+  float* red_m = reinterpret_cast<float*>(&cs0[0][0]);
+  float* red_l = reinterpret_cast<float*>(&cs1[0][0]);
+  {
+    float* mine = red_of(wave);
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      red[(wave * kMaxGroup + m16) * kHeadDim + dt * 16 + 4 * g + i] = oacc[dt][i];
+      for (int i = 0; i < 4; ++i) mine[m16 * kHeadDim + dt * 16 + 4 * g + i] = oacc[dt][i];
+  }
   if (g == 0) {
     red_m[wave * kMaxGroup + m16] = m_run;
     red_l[wave * kMaxGroup + m16] = l_run;
   }
   __syncthreads();
-  float* ws = a.ws;
-  for (int idx = tid; idx < G * kHeadDim; idx += kThreads) {
+  const bool single = a.plan.n_split == 1;
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
     const int h = idx / kHeadDim, d = idx % kHeadDim;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w * kMaxGroup + h]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w * kMaxGroup + h]);
     float acc = 0.f, l = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float sc = fast_exp2(red_m[w * kMaxGroup + h] - M);
-      acc += sc * red[(w * kMaxGroup + h) * kHeadDim + d];
+    for (int w = 0; w < kWaves; ++w) {
+      const float sc = fast_exp2(red_m[w * kMaxGroup + h] - M);  // 0 for a wave with no key
+      acc += sc * red_of(w)[h * kHeadDim + d];
       l += sc * red_l[w * kMaxGroup + h];
     }
-    float* dst = ws + ((static_cast<long long>(b) * a.Hq + kvh * G + h) * a.plan.n_split + split) * kPartial;
-    dst[d] = acc;
-    if (d == 0) {
-      dst[kHeadDim] = M;
-      dst[kHeadDim + 1] = l;
+    const long long bh = static_cast<long long>(b) * a.Hq + kvh * G + h;
+    if (single) {
+      static_cast<bf16_t*>(a.out)[bh * kHeadDim + d] = f32_to_bf16(acc / l);
+    } else {
+      float* dst = a.ws + (bh * a.plan.n_split + split) * kPartial;
+      dst[d] = acc;
+      if (d == 0) {
+        dst[kHeadDim] = M;
+        dst[kHeadDim + 1] = l;
+      }
     }
   }
 }
@@ -296,10 +363,10 @@ __global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(const float* _
 }  // namespace
 
 DecodePlan plan_decode(int B, int Hkv, long long S) {
-  // Aim for ~2048 blocks (8 per CU) with at least kMinChunk keys each and at most
-  // kMaxSplit ranges per (sequence, KV head).
+  // Aim for ~512 blocks (2 per CU, one wave per SIMD each) with at least kMinChunk keys
+  // each and at most kMaxSplit ranges per (sequence, KV head).
   const long long pairs = static_cast<long long>(B) * Hkv;
-  const long long target_blocks = 2048;
+  const long long target_blocks = 512;
   long long n = (target_blocks + pairs - 1) / pairs;
   const long long by_min_chunk = (S + kMinChunk - 1) / kMinChunk;
   if (n > by_min_chunk) n = by_min_chunk;
@@ -314,14 +381,21 @@ DecodePlan plan_decode(int B, int Hkv, long long S) {
 }
 
 size_t decode_workspace_bytes(int B, int Hq, const DecodePlan& plan) {
+  // one split writes the output directly
+  if (plan.n_split == 1) return 0;
   return static_cast<size_t>(B) * Hq * plan.n_split * kPartial * sizeof(float);
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_split_kernel, dim3(a.plan.n_split, a.Hkv, a.B), dim3(kThreads), 0,
-                     stream, a);
+  const dim3 grid(a.plan.n_split, a.Hkv, a.B);
+  if (a.window == 0)
+    hipLaunchKernelGGL(decode_split_kernel<kContiguous>, grid, dim3(kThreads), 0, stream, a);
+  else if (a.window >= kTile)
+    hipLaunchKernelGGL(decode_split_kernel<kRing>, grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<kSmallRing>, grid, dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.plan.n_split == 1) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.Hq), dim3(kHeadDim), 0, stream, a.ws,
                      static_cast<bf16_t*>(a.out), a.plan.n_split);
   return hipGetLastError();

@@ -66,8 +66,10 @@ def test_pure_host_helpers(lib):
 
 def test_decode_workspace_sizes(lib):
     # a workspace holds (acc[128], m, l) fp32 per (sequence, query head, split)
-    n = lib.plamo_attn_decode_workspace_bytes(64, 64, 8, 128, 0, 32767)
-    assert n > 0 and n % (130 * 4 * 64 * 64) == 0
+    n = lib.plamo_attn_decode_workspace_bytes(8, 64, 8, 128, 0, 131071)
+    assert n > 0 and n % (130 * 4 * 8 * 64) == 0 and n // (130 * 4 * 8 * 64) > 1
+    # 512 (sequence, KV head) pairs fill the GPU with one key range each: no split state
+    assert lib.plamo_attn_decode_workspace_bytes(64, 64, 8, 128, 0, 32767) == 0
     assert lib.plamo_attn_decode_workspace_bytes(64, 64, 8, 96, 0, 10) == 0  # d != 128
     assert lib.plamo_attn_decode_workspace_bytes(0, 64, 8, 128, 0, 10) == 0
 
