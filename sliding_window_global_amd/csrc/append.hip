@@ -111,9 +111,12 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
 
   // One pass normalises and rotates kRowsPerPass rows per wave (kUnroll passes in flight).
   // is_k: row r is token t0 + r of the K head; else row r is (token r / G, head r % G).
-  auto rows = [&](const E* __restrict__ src, int n_rows, bool is_k) {
+  // Row passes start at wave `first`, so that with few rows (a decode step) the Q rows, the
+  // K rows and the V copy below run on different waves at the same time.
+  auto rows = [&](const E* __restrict__ src, int n_rows, bool is_k, int first) {
     const float* g = is_k ? gk : gq;
-    for (int base = wave * kRowsPerPass * kUnroll; base < n_rows; base += kWaves * kRowsPerPass * kUnroll) {
+    const int w = (wave + kWaves - first) % kWaves;
+    for (int base = w * kRowsPerPass * kUnroll; base < n_rows; base += kWaves * kRowsPerPass * kUnroll) {
       float x[kUnroll][2 * kVec];
       float ss[kUnroll];
       long long off[kUnroll];
@@ -184,8 +187,8 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
       }
     }
   };
-  rows(q, n_tok * G, false);
-  rows(k, n_tok, true);
+  rows(q, n_tok * G, false, 0);
+  rows(k, n_tok, true, 1);
 
   if (k_rot) {  // zero the padding rows T .. Tp-1 of this block
     for (int i = threadIdx.x; i < kTokBlock * (kHeadDim / kVec); i += kThreads) {
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   // --- values: raw copy into the cache (16-byte chunks), transposed prefill operand ----
   constexpr int kChunks = kHeadDim / kVec;  // 16-byte chunks per row
   if (v_cache) {
-    for (int i = threadIdx.x; i < n_tok * kChunks; i += kThreads) {
+    for (int i = (threadIdx.x + kThreads - 128) % kThreads; i < n_tok * kChunks; i += kThreads) {  // from wave 2
       const int t = t0 + i / kChunks;
       if (!(a.window == 0 || t >= a.T - a.window)) continue;
       const long long n = a.pos_offset + t;

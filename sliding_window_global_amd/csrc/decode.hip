@@ -82,18 +82,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
 
   // ---- Q' fragment (B operand of S^T): head m16, dims of the lane's 16 pairs --------
   // slice 0: 16g+e, slice 1: 16g+8+e, slice 2: 64+16g+e, slice 3: 64+16g+8+e (e = 0..7)
+  // (loaded here, zeroed for the padding heads once the loads have landed, below)
+  const bool q_ok = m16 < G;
+  u32x4 qw[4];
   bf16x8 qf[4];
   {
-    const bool ok = m16 < G;
     const bf16_t* src = static_cast<const bf16_t*>(a.q_rot) +
-                        (static_cast<long long>(b) * a.Hq + kvh * G + (ok ? m16 : 0)) * kHeadDim;
+                        (static_cast<long long>(b) * a.Hq + kvh * G + (q_ok ? m16 : 0)) * kHeadDim;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int d0 = (s >> 1) * kHalf + g * 16 + (s & 1) * 8;
-      u32x4 w = *reinterpret_cast<const u32x4*>(src + d0);
-      if (!ok) w = u32x4{0, 0, 0, 0};
-      qf[s] = __builtin_bit_cast(bf16x8, w);
-    }
+    for (int s = 0; s < 4; ++s) qw[s] = *reinterpret_cast<const u32x4*>(src + (s >> 1) * kHalf + g * 16 + (s & 1) * 8);
   }
 
   // ---- fine rope factors of this lane's key (its position & 63 is fixed) -------------
@@ -101,12 +98,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   float2 fine[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) fine[e] = a.rope[key_in_tile * kHalf + g * 16 + e];
-  // Wait for Q' and the fine factors here, once: the stream below keeps direct loads in
-  // flight, and a use of these inside the loop would otherwise wait for all of them.
-#pragma unroll
-  for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(qf[s]));
-#pragma unroll
-  for (int e = 0; e < 16; ++e) asm volatile("" : "+v"(fine[e].x), "+v"(fine[e].y));
 
   // ---- per-lane pieces of the loads ---------------------------------------------------
   // V direct load i, lane l fills padded slot p = 64 i + l: row p / 17, chunk p % 17 (the
@@ -249,6 +240,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   float2* const c2 = cs2[wave];
   issue(k0, v0, c0);  // tile 0
   issue(k1, v1, c1);  // tile 1
+  // Q' and the fine factors (loaded before the tiles) are in once all but the tiles' loads
+  // have landed; settle that here, once: a first use inside the loop would otherwise wait
+  // for every load in flight.
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerIssue));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(qw[s]));
+#pragma unroll
+  for (int e = 0; e < 16; ++e) asm volatile("" : "+v"(fine[e].x), "+v"(fine[e].y));
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qf[s] = __builtin_bit_cast(bf16x8, q_ok ? qw[s] : u32x4{0, 0, 0, 0});
   // Before computing tile t, an explicit wait leaves the loads of the tiles issued after it
   // in flight (the compiler's own waits cannot follow the ring across loop iterations).
   constexpr unsigned kTwoBehind = wait_vmcnt(2 * kLoadsPerIssue);
@@ -327,36 +330,40 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
 }
 
 // One block per (sequence, query head): the split states are merged in a fixed order
-// (deterministic); thread d owns output component d.
+// (deterministic); thread d owns output component d. All loads (every split's m, l and
+// this thread's accumulators, up to kRegSplits of them in registers) go out together.
+constexpr int kRegSplits = 32;
 __global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(const float* __restrict__ ws,
                                                                   bf16_t* __restrict__ out,
                                                                   int n_split) {
-  __shared__ float wsc[kMaxSplit];
-  __shared__ float red[2][kHeadDim / 64];
+  __shared__ float ms[kMaxSplit], ls[kMaxSplit];
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
-  const int wv = tid >> 6;
   const float* p = ws + static_cast<long long>(bh) * n_split * kPartial;
-  float M = -INFINITY;
-  for (int i = tid; i < n_split; i += kHeadDim) M = fmaxf(M, p[i * kPartial + kHeadDim]);
+  float av[kRegSplits];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
-  if ((tid & 63) == 0) red[0][wv] = M;
-  __syncthreads();
-  M = fmaxf(red[0][0], red[0][1]);
-  float L = 0.f;
+  for (int i = 0; i < kRegSplits; ++i) av[i] = i < n_split ? p[i * kPartial + tid] : 0.f;
   for (int i = tid; i < n_split; i += kHeadDim) {
-    const float w = fast_exp2(p[i * kPartial + kHeadDim] - M);
-    wsc[i] = w;
-    L += w * p[i * kPartial + kHeadDim + 1];
+    ms[i] = p[i * kPartial + kHeadDim];
+    ls[i] = p[i * kPartial + kHeadDim + 1];
   }
-  L = wave_sum(L);
-  if ((tid & 63) == 0) red[1][wv] = L;
   __syncthreads();
-  L = red[1][0] + red[1][1];
-  float acc = 0.f;
-#pragma unroll 8
-  for (int i = 0; i < n_split; ++i) acc += wsc[i] * p[i * kPartial + tid];
+  float M = -INFINITY;
+  for (int i = 0; i < n_split; ++i) M = fmaxf(M, ms[i]);
+  float L = 0.f, acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRegSplits; ++i) {
+    if (i < n_split) {
+      const float w = fast_exp2(ms[i] - M);
+      L += w * ls[i];
+      acc += w * av[i];
+    }
+  }
+  for (int i = kRegSplits; i < n_split; ++i) {
+    const float w = fast_exp2(ms[i] - M);
+    L += w * ls[i];
+    acc += w * p[i * kPartial + tid];
+  }
   out[static_cast<long long>(bh) * kHeadDim + tid] = f32_to_bf16(acc / L);
 }
 
