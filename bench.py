@@ -5,7 +5,8 @@ shape (B=1, T=8192, Hq=64, Hkv=8, d=128, W=2048): plamo_kv_append (QK norm, cach
 write, RoPE, prefill operands) + plamo_attn_prefill, inputs resident in HBM. ``value``
 is algorithmic prefill FLOP (4*d per attended (query, key) pair and query head) per
 second of that step. Also reported: the global-layer prefill (T=32768, YaRN), batched
-decode (B=64; ring W=2048 and global 32768) as KV-read GB/s, the 8-layer period decode
+decode (B=64; ring W=2048 and global 32768) as KV-read GB/s, both prefills fed in
+chunks (2048 local, 8192 global) after cached tokens, the 8-layer period decode
 at 131072 context, the roofline object of the prefill kernel, and the CPU oracle timed
 on a bounded sample of the headline workload.
 
@@ -108,6 +109,48 @@ def bench_prefill(torch, swg, wl, steps, warmup, norm_offset):
     return dict(workload=wl.name, flops=flops, ms_per_step=ms_step, ms_attn=ms_attn,
                 step_tflops=flops / ms_step / 1e9, attn_tflops=flops / ms_attn / 1e9,
                 wall_ms_per_step=wall / steps * 1e3)
+
+
+def bench_chunked_prefill(torch, swg, wl, chunk, steps, warmup):
+    """The same prefill fed in chunks of ``chunk`` tokens: chunk c runs kv_append at
+    pos_offset c*chunk (its operands start with the cached keys it attends) and
+    attn_prefill. One step = every chunk; the FLOP count equals the one-shot prefill's."""
+    from sliding_window_global_amd import layer
+    inp = wl.draw()
+    q, k, v = dev_bf16(torch, inp["q"]), dev_bf16(torch, inp["k"]), dev_bf16(torch, inp["v"])
+    wq, wk = dev_bf16(torch, inp["wq"]), dev_bf16(torch, inp["wk"])
+    tab = swg.make_rope_table(wl.T + 64, rope_params(swg, wl.rope))
+    cap = wl.window if wl.window else wl.T
+    kc = torch.empty((wl.B, wl.Hkv, cap, wl.d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    starts = list(range(0, wl.T, chunk))
+    parts, bufs = [], []
+    for p in starts:
+        n = min(chunk, wl.T - p)
+        parts.append((q[:, p:p + n].contiguous(), k[:, p:p + n].contiguous(), v[:, p:p + n].contiguous()))
+        bufs.append(layer.PrefillBuffers(wl.B, n, wl.Hq, wl.Hkv, wl.d, torch.bfloat16, window=wl.window,
+                                         pos_offset=p))
+
+    def step(t_step=None):
+        if t_step:
+            t_step[0].record()
+        for p, (qc, kc_, vc_), bf in zip(starts, parts, bufs):
+            swg.plamo_kv_append(qc, kc_, vc_, bf.q_rot, window=wl.window, pos_offset=p, rope_table=tab,
+                                q_norm_w=wq, k_norm_w=wk, norm_offset=wl.norm_offset, k_rot_out=bf.k_rot,
+                                v_t_out=bf.v_t, k_cache=kc, v_cache=vc)
+            swg.plamo_attn_prefill(bf.q_rot, bf.k_rot, bf.v_t, bf.out, window=wl.window, pos_offset=p)
+        if t_step:
+            t_step[1].record()
+
+    for _ in range(warmup):
+        step()
+    ts = Timer(torch)
+    for _ in range(steps):
+        step(ts.span())
+    ms = ts.mean_ms()
+    flops = wl.flops()
+    return dict(workload=f"{wl.name}_chunks{chunk}", n_chunks=len(starts), ms_per_step=ms,
+                step_tflops=flops / ms / 1e9)
 
 
 # ----------------------------------------------------------------------------
@@ -225,7 +268,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="", help="prefill_local|prefill_global|decode|period|copy_calibration")
+    ap.add_argument("--only", default="", help="prefill_local|prefill_global|prefill_chunked|decode|period|copy_calibration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--period-steps", type=int, default=128)
@@ -256,6 +299,12 @@ def main():
         log(f"[bench]   {g}")
         extra["prefill_global"] = {k: g[k] for k in ("workload", "ms_per_step", "ms_attn", "step_tflops", "attn_tflops")}
         extra["prefill_global"]["frac_mfma"] = g["attn_tflops"] / PEAK_BF16_TFLOPS
+    if only in ("", "prefill_chunked"):
+        for wl, chunk, n in ((LOCAL_PREFILL, 2048, args.steps), (GLOBAL_PREFILL, 8192, max(3, args.steps // 4))):
+            log(f"[bench] chunked prefill {wl.name} chunk={chunk}")
+            r = bench_chunked_prefill(torch, swg, wl, chunk, n, max(1, args.warmup // 2))
+            log(f"[bench]   {r}")
+            extra[r["workload"]] = r
     if only in ("", "decode"):
         for li in (0, 1):
             log(f"[bench] batched decode layer {li}")

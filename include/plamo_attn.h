@@ -85,8 +85,9 @@ PLAMO_API size_t plamo_rope_table_bytes(long long max_pos, int d);
 PLAMO_API int plamo_rope_table_init(void* table, size_t table_bytes, long long max_pos, int d,
                           const plamo_rope* rope, void* stream);
 
-/* Padded token count used by the prefill operand layouts: T rounded up to 128. */
-PLAMO_API long long plamo_prefill_padded_len(long long T);
+/* Padded key count used by the prefill operand layouts: S rounded up to 128, where a
+ * chunk of T tokens after `kept` cached ones (below) attends S = kept + T keys. */
+PLAMO_API long long plamo_prefill_padded_len(long long S);
 
 /* ---------------------------------------------------------------------------
  * plamo_kv_append -- steps 1-3 for T new tokens of B sequences [P3 §4.3, §4.4, §6]
@@ -100,13 +101,19 @@ PLAMO_API long long plamo_prefill_padded_len(long long T);
  * q_norm_w, k_norm_w [d]   stored norm weights w (gain c + w); both NULL = no norm
  * norm_offset, norm_eps    c (1 for q_norm/k_norm [P3 §3.2]) and eps (1e-6)
  * q_out    [B, T, Hq, d]   normalised and rotated Q                (dtype, required)
- * k_rot_out normalised, cache-rounded and rotated K, Tp = plamo_prefill_padded_len(T)
- *                          tokens per (b, KV head), tokens T..Tp-1 zeroed. NULL = not
- *                          written. (Prefill operand.) Layout per (b, KV head):
+ * k_rot_out rotated K of the S = kept + T keys the chunk attends, Tp =
+ *                          plamo_prefill_padded_len(S) rows per (b, KV head): rows
+ *                          0..kept-1 the cached (pre-RoPE) keys read from k_cache before
+ *                          this call updates it, rotated at renumbered positions
+ *                          0..kept-1; rows kept..S-1 the new tokens (normalised,
+ *                          cache-rounded, rotated); rows S..Tp-1 zero. NULL = not
+ *                          written. (Prefill operand.) With kept > 0 the caches must be
+ *                          given. Layout per (b, KV head):
  *                            fp32: [Tp][d];
  *                            bf16: Tp/64 tiles of 64 tokens, tile = [16][64][8]
  *                                  (dim / 8, token in tile, dim % 8), 16 KiB.
- * v_t_out  V transposed, pad zeroed. NULL = not written. (Prefill operand.) Layout
+ * v_t_out  V of the same S keys (cached, then new) transposed, pad zeroed. NULL = not
+ *                          written. (Prefill operand.) Layout
  *                          per (b, KV head):
  *                            fp32: [d][Tp] (token index fastest);
  *                            bf16: Tp/64 tiles, tile = [8][128][8]
@@ -129,15 +136,17 @@ PLAMO_API int plamo_kv_append(int dtype, const void* q, const void* k, const voi
                     const void* rope_table, size_t rope_table_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
- * plamo_attn_prefill -- step 4 for a prefill from an empty cache [P3 §4.5, §5.1]
+ * plamo_attn_prefill -- step 4 for a prefill of T tokens [P3 §4.5, §5.1]
  *
  * q_rot [B, T, Hq, d]; k_rot and v_t in the dtype's layout written by
- * plamo_kv_append (Tp = plamo_prefill_padded_len(T)); out [B, T, Hq, d] (token
- * major, i.e. [B, T, Hq*d] ready for the output projection [P3 §4.5]).
- * Query i (0..T-1) attends keys j <= i, and i - j < window when window > 0.
+ * plamo_kv_append with the same window and pos_offset (Tp =
+ * plamo_prefill_padded_len(kept + T), kept as for plamo_kv_append); out
+ * [B, T, Hq, d] (token major, i.e. [B, T, Hq*d] ready for the output projection
+ * [P3 §4.5]). Query t (0..T-1) sits at renumbered position i = kept + t and
+ * attends operand keys j <= i, and i - j < window when window > 0: a chunk after
+ * pos_offset cached tokens sees the cached keys first, then its own causally.
  * softmax_scale is 1/sqrt(d) [P3 §4.5]; the YaRN amplitude is already in q_rot
- * and k_rot. pos_offset must be 0 (a prefill on top of a populated cache is not
- * implemented: PLAMO_ERR_UNSUPPORTED).
+ * and k_rot.
  * ------------------------------------------------------------------------- */
 PLAMO_API int plamo_attn_prefill(int dtype, const void* q_rot, const void* k_rot, const void* v_t,
                        void* out, int B, int T, int Hq, int Hkv, int d, int window,

@@ -120,17 +120,25 @@ def plamo_prefill_padded_len(T: int) -> int:
 PREFILL_KEY_TILE = 64
 
 
-def prefill_operand_shapes(B: int, T: int, Hkv: int, d: int, dtype) -> tuple[tuple, tuple]:
-    """Shapes of (k_rot, v_t) as plamo_kv_append writes them (include/plamo_attn.h).
+def kept_tokens(window: int, pos_offset: int) -> int:
+    """Cached tokens a chunk at pos_offset attends before its own (global: all of them; local:
+    the last window-1)."""
+    return int(pos_offset) if window == 0 else min(int(pos_offset), int(window) - 1)
 
-    fp32: [B, Hkv, Tp, d] and [B, Hkv, d, Tp]. bf16: tiled by 64 tokens,
-    [B, Hkv, Tp/64, d/8, 64, 8] and [B, Hkv, Tp/64, 8, d, 8].
+
+def prefill_operand_shapes(B: int, T: int, Hkv: int, d: int, dtype, window: int = 0,
+                           pos_offset: int = 0) -> tuple[tuple, tuple]:
+    """Shapes of (k_rot, v_t) as plamo_kv_append writes them (include/plamo_attn.h), for the
+    S = kept + T keys a chunk of T tokens at pos_offset attends.
+
+    fp32: [B, Hkv, Sp, d] and [B, Hkv, d, Sp]. bf16: tiled by 64 keys,
+    [B, Hkv, Sp/64, d/8, 64, 8] and [B, Hkv, Sp/64, 8, d, 8]. Sp = plamo_prefill_padded_len(S).
     """
-    Tp = plamo_prefill_padded_len(T)
+    Sp = plamo_prefill_padded_len(kept_tokens(window, pos_offset) + T)
     if dtype == torch.bfloat16:
-        nt = Tp // PREFILL_KEY_TILE
+        nt = Sp // PREFILL_KEY_TILE
         return (B, Hkv, nt, d // 8, PREFILL_KEY_TILE, 8), (B, Hkv, nt, PREFILL_KEY_TILE // 8, d, 8)
-    return (B, Hkv, Tp, d), (B, Hkv, d, Tp)
+    return (B, Hkv, Sp, d), (B, Hkv, d, Sp)
 
 
 def plamo_kv_append(q, k, v, q_out, *, window: int, pos_offset: int, rope_table,
@@ -144,7 +152,7 @@ def plamo_kv_append(q, k, v, q_out, *, window: int, pos_offset: int, rope_table,
         raise ValueError("k and v must be [B, T, Hkv, d] matching q")
     if tuple(q_out.shape) != (B, T, Hq, d):
         raise ValueError("q_out must match q")
-    k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dt)
+    k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dt, window, pos_offset)
     if k_rot_out is not None and tuple(k_rot_out.shape) != k_shape:
         raise ValueError(f"k_rot_out must be {list(k_shape)}")
     if v_t_out is not None and tuple(v_t_out.shape) != v_shape:
@@ -170,7 +178,7 @@ def plamo_attn_prefill(q_rot, k_rot, v_t, out, *, window: int, pos_offset: int =
     dt = q_rot.dtype
     B, T, Hq, d = q_rot.shape
     Hkv = k_rot.shape[1]
-    k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dt)
+    k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dt, window, pos_offset)
     if tuple(k_rot.shape) != k_shape or tuple(v_t.shape) != v_shape:
         raise ValueError(f"k_rot must be {list(k_shape)} and v_t {list(v_shape)}")
     if tuple(out.shape) != (B, T, Hq, d):

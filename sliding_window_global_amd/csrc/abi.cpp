@@ -141,6 +141,8 @@ int plamo_kv_append(int dtype, const void* q, const void* k, const void* v, cons
     if (window == 0 && cap < pos_offset + T) return fail(PLAMO_ERR_INVALID_ARG, "global cache needs cap >= pos_offset + T");
   }
   const long long kept = kept_tokens(window, pos_offset);
+  if (kept > 0 && (k_rot_out || v_t_out) && !k_cache)
+    return fail(PLAMO_ERR_INVALID_ARG, "prefill operands after cached tokens need the caches");
   if (!rope_table) return fail(PLAMO_ERR_INVALID_ARG, "rope_table must be non-NULL");
   const long long covered = table_positions(rope_table_bytes);
   if (covered < 0) return fail(PLAMO_ERR_INVALID_ARG, "rope_table_bytes is not a whole number of rows");
@@ -152,7 +154,7 @@ int plamo_kv_append(int dtype, const void* q, const void* k, const void* v, cons
   a.q_out = q_out; a.k_rot_out = k_rot_out; a.v_t_out = v_t_out;
   a.k_cache = k_cache; a.v_cache = v_cache; a.cap = cap;
   a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.window = window;
-  a.Tp = plamo_prefill_padded_len(T);
+  a.Tp = plamo_prefill_padded_len(kept + T);
   a.pos_offset = pos_offset; a.kept = kept;
   a.rope = static_cast<const float2*>(rope_table);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -164,8 +166,9 @@ int plamo_attn_prefill(int dtype, const void* q_rot, const void* k_rot, const vo
                        float softmax_scale, void* stream) {
   if (dtype != PLAMO_F32 && dtype != PLAMO_BF16) return fail(PLAMO_ERR_INVALID_ARG, "unknown dtype");
   if (int st = check_heads(B, T, Hq, Hkv, d, window, pos_offset)) return st;
-  if (pos_offset != 0) return fail(PLAMO_ERR_UNSUPPORTED, "prefill on a populated cache (pos_offset > 0)");
   if (B == 0 || T == 0) return ok();
+  const long long kept = kept_tokens(window, pos_offset);
+  if (kept + T > (1LL << 30)) return fail(PLAMO_ERR_UNSUPPORTED, "kept + T must be <= 2^30");
   if (!q_rot || !k_rot || !v_t || !out) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be non-NULL");
   const void* ptrs[] = {q_rot, k_rot, v_t, out};
   for (const void* p : ptrs)
@@ -177,7 +180,8 @@ int plamo_attn_prefill(int dtype, const void* q_rot, const void* k_rot, const vo
   plamo::PrefillArgs a;
   a.q_rot = q_rot; a.k_rot = k_rot; a.v_t = v_t; a.out = out;
   a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.window = window;
-  a.Tp = plamo_prefill_padded_len(T);
+  a.Tp = plamo_prefill_padded_len(kept + T);
+  a.kept = kept;
   a.scale = softmax_scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return launched(dtype == PLAMO_BF16 ? plamo::launch_prefill_bf16(a, s) : plamo::launch_prefill_f32(a, s));

@@ -173,13 +173,15 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
           y[e] = x0 * z.x - x1 * z.y;
           y[kVec + e] = x0 * z.y + x1 * z.x;
         }
-        if (kTiled && is_k) {  // chunks c and c + 8 of key t within its tile
-          E* dst = k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t0) * kHeadDim +
-                   (c * kTokBlock + tt[u]) * kVec;
+        // the operand row of new token t follows the kept cached keys
+        const long long R = a.kept + t;
+        if (kTiled && is_k) {  // chunks c and c + 8 of key R within its tile
+          E* dst = k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + (R & ~63LL)) * kHeadDim +
+                   (c * kTokBlock + (R & 63)) * kVec;
           *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(y);
           *reinterpret_cast<u32x4*>(dst + 8 * kTokBlock * kVec) = Io<E>::pack(y + kVec);
         } else {
-          E* dst = is_k ? k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t) * kHeadDim + c * kVec
+          E* dst = is_k ? k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + R) * kHeadDim + c * kVec
                         : q_out + off[u];
           *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(y);
           *reinterpret_cast<u32x4*>(dst + kHalf) = Io<E>::pack(y + kVec);
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   rows(q, n_tok * G, false, 0);
   rows(k, n_tok, true, 1);
 
-  if (k_rot) {  // zero the padding rows T .. Tp-1 of this block
+  if (k_rot && a.kept == 0) {  // zero the padding rows T .. Tp-1 of this block
     for (int i = threadIdx.x; i < kTokBlock * (kHeadDim / kVec); i += kThreads) {
       if (kTiled) {  // i = chunk * 64 + key in tile
         const long long t = t0 + i % kTokBlock;
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
       reinterpret_cast<u32x4*>(v_cache + crow)[cidx] = reinterpret_cast<const u32x4*>(v + row)[cidx];
     }
   }
-  if (v_t) {
+  if (v_t && a.kept == 0) {  // (after cached keys the operand kernel writes all of V^T)
     constexpr int kTS = kTokBlock + kVec;  // LDS row stride (tokens), keeps rows 16-byte aligned
     __shared__ __attribute__((aligned(16))) E tile[kHeadDim * kTS];
     for (int i = threadIdx.x; i < kTokBlock * kChunks; i += kThreads) {
@@ -260,9 +262,126 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   }
 }
 
+// Prefill operands of a chunk that follows kept > 0 cached keys (「PLaMo 3アーキテクチャ徹底解析」
+// §4.4: the attention reads every key the cache returns). One block = one 64-key operand
+// tile of one (sequence, KV head): K' rows of the kept keys (pre-RoPE K from the cache,
+// rotated at their renumbered positions 0 .. kept-1), V^T of all kept + T keys (cached V,
+// then the chunk's own V), zeros past kept + T. Runs before the append kernel, which may
+// overwrite ring slots these keys still occupy and writes the chunk's own K' rows.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a) {
+  constexpr int kVec = 16 / sizeof(E);
+  constexpr int kLanesPerRow = kHalf / kVec;
+  constexpr int kRowsPerPass = 64 / kLanesPerRow;
+  constexpr bool kTiled = sizeof(E) == 2;
+  constexpr int kChunks = kHeadDim / kVec;
+  constexpr int kTS = kTokBlock + kVec;  // LDS row stride (tokens) of the V^T staging tile
+  __shared__ __attribute__((aligned(16))) float2 zs[kTokBlock][kHalf];
+  __shared__ __attribute__((aligned(16))) E tile[kHeadDim * kTS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = lane % kLanesPerRow;
+  const int slot = lane / kLanesPerRow;
+  const long long R0 = static_cast<long long>(blockIdx.x) * kTokBlock;  // first operand row
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const long long S = a.kept + a.T;
+  const long long base = a.pos_offset - a.kept;  // absolute position of renumbered key 0
+  const long long bh = static_cast<long long>(b) * a.Hkv + kvh;
+  const E* __restrict__ kc = static_cast<const E*>(a.k_cache) + bh * a.cap * kHeadDim;
+  const E* __restrict__ vc = static_cast<const E*>(a.v_cache) + bh * a.cap * kHeadDim;
+  const E* __restrict__ v = static_cast<const E*>(a.v);
+  E* __restrict__ k_rot = static_cast<E*>(a.k_rot_out);
+  E* __restrict__ v_t = static_cast<E*>(a.v_t_out);
+  auto cache_row = [&](long long R) {
+    const long long n = base + R;
+    return (a.window == 0 ? n : n % a.window) * kHeadDim;
+  };
+
+  if (k_rot) {
+    for (int i = threadIdx.x; i < kTokBlock * kHalf; i += kThreads) {
+      const int r = i / kHalf, j = i % kHalf;
+      if (R0 + r < a.kept) zs[r][j] = rope_factor(a.rope, R0 + r, j);
+    }
+    __syncthreads();
+    for (int r = wave * kRowsPerPass + slot; r < kTokBlock; r += kWaves * kRowsPerPass) {
+      const long long R = R0 + r;
+      if (R >= a.kept && R < S) continue;  // the chunk's own keys: the append kernel
+      float y[2 * kVec];
+      if (R < a.kept) {
+        float x[2 * kVec];
+        const E* src = kc + cache_row(R) + c * kVec;
+        Io<E>::unpack(*reinterpret_cast<const u32x4*>(src), x);
+        Io<E>::unpack(*reinterpret_cast<const u32x4*>(src + kHalf), x + kVec);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+          const float2 z = zs[r][c * kVec + e];
+          y[e] = x[e] * z.x - x[kVec + e] * z.y;
+          y[kVec + e] = x[e] * z.y + x[kVec + e] * z.x;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 2 * kVec; ++e) y[e] = 0.f;
+      }
+      if (kTiled) {
+        E* dst = k_rot + (bh * a.Tp + R0) * kHeadDim + (c * kTokBlock + r) * kVec;
+        *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(y);
+        *reinterpret_cast<u32x4*>(dst + 8 * kTokBlock * kVec) = Io<E>::pack(y + kVec);
+      } else {
+        E* dst = k_rot + (bh * a.Tp + R) * kHeadDim + c * kVec;
+        *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(y);
+        *reinterpret_cast<u32x4*>(dst + kHalf) = Io<E>::pack(y + kVec);
+      }
+    }
+  }
+
+  if (v_t) {
+    for (int i = threadIdx.x; i < kTokBlock * kChunks; i += kThreads) {
+      const int r = i / kChunks, cidx = i % kChunks;
+      const long long R = R0 + r;
+      E x[kVec];
+      if (R < S) {
+        const E* src = R < a.kept ? vc + cache_row(R)
+                                  : v + ((static_cast<long long>(b) * a.T + (R - a.kept)) * a.Hkv + kvh) * kHeadDim;
+        const u32x4 w = reinterpret_cast<const u32x4*>(src)[cidx];
+        __builtin_memcpy(x, &w, 16);
+      } else {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) x[e] = E(0);
+      }
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) tile[(cidx * kVec + e) * kTS + r] = x[e];
+    }
+    __syncthreads();
+    constexpr int kTokChunks = kTokBlock / kVec;
+    if (kTiled) {
+      u32x4* dst = reinterpret_cast<u32x4*>(v_t + (bh * a.Tp + R0) * kHeadDim);
+      for (int i = threadIdx.x; i < kHeadDim * kTokChunks; i += kThreads) {  // i = key chunk * 128 + dim
+        const int cc = i % kHeadDim, tc = i / kHeadDim;
+        dst[i] = *reinterpret_cast<const u32x4*>(&tile[cc * kTS + tc * kVec]);
+      }
+    } else {
+      for (int i = threadIdx.x; i < kHeadDim * kTokChunks; i += kThreads) {
+        const int cc = i / kTokChunks, tc = i % kTokChunks;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(&tile[cc * kTS + tc * kVec]);
+        *reinterpret_cast<u32x4*>(v_t + (bh * kHeadDim + cc) * a.Tp + R0 + tc * kVec) = w;
+      }
+    }
+  }
+}
+
 template <typename E>
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
-  const long long tokens = (a.k_rot_out || a.v_t_out) ? a.Tp : a.T;
+  const bool operands = a.k_rot_out || a.v_t_out;
+  if (operands && a.kept > 0) {
+    const unsigned tiles = static_cast<unsigned>(a.Tp / kTokBlock);
+    hipLaunchKernelGGL(prefill_operands_kernel<E>, dim3(tiles, a.Hkv, a.B), dim3(kThreads), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // with kept == 0 the append kernel also covers the padding tokens T .. Tp-1
+  const long long tokens = (operands && a.kept == 0) ? a.Tp : a.T;
   const unsigned gx = static_cast<unsigned>((tokens + kTokBlock - 1) / kTokBlock);
   hipLaunchKernelGGL(kv_append_kernel<E>, dim3(gx, a.Hkv, a.B), dim3(kThreads), 0, stream, a);
   return hipGetLastError();

@@ -25,11 +25,14 @@ struct AppendArgs {
   void* v_cache;
   long long cap;
   int B, T, Hq, Hkv, window;
-  long long Tp;          // padded token count of the prefill operands
+  long long Tp;          // padded key count of the prefill operands (kept + T keys)
   long long pos_offset;  // absolute position of the first new token
   long long kept;        // cached tokens returned before the new ones
   const float2* rope;
 };
+// Both launch, when a chunk follows kept > 0 cached tokens and prefill operands are
+// requested, first the operand kernel (the kept keys from the cache, all of V^T and the
+// padding) and then the append kernel (new tokens).
 hipError_t launch_kv_append_bf16(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_kv_append_f32(const AppendArgs& a, hipStream_t stream);
 
@@ -39,7 +42,8 @@ struct PrefillArgs {
   const void* v_t;    // [B, Hkv, d, Tp]
   void* out;          // [B, T, Hq, d]
   int B, T, Hq, Hkv, window;
-  long long Tp;
+  long long Tp;    // padded key count of K', V^T
+  long long kept;  // keys before the chunk: query t sits at renumbered position kept + t
   float scale;
 };
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);

@@ -7,23 +7,29 @@
 // costs O(T W) (§5.3).
 //
 // Work decomposition
-//   block  = 128 query rows of one (sequence, query head); 4 waves x 32 rows.
-//   tile   = 64 keys. K' and V^T tiles go straight from HBM into LDS
-//            (global_load_lds_dwordx4, no register staging), double buffered, with
-//            16-byte chunks XOR-swizzled so that the MFMA operand reads are free of
-//            bank conflicts.
-//   order  = key tiles from the diagonal downwards, so every row sees its own key in
-//            the first tile it computes.
+//   block  = 128 query rows of one (sequence, query head); 4 waves x 32 rows. Query row t
+//            sits at renumbered position kept + t: a chunk after `kept` cached keys
+//            (§4.4) attends keys 0 .. kept+t, all of them in the K' / V^T operands.
+//   tile   = 64 keys. K' and V^T arrive tiled in HBM in exactly the LDS order, so each
+//            tile is one contiguous copy straight into LDS (global_load_lds_dwordx4, no
+//            register staging), double buffered. The LDS order is chunk-major: the
+//            operand reads of one MFMA are 64 consecutive 16-byte slots (no bank
+//            conflicts) and the reads of different chunks differ by constant offsets.
+//   order  = key tiles from the diagonal downwards. A row with no visible key in the
+//            first tiles keeps a -inf reference until its first visible key.
 //   math   = S^T = K' Q'^T and O^T = V^T P^T with v_mfma_f32_32x32x16_bf16: the query
 //            index is the MFMA column in both, so each lane owns one query row for the
 //            online softmax and for the rescaling of its O^T accumulators. K' rows are
 //            read in the order that makes each lane's eight consecutive S^T entries
 //            eight consecutive keys, which is what the P^T operand of the next MFMA
 //            needs; V^T is then read in natural key order.
-//   pipeline = the K' tile runs one step ahead of V^T: while the softmax of tile k runs
-//            on the vector ALUs, the matrix cores already compute S for tile k+1.
-//   softmax = exp2 domain, lazy rescaling (the running max moves only when a row gains
-//            more than 2^8), row sums taken from the same bf16-rounded P as P V.
+//   pipeline = one basic block per step: the QK MFMAs of tile t+1 interleaved with the
+//            exp2 / pack / row-sum work of tile t, then the P V MFMAs of tile t
+//            interleaved with the row maxima of tile t+1.
+//   softmax = exp2 domain; Q' is pre-scaled by scale * log2(e) and the S accumulator
+//            starts at -m, so the numerator is a bare exp2; lazy rescaling (the
+//            reference moves only when a row gains more than 2^8); row sums taken from
+//            the same bf16-rounded P as P V.
 //   launch = 1-D grid remapped so that the query heads sharing a KV head and
 //            neighbouring query blocks land on the same XCD (shared K/V in its L2);
 //            causal work is ordered longest-first.
@@ -101,9 +107,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
       static_cast<const bf16_t*>(a.v_t) + (static_cast<long long>(b) * a.Hkv + kvh) * kHeadDim * a.Tp;
 
   // ---- key tiles this block touches, processed from kt_hi down to kt_lo -------------
+  // Query row t sits at renumbered position kept + t; keys 0 .. kept-1 came from the cache.
+  const int kept = static_cast<int>(a.kept);
   const int last_row = min(i0 + BM, a.T) - 1;
-  const int lo = kLocal ? max(0, i0 - a.window + 1) : 0;
-  const int kt_hi = last_row / BN;
+  const int lo = kLocal ? max(0, kept + i0 - a.window + 1) : 0;
+  const int kt_hi = (kept + last_row) / BN;
   const int n_tiles = kt_hi - lo / BN + 1;
 
   // K' and V^T arrive tiled by 64 keys, each tile 16 KiB in exactly the LDS order below, so
@@ -126,6 +134,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   const float c = a.scale * 1.4426950408889634f;
   const int r0 = i0 + wave * 32;
   const int qrow = r0 + n;
+  const int p0 = kept + r0;  // position of the wave's first row
   bf16x8 qf[8];
   {
     const bool ok = qrow < a.T;
@@ -141,13 +150,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     }
   }
 
-  // wave-uniform: does tile `step` hold a masked pair for some row r0..r0+31? (A tile that
+  // wave-uniform: does tile `step` hold a masked pair for some row of the wave? (A tile that
   // lies wholly outside the wave's rows' windows is computed fully masked: the four waves
   // of a block move through the tiles in step, so skipping it would not end the step
   // sooner.)
   auto needs_mask = [&](int step) __attribute__((always_inline)) {
     const int j0 = (kt_hi - step) * BN;
-    return (j0 + BN - 1 > r0) || (kLocal && r0 + 31 - j0 >= a.window);
+    return (j0 + BN - 1 > p0) || (kLocal && p0 + 31 - j0 >= a.window);
   };
 
   // MFMA operand i of one step: i < 16 is K' chunk (s = i/2, key block i%2) of the next
@@ -224,9 +233,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     // the last step has no next tile: its S^T is never used
     const bool real_next = step + 1 < n_tiles;
     if (kQK && real_next && needs_mask(step + 1)) {
-      // key k of the tile is visible to row qrow iff k <= qrow - j0 and, on local layers,
-      // k > qrow - j0 - window
-      const int dq = qrow - (kt_hi - step - 1) * BN - hl * 8;
+      // key k of the tile is visible to the row at position kept + qrow iff
+      // k <= kept + qrow - j0 and, on local layers, k > kept + qrow - j0 - window
+      const int dq = kept + qrow - (kt_hi - step - 1) * BN - hl * 8;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll

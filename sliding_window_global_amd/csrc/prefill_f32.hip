@@ -46,8 +46,11 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c = a.scale * 1.4426950408889634f;
 
-  const int last = min(i0 + kRows, a.T) - 1;
-  const int lo = a.window > 0 ? max(0, i0 - a.window + 1) : 0;
+  // query row t sits at renumbered position kept + t; keys 0 .. kept-1 came from the cache
+  const int kept = static_cast<int>(a.kept);
+  const int pos = kept + row;
+  const int last = kept + min(i0 + kRows, a.T) - 1;
+  const int lo = a.window > 0 ? max(0, kept + i0 - a.window + 1) : 0;
   for (int j0 = (lo / kKeys) * kKeys; j0 <= last; j0 += kKeys) {
     __syncthreads();
     for (int e = tid; e < kKeys * kHeadDim; e += kThreads) {
@@ -68,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillArgs a) {
       for (int r = 0; r < kHalf; ++r) part = fmaf(qv[r], ks[kk][half * kHalf + r], part);
       float dot = part + __shfl_xor(part, 1, 64);
       const int key = j0 + kk;
-      const bool ok = key <= row && (a.window == 0 || row - key < a.window);
+      const bool ok = key <= pos && (a.window == 0 || pos - key < a.window);
       s[kk] = ok ? dot * c : -INFINITY;
       mx = fmaxf(mx, s[kk]);
     }

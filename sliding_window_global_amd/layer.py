@@ -16,10 +16,11 @@ from . import (plamo_attn_decode, plamo_attn_decode_workspace_bytes, plamo_attn_
 
 
 class PrefillBuffers:
-    """Operands of one prefill: normalised/rotated Q, rotated K and transposed V."""
+    """Operands of one prefill chunk: normalised/rotated Q, rotated K and transposed V of the
+    kept + T keys it attends."""
 
-    def __init__(self, B, T, Hq, Hkv, d, dtype, device="cuda"):
-        k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dtype)
+    def __init__(self, B, T, Hq, Hkv, d, dtype, device="cuda", window=0, pos_offset=0):
+        k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dtype, window, pos_offset)
         self.q_rot = torch.empty((B, T, Hq, d), dtype=dtype, device=device)
         self.k_rot = torch.empty(k_shape, dtype=dtype, device=device)
         self.v_t = torch.empty(v_shape, dtype=dtype, device=device)
@@ -28,17 +29,19 @@ class PrefillBuffers:
 
 def prefill(q, k, v, *, window, rope_table, q_norm_w=None, k_norm_w=None, norm_offset=1.0,
             norm_eps=1e-6, k_cache=None, v_cache=None, bufs: PrefillBuffers | None = None,
-            softmax_scale=None, stream=None) -> PrefillBuffers:
-    """Prefill from an empty cache: q [B,T,Hq,d], k/v [B,T,Hkv,d] on the GPU."""
+            softmax_scale=None, stream=None, pos_offset=0) -> PrefillBuffers:
+    """Prefill of a chunk q [B,T,Hq,d], k/v [B,T,Hkv,d] on the GPU whose first token sits at
+    absolute position pos_offset. With pos_offset > 0 the caches must hold the earlier tokens
+    (they are read for the chunk's attention, then updated with the chunk)."""
     B, T, Hq, d = q.shape
     Hkv = k.shape[2]
     if bufs is None:
-        bufs = PrefillBuffers(B, T, Hq, Hkv, d, q.dtype, q.device)
-    plamo_kv_append(q, k, v, bufs.q_rot, window=window, pos_offset=0, rope_table=rope_table,
+        bufs = PrefillBuffers(B, T, Hq, Hkv, d, q.dtype, q.device, window, pos_offset)
+    plamo_kv_append(q, k, v, bufs.q_rot, window=window, pos_offset=pos_offset, rope_table=rope_table,
                     q_norm_w=q_norm_w, k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps,
                     k_rot_out=bufs.k_rot, v_t_out=bufs.v_t, k_cache=k_cache, v_cache=v_cache,
                     stream=stream)
-    plamo_attn_prefill(bufs.q_rot, bufs.k_rot, bufs.v_t, bufs.out, window=window, pos_offset=0,
+    plamo_attn_prefill(bufs.q_rot, bufs.k_rot, bufs.v_t, bufs.out, window=window, pos_offset=pos_offset,
                        softmax_scale=softmax_scale, stream=stream)
     return bufs
 

@@ -94,3 +94,24 @@ def untile_v_t(vt):
     """bf16 V^T operand [B, Hkv, Tp/64, 8, d, 8] (include/plamo_attn.h) -> [B, Hkv, d, Tp]."""
     B, H, nt, nc, d, w = vt.shape
     return vt.transpose(0, 1, 4, 2, 3, 5).reshape(B, H, d, nt * nc * w)
+
+
+def oracle_chunks(q, k, v, chunks, *, window, rope, wq=None, wk=None, norm_offset=1.0, eps=1e-6,
+                  rows_of=None):
+    """Oracle of a prefill in consecutive chunks (each chunk attends the cache the previous
+    ones left, then updates it): q [B,n,Hq,d] etc., chunks = chunk lengths summing to n.
+    rows_of(T) -> row indices kept per chunk (default all). Returns a list per chunk of
+    [B, rows, Hq, d] float64."""
+    B, n, Hq, d = q.shape
+    Hkv = k.shape[2]
+    caches = [LayerKVCache(Hkv, d, window) for _ in range(B)]
+    outs, p = [], 0
+    for T in chunks:
+        rows = None if rows_of is None else rows_of(T)
+        outs.append(np.stack([attention_layer_step(
+            q[b, p:p + T], k[b, p:p + T], v[b, p:p + T], caches[b], theta=rope.theta,
+            yarn_factor=rope.yarn_factor, orig_ctx=rope.orig_ctx, beta_fast=rope.beta_fast,
+            beta_slow=rope.beta_slow, q_norm_w=wq, k_norm_w=wk, norm_offset=norm_offset, eps=eps,
+            scale=1.0 / math.sqrt(d), rows=rows) for b in range(B)]))
+        p += T
+    return outs

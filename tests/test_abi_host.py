@@ -105,6 +105,7 @@ def _append(lib, **over):
     (dict(table_bytes=100), INVALID),               # not whole rows
     (dict(pos=64, window=0, table_bytes=(64 + 1) * 512), WORKSPACE),  # table too short
     (dict(eps=-1.0), INVALID),
+    (dict(pos=3, k_rot=FAKE), INVALID),             # operands after cached keys need the caches
 ])
 def test_kv_append_validation(lib, over, status):
     assert _append(lib, **over) == status
@@ -126,7 +127,7 @@ def _prefill(lib, **over):
 
 @pytest.mark.parametrize("over,status", [
     (dict(dtype=3), INVALID), (dict(d=64), UNSUPPORTED), (dict(Hq=9, Hkv=2), INVALID),
-    (dict(pos=10), UNSUPPORTED), (dict(out=None), INVALID), (dict(k=MISALIGNED), INVALID),
+    (dict(out=None), INVALID), (dict(k=MISALIGNED), INVALID),
     (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID), (dict(T=-3), INVALID),
 ])
 def test_prefill_validation(lib, over, status):

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import (TOL_BF16, TOL_F32, assert_parity, kept_slots, oracle_decode_one,
+from helpers import (TOL_BF16, TOL_F32, assert_parity, kept_slots, oracle_chunks, oracle_decode_one,
                      oracle_prefill, window_mean_closed_form, untile_k_rot, untile_v_t)
 from oracle import apply_rope, offset_rms_norm, rope_frequencies
 from synthetic import Draw
@@ -78,10 +78,12 @@ def test_rope_table_factors(rope):
 
 @pytest.mark.parametrize("window,pos_offset,T", [(0, 0, 200), (2048, 0, 300), (2048, 2046, 1),
                                                  (2048, 2047, 1), (2048, 2048, 1), (0, 32767, 1),
-                                                 (16, 5, 40), (16, 100, 3)])
+                                                 (16, 5, 40), (16, 100, 3), (2048, 1000, 1200),
+                                                 (0, 77, 130)])
 def test_kv_append_intermediates(window, pos_offset, T):
     """Q' (normalised, rotated at kept + t), the cache contents (pre-RoPE K, raw V, ring slot
-    n mod W, only the last W of a chunk) and the prefill operands K' and V^T."""
+    n mod W, only the last W of a chunk) and the prefill operands K' and V^T of all kept + T
+    keys: the kept cached keys rotated at 0 .. kept-1, then the chunk, then zero padding."""
     B, Hq, Hkv, d = 2, 8, 2, 128
     dr = Draw(1234 + pos_offset + T, True)
     q, k, v = dr.normal((B, T, Hq, d)), dr.normal((B, T, Hkv, d)), dr.normal((B, T, Hkv, d))
@@ -89,30 +91,41 @@ def test_kv_append_intermediates(window, pos_offset, T):
     rope = Rope(1e6, 64.0) if window == 0 else Rope(1e4)
     c = 1.0
     cap = window if window else pos_offset + T
+    kept = pos_offset if window == 0 else min(pos_offset, window - 1)
+    prior = kept_slots(pos_offset, window)  # slots of the kept tokens, in token order
+    prior_k, prior_v = dr.normal((B, kept, Hkv, d)), dr.normal((B, kept, Hkv, d))
     kc = torch.full((B, Hkv, cap, d), float("nan"), dtype=torch.bfloat16, device="cuda")
     vc = torch.full_like(kc, float("nan"))
+    if kept:
+        idx = torch.from_numpy(prior).cuda()
+        kc[:, :, idx] = dev(prior_k).transpose(1, 2)
+        vc[:, :, idx] = dev(prior_v).transpose(1, 2)
     q_out = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device="cuda")
-    k_shape, v_shape = swg.prefill_operand_shapes(B, T, Hkv, d, torch.bfloat16)
+    k_shape, v_shape = swg.prefill_operand_shapes(B, T, Hkv, d, torch.bfloat16, window, pos_offset)
     k_rot = torch.full(k_shape, float("nan"), dtype=torch.bfloat16, device="cuda")
     v_t = torch.full(v_shape, float("nan"), dtype=torch.bfloat16, device="cuda")
-    kept = pos_offset if window == 0 else min(pos_offset, window - 1)
     swg.plamo_kv_append(dev(q), dev(k), dev(v), q_out, window=window, pos_offset=pos_offset,
                         rope_table=rope_table(rope, 40000), q_norm_w=dev(wq), k_norm_w=dev(wk),
                         norm_offset=c, k_rot_out=k_rot, v_t_out=v_t, k_cache=kc, v_cache=vc)
     torch.cuda.synchronize()
     omega, amp = rope_frequencies(d, rope.theta, rope.yarn_factor)
     pos = kept + np.arange(T)
+    S = kept + T
     qn = offset_rms_norm(q, wq, c)
     kn = offset_rms_norm(k, wk, c)
     q_ref = np.stack([apply_rope(qn[b], pos, omega, amp) for b in range(B)])
     assert_parity(host(q_out), q_ref, TOL_BF16, "q_out")
     k_ref = np.stack([apply_rope(kn[b], pos, omega, amp) for b in range(B)])
     kr = untile_k_rot(host(k_rot))
-    assert_parity(kr[:, :, :T].transpose(0, 2, 1, 3), k_ref, TOL_BF16, "k_rot")
-    assert np.all(kr[:, :, T:] == 0)
+    assert_parity(kr[:, :, kept:S].transpose(0, 2, 1, 3), k_ref, TOL_BF16, "k_rot (chunk)")
+    if kept:
+        kp_ref = np.stack([apply_rope(prior_k[b], np.arange(kept), omega, amp) for b in range(B)])
+        assert_parity(kr[:, :, :kept].transpose(0, 2, 1, 3), kp_ref, TOL_BF16, "k_rot (cached keys)")
+    assert np.all(kr[:, :, S:] == 0)
     vt = untile_v_t(host(v_t))
-    assert np.array_equal(vt[..., :T].transpose(0, 3, 1, 2), v)  # exact copy
-    assert np.all(vt[..., T:] == 0)
+    assert np.array_equal(vt[..., kept:S].transpose(0, 3, 1, 2), v)  # exact copies
+    assert np.array_equal(vt[..., :kept].transpose(0, 3, 1, 2), prior_v)
+    assert np.all(vt[..., S:] == 0)
     kch, vch = host(kc), host(vc)
     written = np.arange(T) if window == 0 else np.arange(max(0, T - window), T)
     for t in written:
@@ -121,7 +134,7 @@ def test_kv_append_intermediates(window, pos_offset, T):
         assert_parity(kch[:, :, slot], kn[:, t], TOL_BF16, f"k_cache slot {slot}")
         assert np.array_equal(vch[:, :, slot], v[:, t])
     touched = {(pos_offset + t) if window == 0 else (pos_offset + t) % window for t in written}
-    untouched = [s for s in range(cap) if s not in touched]
+    untouched = [s for s in range(cap) if s not in touched and s not in set(prior.tolist())]
     assert np.all(np.isnan(kch[:, :, untouched])) and np.all(np.isnan(vch[:, :, untouched]))
 
 
@@ -333,3 +346,38 @@ def test_prefill_then_decode_matches_oracle(window):
     rows = np.concatenate([np.array([0, 1, T // 2, T - 1]), T + np.arange(steps)])
     ref = oracle_prefill(q, k, v, window=window, rope=rope, wq=wq, wk=wk, norm_offset=1.0, rows=rows)
     assert_parity(got[:, rows], ref, TOL_BF16, f"prefill+decode W={window}")
+
+
+@pytest.mark.parametrize("window,chunks,bf16", [(0, [100, 37, 300], True), (16, [5, 20, 3, 40], True),
+                                                (2048, [1500, 700, 900, 64], True),
+                                                (128, [200, 1, 311], False)],
+                         ids=["global", "ring16", "ring2048", "fp32_ring128"])
+def test_chunked_prefill_matches_oracle(window, chunks, bf16):
+    """A prefill in chunks (pos_offset > 0: each chunk attends the cached keys the previous
+    chunks left, then appends itself) equals the oracle run on the same token stream
+    chunk by chunk (「PLaMo 3アーキテクチャ徹底解析」 §4.4, §10)."""
+    B, Hq, Hkv, d = 2, 8, 2, 128
+    n = sum(chunks)
+    rope = Rope(1e4) if window else Rope(1e6, 64.0)
+    dr = Draw(777 + window + n, bf16)
+    q, k, v = dr.normal((B, n, Hq, d)), dr.normal((B, n, Hkv, d)), dr.normal((B, n, Hkv, d))
+    wq, wk = (dr.normal((d,), 0.02), dr.normal((d,), 0.02)) if bf16 else (None, None)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    cap = window if window else n
+    kc = torch.zeros((B, Hkv, cap, d), dtype=dt, device="cuda")
+    vc = torch.zeros_like(kc)
+    tab = rope_table(rope, n + 64)
+    put = lambda x: dev(x, bf16)
+    norm = dict(q_norm_w=put(wq), k_norm_w=put(wk), norm_offset=1.0) if bf16 else {}
+    got, p = [], 0
+    for T in chunks:
+        bufs = layer.prefill(put(q[:, p:p + T]), put(k[:, p:p + T]), put(v[:, p:p + T]), window=window,
+                             rope_table=tab, k_cache=kc, v_cache=vc, pos_offset=p, **norm)
+        torch.cuda.synchronize()
+        got.append(host(bufs.out))
+        p += T
+    rows_of = lambda T: np.unique(np.array([0, 1, T // 3, T // 2, T - 2, T - 1]).clip(0, T - 1))
+    ref = oracle_chunks(q, k, v, chunks, window=window, rope=rope, wq=wq, wk=wk, rows_of=rows_of)
+    for i, (g, r) in enumerate(zip(got, ref)):
+        assert_parity(g[:, rows_of(chunks[i])], r, TOL_BF16 if bf16 else TOL_F32,
+                      f"chunk {i} (T={chunks[i]}) W={window}")
