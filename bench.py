@@ -5,8 +5,9 @@ shape (B=1, T=8192, Hq=64, Hkv=8, d=128, W=2048): plamo_kv_append (QK norm, cach
 write, RoPE, prefill operands) + plamo_attn_prefill, inputs resident in HBM. ``value``
 is algorithmic prefill FLOP (4*d per attended (query, key) pair and query head) per
 second of that step. Also reported: the global-layer prefill (T=32768, YaRN), batched
-decode (B=64; ring W=2048 and global 32768) as KV-read GB/s, both prefills fed in
-chunks (2048 local, 8192 global) after cached tokens, the 8-layer period decode
+decode (B=64; ring W=2048 and global 32768) as KV-read GB/s, the same global decode with
+each sequence at its own position (ragged), both prefills fed in chunks (2048 local, 8192
+global) after cached tokens, the 8-layer period decode
 at 131072 context, the roofline object of the prefill kernel, and the CPU oracle timed
 on a bounded sample of the headline workload.
 
@@ -194,6 +195,49 @@ def bench_decode_batched(torch, swg, wl, layer_idx, steps, warmup):
                 keys=wl.keys_attended(ly), ms=ms, gbs=nbytes / ms / 1e6, frac_hbm=nbytes / ms / 1e6 / PEAK_HBM_GBS)
 
 
+def bench_decode_ragged(torch, swg, wl, layer_idx, steps, warmup):
+    """attn_decode of a ragged batch: the batched-decode shape with every sequence at its own
+    position (uniform in [0, max], seeded), the cache at the largest one's size."""
+    from sliding_window_global_amd import layer
+    from synthetic.workloads import RAGGED_DECODE_SEED, device_normal_bf16, ragged_positions
+    ly = wl.layers[layer_idx]
+    pos = ragged_positions(wl.B, wl.pos_offset, RAGGED_DECODE_SEED)
+    maxp = int(pos.max())
+    cap = wl.cache_cap(ly)
+    kc = device_normal_bf16((wl.B, wl.Hkv, cap, wl.d), wl.cache_seed(layer_idx), "cuda")
+    vc = device_normal_bf16((wl.B, wl.Hkv, cap, wl.d), wl.cache_seed(layer_idx) + 1, "cuda")
+    new = wl.draw_new_tokens(0, layer_idx)
+    tab = swg.make_rope_table(maxp + 64, rope_params(swg, ly.rope))
+    sp = torch.from_numpy(pos).cuda()
+    bufs = layer.DecodeBuffers(wl.B, wl.Hq, wl.Hkv, wl.d, ly.window, maxp, ragged=True)
+    swg.plamo_kv_append_ragged(dev_bf16(torch, new["q"]), dev_bf16(torch, new["k"]), dev_bf16(torch, new["v"]),
+                               bufs.q_rot, window=ly.window, seq_pos_offsets=sp, max_pos_offset=maxp,
+                               rope_table=tab, q_norm_w=dev_bf16(torch, new["wq"]),
+                               k_norm_w=dev_bf16(torch, new["wk"]), norm_offset=wl.norm_offset,
+                               k_cache=kc, v_cache=vc)
+
+    def run():
+        swg.plamo_attn_decode_ragged(bufs.q_rot, kc, vc, bufs.out, bufs.workspace, window=ly.window,
+                                     seq_pos_offsets=sp, max_pos_offset=maxp, rope_table=tab)
+
+    for _ in range(warmup):
+        run()
+    t = Timer(torch)
+    for _ in range(steps):
+        a, b = t.span()
+        a.record()
+        run()
+        b.record()
+    ms = t.mean_ms()
+    keys = [int(p) + 1 if ly.window == 0 else min(int(p), ly.window - 1) + 1 for p in pos]
+    nbytes = 2 * 2 * wl.Hkv * wl.d * sum(keys)
+    del kc, vc
+    torch.cuda.empty_cache()
+    return dict(workload=f"ragged_decode_B{wl.B}_{'global' if ly.window == 0 else 'local'}_max{maxp + 1}",
+                kv_bytes=nbytes, mean_keys=sum(keys) / len(keys), ms=ms, gbs=nbytes / ms / 1e6,
+                frac_hbm=nbytes / ms / 1e6 / PEAK_HBM_GBS)
+
+
 def bench_period(torch, swg, wl, n_steps):
     """The 8-layer period (7 local W=2048 + 1 global), append + decode per layer per step,
     at 131072+k global context, batch 8."""
@@ -311,6 +355,10 @@ def main():
             r = bench_decode_batched(torch, swg, BATCHED_DECODE, li, args.steps, args.warmup)
             log(f"[bench]   {r}")
             extra[r["workload"]] = r
+        log("[bench] ragged batched decode, global layer")
+        r = bench_decode_ragged(torch, swg, BATCHED_DECODE, 1, args.steps, args.warmup)
+        log(f"[bench]   {r}")
+        extra[r["workload"]] = r
     if only in ("", "period"):
         log("[bench] 8-layer period decode")
         r = bench_period(torch, swg, PERIOD_DECODE, args.period_steps)

@@ -30,7 +30,8 @@
  *     tensors and arithmetic (prefill path only).
  *   - Head dimension d must be 128 (PLaMo 3's head_dim [P3 §2.1]); Hq must be a
  *     multiple of Hkv and Hq/Hkv <= 16.
- *   - Positions are 64-bit; one pos_offset serves every sequence of the batch.
+ *   - Positions are 64-bit; one pos_offset serves every sequence of the batch
+ *     (the *_ragged calls take one position per sequence).
  *   - Entry points hold no mutable global state and may be called from several
  *     host threads on different streams.
  */
@@ -175,6 +176,60 @@ PLAMO_API int plamo_attn_decode(int dtype, const void* q_rot, const void* k_cach
                       size_t workspace_bytes, int B, int T, int Hq, int Hkv, int d,
                       int window, long long pos_offset, const void* rope_table,
                       size_t rope_table_bytes, float softmax_scale, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Ragged batches: every sequence at its own position [P3 §4.4]
+ *
+ * The three calls below are plamo_kv_append, plamo_attn_prefill and
+ * plamo_attn_decode for a batch whose sequences sit at different positions and
+ * (append, prefill) carry different numbers of new tokens. Tensors keep the padded
+ * batch layout of the uniform calls with T = the largest token count: sequence b
+ * uses rows 0 .. seq_lens[b]-1 of its [T, ...] slab; its other rows of q_out and
+ * out are left untouched and its other input rows are not read.
+ *
+ * seq_pos_offsets  device int64 [B]: absolute position of sequence b's first new
+ *                  token. Required, 8-byte aligned.
+ * seq_lens         device int32 [B]: new tokens of sequence b (0 .. T; 0 = the
+ *                  sequence sits this call out). NULL = T for every sequence.
+ *                  4-byte aligned.
+ * max_pos_offset   host bound of every seq_pos_offsets entry. The library validates
+ *                  cache capacity, rope table, operand sizes and workspace against
+ *                  it, exactly as it validates pos_offset in the uniform calls: for
+ *                  sequence b, kept_b = seq_pos_offsets[b] (global) or
+ *                  min(seq_pos_offsets[b], window-1) (local), and all sizes
+ *                  plamo_prefill_padded_len is that of the uniform call at
+ *                  pos_offset = max_pos_offset.
+ * The kernels read the arrays on the device and clamp each entry into
+ * [0, max_pos_offset] and [0, T], so a wrong entry can only give its own sequence a
+ * wrong result, never an access outside the buffers.
+ * Operand rows of sequence b: 0 .. kept_b-1 cached keys, kept_b .. kept_b+n_b-1 its
+ * new tokens, zero up to Tp. Decode needs plamo_kv_append_ragged(T = 1) before it and
+ * a workspace of plamo_attn_decode_ragged_workspace_bytes(...) bytes (NULL allowed
+ * when that is 0): its key ranges are planned for the longest sequence and cut finer
+ * than the uniform call's, so that sequences of different lengths even out.
+ * ------------------------------------------------------------------------- */
+PLAMO_API size_t plamo_attn_decode_ragged_workspace_bytes(int B, int Hq, int Hkv, int d,
+                                                int window, long long max_pos_offset);
+
+PLAMO_API int plamo_kv_append_ragged(int dtype, const void* q, const void* k, const void* v,
+                    const void* q_norm_w, const void* k_norm_w, float norm_offset,
+                    float norm_eps, void* q_out, void* k_rot_out, void* v_t_out,
+                    void* k_cache, void* v_cache, long long cap, int B, int T, int Hq,
+                    int Hkv, int d, int window, const long long* seq_pos_offsets,
+                    const int* seq_lens, long long max_pos_offset, const void* rope_table,
+                    size_t rope_table_bytes, void* stream);
+
+PLAMO_API int plamo_attn_prefill_ragged(int dtype, const void* q_rot, const void* k_rot,
+                    const void* v_t, void* out, int B, int T, int Hq, int Hkv, int d,
+                    int window, const long long* seq_pos_offsets, const int* seq_lens,
+                    long long max_pos_offset, float softmax_scale, void* stream);
+
+PLAMO_API int plamo_attn_decode_ragged(int dtype, const void* q_rot, const void* k_cache,
+                    const void* v_cache, long long cap, void* out, void* workspace,
+                    size_t workspace_bytes, int B, int Hq, int Hkv, int d, int window,
+                    const long long* seq_pos_offsets, long long max_pos_offset,
+                    const void* rope_table, size_t rope_table_bytes, float softmax_scale,
+                    void* stream);
 
 /* Human-readable text for a status code (static storage). */
 PLAMO_API const char* plamo_status_str(int status);

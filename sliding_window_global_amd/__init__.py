@@ -25,7 +25,9 @@ __all__ = [
     "PlamoError", "RopeParams", "LOCAL_ROPE", "GLOBAL_ROPE",
     "plamo_rope_table_bytes", "plamo_rope_table_init", "make_rope_table",
     "plamo_prefill_padded_len", "plamo_kv_append", "plamo_attn_prefill",
-    "plamo_attn_decode_workspace_bytes", "plamo_attn_decode", "library_path",
+    "plamo_attn_decode_workspace_bytes", "plamo_attn_decode", "plamo_kv_append_ragged",
+    "plamo_attn_prefill_ragged", "plamo_attn_decode_ragged_workspace_bytes", "plamo_attn_decode_ragged",
+    "library_path",
 ]
 
 
@@ -213,3 +215,100 @@ def plamo_attn_decode(q_rot, k_cache, v_cache, out, workspace, *, window: int, p
         int(window), int(pos_offset), _dev(rope_table, "rope_table", torch.float32), rope_table.numel() * 4,
         scale, _stream(stream))
     _check(st, "plamo_attn_decode")
+
+
+# ----------------------------------------------------------------------------
+# ragged batches: one position (and, for append / prefill, one token count) per sequence
+# ----------------------------------------------------------------------------
+
+def _ragged_arrays(B: int, seq_pos_offsets, seq_lens):
+    if seq_pos_offsets is None or tuple(seq_pos_offsets.shape) != (B,):
+        raise ValueError("seq_pos_offsets must be an int64 GPU tensor of shape [B]")
+    if seq_lens is not None and tuple(seq_lens.shape) != (B,):
+        raise ValueError("seq_lens must be an int32 GPU tensor of shape [B]")
+    return _dev(seq_pos_offsets, "seq_pos_offsets", torch.int64), _dev(seq_lens, "seq_lens", torch.int32)
+
+
+def plamo_kv_append_ragged(q, k, v, q_out, *, window: int, seq_pos_offsets, max_pos_offset: int,
+                           rope_table, seq_lens=None, q_norm_w=None, k_norm_w=None,
+                           norm_offset: float = 1.0, norm_eps: float = 1e-6, k_rot_out=None, v_t_out=None,
+                           k_cache=None, v_cache=None, stream=None) -> None:
+    """plamo_kv_append with per-sequence positions seq_pos_offsets [B] (int64, GPU) bounded by
+    max_pos_offset and token counts seq_lens [B] (int32, GPU; None = T each)."""
+    dt = q.dtype
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, T, Hkv, d) or tuple(v.shape) != (B, T, Hkv, d):
+        raise ValueError("k and v must be [B, T, Hkv, d] matching q")
+    if tuple(q_out.shape) != (B, T, Hq, d):
+        raise ValueError("q_out must match q")
+    k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dt, window, max_pos_offset)
+    if k_rot_out is not None and tuple(k_rot_out.shape) != k_shape:
+        raise ValueError(f"k_rot_out must be {list(k_shape)}")
+    if v_t_out is not None and tuple(v_t_out.shape) != v_shape:
+        raise ValueError(f"v_t_out must be {list(v_shape)}")
+    cap = 0
+    if k_cache is not None:
+        cap = k_cache.shape[2]
+        if tuple(k_cache.shape) != (B, Hkv, cap, d) or v_cache is None or tuple(v_cache.shape) != tuple(k_cache.shape):
+            raise ValueError("caches must both be [B, Hkv, cap, d]")
+    pos_p, len_p = _ragged_arrays(B, seq_pos_offsets, seq_lens)
+    st = _lib.load().plamo_kv_append_ragged(
+        _dtype_code(dt), _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt),
+        _dev(q_norm_w, "q_norm_w", dt), _dev(k_norm_w, "k_norm_w", dt), float(norm_offset), float(norm_eps),
+        _dev(q_out, "q_out", dt), _dev(k_rot_out, "k_rot_out", dt), _dev(v_t_out, "v_t_out", dt),
+        _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), int(cap), B, T, Hq, Hkv, d,
+        int(window), pos_p, len_p, int(max_pos_offset), _dev(rope_table, "rope_table", torch.float32),
+        rope_table.numel() * 4, _stream(stream))
+    _check(st, "plamo_kv_append_ragged")
+
+
+def plamo_attn_prefill_ragged(q_rot, k_rot, v_t, out, *, window: int, seq_pos_offsets, max_pos_offset: int,
+                              seq_lens=None, softmax_scale: float | None = None, stream=None) -> None:
+    """plamo_attn_prefill with per-sequence positions and token counts (as plamo_kv_append_ragged)."""
+    dt = q_rot.dtype
+    B, T, Hq, d = q_rot.shape
+    Hkv = k_rot.shape[1]
+    k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dt, window, max_pos_offset)
+    if tuple(k_rot.shape) != k_shape or tuple(v_t.shape) != v_shape:
+        raise ValueError(f"k_rot must be {list(k_shape)} and v_t {list(v_shape)}")
+    if tuple(out.shape) != (B, T, Hq, d):
+        raise ValueError("out must match q_rot")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    pos_p, len_p = _ragged_arrays(B, seq_pos_offsets, seq_lens)
+    st = _lib.load().plamo_attn_prefill_ragged(
+        _dtype_code(dt), _dev(q_rot, "q_rot", dt), _dev(k_rot, "k_rot", dt), _dev(v_t, "v_t", dt),
+        _dev(out, "out", dt), B, T, Hq, Hkv, d, int(window), pos_p, len_p, int(max_pos_offset), scale,
+        _stream(stream))
+    _check(st, "plamo_attn_prefill_ragged")
+
+
+def plamo_attn_decode_ragged_workspace_bytes(B: int, Hq: int, Hkv: int, window: int, max_pos_offset: int,
+                                             d: int = HEAD_DIM) -> int:
+    return int(_lib.load().plamo_attn_decode_ragged_workspace_bytes(B, Hq, Hkv, d, int(window),
+                                                                    int(max_pos_offset)))
+
+
+def plamo_attn_decode_ragged(q_rot, k_cache, v_cache, out, workspace, *, window: int, seq_pos_offsets,
+                             max_pos_offset: int, rope_table, softmax_scale: float | None = None,
+                             stream=None) -> None:
+    """plamo_attn_decode with one position per sequence; workspace sized by
+    plamo_attn_decode_ragged_workspace_bytes."""
+    dt = q_rot.dtype
+    B, T, Hq, d = q_rot.shape
+    if T != 1:
+        raise ValueError("decode takes one token per sequence")
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, cap, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches must both be [B, Hkv, cap, d]")
+    if tuple(out.shape) != (B, T, Hq, d):
+        raise ValueError("out must match q_rot")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    pos_p, _ = _ragged_arrays(B, seq_pos_offsets, None)
+    st = _lib.load().plamo_attn_decode_ragged(
+        _dtype_code(dt), _dev(q_rot, "q_rot", dt), _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        int(cap), _dev(out, "out", dt), _dev(workspace, "workspace"), ws_bytes, B, Hq, Hkv, d, int(window),
+        pos_p, int(max_pos_offset), _dev(rope_table, "rope_table", torch.float32), rope_table.numel() * 4,
+        scale, _stream(stream))
+    _check(st, "plamo_attn_decode_ragged")

@@ -119,11 +119,25 @@ int plamo_rope_table_init(void* table, size_t table_bytes, long long max_pos, in
                                            j_low, j_high, amp, static_cast<hipStream_t>(stream)));
 }
 
-int plamo_kv_append(int dtype, const void* q, const void* k, const void* v, const void* q_norm_w,
-                    const void* k_norm_w, float norm_offset, float norm_eps, void* q_out,
-                    void* k_rot_out, void* v_t_out, void* k_cache, void* v_cache, long long cap,
-                    int B, int T, int Hq, int Hkv, int d, int window, long long pos_offset,
-                    const void* rope_table, size_t rope_table_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Per-sequence arrays of a ragged batch: device memory, 8- and 4-byte aligned.
+int check_ragged(const long long* seq_pos, const int* seq_len) {
+  if (!seq_pos) return fail(PLAMO_ERR_INVALID_ARG, "seq_pos_offsets must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(seq_pos) & 7u) return fail(PLAMO_ERR_INVALID_ARG, "seq_pos_offsets must be 8-byte aligned");
+  if (reinterpret_cast<uintptr_t>(seq_len) & 3u) return fail(PLAMO_ERR_INVALID_ARG, "seq_lens must be 4-byte aligned");
+  return PLAMO_OK;
+}
+
+// pos_offset is the batch's position (uniform) or the bound of every seq_pos entry (ragged).
+int kv_append_impl(int dtype, const void* q, const void* k, const void* v, const void* q_norm_w,
+                   const void* k_norm_w, float norm_offset, float norm_eps, void* q_out,
+                   void* k_rot_out, void* v_t_out, void* k_cache, void* v_cache, long long cap,
+                   int B, int T, int Hq, int Hkv, int d, int window, long long pos_offset,
+                   const long long* seq_pos, const int* seq_len, const void* rope_table,
+                   size_t rope_table_bytes, void* stream) {
   if (dtype != PLAMO_F32 && dtype != PLAMO_BF16) return fail(PLAMO_ERR_INVALID_ARG, "unknown dtype");
   if (int st = check_heads(B, T, Hq, Hkv, d, window, pos_offset)) return st;
   if (B == 0 || T == 0) return ok();
@@ -156,14 +170,16 @@ int plamo_kv_append(int dtype, const void* q, const void* k, const void* v, cons
   a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.window = window;
   a.Tp = plamo_prefill_padded_len(kept + T);
   a.pos_offset = pos_offset; a.kept = kept;
+  a.seq_pos = seq_pos; a.seq_len = seq_len;
+  a.ops_kernel = (k_rot_out || v_t_out) && (kept > 0 || seq_pos || seq_len);
   a.rope = static_cast<const float2*>(rope_table);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return launched(dtype == PLAMO_BF16 ? plamo::launch_kv_append_bf16(a, s) : plamo::launch_kv_append_f32(a, s));
 }
 
-int plamo_attn_prefill(int dtype, const void* q_rot, const void* k_rot, const void* v_t, void* out,
-                       int B, int T, int Hq, int Hkv, int d, int window, long long pos_offset,
-                       float softmax_scale, void* stream) {
+int attn_prefill_impl(int dtype, const void* q_rot, const void* k_rot, const void* v_t, void* out,
+                      int B, int T, int Hq, int Hkv, int d, int window, long long pos_offset,
+                      const long long* seq_pos, const int* seq_len, float softmax_scale, void* stream) {
   if (dtype != PLAMO_F32 && dtype != PLAMO_BF16) return fail(PLAMO_ERR_INVALID_ARG, "unknown dtype");
   if (int st = check_heads(B, T, Hq, Hkv, d, window, pos_offset)) return st;
   if (B == 0 || T == 0) return ok();
@@ -182,23 +198,18 @@ int plamo_attn_prefill(int dtype, const void* q_rot, const void* k_rot, const vo
   a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.window = window;
   a.Tp = plamo_prefill_padded_len(kept + T);
   a.kept = kept;
+  a.pos_offset = pos_offset;
+  a.seq_pos = seq_pos; a.seq_len = seq_len;
   a.scale = softmax_scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return launched(dtype == PLAMO_BF16 ? plamo::launch_prefill_bf16(a, s) : plamo::launch_prefill_f32(a, s));
 }
 
-size_t plamo_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int window, long long pos_offset) {
-  if (check_heads(B, 1, Hq, Hkv, d, window, pos_offset) != PLAMO_OK) return 0;
-  if (B == 0) return 0;
-  const long long S = kept_tokens(window, pos_offset) + 1;
-  return plamo::decode_workspace_bytes(B, Hq, plamo::plan_decode(B, Hkv, S));
-}
-
-int plamo_attn_decode(int dtype, const void* q_rot, const void* k_cache, const void* v_cache,
-                      long long cap, void* out, void* workspace, size_t workspace_bytes, int B, int T,
-                      int Hq, int Hkv, int d, int window, long long pos_offset,
-                      const void* rope_table, size_t rope_table_bytes, float softmax_scale,
-                      void* stream) {
+int attn_decode_impl(int dtype, const void* q_rot, const void* k_cache, const void* v_cache,
+                     long long cap, void* out, void* workspace, size_t workspace_bytes, int B, int T,
+                     int Hq, int Hkv, int d, int window, long long pos_offset, const long long* seq_pos,
+                     const void* rope_table, size_t rope_table_bytes, float softmax_scale,
+                     void* stream) {
   if (dtype != PLAMO_BF16) return fail(dtype == PLAMO_F32 ? PLAMO_ERR_UNSUPPORTED : PLAMO_ERR_INVALID_ARG,
                                        "decode reads a bf16 cache");
   if (T != 1) return fail(T < 0 ? PLAMO_ERR_INVALID_ARG : PLAMO_ERR_UNSUPPORTED, "decode takes T = 1");
@@ -217,7 +228,7 @@ int plamo_attn_decode(int dtype, const void* q_rot, const void* k_cache, const v
   const long long covered = table_positions(rope_table_bytes);
   if (covered < 0) return fail(PLAMO_ERR_INVALID_ARG, "rope_table_bytes is not a whole number of rows");
   if (covered < S) return fail(PLAMO_ERR_WORKSPACE, "rope table does not cover positions < kept + 1");
-  const plamo::DecodePlan plan = plamo::plan_decode(B, Hkv, S);
+  const plamo::DecodePlan plan = plamo::plan_decode(B, Hkv, S, seq_pos != nullptr);
   const size_t need = plamo::decode_workspace_bytes(B, Hq, plan);
   if (need > 0 && (!workspace || workspace_bytes < need)) return fail(PLAMO_ERR_WORKSPACE, "workspace too small");
   if (static_cast<long long>(B) * Hq > 0x7fffffffLL) return fail(PLAMO_ERR_UNSUPPORTED, "grid too large");
@@ -227,9 +238,92 @@ int plamo_attn_decode(int dtype, const void* q_rot, const void* k_cache, const v
   a.ws = static_cast<float*>(workspace);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.window = window;
   a.S = S; a.base = pos_offset - kept; a.plan = plan;
+  a.pos_offset = pos_offset; a.seq_pos = seq_pos;
   a.rope = static_cast<const float2*>(rope_table);
   a.scale = softmax_scale;
   return launched(plamo::launch_decode_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int plamo_kv_append(int dtype, const void* q, const void* k, const void* v, const void* q_norm_w,
+                    const void* k_norm_w, float norm_offset, float norm_eps, void* q_out,
+                    void* k_rot_out, void* v_t_out, void* k_cache, void* v_cache, long long cap,
+                    int B, int T, int Hq, int Hkv, int d, int window, long long pos_offset,
+                    const void* rope_table, size_t rope_table_bytes, void* stream) {
+  return kv_append_impl(dtype, q, k, v, q_norm_w, k_norm_w, norm_offset, norm_eps, q_out, k_rot_out,
+                        v_t_out, k_cache, v_cache, cap, B, T, Hq, Hkv, d, window, pos_offset, nullptr,
+                        nullptr, rope_table, rope_table_bytes, stream);
+}
+
+int plamo_kv_append_ragged(int dtype, const void* q, const void* k, const void* v, const void* q_norm_w,
+                           const void* k_norm_w, float norm_offset, float norm_eps, void* q_out,
+                           void* k_rot_out, void* v_t_out, void* k_cache, void* v_cache, long long cap,
+                           int B, int T, int Hq, int Hkv, int d, int window,
+                           const long long* seq_pos_offsets, const int* seq_lens,
+                           long long max_pos_offset, const void* rope_table, size_t rope_table_bytes,
+                           void* stream) {
+  if (B > 0 && T > 0)
+    if (int st = check_ragged(seq_pos_offsets, seq_lens)) return st;
+  return kv_append_impl(dtype, q, k, v, q_norm_w, k_norm_w, norm_offset, norm_eps, q_out, k_rot_out,
+                        v_t_out, k_cache, v_cache, cap, B, T, Hq, Hkv, d, window, max_pos_offset,
+                        seq_pos_offsets, seq_lens, rope_table, rope_table_bytes, stream);
+}
+
+int plamo_attn_prefill(int dtype, const void* q_rot, const void* k_rot, const void* v_t, void* out,
+                       int B, int T, int Hq, int Hkv, int d, int window, long long pos_offset,
+                       float softmax_scale, void* stream) {
+  return attn_prefill_impl(dtype, q_rot, k_rot, v_t, out, B, T, Hq, Hkv, d, window, pos_offset, nullptr,
+                           nullptr, softmax_scale, stream);
+}
+
+int plamo_attn_prefill_ragged(int dtype, const void* q_rot, const void* k_rot, const void* v_t, void* out,
+                              int B, int T, int Hq, int Hkv, int d, int window,
+                              const long long* seq_pos_offsets, const int* seq_lens,
+                              long long max_pos_offset, float softmax_scale, void* stream) {
+  if (B > 0 && T > 0)
+    if (int st = check_ragged(seq_pos_offsets, seq_lens)) return st;
+  return attn_prefill_impl(dtype, q_rot, k_rot, v_t, out, B, T, Hq, Hkv, d, window, max_pos_offset,
+                           seq_pos_offsets, seq_lens, softmax_scale, stream);
+}
+
+size_t plamo_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int window, long long pos_offset) {
+  if (check_heads(B, 1, Hq, Hkv, d, window, pos_offset) != PLAMO_OK) return 0;
+  if (B == 0) return 0;
+  const long long S = kept_tokens(window, pos_offset) + 1;
+  return plamo::decode_workspace_bytes(B, Hq, plamo::plan_decode(B, Hkv, S, false));
+}
+
+size_t plamo_attn_decode_ragged_workspace_bytes(int B, int Hq, int Hkv, int d, int window,
+                                                long long max_pos_offset) {
+  if (check_heads(B, 1, Hq, Hkv, d, window, max_pos_offset) != PLAMO_OK) return 0;
+  if (B == 0) return 0;
+  const long long S = kept_tokens(window, max_pos_offset) + 1;
+  return plamo::decode_workspace_bytes(B, Hq, plamo::plan_decode(B, Hkv, S, true));
+}
+
+int plamo_attn_decode(int dtype, const void* q_rot, const void* k_cache, const void* v_cache,
+                      long long cap, void* out, void* workspace, size_t workspace_bytes, int B, int T,
+                      int Hq, int Hkv, int d, int window, long long pos_offset,
+                      const void* rope_table, size_t rope_table_bytes, float softmax_scale,
+                      void* stream) {
+  return attn_decode_impl(dtype, q_rot, k_cache, v_cache, cap, out, workspace, workspace_bytes, B, T, Hq,
+                          Hkv, d, window, pos_offset, nullptr, rope_table, rope_table_bytes,
+                          softmax_scale, stream);
+}
+
+int plamo_attn_decode_ragged(int dtype, const void* q_rot, const void* k_cache, const void* v_cache,
+                             long long cap, void* out, void* workspace, size_t workspace_bytes, int B,
+                             int Hq, int Hkv, int d, int window, const long long* seq_pos_offsets,
+                             long long max_pos_offset, const void* rope_table, size_t rope_table_bytes,
+                             float softmax_scale, void* stream) {
+  if (B > 0)
+    if (int st = check_ragged(seq_pos_offsets, nullptr)) return st;
+  return attn_decode_impl(dtype, q_rot, k_cache, v_cache, cap, out, workspace, workspace_bytes, B, 1, Hq,
+                          Hkv, d, window, max_pos_offset, seq_pos_offsets, rope_table, rope_table_bytes,
+                          softmax_scale, stream);
 }
 
 }  // extern "C"

@@ -91,12 +91,15 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   E* __restrict__ k_cache = static_cast<E*>(a.k_cache);
   E* __restrict__ v_cache = static_cast<E*>(a.v_cache);
   const bool norm = wq != nullptr;
-  const int n_tok = min(kTokBlock, a.T - t0);  // may be <= 0 in the padding blocks
+  // this sequence's first position, kept keys and token count (a.T is the row stride)
+  const SeqPos sp = seq_pos_of(a.seq_pos, a.seq_len, a.pos_offset, a.T, a.window, b);
+  const int n_tok = min(kTokBlock, sp.T - t0);  // may be <= 0 in the padding blocks
+  if (n_tok <= 0 && (a.ops_kernel || !(k_rot || v_t))) return;  // block-uniform
 
   // rotation factors of this block's renumbered positions kept + t
   for (int i = threadIdx.x; i < kTokBlock * kHalf; i += kThreads) {
     const int r = i / kHalf, j = i % kHalf;
-    if (r < n_tok) zs[r][j] = rope_factor(a.rope, a.kept + t0 + r, j);
+    if (r < n_tok) zs[r][j] = rope_factor(a.rope, sp.kept + t0 + r, j);
   }
   float gq[2 * kVec], gk[2 * kVec];  // gains c + w of this lane's dims (both halves)
 #pragma unroll
@@ -156,8 +159,8 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
         if (is_k) {
 #pragma unroll
           for (int e = 0; e < 2 * kVec; ++e) x[u][e] = Io<E>::rnd(x[u][e]);  // the cached value
-          if (k_cache && (a.window == 0 || t >= a.T - a.window)) {
-            const long long n = a.pos_offset + t;
+          if (k_cache && (a.window == 0 || t >= sp.T - a.window)) {
+            const long long n = sp.pos + t;
             const long long s = a.window == 0 ? n : n % a.window;
             E* dst = k_cache + ((static_cast<long long>(b) * a.Hkv + kvh) * a.cap + s) * kHeadDim + c * kVec;
             *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(x[u]);
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
           y[kVec + e] = x0 * z.y + x1 * z.x;
         }
         // the operand row of new token t follows the kept cached keys
-        const long long R = a.kept + t;
+        const long long R = sp.kept + t;
         if (kTiled && is_k) {  // chunks c and c + 8 of key R within its tile
           E* dst = k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + (R & ~63LL)) * kHeadDim +
                    (c * kTokBlock + (R & 63)) * kVec;
@@ -192,16 +195,16 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   rows(q, n_tok * G, false, 0);
   rows(k, n_tok, true, 1);
 
-  if (k_rot && a.kept == 0) {  // zero the padding rows T .. Tp-1 of this block
+  if (k_rot && !a.ops_kernel) {  // zero the padding rows T .. Tp-1 of this block
     for (int i = threadIdx.x; i < kTokBlock * (kHeadDim / kVec); i += kThreads) {
       if (kTiled) {  // i = chunk * 64 + key in tile
         const long long t = t0 + i % kTokBlock;
-        if (t >= a.T && t < a.Tp)
+        if (t >= sp.T && t < a.Tp)
           reinterpret_cast<u32x4*>(k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t0) * kHeadDim)[i] =
               u32x4{0, 0, 0, 0};
       } else {
         const long long t = t0 + i / (kHeadDim / kVec);
-        if (t >= a.T && t < a.Tp)
+        if (t >= sp.T && t < a.Tp)
           reinterpret_cast<u32x4*>(k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t) * kHeadDim)
               [i % (kHeadDim / kVec)] = u32x4{0, 0, 0, 0};
       }
@@ -213,8 +216,8 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   if (v_cache) {
     for (int i = (threadIdx.x + kThreads - 128) % kThreads; i < n_tok * kChunks; i += kThreads) {  // from wave 2
       const int t = t0 + i / kChunks;
-      if (!(a.window == 0 || t >= a.T - a.window)) continue;
-      const long long n = a.pos_offset + t;
+      if (!(a.window == 0 || t >= sp.T - a.window)) continue;
+      const long long n = sp.pos + t;
       const long long s = a.window == 0 ? n : n % a.window;
       const int cidx = i % kChunks;
       const long long row = ((static_cast<long long>(b) * a.T + t) * a.Hkv + kvh) * kHeadDim;
@@ -222,14 +225,14 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
       reinterpret_cast<u32x4*>(v_cache + crow)[cidx] = reinterpret_cast<const u32x4*>(v + row)[cidx];
     }
   }
-  if (v_t && a.kept == 0) {  // (after cached keys the operand kernel writes all of V^T)
+  if (v_t && !a.ops_kernel) {  // (otherwise the operand kernel writes all of V^T)
     constexpr int kTS = kTokBlock + kVec;  // LDS row stride (tokens), keeps rows 16-byte aligned
     __shared__ __attribute__((aligned(16))) E tile[kHeadDim * kTS];
     for (int i = threadIdx.x; i < kTokBlock * kChunks; i += kThreads) {
       const int r = i / kChunks, cidx = i % kChunks;
       const int t = t0 + r;
       E x[kVec];
-      if (t < a.T) {
+      if (t < sp.T) {
         const u32x4 w = reinterpret_cast<const u32x4*>(v + ((static_cast<long long>(b) * a.T + t) * a.Hkv + kvh) * kHeadDim)[cidx];
         __builtin_memcpy(x, &w, 16);
       } else {
@@ -262,12 +265,13 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   }
 }
 
-// Prefill operands of a chunk that follows kept > 0 cached keys (「PLaMo 3アーキテクチャ徹底解析」
-// §4.4: the attention reads every key the cache returns). One block = one 64-key operand
-// tile of one (sequence, KV head): K' rows of the kept keys (pre-RoPE K from the cache,
-// rotated at their renumbered positions 0 .. kept-1), V^T of all kept + T keys (cached V,
-// then the chunk's own V), zeros past kept + T. Runs before the append kernel, which may
-// overwrite ring slots these keys still occupy and writes the chunk's own K' rows.
+// Prefill operands of a chunk that follows kept > 0 cached keys, or of a ragged batch
+// (「PLaMo 3アーキテクチャ徹底解析」 §4.4: the attention reads every key the cache returns).
+// One block = one 64-key operand tile of one (sequence, KV head): K' rows of the kept keys
+// (pre-RoPE K from the cache, rotated at their renumbered positions 0 .. kept-1), V^T of
+// all kept + T keys (cached V, then the chunk's own V), zeros past kept + T, with kept and
+// T those of the block's sequence. Runs before the append kernel, which may overwrite
+// ring slots these keys still occupy and writes the chunk's own K' rows.
 template <typename E>
 __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a) {
   constexpr int kVec = 16 / sizeof(E);
@@ -286,8 +290,10 @@ __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a
   const long long R0 = static_cast<long long>(blockIdx.x) * kTokBlock;  // first operand row
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
-  const long long S = a.kept + a.T;
-  const long long base = a.pos_offset - a.kept;  // absolute position of renumbered key 0
+  const SeqPos sp = seq_pos_of(a.seq_pos, a.seq_len, a.pos_offset, a.T, a.window, b);
+  const long long kept = sp.kept;
+  const long long S = kept + sp.T;
+  const long long base = sp.pos - kept;  // absolute position of renumbered key 0
   const long long bh = static_cast<long long>(b) * a.Hkv + kvh;
   const E* __restrict__ kc = static_cast<const E*>(a.k_cache) + bh * a.cap * kHeadDim;
   const E* __restrict__ vc = static_cast<const E*>(a.v_cache) + bh * a.cap * kHeadDim;
@@ -302,14 +308,14 @@ __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a
   if (k_rot) {
     for (int i = threadIdx.x; i < kTokBlock * kHalf; i += kThreads) {
       const int r = i / kHalf, j = i % kHalf;
-      if (R0 + r < a.kept) zs[r][j] = rope_factor(a.rope, R0 + r, j);
+      if (R0 + r < kept) zs[r][j] = rope_factor(a.rope, R0 + r, j);
     }
     __syncthreads();
     for (int r = wave * kRowsPerPass + slot; r < kTokBlock; r += kWaves * kRowsPerPass) {
       const long long R = R0 + r;
-      if (R >= a.kept && R < S) continue;  // the chunk's own keys: the append kernel
+      if (R >= kept && R < S) continue;  // the chunk's own keys: the append kernel
       float y[2 * kVec];
-      if (R < a.kept) {
+      if (R < kept) {
         float x[2 * kVec];
         const E* src = kc + cache_row(R) + c * kVec;
         Io<E>::unpack(*reinterpret_cast<const u32x4*>(src), x);
@@ -342,8 +348,8 @@ __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a
       const long long R = R0 + r;
       E x[kVec];
       if (R < S) {
-        const E* src = R < a.kept ? vc + cache_row(R)
-                                  : v + ((static_cast<long long>(b) * a.T + (R - a.kept)) * a.Hkv + kvh) * kHeadDim;
+        const E* src = R < kept ? vc + cache_row(R)
+                                : v + ((static_cast<long long>(b) * a.T + (R - kept)) * a.Hkv + kvh) * kHeadDim;
         const u32x4 w = reinterpret_cast<const u32x4*>(src)[cidx];
         __builtin_memcpy(x, &w, 16);
       } else {
@@ -374,14 +380,14 @@ __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a
 template <typename E>
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   const bool operands = a.k_rot_out || a.v_t_out;
-  if (operands && a.kept > 0) {
+  if (operands && a.ops_kernel) {
     const unsigned tiles = static_cast<unsigned>(a.Tp / kTokBlock);
     hipLaunchKernelGGL(prefill_operands_kernel<E>, dim3(tiles, a.Hkv, a.B), dim3(kThreads), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // with kept == 0 the append kernel also covers the padding tokens T .. Tp-1
-  const long long tokens = (operands && a.kept == 0) ? a.Tp : a.T;
+  // without the operand kernel the append kernel also covers the padding tokens T .. Tp-1
+  const long long tokens = (operands && !a.ops_kernel) ? a.Tp : a.T;
   const unsigned gx = static_cast<unsigned>((tokens + kTokBlock - 1) / kTokBlock);
   hipLaunchKernelGGL(kv_append_kernel<E>, dim3(gx, a.Hkv, a.B), dim3(kThreads), 0, stream, a);
   return hipGetLastError();

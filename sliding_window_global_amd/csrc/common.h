@@ -60,6 +60,34 @@ __device__ __forceinline__ float2 rope_factor(const float2* __restrict__ table, 
   return make_float2(c.x * f.x - c.y * f.y, c.x * f.y + c.y * f.x);
 }
 
+// Positions of sequence b of a batch (「PLaMo 3アーキテクチャ徹底解析」 §4.4): its first new
+// token sits at absolute position `pos`, the cache returns `kept` earlier tokens (all of
+// them on a global layer, at most window - 1 on a local one) and the call carries `T` new
+// tokens. A uniform batch passes no per-sequence arrays. A ragged batch passes seq_pos
+// (and, for more than one new token, seq_len) in device memory; each value is clamped to
+// the bounds the host validated (0 .. pos_max, 0 .. T_max), so a bad entry can give a
+// wrong result for its own sequence but never an access outside the buffers.
+struct SeqPos {
+  long long pos;
+  long long kept;
+  int T;
+};
+__device__ __forceinline__ SeqPos seq_pos_of(const long long* seq_pos, const int* seq_len, long long pos_max,
+                                             int T_max, int window, int b) {
+  long long p = pos_max;
+  if (seq_pos) {
+    p = seq_pos[b];
+    p = p < 0 ? 0 : (p > pos_max ? pos_max : p);
+  }
+  int t = T_max;
+  if (seq_len) {
+    t = seq_len[b];
+    t = t < 0 ? 0 : (t > T_max ? T_max : t);
+  }
+  const long long kept = window == 0 ? p : (p < window - 1 ? p : static_cast<long long>(window - 1));
+  return SeqPos{p, kept, t};
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);

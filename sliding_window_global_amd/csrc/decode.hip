@@ -72,8 +72,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   const int b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
 
+  // keys of this sequence: all of them on a uniform batch, its own count on a ragged one
+  long long S = a.S, base = a.base;
+  if (a.seq_pos) {
+    const SeqPos sp = seq_pos_of(a.seq_pos, nullptr, a.pos_offset, 1, a.window, b);
+    S = sp.kept + 1;
+    base = sp.pos - sp.kept;
+  }
   const long long s_begin = static_cast<long long>(split) * a.plan.chunk;
-  const long long s_end = min(a.S, s_begin + a.plan.chunk);
+  if (s_begin >= S) return;  // (ragged) a shorter sequence has fewer ranges; block-uniform
+  const long long s_end = min(S, s_begin + a.plan.chunk);
   const int n_tiles = static_cast<int>((s_end - s_begin + kTile - 1) / kTile);
   const bf16_t* __restrict__ kc =
       static_cast<const bf16_t*>(a.k_cache) + (static_cast<long long>(b) * a.Hkv + kvh) * a.cap * kHeadDim;
@@ -117,10 +125,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   // W >= 64), or base + tb + j on global layers.
   int t_issue = 0;
   long long tb_issue = s_begin;
-  int s0 = kMode != kContiguous ? static_cast<int>((a.base + s_begin) % a.window) : 0;
+  int s0 = kMode != kContiguous ? static_cast<int>((base + s_begin) % a.window) : 0;
   auto cache_row = [&](int j) __attribute__((always_inline)) {
     j = min(j, static_cast<int>(s_end - 1 - tb_issue));
-    if (kMode == kContiguous) return a.base + tb_issue + j;
+    if (kMode == kContiguous) return base + tb_issue + j;
     int sl = s0 + j;
     if (kMode == kRing) sl -= sl >= a.window ? a.window : 0;
     else sl %= a.window;
@@ -332,14 +340,19 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
 // One block per (sequence, query head): the split states are merged in a fixed order
 // (deterministic); thread d owns output component d. All loads (every split's m, l and
 // this thread's accumulators, up to kRegSplits of them in registers) go out together.
+// A sequence of a ragged batch merges only the ranges its keys reach.
 constexpr int kRegSplits = 32;
-__global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(const float* __restrict__ ws,
-                                                                  bf16_t* __restrict__ out,
-                                                                  int n_split) {
+__global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(DecodeArgs a) {
   __shared__ float ms[kMaxSplit], ls[kMaxSplit];
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
-  const float* p = ws + static_cast<long long>(bh) * n_split * kPartial;
+  int n_split = a.plan.n_split;
+  if (a.seq_pos) {
+    const SeqPos sp = seq_pos_of(a.seq_pos, nullptr, a.pos_offset, 1, a.window, bh / a.Hq);
+    n_split = static_cast<int>((sp.kept + 1 + a.plan.chunk - 1) / a.plan.chunk);
+  }
+  const float* p = a.ws + static_cast<long long>(bh) * a.plan.n_split * kPartial;
+  bf16_t* __restrict__ out = static_cast<bf16_t*>(a.out);
   float av[kRegSplits];
 #pragma unroll
   for (int i = 0; i < kRegSplits; ++i) av[i] = i < n_split ? p[i * kPartial + tid] : 0.f;
@@ -369,11 +382,13 @@ __global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(const float* _
 
 }  // namespace
 
-DecodePlan plan_decode(int B, int Hkv, long long S) {
+DecodePlan plan_decode(int B, int Hkv, long long S, bool ragged) {
   // Aim for ~512 blocks (2 per CU, one wave per SIMD each) with at least kMinChunk keys
-  // each and at most kMaxSplit ranges per (sequence, KV head).
+  // each and at most kMaxSplit ranges per (sequence, KV head). A ragged batch only knows
+  // its longest sequence here; its ranges are cut finer (~4 blocks per slot at the
+  // longest length) so that short and long sequences even out over the CUs.
   const long long pairs = static_cast<long long>(B) * Hkv;
-  const long long target_blocks = 512;
+  const long long target_blocks = ragged ? 4 * 512 : 512;
   long long n = (target_blocks + pairs - 1) / pairs;
   const long long by_min_chunk = (S + kMinChunk - 1) / kMinChunk;
   if (n > by_min_chunk) n = by_min_chunk;
@@ -403,8 +418,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(decode_split_kernel<kSmallRing>, grid, dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.plan.n_split == 1) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.Hq), dim3(kHeadDim), 0, stream, a.ws,
-                     static_cast<bf16_t*>(a.out), a.plan.n_split);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.Hq), dim3(kHeadDim), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -26,12 +26,15 @@ struct AppendArgs {
   long long cap;
   int B, T, Hq, Hkv, window;
   long long Tp;          // padded key count of the prefill operands (kept + T keys)
-  long long pos_offset;  // absolute position of the first new token
-  long long kept;        // cached tokens returned before the new ones
+  long long pos_offset;  // absolute position of the first new token (ragged: the largest)
+  long long kept;        // cached tokens returned before the new ones (ragged: the largest)
+  const long long* seq_pos;  // ragged batch: per-sequence pos_offset (device), else NULL
+  const int* seq_len;        // ragged batch: per-sequence new-token count (device), else NULL
+  bool ops_kernel;           // the operand kernel writes every operand row outside the chunk
   const float2* rope;
 };
-// Both launch, when a chunk follows kept > 0 cached tokens and prefill operands are
-// requested, first the operand kernel (the kept keys from the cache, all of V^T and the
+// Both launch, when prefill operands are requested after cached tokens or for a ragged
+// batch, first the operand kernel (the kept keys from the cache, all of V^T and the
 // padding) and then the append kernel (new tokens).
 hipError_t launch_kv_append_bf16(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_kv_append_f32(const AppendArgs& a, hipStream_t stream);
@@ -44,6 +47,9 @@ struct PrefillArgs {
   int B, T, Hq, Hkv, window;
   long long Tp;    // padded key count of K', V^T
   long long kept;  // keys before the chunk: query t sits at renumbered position kept + t
+  long long pos_offset;      // absolute position of the first new token (ragged: the largest)
+  const long long* seq_pos;  // ragged batch: per-sequence pos_offset (device), else NULL
+  const int* seq_len;        // ragged batch: per-sequence token count (device), else NULL
   float scale;
 };
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
@@ -53,7 +59,7 @@ struct DecodePlan {
   int n_split;         // key ranges per (sequence, KV head)
   long long chunk;     // keys per range, a multiple of the key tile
 };
-DecodePlan plan_decode(int B, int Hkv, long long S);
+DecodePlan plan_decode(int B, int Hkv, long long S, bool ragged);
 size_t decode_workspace_bytes(int B, int Hq, const DecodePlan& plan);
 
 struct DecodeArgs {
@@ -64,8 +70,10 @@ struct DecodeArgs {
   void* out;            // [B, 1, Hq, d]
   float* ws;            // [B, Hq, n_split, d + 2]
   int B, Hq, Hkv, window;
-  long long S;          // attended keys (renumbered 0 .. S-1)
-  long long base;       // absolute position of renumbered key 0
+  long long S;          // attended keys (renumbered 0 .. S-1; ragged: the largest)
+  long long base;       // absolute position of renumbered key 0 (uniform batch)
+  long long pos_offset; // position of the new token (ragged: the largest)
+  const long long* seq_pos;  // ragged batch: per-sequence position (device), else NULL
   DecodePlan plan;
   const float2* rope;
   float scale;

@@ -108,8 +108,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 
   // ---- key tiles this block touches, processed from kt_hi down to kt_lo -------------
   // Query row t sits at renumbered position kept + t; keys 0 .. kept-1 came from the cache.
-  const int kept = static_cast<int>(a.kept);
-  const int last_row = min(i0 + BM, a.T) - 1;
+  // (a.T is the row stride; the sequence's own token count n_rows may be smaller.)
+  const SeqPos sp = seq_pos_of(a.seq_pos, a.seq_len, a.pos_offset, a.T, a.window, b);
+  const int kept = static_cast<int>(sp.kept);
+  const int n_rows = sp.T;
+  if (i0 >= n_rows) return;  // block-uniform, before any barrier
+  const int last_row = min(i0 + BM, n_rows) - 1;
   const int lo = kLocal ? max(0, kept + i0 - a.window + 1) : 0;
   const int kt_hi = (kept + last_row) / BN;
   const int n_tiles = kt_hi - lo / BN + 1;
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   const int p0 = kept + r0;  // position of the wave's first row
   bf16x8 qf[8];
   {
-    const bool ok = qrow < a.T;
+    const bool ok = qrow < n_rows;
     const bf16_t* src = q + (static_cast<long long>(b) * a.T + (ok ? qrow : 0)) * a.Hq * kHeadDim +
                         static_cast<long long>(hq) * kHeadDim + hl * 8;
 #pragma unroll
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   // ---- normalise and store: lane writes d = dt*32 + i*8 + hl*4 + 0..3 of its row ----
   const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
   const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
-  if (qrow < a.T) {
+  if (qrow < n_rows) {
     const float inv = 1.f / l_tot;
     bf16_t* dst = static_cast<bf16_t*>(a.out) +
                   (static_cast<long long>(b) * a.T + qrow) * a.Hq * kHeadDim +

@@ -27,7 +27,10 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillArgs a) {
   const int kvh = hq / (a.Hq / a.Hkv);
   const int i0 = qb * kRows;
   const int row = i0 + tid / 2;
-  const bool valid = row < a.T;
+  // this sequence's kept keys and token count (a.T is the row stride)
+  const SeqPos sp = seq_pos_of(a.seq_pos, a.seq_len, a.pos_offset, a.T, a.window, b);
+  if (i0 >= sp.T) return;  // block-uniform, before any barrier
+  const bool valid = row < sp.T;
 
   const float* __restrict__ qp = static_cast<const float*>(a.q_rot) +
                                  (static_cast<long long>(b) * a.T + (valid ? row : 0)) * a.Hq * kHeadDim +
@@ -47,9 +50,9 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillArgs a) {
   const float c = a.scale * 1.4426950408889634f;
 
   // query row t sits at renumbered position kept + t; keys 0 .. kept-1 came from the cache
-  const int kept = static_cast<int>(a.kept);
+  const int kept = static_cast<int>(sp.kept);
   const int pos = kept + row;
-  const int last = kept + min(i0 + kRows, a.T) - 1;
+  const int last = kept + min(i0 + kRows, sp.T) - 1;
   const int lo = a.window > 0 ? max(0, kept + i0 - a.window + 1) : 0;
   for (int j0 = (lo / kKeys) * kKeys; j0 <= last; j0 += kKeys) {
     __syncthreads();

@@ -11,8 +11,10 @@ import math
 
 import torch
 
-from . import (plamo_attn_decode, plamo_attn_decode_workspace_bytes, plamo_attn_prefill,
-               plamo_kv_append, prefill_operand_shapes)
+from . import (plamo_attn_decode, plamo_attn_decode_ragged, plamo_attn_decode_ragged_workspace_bytes,
+               plamo_attn_decode_workspace_bytes,
+               plamo_attn_prefill, plamo_attn_prefill_ragged, plamo_kv_append, plamo_kv_append_ragged,
+               prefill_operand_shapes)
 
 
 class PrefillBuffers:
@@ -47,10 +49,14 @@ def prefill(q, k, v, *, window, rope_table, q_norm_w=None, k_norm_w=None, norm_o
 
 
 class DecodeBuffers:
-    def __init__(self, B, Hq, Hkv, d, window, pos_offset, dtype=torch.bfloat16, device="cuda"):
+    """Q', output and split workspace of one decode step (ragged: sized for a ragged batch
+    whose positions are at most pos_offset)."""
+
+    def __init__(self, B, Hq, Hkv, d, window, pos_offset, dtype=torch.bfloat16, device="cuda", ragged=False):
         self.q_rot = torch.empty((B, 1, Hq, d), dtype=dtype, device=device)
         self.out = torch.empty((B, 1, Hq, d), dtype=dtype, device=device)
-        nbytes = plamo_attn_decode_workspace_bytes(B, Hq, Hkv, window, pos_offset, d)
+        size = plamo_attn_decode_ragged_workspace_bytes if ragged else plamo_attn_decode_workspace_bytes
+        nbytes = size(B, Hq, Hkv, window, pos_offset, d)
         self.workspace = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device=device)
 
 
@@ -69,4 +75,43 @@ def decode(q, k, v, k_cache, v_cache, *, window, pos_offset, rope_table, q_norm_
                       pos_offset=pos_offset, rope_table=rope_table,
                       softmax_scale=1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale,
                       stream=stream)
+    return bufs
+
+
+def prefill_ragged(q, k, v, *, window, rope_table, seq_pos_offsets, max_pos_offset, seq_lens=None,
+                   q_norm_w=None, k_norm_w=None, norm_offset=1.0, norm_eps=1e-6, k_cache=None,
+                   v_cache=None, bufs: PrefillBuffers | None = None, softmax_scale=None,
+                   stream=None) -> PrefillBuffers:
+    """Prefill of a ragged batch: sequence b's seq_lens[b] new tokens (rows of its [T] slab)
+    start at absolute position seq_pos_offsets[b] <= max_pos_offset."""
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if bufs is None:
+        bufs = PrefillBuffers(B, T, Hq, Hkv, d, q.dtype, q.device, window, max_pos_offset)
+    plamo_kv_append_ragged(q, k, v, bufs.q_rot, window=window, seq_pos_offsets=seq_pos_offsets,
+                           max_pos_offset=max_pos_offset, seq_lens=seq_lens, rope_table=rope_table,
+                           q_norm_w=q_norm_w, k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps,
+                           k_rot_out=bufs.k_rot, v_t_out=bufs.v_t, k_cache=k_cache, v_cache=v_cache,
+                           stream=stream)
+    plamo_attn_prefill_ragged(bufs.q_rot, bufs.k_rot, bufs.v_t, bufs.out, window=window,
+                              seq_pos_offsets=seq_pos_offsets, max_pos_offset=max_pos_offset,
+                              seq_lens=seq_lens, softmax_scale=softmax_scale, stream=stream)
+    return bufs
+
+
+def decode_ragged(q, k, v, k_cache, v_cache, *, window, seq_pos_offsets, max_pos_offset, rope_table,
+                  q_norm_w=None, k_norm_w=None, norm_offset=1.0, norm_eps=1e-6,
+                  bufs: DecodeBuffers | None = None, softmax_scale=None, stream=None) -> DecodeBuffers:
+    """One decode step of a ragged batch: sequence b's new token sits at seq_pos_offsets[b]."""
+    B, _, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if bufs is None:
+        bufs = DecodeBuffers(B, Hq, Hkv, d, window, max_pos_offset, q.dtype, q.device, ragged=True)
+    plamo_kv_append_ragged(q, k, v, bufs.q_rot, window=window, seq_pos_offsets=seq_pos_offsets,
+                           max_pos_offset=max_pos_offset, rope_table=rope_table, q_norm_w=q_norm_w,
+                           k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps, k_cache=k_cache,
+                           v_cache=v_cache, stream=stream)
+    plamo_attn_decode_ragged(bufs.q_rot, k_cache, v_cache, bufs.out, bufs.workspace, window=window,
+                             seq_pos_offsets=seq_pos_offsets, max_pos_offset=max_pos_offset,
+                             rope_table=rope_table, softmax_scale=softmax_scale, stream=stream)
     return bufs

@@ -157,6 +157,19 @@ PERIOD_DECODE = DecodeWorkload(
     steps=128, seed=BASE_SEED + 5)
 
 
+def ragged_positions(B: int, max_pos: int, seed: int) -> np.ndarray:
+    """Positions of the new token of each sequence of a ragged decode batch: independent
+    uniform integers in [0, max_pos], the last one set to max_pos so that the batch's bound
+    is reached (int64 [B])."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    p = rng.integers(0, max_pos + 1, size=B, dtype=np.int64)
+    p[-1] = max_pos
+    return p
+
+
+RAGGED_DECODE_SEED = BASE_SEED + 6  # positions of the ragged batched-decode case
+
+
 def device_normal_bf16(shape, seed: int, device):
     """N(0, 1) draws rounded to bfloat16, generated by torch on ``device`` (used for
     decode caches of several GiB). The same (shape, seed, device type) gives the same

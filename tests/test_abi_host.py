@@ -72,6 +72,9 @@ def test_decode_workspace_sizes(lib):
     assert lib.plamo_attn_decode_workspace_bytes(64, 64, 8, 128, 0, 32767) == 0
     assert lib.plamo_attn_decode_workspace_bytes(64, 64, 8, 96, 0, 10) == 0  # d != 128
     assert lib.plamo_attn_decode_workspace_bytes(0, 64, 8, 128, 0, 10) == 0
+    # a ragged batch cuts its key ranges finer than the uniform plan of its longest sequence
+    n = lib.plamo_attn_decode_ragged_workspace_bytes(64, 64, 8, 128, 0, 32767)
+    assert n > 0 and n % (130 * 4 * 64 * 64) == 0 and n // (130 * 4 * 64 * 64) > 1
 
 
 def _append(lib, **over):
@@ -185,3 +188,45 @@ def test_tiled_operand_helpers_invert_documented_layout():
             v_tiled[:, :, t // 64, (t % 64) // 8, j, t % 8] = vt[:, :, j, t]
     assert np.array_equal(untile_k_rot(k_tiled), k)
     assert np.array_equal(untile_v_t(v_tiled), vt)
+
+
+def test_ragged_entry_points_validate_their_arrays(lib):
+    ALIGNED4 = ctypes.c_void_p(0x7F0000000004)
+    base = dict(dtype=BF16, q=FAKE, k=FAKE, v=FAKE, wq=None, wk=None, c=1.0, eps=1e-6, q_out=FAKE, k_rot=None,
+                v_t=None, kc=None, vc=None, cap=0, B=2, T=4, Hq=8, Hkv=2, d=128, window=16, table=FAKE,
+                table_bytes=(64 + 1) * 512)
+
+    def append(seq_pos, seq_len, max_pos=0, **over):
+        a = dict(base, **over)
+        return lib.plamo_kv_append_ragged(a["dtype"], a["q"], a["k"], a["v"], a["wq"], a["wk"], a["c"], a["eps"],
+                                          a["q_out"], a["k_rot"], a["v_t"], a["kc"], a["vc"], a["cap"], a["B"],
+                                          a["T"], a["Hq"], a["Hkv"], a["d"], a["window"], seq_pos, seq_len,
+                                          max_pos, a["table"], a["table_bytes"], None)
+    assert append(None, None) == INVALID                  # positions are required
+    assert append(ALIGNED4, None) == INVALID              # int64 array not 8-byte aligned
+    assert append(FAKE, ctypes.c_void_p(0x7F0000000002)) == INVALID  # int32 array not 4-byte aligned
+    assert append(FAKE, None, max_pos=-1) == INVALID
+    assert append(FAKE, None, max_pos=3, k_rot=FAKE) == INVALID  # operands after cached keys need caches
+    assert append(FAKE, None, max_pos=64, window=0) == WORKSPACE  # table must cover kept_max + T
+    assert append(None, None, B=0) == OK and append(None, None, T=0) == OK
+
+    def prefill(seq_pos, seq_len, max_pos=0, **over):
+        a = dict(dtype=BF16, B=2, T=100, Hq=8, Hkv=2, window=0, scale=0.0884)
+        a.update(over)
+        return lib.plamo_attn_prefill_ragged(a["dtype"], FAKE, FAKE, FAKE, FAKE, a["B"], a["T"], a["Hq"], a["Hkv"],
+                                             128, a["window"], seq_pos, seq_len, max_pos, a["scale"], None)
+    assert prefill(None, FAKE) == INVALID
+    assert prefill(FAKE, ctypes.c_void_p(0x7F0000000001)) == INVALID
+    assert prefill(FAKE, None, scale=0.0) == INVALID
+
+    def decode(seq_pos, max_pos=5000, **over):
+        a = dict(B=4, window=2048, cap=2048, ws=FAKE, ws_bytes=1 << 30, table_bytes=(64 + 32) * 512)
+        a.update(over)
+        return lib.plamo_attn_decode_ragged(BF16, FAKE, FAKE, FAKE, a["cap"], FAKE, a["ws"], a["ws_bytes"], a["B"],
+                                            64, 8, 128, a["window"], seq_pos, max_pos, FAKE, a["table_bytes"],
+                                            0.0884, None)
+    assert decode(None) == INVALID
+    assert decode(ALIGNED4) == INVALID
+    assert decode(FAKE, window=0, cap=4000) == INVALID     # global cap must exceed max_pos_offset
+    assert decode(FAKE, ws=None) == WORKSPACE
+    assert decode(FAKE, table_bytes=(64 + 31) * 512) == WORKSPACE

@@ -381,3 +381,104 @@ def test_chunked_prefill_matches_oracle(window, chunks, bf16):
     for i, (g, r) in enumerate(zip(got, ref)):
         assert_parity(g[:, rows_of(chunks[i])], r, TOL_BF16 if bf16 else TOL_F32,
                       f"chunk {i} (T={chunks[i]}) W={window}")
+
+
+@pytest.mark.parametrize("window,steps,bf16", [
+    (0, [[150, 37, 600], [70, 200, 0]], True),
+    (16, [[40, 3, 17], [9, 30, 0]], True),
+    (2048, [[2500, 100, 1300], [300, 500, 0]], True),
+    (128, [[300, 5, 130], [64, 190, 0]], False),
+], ids=["global", "ring16", "ring2048", "fp32_ring128"])
+def test_ragged_batch_matches_oracle(window, steps, bf16):
+    """A ragged batch (「PLaMo 3アーキテクチャ徹底解析」 §4.4 per sequence): each step gives every
+    sequence its own position and token count (0 = it sits the step out); then (bf16) one
+    ragged decode step. Every sequence equals the oracle run on its own token stream in the
+    same chunks. Input rows past a sequence's count are NaN (they must not be read) and output
+    rows past it keep a sentinel (they must not be written)."""
+    B, Hq, Hkv, d = 3, 8, 2, 128
+    lens = np.array(steps, dtype=np.int64)
+    n_tot = lens.sum(0) + (1 if bf16 else 0)
+    rope = Rope(1e4) if window else Rope(1e6, 64.0)
+    dr = Draw(4242 + window, bf16)
+    streams = [(dr.normal((1, n, Hq, d)), dr.normal((1, n, Hkv, d)), dr.normal((1, n, Hkv, d))) for n in n_tot]
+    wq, wk = (dr.normal((d,), 0.02), dr.normal((d,), 0.02)) if bf16 else (None, None)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    cap = window if window else int(n_tot.sum())  # global: >= the largest position + T of any step
+    kc = torch.zeros((B, Hkv, cap, d), dtype=dt, device="cuda")
+    vc = torch.zeros_like(kc)
+    tab = rope_table(rope, int(n_tot.sum()) + 64)  # renumbered positions stay below kept + T
+    put = lambda x: dev(x, bf16)
+    norm = dict(q_norm_w=put(wq), k_norm_w=put(wk), norm_offset=1.0) if bf16 else {}
+    pos = np.zeros(B, np.int64)
+    got = [[] for _ in range(B)]
+    sentinel = 123.0
+
+    def slab(i, L, T):
+        x = np.full((B, T) + streams[0][i].shape[2:], np.nan, np.float32)
+        for b in range(B):
+            x[b, :L[b]] = streams[b][i][0, pos[b]:pos[b] + L[b]]
+        return put(x)
+
+    for L in lens:
+        T = int(L.max())
+        maxp = int(pos.max())
+        sp = torch.tensor(pos, dtype=torch.int64, device="cuda")
+        sl = torch.tensor(L, dtype=torch.int32, device="cuda")
+        bufs = layer.PrefillBuffers(B, T, Hq, Hkv, d, dt, "cuda", window, maxp)
+        bufs.out.fill_(sentinel)
+        layer.prefill_ragged(slab(0, L, T), slab(1, L, T), slab(2, L, T), window=window, rope_table=tab,
+                             seq_pos_offsets=sp, max_pos_offset=maxp, seq_lens=sl, k_cache=kc, v_cache=vc,
+                             bufs=bufs, **norm)
+        torch.cuda.synchronize()
+        out = host(bufs.out)
+        for b in range(B):
+            assert np.all(out[b, L[b]:] == sentinel), f"rows past sequence {b}'s count were written"
+            if L[b]:
+                got[b].append(out[b, :L[b]])
+        pos += L
+    if bf16:
+        one = np.ones(B, np.int64)
+        sp = torch.tensor(pos, dtype=torch.int64, device="cuda")
+        db = layer.decode_ragged(slab(0, one, 1), slab(1, one, 1), slab(2, one, 1), kc, vc, window=window,
+                                 seq_pos_offsets=sp, max_pos_offset=int(pos.max()), rope_table=tab, **norm)
+        torch.cuda.synchronize()
+        out = host(db.out)
+        for b in range(B):
+            got[b].append(out[b])
+    for b in range(B):
+        chunks = [int(L[b]) for L in lens if L[b]] + ([1] if bf16 else [])
+        q, k, v = streams[b]
+        ref = oracle_chunks(q, k, v, chunks, window=window, rope=rope, wq=wq, wk=wk)
+        for i, (g, r) in enumerate(zip(got[b], ref)):
+            assert_parity(g, r[0], TOL_BF16 if bf16 else TOL_F32, f"sequence {b} chunk {i} W={window}")
+
+
+def test_decode_ragged_full_size():
+    """Ragged batched decode at its real shape (B=64, Hq=64, Hkv=8, global cache sized for
+    32768 keys, each sequence at its own seeded position): sampled sequences, including the
+    shortest and the longest, vs the oracle."""
+    from synthetic.workloads import RAGGED_DECODE_SEED, ragged_positions
+    wl = BATCHED_DECODE
+    li = 1
+    ly = wl.layers[li]
+    d = wl.d
+    pos = ragged_positions(wl.B, wl.pos_offset, RAGGED_DECODE_SEED)
+    maxp = int(pos.max())
+    cap = wl.cache_cap(ly)
+    kc = device_normal_bf16((wl.B, wl.Hkv, cap, d), wl.cache_seed(li), "cuda")
+    vc = device_normal_bf16((wl.B, wl.Hkv, cap, d), wl.cache_seed(li) + 1, "cuda")
+    check_b = sorted({0, 31, int(np.argmin(pos)), int(np.argmax(pos))})
+    prior_k = {b: host(kc[b, :, :pos[b]]).transpose(1, 0, 2) for b in check_b}
+    prior_v = {b: host(vc[b, :, :pos[b]]).transpose(1, 0, 2) for b in check_b}
+    new = wl.draw_new_tokens(0, li)
+    tab = rope_table(ly.rope, maxp + 64)
+    sp = torch.from_numpy(pos).cuda()
+    bufs = layer.decode_ragged(dev(new["q"]), dev(new["k"]), dev(new["v"]), kc, vc, window=0, seq_pos_offsets=sp,
+                               max_pos_offset=maxp, rope_table=tab, q_norm_w=dev(new["wq"]),
+                               k_norm_w=dev(new["wk"]), norm_offset=wl.norm_offset)
+    torch.cuda.synchronize()
+    out = host(bufs.out)
+    for b in check_b:
+        ref = oracle_decode_one(new["q"][b], new["k"][b], new["v"][b], prior_k[b], prior_v[b], int(pos[b]),
+                                window=0, rope=ly.rope, wq=new["wq"], wk=new["wk"], norm_offset=wl.norm_offset)
+        assert_parity(out[b], ref, TOL_BF16, f"ragged decode b={b} p={pos[b]}")
