@@ -147,7 +147,7 @@ PLAMO_API int plamo_kv_append(int dtype, const void* q, const void* k, const voi
  * attends operand keys j <= i, and i - j < window when window > 0: a chunk after
  * pos_offset cached tokens sees the cached keys first, then its own causally.
  * softmax_scale is 1/sqrt(d) [P3 §4.5]; the YaRN amplitude is already in q_rot
- * and k_rot.
+ * and k_rot. bf16: kept + T <= 2^22 (PLAMO_ERR_UNSUPPORTED beyond).
  * ------------------------------------------------------------------------- */
 PLAMO_API int plamo_attn_prefill(int dtype, const void* q_rot, const void* k_rot, const void* v_t,
                        void* out, int B, int T, int Hq, int Hkv, int d, int window,

@@ -185,6 +185,9 @@ int attn_prefill_impl(int dtype, const void* q_rot, const void* k_rot, const voi
   if (B == 0 || T == 0) return ok();
   const long long kept = kept_tokens(window, pos_offset);
   if (kept + T > (1LL << 30)) return fail(PLAMO_ERR_UNSUPPORTED, "kept + T must be <= 2^30");
+  // bf16 operand tiles are addressed with 32-bit buffer offsets within one (b, KV head)
+  if (dtype == PLAMO_BF16 && kept + T > (1LL << 22))
+    return fail(PLAMO_ERR_UNSUPPORTED, "bf16 prefill needs kept + T <= 2^22");
   if (!q_rot || !k_rot || !v_t || !out) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be non-NULL");
   const void* ptrs[] = {q_rot, k_rot, v_t, out};
   for (const void* p : ptrs)

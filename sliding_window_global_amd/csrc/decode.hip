@@ -67,9 +67,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m16 = lane & 15;  // MFMA row/col index within 16
   const int g = lane >> 4;    // lane group 0..3
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  // a ragged batch launches its key ranges range-major (see the launcher)
+  const bool range_major = a.seq_pos != nullptr;
+  const int split = range_major ? blockIdx.z : blockIdx.x;
+  const int kvh = range_major ? blockIdx.x : blockIdx.y;
+  const int b = range_major ? blockIdx.y : blockIdx.z;
   const int G = a.Hq / a.Hkv;
 
   // keys of this sequence: all of them on a uniform batch, its own count on a ragged one
@@ -385,10 +387,10 @@ __global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(DecodeArgs a) 
 DecodePlan plan_decode(int B, int Hkv, long long S, bool ragged) {
   // Aim for ~512 blocks (2 per CU, one wave per SIMD each) with at least kMinChunk keys
   // each and at most kMaxSplit ranges per (sequence, KV head). A ragged batch only knows
-  // its longest sequence here; its ranges are cut finer (~4 blocks per slot at the
+  // its longest sequence here; its ranges are cut finer (~8 blocks per slot at the
   // longest length) so that short and long sequences even out over the CUs.
   const long long pairs = static_cast<long long>(B) * Hkv;
-  const long long target_blocks = ragged ? 4 * 512 : 512;
+  const long long target_blocks = ragged ? 8 * 512 : 512;
   long long n = (target_blocks + pairs - 1) / pairs;
   const long long by_min_chunk = (S + kMinChunk - 1) / kMinChunk;
   if (n > by_min_chunk) n = by_min_chunk;
@@ -409,7 +411,11 @@ size_t decode_workspace_bytes(int B, int Hq, const DecodePlan& plan) {
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.plan.n_split, a.Hkv, a.B);
+  // Blocks are dispatched in index order. A ragged batch puts the key range slowest: the
+  // first ranges of every (sequence, KV head) start together, later ranges (only the longer
+  // sequences have them) fill the slots as they free up, and the empty ranges of short
+  // sequences come last.
+  const dim3 grid = a.seq_pos ? dim3(a.Hkv, a.B, a.plan.n_split) : dim3(a.plan.n_split, a.Hkv, a.B);
   if (a.window == 0)
     hipLaunchKernelGGL(decode_split_kernel<kContiguous>, grid, dim3(kThreads), 0, stream, a);
   else if (a.window >= kTile)

@@ -11,7 +11,7 @@
 //            sits at renumbered position kept + t: a chunk after `kept` cached keys
 //            (§4.4) attends keys 0 .. kept+t, all of them in the K' / V^T operands.
 //   tile   = 64 keys. K' and V^T arrive tiled in HBM in exactly the LDS order, so each
-//            tile is one contiguous copy straight into LDS (global_load_lds_dwordx4, no
+//            tile is one contiguous copy straight into LDS (buffer_load_dwordx4 ... lds, no
 //            register staging), double buffered. The LDS order is chunk-major: the
 //            operand reads of one MFMA are 64 consecutive 16-byte slots (no bank
 //            conflicts) and the reads of different chunks differ by constant offsets.
@@ -48,6 +48,13 @@ constexpr int kTileElems = BN * kHeadDim;  // K' tile and V^T tile alike: 16 KiB
 constexpr float kRescaleLog2 = 8.f;        // lazy-rescale threshold (log2 units)
 // s_waitcnt vmcnt(0) with expcnt / lgkmcnt left alone (gfx9 encoding)
 constexpr unsigned kWaitVmcnt0 = 0x0F70;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 word 3: 32-bit data, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -120,18 +127,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 
   // K' and V^T arrive tiled by 64 keys, each tile 16 KiB in exactly the LDS order below, so
   // a tile is one contiguous copy: direct load g = wave*4 + i moves bytes 1024g .. +1023
-  // (lane l: 16 bytes at 1024g + 16l), a wave-uniform base plus a per-lane offset.
-  const uint32_t lane_off = static_cast<uint32_t>(lane) * 16;
-  auto issue = [&](const bf16_t* base, int step, bf16_t* buf) __attribute__((always_inline)) {
-    const char* src = reinterpret_cast<const char*>(base + static_cast<long long>(kt_hi - step) * kTileElems);
+  // (lane l: 16 bytes at 1024g + 16l). The copies are buffer loads with the LDS bit over a
+  // resource spanning this (sequence, KV head)'s operand (out-of-range reads return 0):
+  // the tile offset goes in the scalar offset, the lane's in the vector one. (The global-
+  // segment form of the same copy makes the compiler wait for every outstanding LDS read
+  // before each MFMA operand use while a copy is in flight; with the buffer form its waits
+  // leave the three younger operand reads in flight.)
+  const uint32_t lane_off = static_cast<uint32_t>(lane) * 16 + static_cast<uint32_t>(wave) * 4096;
+  const int op_bytes = static_cast<int>(a.Tp * kHeadDim * sizeof(bf16_t));
+  const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(kbase, op_bytes);
+  const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(vbase, op_bytes);
+  auto issue = [&](__amdgpu_buffer_rsrc_t rsrc, int step, bf16_t* buf) __attribute__((always_inline)) {
+    const int tile_off = (kt_hi - step) * kTileElems * static_cast<int>(sizeof(bf16_t));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int g = wave * 4 + i;
-      __builtin_amdgcn_global_load_lds(src + g * 1024 + lane_off, buf + g * 512, 16, 0, 0);
+      lds_ptr_t dst = (lds_ptr_t)(buf + (wave * 4 + i) * 512);  // generic -> LDS address space
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, lane_off + i * 1024, tile_off, 0, 0);
     }
   };
-  auto issue_k = [&](int step, bf16_t* buf) __attribute__((always_inline)) { issue(kbase, step, buf); };
-  auto issue_v = [&](int step, bf16_t* buf) __attribute__((always_inline)) { issue(vbase, step, buf); };
+  auto issue_k = [&](int step, bf16_t* buf) __attribute__((always_inline)) { issue(k_rsrc, step, buf); };
+  auto issue_v = [&](int step, bf16_t* buf) __attribute__((always_inline)) { issue(v_rsrc, step, buf); };
 
   // ---- Q' fragment (MFMA B operand): lane holds dims s*16 + hl*8 .. +7 of its row ----
   // Pre-multiplied by scale * log2(e), so that S comes out of the MFMA in exp2 units.

@@ -132,6 +132,7 @@ def _prefill(lib, **over):
     (dict(dtype=3), INVALID), (dict(d=64), UNSUPPORTED), (dict(Hq=9, Hkv=2), INVALID),
     (dict(out=None), INVALID), (dict(k=MISALIGNED), INVALID),
     (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID), (dict(T=-3), INVALID),
+    (dict(T=(1 << 22) + 1), UNSUPPORTED),            # bf16 operands use 32-bit buffer offsets
 ])
 def test_prefill_validation(lib, over, status):
     assert _prefill(lib, **over) == status
