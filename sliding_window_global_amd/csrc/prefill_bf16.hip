@@ -198,6 +198,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   // -m_run), so the softmax numerator is a bare exp2.
   float m_run = -INFINITY;
   float l_run = 0.f;
+  // -reference in all 16 accumulator slots: the start value of every S^T accumulator
+  // (rewritten only when the reference moves)
+  f32x16 neg_m;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) neg_m[e] = 0.f;
   constexpr int kDepth = 4;  // MFMA operands read ahead from LDS
 
   // One pipeline step: S^T(step+1) = K'(step+1) Q'^T (if kQK) on the matrix cores while
@@ -209,9 +214,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     constexpr bool kQK = decltype(QK)::value, kPV = decltype(PV)::value;
     constexpr int i_first = kQK ? 0 : 16, i_last = kPV ? 32 : 16;
     const float m_base = m_run == -INFINITY ? 0.f : m_run;
-    f32x16 init;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) init[e] = -m_base;
 
     u32x4 fr[kDepth];
 #pragma unroll
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     for (int i = 0; i < 16; ++i) {
       if (kQK) {
         const int kb = i & 1, s = i >> 1;
-        s_next[kb] = mfma32(__builtin_bit_cast(bf16x8, fr[i % kDepth]), qf[s], s == 0 ? init : s_next[kb]);
+        s_next[kb] = mfma32(__builtin_bit_cast(bf16x8, fr[i % kDepth]), qf[s], s == 0 ? neg_m : s_next[kb]);
         if (i + kDepth < i_last) fr[i % kDepth] = frag(i + kDepth, kbuf, vbuf);
       }
       if (kPV) {
@@ -310,6 +312,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
           for (int e = 0; e < 16; ++e) s_next[kb][e] -= bump;
         m_run = (first && mx == -INFINITY) ? -INFINITY : m_base + bump;
+        const float nb = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) neg_m[e] = nb;
       }
     }
   };
