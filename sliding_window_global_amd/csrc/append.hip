@@ -30,6 +30,17 @@ constexpr int kTokBlock = 64;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
+// One LDS area per block, used first for the rotation factors of the block's 64 positions
+// ([64][64] float2, 32 KiB) and afterwards, behind a barrier, for the V^T staging tile
+// ([128 dims][64 + 16/sizeof(E) tokens]). Sharing it keeps a block within 36 KiB, so that
+// four blocks (all of a 64-token x 8-KV-head step) fit on a CU.
+template <typename E>
+constexpr int kTileStride = kTokBlock + 16 / static_cast<int>(sizeof(E));  // tokens, 16-byte rows
+template <typename E>
+constexpr int kSmemBytes = kTokBlock * kHalf * 8 > kHeadDim * kTileStride<E> * static_cast<int>(sizeof(E))
+                               ? kTokBlock * kHalf * 8
+                               : kHeadDim * kTileStride<E> * static_cast<int>(sizeof(E));
+
 template <typename E>
 struct Io;
 
@@ -70,7 +81,8 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   constexpr int kRowsPerPass = 64 / kLanesPerRow;
   constexpr int kUnroll = 2;
   constexpr bool kTiled = sizeof(E) == 2;      // bf16 prefill operands are tiled
-  __shared__ __attribute__((aligned(16))) float2 zs[kTokBlock][kHalf];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes<E>];
+  float2 (*zs)[kHalf] = reinterpret_cast<float2 (*)[kHalf]>(smem);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -226,8 +238,9 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
     }
   }
   if (v_t && !a.ops_kernel) {  // (otherwise the operand kernel writes all of V^T)
-    constexpr int kTS = kTokBlock + kVec;  // LDS row stride (tokens), keeps rows 16-byte aligned
-    __shared__ __attribute__((aligned(16))) E tile[kHeadDim * kTS];
+    constexpr int kTS = kTileStride<E>;
+    E* tile = reinterpret_cast<E*>(smem);
+    __syncthreads();  // every wave is done with the rotation factors
     for (int i = threadIdx.x; i < kTokBlock * kChunks; i += kThreads) {
       const int r = i / kChunks, cidx = i % kChunks;
       const int t = t0 + r;
@@ -279,9 +292,10 @@ __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a
   constexpr int kRowsPerPass = 64 / kLanesPerRow;
   constexpr bool kTiled = sizeof(E) == 2;
   constexpr int kChunks = kHeadDim / kVec;
-  constexpr int kTS = kTokBlock + kVec;  // LDS row stride (tokens) of the V^T staging tile
-  __shared__ __attribute__((aligned(16))) float2 zs[kTokBlock][kHalf];
-  __shared__ __attribute__((aligned(16))) E tile[kHeadDim * kTS];
+  constexpr int kTS = kTileStride<E>;  // LDS row stride (tokens) of the V^T staging tile
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes<E>];
+  float2 (*zs)[kHalf] = reinterpret_cast<float2 (*)[kHalf]>(smem);
+  E* tile = reinterpret_cast<E*>(smem);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -343,6 +357,7 @@ __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a
   }
 
   if (v_t) {
+    __syncthreads();  // every wave is done with the rotation factors
     for (int i = threadIdx.x; i < kTokBlock * kChunks; i += kThreads) {
       const int r = i / kChunks, cidx = i % kChunks;
       const long long R = R0 + r;
