@@ -46,7 +46,9 @@ def _per_dispatch(path, kernel, grid, counter, nth=None):
     return sum(vals) / len(vals), len(vals)
 
 
-def summarize_trace(stats_csv, out, cmds):
+def summarize_trace(stats_csv, out, cmds, trace_csv=None, prefix="plamo"):
+    """Kernel statistics table; with the per-dispatch trace, also one line per (kernel, grid)
+    for the library's kernels (one kernel serves several workloads of different grids)."""
     rows = list(csv.DictReader(open(stats_csv)))
     lines = [f"# rocprofv3 kernel trace summary", ""]
     lines += [f"command: {c}" for c in cmds]
@@ -54,6 +56,18 @@ def summarize_trace(stats_csv, out, cmds):
     for r in rows:
         lines.append(f"{r['Name'][:78]:<78} {int(r['Calls']):>6} {float(r['AverageNs'])/1e3:>11.2f} "
                      f"{float(r['MinNs'])/1e3:>10.2f} {float(r['MaxNs'])/1e3:>10.2f} {float(r['Percentage']):>6.2f}")
+    if trace_csv:
+        by = collections.defaultdict(list)
+        for r in csv.DictReader(open(trace_csv)):
+            name = r["Kernel_Name"]
+            if prefix not in name:
+                continue
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            by[(name, grid)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines += ["", "per (kernel, grid threads):",
+                  f"{'kernel':<66} {'grid':>10} {'calls':>6} {'avg_us':>11} {'min_us':>10} {'max_us':>10}"]
+        for (name, grid), v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"{name[:66]:<66} {grid:>10} {len(v):>6} {sum(v)/len(v):>11.2f} {min(v):>10.2f} {max(v):>10.2f}")
     open(out, "w").write("\n".join(lines) + "\n")
 
 
@@ -128,6 +142,7 @@ def main():
     t = sub.add_parser("trace")
     t.add_argument("stats_csv")
     t.add_argument("out")
+    t.add_argument("--trace-csv", default=None)
     t.add_argument("--cmd", action="append", default=[])
     f = sub.add_parser("traffic")
     f.add_argument("--kernel", required=True)
@@ -149,7 +164,7 @@ def main():
     c.add_argument("--cmd", action="append", default=[])
     a = ap.parse_args()
     if a.what == "trace":
-        summarize_trace(a.stats_csv, a.out, a.cmd)
+        summarize_trace(a.stats_csv, a.out, a.cmd, trace_csv=a.trace_csv)
     elif a.what == "traffic":
         summarize_traffic(a.kernel, a.grid, a.fetch, a.write, a.copy_fetch, a.copy_write, a.out, a.cmd,
                           sources=SOURCES[a.sources], nth=a.nth, algorithmic=a.algorithmic)
