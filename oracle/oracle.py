@@ -109,14 +109,20 @@ def apply_rope(x, positions, omega, amplitude: float) -> np.ndarray:
 # Masks and attention  [P3 §4.2, §4.5, §5.1]
 # ----------------------------------------------------------------------------
 
-def allowed(q_pos, k_pos, window: int) -> np.ndarray:
+def allowed(q_pos, k_pos, window: int, legacy_4k: bool = False) -> np.ndarray:
     """[P3 §5.1] Query at position i may read key at position j iff j <= i, and on a
-    local layer (window W > 0) also i - j < W, so W keys including itself."""
+    local layer (window W > 0) also i - j < W, so W keys including itself.
+
+    legacy_4k: the band of the implementation shipped with the 4K release (same section),
+    which reads up to distance W, i.e. W + 1 keys including itself."""
     i = np.asarray(q_pos, dtype=np.int64)[:, None]
     j = np.asarray(k_pos, dtype=np.int64)[None, :]
     ok = j <= i
     if window > 0:
-        ok &= (i - j) < window
+        if legacy_4k:
+            ok &= (i - j) <= window
+        else:
+            ok &= (i - j) < window
     return ok
 
 
@@ -126,7 +132,7 @@ def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
 
 
 def gqa_attention(q_rot, k_rot, v, q_pos, k_pos, window: int, scale: float,
-                  rows_per_slice: int = 512, return_weights: bool = False):
+                  rows_per_slice: int = 512, return_weights: bool = False, legacy_4k: bool = False):
     """[P3 §4.5] A = softmax_s(Q'K'^T * scale + M), O = A V, per query head, with
     M = 0 where allowed and -inf elsewhere; K/V head g(h) for query head h.
 
@@ -145,7 +151,7 @@ def gqa_attention(q_rot, k_rot, v, q_pos, k_pos, window: int, scale: float,
     weights = np.zeros((Hq, T, S), dtype=F64) if return_weights else None
     for r0 in range(0, T, rows_per_slice):
         r1 = min(T, r0 + rows_per_slice)
-        mask = allowed(q_pos[r0:r1], k_pos, window)
+        mask = allowed(q_pos[r0:r1], k_pos, window, legacy_4k)
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
             scores = (q_rot[r0:r1, h, :] @ k_rot[:, g, :].T) * scale
@@ -171,22 +177,24 @@ class LayerKVCache:
     Stores normalised K before RoPE and raw V. A global layer (window 0) keeps
     every token. A local layer keeps, after each update, at most the last W - 1
     tokens; the update itself returns all previously kept tokens plus the new
-    ones, and that is what attention reads."""
+    ones, and that is what attention reads. legacy_4k: the cache class of the 4K
+    release's implementation (§5.1), which keeps the last W tokens, for its W + 1 band."""
 
-    def __init__(self, Hkv: int, d: int, window: int):
+    def __init__(self, Hkv: int, d: int, window: int, legacy_4k: bool = False):
         self.window = int(window)
+        self.legacy_4k = bool(legacy_4k)
         self.k = np.zeros((0, Hkv, d), dtype=F64)
         self.v = np.zeros((0, Hkv, d), dtype=F64)
         self.seen = 0  # tokens appended so far (absolute position of the next token)
 
     @classmethod
-    def with_prior(cls, k_prior, v_prior, seen: int, window: int):
+    def with_prior(cls, k_prior, v_prior, seen: int, window: int, legacy_4k: bool = False):
         """A cache that already holds ``k_prior``/``v_prior`` [n, Hkv, d] as its kept
         tokens, after ``seen`` tokens in total."""
         k_prior = np.asarray(k_prior, dtype=F64)
-        c = cls(k_prior.shape[1], k_prior.shape[2], window)
+        c = cls(k_prior.shape[1], k_prior.shape[2], window, legacy_4k)
         keep = k_prior.shape[0]
-        expect = seen if window == 0 else min(seen, window - 1)
+        expect = seen if window == 0 else min(seen, window if legacy_4k else window - 1)
         if keep != expect:
             raise ValueError(f"a cache after {seen} tokens keeps {expect}, got {keep}")
         c.k = k_prior.copy()
@@ -200,6 +208,8 @@ class LayerKVCache:
         self.seen += np.asarray(k_new).shape[0]
         n = k_all.shape[0]
         keep = n if self.window == 0 else min(n, self.window - 1)
+        if self.legacy_4k and self.window > 0:
+            keep = min(n, self.window)
         self.k = k_all[n - keep:]
         self.v = v_all[n - keep:]
         return k_all, v_all
@@ -242,7 +252,8 @@ def attention_layer_step(q, k, v, cache: LayerKVCache, *, theta: float,
     k_rot = apply_rope(k_all, k_pos, omega, amp)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    out = gqa_attention(q_rot, k_rot, v_all, q_pos, k_pos, cache.window, scale)
+    out = gqa_attention(q_rot, k_rot, v_all, q_pos, k_pos, cache.window, scale,
+                        legacy_4k=cache.legacy_4k)
     if return_intermediates:
         return out, dict(q_norm=q, k_all=k_all, v_all=v_all, q_rot=q_rot, k_rot=k_rot,
                          q_pos=q_pos, k_pos=k_pos)

@@ -428,11 +428,47 @@ def pin_kv_accounting(o):
     assert o.kv_bytes(1, 8, 128, 8) == ap["global"] * 1024
 
 
+def pin_legacy_4k_band(o):
+    """「PLaMo 3アーキテクチャ徹底解析」 §5.1: the 4K release's implementation builds its band
+    with triu(diagonal=-W) (W + 1 keys including self) and its cache keeps the last W; the
+    current release uses triu(diagonal=-(W-1)). Masks against NumPy's tril/triu, attention
+    against float64 SDPA with that mask, and the cache trimming."""
+    n = 11
+    pos = np.arange(n)
+    ones = np.ones((n, n), dtype=bool)
+    for W in (1, 2, 4, 7):
+        assert np.array_equal(o.allowed(pos, pos, W, legacy_4k=True), np.tril(ones) & np.triu(ones, -W))
+        assert np.array_equal(o.allowed(pos, pos, W), np.tril(ones) & np.triu(ones, -(W - 1)))
+    T, Hq, Hkv, d, W = 13, 4, 2, 8, 3
+    q, k, v = _rand((T, Hq, d), 71), _rand((T, Hkv, d), 72), _rand((T, Hkv, d), 73)
+    scale = 1.0 / math.sqrt(d)
+    got = o.gqa_attention(q, k, v, np.arange(T), np.arange(T), W, scale, legacy_4k=True)
+    mask = torch.from_numpy(np.tril(np.ones((T, T), dtype=bool)) & np.triu(np.ones((T, T), dtype=bool), -W))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2)[None], torch.from_numpy(k).permute(1, 0, 2)[None],
+        torch.from_numpy(v).permute(1, 0, 2)[None], attn_mask=mask, scale=scale, enable_gqa=True)
+    assert np.max(np.abs(got - ref[0].permute(1, 0, 2).numpy())) < 1e-12
+    cache = o.LayerKVCache(1, 1, W, legacy_4k=True)
+    seen = 0
+    for t in (2, 1, 5, 1, 1):
+        x = np.arange(seen, seen + t, dtype=float)[:, None, None]
+        cache.update(x, x)
+        seen += t
+        keep = min(seen, W)
+        assert np.array_equal(cache.k[:, 0, 0], np.arange(seen - keep, seen, dtype=float))
+    # prefill equals token-by-token decode under the legacy band as well
+    full = o.attention_layer_step(q, k, v, o.LayerKVCache(Hkv, d, W, legacy_4k=True), theta=1e4)
+    c2 = o.LayerKVCache(Hkv, d, W, legacy_4k=True)
+    steps = np.concatenate([o.attention_layer_step(q[t:t + 1], k[t:t + 1], v[t:t + 1], c2, theta=1e4)
+                            for t in range(T)])
+    assert np.max(np.abs(steps - full)) < 1e-12
+
+
 PINS = [pin_worked_example, pin_fig4_masks, pin_sdpa_float64, pin_bruteforce_layer,
         pin_rows_sum_to_one, pin_swa_equals_global_short, pin_uniform_closed_form,
         pin_gqa_grouping, pin_rope_library, pin_rope_complex, pin_rope_shift_invariance,
         pin_yarn_printed, pin_yarn_figure7, pin_rmsnorm, pin_cache_trim,
-        pin_decode_equivalence, pin_kv_accounting]
+        pin_decode_equivalence, pin_kv_accounting, pin_legacy_4k_band]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -472,6 +508,8 @@ MISTAKES = {
     "norm_eps_outside_sqrt": ("return gain * (x / np.sqrt(mean_sq + eps))", "return gain * (x / (np.sqrt(mean_sq) + eps))"),
     "cache_keeps_W": ("keep = n if self.window == 0 else min(n, self.window - 1)",
                       "keep = n if self.window == 0 else min(n, self.window)"),
+    "legacy_band_minus_one": ("ok &= (i - j) <= window", "ok &= (i - j) < window + 0"),
+    "legacy_cache_keeps_W_minus_one": ("keep = min(n, self.window)\n", "keep = min(n, self.window - 1)\n"),
     "query_positions_from_zero": ("q_pos = np.arange(S - T, S)", "q_pos = np.arange(T)"),
     "default_scale_inverse_d": ("scale = 1.0 / math.sqrt(d)", "scale = 1.0 / d"),
     "weighted_sum_uses_keys": ("out[r0:r1, h, :] = a @ v[:, g, :]", "out[r0:r1, h, :] = a @ k_rot[:, g, :]"),
