@@ -125,7 +125,10 @@ PLAMO_API long long plamo_prefill_padded_len(long long S);
  *                          cap >= pos_offset + T. Local: slot n mod window (a ring of
  *                          `window` slots, cap >= window); only the last `window`
  *                          new tokens are written.
- * window   0 = global layer, W > 0 = local layer with W keys including self.
+ * window   0 = global layer, W > 0 = local layer with W keys including self. The
+ *          4K release's local layer (band up to distance W, cache of W tokens [P3
+ *          §5.1]) is window = W + 1 here. A global layer without YaRN (also the 4K
+ *          release [P3 §6.3]) is a rope table built with yarn_factor <= 1.
  * rope_table / rope_table_bytes  a table built for this layer type covering every
  *                          renumbered position < kept + T.
  * ------------------------------------------------------------------------- */

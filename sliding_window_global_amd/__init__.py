@@ -24,7 +24,7 @@ HEAD_DIM = 128
 __all__ = [
     "PlamoError", "RopeParams", "LOCAL_ROPE", "GLOBAL_ROPE",
     "plamo_rope_table_bytes", "plamo_rope_table_init", "make_rope_table",
-    "plamo_prefill_padded_len", "plamo_kv_append", "plamo_attn_prefill",
+    "plamo_prefill_padded_len", "legacy_4k_window", "plamo_kv_append", "plamo_attn_prefill",
     "plamo_attn_decode_workspace_bytes", "plamo_attn_decode", "plamo_kv_append_ragged",
     "plamo_attn_prefill_ragged", "plamo_attn_decode_ragged_workspace_bytes", "plamo_attn_decode_ragged",
     "library_path",
@@ -126,6 +126,13 @@ def kept_tokens(window: int, pos_offset: int) -> int:
     """Cached tokens a chunk at pos_offset attends before its own (global: all of them; local:
     the last window-1)."""
     return int(pos_offset) if window == 0 else min(int(pos_offset), int(window) - 1)
+
+
+def legacy_4k_window(window: int) -> int:
+    """Window argument that gives the 4K release's local layer (「PLaMo 3アーキテクチャ徹底解析」
+    §5.1): its band reaches distance W (W + 1 keys including self) and its cache keeps W
+    tokens, which is this library's window W + 1 (ring capacity >= W + 1). Global: 0."""
+    return int(window) + 1 if window > 0 else 0
 
 
 def prefill_operand_shapes(B: int, T: int, Hkv: int, d: int, dtype, window: int = 0,

@@ -482,3 +482,52 @@ def test_decode_ragged_full_size():
         ref = oracle_decode_one(new["q"][b], new["k"][b], new["v"][b], prior_k[b], prior_v[b], int(pos[b]),
                                 window=0, rope=ly.rope, wq=new["wq"], wk=new["wk"], norm_offset=wl.norm_offset)
         assert_parity(out[b], ref, TOL_BF16, f"ragged decode b={b} p={pos[b]}")
+
+
+def _stream_case(window_arg, oracle_window, legacy_4k, rope, chunks, steps, seed):
+    """Prefill in chunks, then `steps` decode steps, on one token stream of B=2 sequences;
+    each call's output rows (sampled) against the oracle run on the same stream."""
+    B, Hq, Hkv, d = 2, 8, 2, 128
+    n = sum(chunks) + steps
+    dr = Draw(seed, True)
+    q, k, v = dr.normal((B, n, Hq, d)), dr.normal((B, n, Hkv, d)), dr.normal((B, n, Hkv, d))
+    wq, wk = dr.normal((d,), 0.02), dr.normal((d,), 0.02)
+    cap = window_arg if window_arg else n
+    kc = torch.zeros((B, Hkv, cap, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    tab = rope_table(rope, n + 64)
+    norm = dict(q_norm_w=dev(wq), k_norm_w=dev(wk), norm_offset=1.0)
+    got, p = [], 0
+    for T in chunks:
+        bufs = layer.prefill(dev(q[:, p:p + T]), dev(k[:, p:p + T]), dev(v[:, p:p + T]), window=window_arg,
+                             rope_table=tab, k_cache=kc, v_cache=vc, pos_offset=p, **norm)
+        torch.cuda.synchronize()
+        got.append(host(bufs.out))
+        p += T
+    for _ in range(steps):
+        db = layer.decode(dev(q[:, p:p + 1]), dev(k[:, p:p + 1]), dev(v[:, p:p + 1]), kc, vc, window=window_arg,
+                          pos_offset=p, rope_table=tab, **norm)
+        torch.cuda.synchronize()
+        got.append(host(db.out))
+        p += 1
+    all_chunks = list(chunks) + [1] * steps
+    edges = [0, 1, 15, 16, 17, 2046, 2047, 2048, 2049, 2050]
+    rows_of = lambda T: np.unique(np.array(edges + [T // 3, T // 2, T - 2, T - 1]).clip(0, T - 1))
+    ref = oracle_chunks(q, k, v, all_chunks, window=oracle_window, rope=rope, wq=wq, wk=wk, rows_of=rows_of,
+                        legacy_4k=legacy_4k)
+    for i, (g, r) in enumerate(zip(got, ref)):
+        assert_parity(g[:, rows_of(all_chunks[i])], r, TOL_BF16, f"call {i} (T={all_chunks[i]})")
+
+
+@pytest.mark.parametrize("W,chunks", [(2048, [2500, 300]), (16, [40, 5])], ids=["W2048", "W16"])
+def test_legacy_4k_window(W, chunks):
+    """The 4K release's local layer (「PLaMo 3アーキテクチャ徹底解析」 §5.1: band to distance W,
+    cache of the last W tokens) run as window W + 1: chunked prefill then decode, against the
+    oracle's own reading of that band (legacy_4k) at window W."""
+    _stream_case(swg.legacy_4k_window(W), W, True, Rope(1e4), chunks, 3, 5150 + W)
+
+
+def test_global_without_yarn():
+    """A global layer without YaRN (the 4K release, 「PLaMo 3アーキテクチャ徹底解析」 §6.3): table
+    built with yarn_factor 0; chunked prefill then decode against the oracle."""
+    _stream_case(0, 0, False, Rope(1e6), [300, 200], 3, 5199)
