@@ -178,21 +178,27 @@ class LayerKVCache:
     every token. A local layer keeps, after each update, at most the last W - 1
     tokens; the update itself returns all previously kept tokens plus the new
     ones, and that is what attention reads. legacy_4k: the cache class of the 4K
-    release's implementation (§5.1), which keeps the last W tokens, for its W + 1 band."""
+    release's implementation (§5.1), which keeps the last W tokens, for its W + 1 band.
 
-    def __init__(self, Hkv: int, d: int, window: int, legacy_4k: bool = False):
+    post_rope: the other order the page contrasts with PLaMo's (§4.4, the Gemma-style
+    layer): K is rotated at its absolute position before it is stored, queries are
+    rotated at theirs, and the cache returns K ready for use."""
+
+    def __init__(self, Hkv: int, d: int, window: int, legacy_4k: bool = False, post_rope: bool = False):
         self.window = int(window)
         self.legacy_4k = bool(legacy_4k)
+        self.post_rope = bool(post_rope)
         self.k = np.zeros((0, Hkv, d), dtype=F64)
         self.v = np.zeros((0, Hkv, d), dtype=F64)
         self.seen = 0  # tokens appended so far (absolute position of the next token)
 
     @classmethod
-    def with_prior(cls, k_prior, v_prior, seen: int, window: int, legacy_4k: bool = False):
+    def with_prior(cls, k_prior, v_prior, seen: int, window: int, legacy_4k: bool = False,
+                   post_rope: bool = False):
         """A cache that already holds ``k_prior``/``v_prior`` [n, Hkv, d] as its kept
-        tokens, after ``seen`` tokens in total."""
+        tokens (as stored: rotated when post_rope), after ``seen`` tokens in total."""
         k_prior = np.asarray(k_prior, dtype=F64)
-        c = cls(k_prior.shape[1], k_prior.shape[2], window, legacy_4k)
+        c = cls(k_prior.shape[1], k_prior.shape[2], window, legacy_4k, post_rope)
         keep = k_prior.shape[0]
         expect = seen if window == 0 else min(seen, window if legacy_4k else window - 1)
         if keep != expect:
@@ -223,7 +229,8 @@ def attention_layer_step(q, k, v, cache: LayerKVCache, *, theta: float,
                          rows=None, return_intermediates: bool = False):
     """One attention layer for one sequence, in the order of [P3 §4.4]:
     per-head Q/K RMSNorm -> cache update -> RoPE on the current Q and on every K the
-    cache returns -> masked GQA attention.
+    cache returns -> masked GQA attention. (A post_rope cache instead rotates K at its
+    absolute position before the update and Q at its absolute position.)
 
     q [T, Hq, d]; k, v [T, Hkv, d] (projected, before norm). Positions are the
     internal running numbers of [P3 §4.4]: the S keys returned by the cache get
@@ -239,17 +246,26 @@ def attention_layer_step(q, k, v, cache: LayerKVCache, *, theta: float,
     if q_norm_w is not None:
         q = offset_rms_norm(q, q_norm_w, norm_offset, eps)
         k = offset_rms_norm(k, k_norm_w, norm_offset, eps)
-    k_all, v_all = cache.update(k, v)
-    S = k_all.shape[0]
-    k_pos = np.arange(S)
-    q_pos = np.arange(S - T, S)
     omega, amp = rope_frequencies(d, theta, yarn_factor, orig_ctx, beta_fast, beta_slow)
+    if cache.post_rope:
+        # rotate the new K at its absolute positions, then store; the cache returns the
+        # rotated K of the kept tokens and the new ones; queries at absolute positions
+        first = cache.seen
+        k_all, v_all = cache.update(apply_rope(k, np.arange(first, first + T), omega, amp), v)
+        S = k_all.shape[0]
+        k_pos = np.arange(first + T - S, first + T)
+        q_pos = np.arange(first, first + T)
+    else:
+        k_all, v_all = cache.update(k, v)
+        S = k_all.shape[0]
+        k_pos = np.arange(S)
+        q_pos = np.arange(S - T, S)
     if rows is not None:
         rows = np.asarray(rows)
         q = q[rows]
         q_pos = q_pos[rows]
     q_rot = apply_rope(q, q_pos, omega, amp)
-    k_rot = apply_rope(k_all, k_pos, omega, amp)
+    k_rot = k_all if cache.post_rope else apply_rope(k_all, k_pos, omega, amp)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out = gqa_attention(q_rot, k_rot, v_all, q_pos, k_pos, cache.window, scale,

@@ -464,11 +464,43 @@ def pin_legacy_4k_band(o):
     assert np.max(np.abs(steps - full)) < 1e-12
 
 
+def pin_post_rope_cache(o):
+    """「PLaMo 3アーキテクチャ徹底解析」 §4.4 contrasts PLaMo's order (cache pre-RoPE K, rotate
+    every returned K at renumbered positions) with rotating K before the store at absolute
+    positions. Rotations compose (the score depends on i - j only, and the YaRN amplitude
+    multiplies both sides), so both orders give the same outputs, for prefill, chunks and
+    decode, on local and global layers, also past positions where absolute and renumbered
+    positions differ. The post-RoPE cache then holds K rotated at the absolute position."""
+    T, Hq, Hkv, d = 14, 4, 2, 16
+    q, k, v = _rand((T, Hq, d), 61), _rand((T, Hkv, d), 62), _rand((T, Hkv, d), 63)
+    wq, wk = _rand((d,), 64) * 0.1, _rand((d,), 65) * 0.1
+    for W, theta, yarn in ((4, 1e4, 0.0), (0, 1e6, 64.0), (6, 1e4, 0.0)):
+        kw = dict(theta=theta, yarn_factor=yarn, q_norm_w=wq, k_norm_w=wk, norm_offset=1.0)
+        for chunks in ([T], [5, 1, 1, 7], [1] * T):
+            pre, post = o.LayerKVCache(Hkv, d, W), o.LayerKVCache(Hkv, d, W, post_rope=True)
+            t0 = 0
+            for n in chunks:
+                a = o.attention_layer_step(q[t0:t0 + n], k[t0:t0 + n], v[t0:t0 + n], pre, **kw)
+                b = o.attention_layer_step(q[t0:t0 + n], k[t0:t0 + n], v[t0:t0 + n], post, **kw)
+                assert np.max(np.abs(a - b)) < 1e-10, (W, chunks)
+                t0 += n
+            # what the post-RoPE cache holds: the kept tokens' normalised K, rotated at their
+            # absolute positions (the rotation of each pair written out with cos / sin)
+            omega, amp = o.rope_frequencies(d, theta, yarn)
+            keep = post.k.shape[0]
+            kn = o.offset_rms_norm(k[T - keep:], wk, 1.0)
+            ang = np.arange(T - keep, T)[:, None, None] * omega[None, None, :]
+            x0, x1 = kn[..., :d // 2], kn[..., d // 2:]
+            want = np.concatenate([amp * (x0 * np.cos(ang) - x1 * np.sin(ang)),
+                                   amp * (x0 * np.sin(ang) + x1 * np.cos(ang))], axis=-1)
+            assert np.max(np.abs(post.k - want)) < 1e-12
+
+
 PINS = [pin_worked_example, pin_fig4_masks, pin_sdpa_float64, pin_bruteforce_layer,
         pin_rows_sum_to_one, pin_swa_equals_global_short, pin_uniform_closed_form,
         pin_gqa_grouping, pin_rope_library, pin_rope_complex, pin_rope_shift_invariance,
         pin_yarn_printed, pin_yarn_figure7, pin_rmsnorm, pin_cache_trim,
-        pin_decode_equivalence, pin_kv_accounting, pin_legacy_4k_band]
+        pin_decode_equivalence, pin_kv_accounting, pin_legacy_4k_band, pin_post_rope_cache]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -510,6 +542,10 @@ MISTAKES = {
                       "keep = n if self.window == 0 else min(n, self.window)"),
     "legacy_band_minus_one": ("ok &= (i - j) <= window", "ok &= (i - j) < window + 0"),
     "legacy_cache_keeps_W_minus_one": ("keep = min(n, self.window)\n", "keep = min(n, self.window - 1)\n"),
+    "post_rope_renumbered_keys": ("k_all, v_all = cache.update(apply_rope(k, np.arange(first, first + T), omega, amp), v)",
+                                  "k_all, v_all = cache.update(apply_rope(k, np.arange(T), omega, amp), v)"),
+    "post_rope_rotates_twice": ("k_rot = k_all if cache.post_rope else apply_rope(k_all, k_pos, omega, amp)",
+                                "k_rot = apply_rope(k_all, k_pos, omega, amp)"),
     "query_positions_from_zero": ("q_pos = np.arange(S - T, S)", "q_pos = np.arange(T)"),
     "default_scale_inverse_d": ("scale = 1.0 / math.sqrt(d)", "scale = 1.0 / d"),
     "weighted_sum_uses_keys": ("out[r0:r1, h, :] = a @ v[:, g, :]", "out[r0:r1, h, :] = a @ k_rot[:, g, :]"),
