@@ -158,8 +158,9 @@ def bench_chunked_prefill(torch, swg, wl, chunk, steps, warmup):
 # decode
 # ----------------------------------------------------------------------------
 
-def bench_decode_batched(torch, swg, wl, layer_idx, steps, warmup):
-    """attn_decode alone (the split kernel + combine) over a cache at its real size."""
+def bench_decode_batched(torch, swg, wl, layer_idx, steps, warmup, post_rope=False):
+    """attn_decode alone (the split kernel + combine) over a cache at its real size (post_rope:
+    a cache that holds K already rotated, read as stored)."""
     from sliding_window_global_amd import layer
     from synthetic.workloads import device_normal_bf16
     ly = wl.layers[layer_idx]
@@ -173,11 +174,11 @@ def bench_decode_batched(torch, swg, wl, layer_idx, steps, warmup):
     swg.plamo_kv_append(dev_bf16(torch, new["q"]), dev_bf16(torch, new["k"]), dev_bf16(torch, new["v"]),
                         bufs.q_rot, window=ly.window, pos_offset=p, rope_table=tab,
                         q_norm_w=dev_bf16(torch, new["wq"]), k_norm_w=dev_bf16(torch, new["wk"]),
-                        norm_offset=wl.norm_offset, k_cache=kc, v_cache=vc)
+                        norm_offset=wl.norm_offset, k_cache=kc, v_cache=vc, cache_post_rope=post_rope)
 
     def run():
         swg.plamo_attn_decode(bufs.q_rot, kc, vc, bufs.out, bufs.workspace, window=ly.window,
-                              pos_offset=p, rope_table=tab)
+                              pos_offset=p, rope_table=tab, cache_post_rope=post_rope)
 
     for _ in range(warmup):
         run()
@@ -191,7 +192,8 @@ def bench_decode_batched(torch, swg, wl, layer_idx, steps, warmup):
     nbytes = wl.kv_bytes(ly)
     del kc, vc
     torch.cuda.empty_cache()
-    return dict(workload=f"{wl.name}_{'global' if ly.window == 0 else 'local'}", kv_bytes=nbytes,
+    return dict(workload=f"{wl.name}_{'global' if ly.window == 0 else 'local'}{'_post_rope' if post_rope else ''}",
+                kv_bytes=nbytes,
                 keys=wl.keys_attended(ly), ms=ms, gbs=nbytes / ms / 1e6, frac_hbm=nbytes / ms / 1e6 / PEAK_HBM_GBS)
 
 
@@ -355,6 +357,10 @@ def main():
             r = bench_decode_batched(torch, swg, BATCHED_DECODE, li, args.steps, args.warmup)
             log(f"[bench]   {r}")
             extra[r["workload"]] = r
+        log("[bench] batched decode, global layer, post-RoPE cache")
+        r = bench_decode_batched(torch, swg, BATCHED_DECODE, 1, args.steps, args.warmup, post_rope=True)
+        log(f"[bench]   {r}")
+        extra[r["workload"]] = r
         log("[bench] ragged batched decode, global layer")
         r = bench_decode_ragged(torch, swg, BATCHED_DECODE, 1, args.steps, args.warmup)
         log(f"[bench]   {r}")

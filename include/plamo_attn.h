@@ -60,6 +60,16 @@ typedef enum {
 
 typedef enum { PLAMO_F32 = 0, PLAMO_BF16 = 1 } plamo_dtype;
 
+/* What the K cache holds [P3 §4.4]. PRE_ROPE is PLaMo 3's order: normalised K before
+ * RoPE, rotated at renumbered positions 0..S-1 every time the cache returns it.
+ * POST_ROPE is the other order the page contrasts it with (the Gemma-style layer, for
+ * engines whose caches hold rotated K): K rotated at its absolute position before it is
+ * stored, queries rotated at their absolute positions, the cache read as stored. Both
+ * give the same attention up to rounding; the rope table must then cover absolute
+ * positions < pos_offset + T, and decode needs no table. A cache is written and read in
+ * one order only. */
+typedef enum { PLAMO_CACHE_PRE_ROPE = 0, PLAMO_CACHE_POST_ROPE = 1 } plamo_cache_order;
+
 /* RoPE parameters of one layer type [P3 §2.1, §6.2, §6.3].
  * Local layers: theta = 1e4, no YaRN. Global layers: theta = 1e6 with YaRN. */
 typedef struct {
@@ -130,14 +140,16 @@ PLAMO_API long long plamo_prefill_padded_len(long long S);
  *          §5.1]) is window = W + 1 here. A global layer without YaRN (also the 4K
  *          release [P3 §6.3]) is a rope table built with yarn_factor <= 1.
  * rope_table / rope_table_bytes  a table built for this layer type covering every
- *                          renumbered position < kept + T.
+ *                          renumbered position < kept + T (POST_ROPE: absolute < pos_offset + T).
+ * cache_order PLAMO_CACHE_PRE_ROPE or PLAMO_CACHE_POST_ROPE (above).
  * ------------------------------------------------------------------------- */
 PLAMO_API int plamo_kv_append(int dtype, const void* q, const void* k, const void* v,
                     const void* q_norm_w, const void* k_norm_w, float norm_offset,
                     float norm_eps, void* q_out, void* k_rot_out, void* v_t_out,
                     void* k_cache, void* v_cache, long long cap, int B, int T, int Hq,
                     int Hkv, int d, int window, long long pos_offset,
-                    const void* rope_table, size_t rope_table_bytes, void* stream);
+                    const void* rope_table, size_t rope_table_bytes, int cache_order,
+                    void* stream);
 
 /* ---------------------------------------------------------------------------
  * plamo_attn_prefill -- step 4 for a prefill of T tokens [P3 §4.5, §5.1]
@@ -169,7 +181,8 @@ PLAMO_API int plamo_attn_prefill(int dtype, const void* q_rot, const void* k_rot
  * workspace: device scratch of at least plamo_attn_decode_workspace_bytes(...)
  * bytes (split-K partial results); contents on entry do not matter. When that
  * size is 0 (one key range per sequence and KV head) workspace may be NULL.
- * dtype must be PLAMO_BF16; T must be 1.
+ * dtype must be PLAMO_BF16; T must be 1. cache_order as given to plamo_kv_append
+ * (POST_ROPE: rope_table may be NULL and is not read).
  * ------------------------------------------------------------------------- */
 PLAMO_API size_t plamo_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int window,
                                          long long pos_offset);
@@ -178,7 +191,8 @@ PLAMO_API int plamo_attn_decode(int dtype, const void* q_rot, const void* k_cach
                       const void* v_cache, long long cap, void* out, void* workspace,
                       size_t workspace_bytes, int B, int T, int Hq, int Hkv, int d,
                       int window, long long pos_offset, const void* rope_table,
-                      size_t rope_table_bytes, float softmax_scale, void* stream);
+                      size_t rope_table_bytes, float softmax_scale, int cache_order,
+                      void* stream);
 
 /* ---------------------------------------------------------------------------
  * Ragged batches: every sequence at its own position [P3 §4.4]
@@ -220,7 +234,7 @@ PLAMO_API int plamo_kv_append_ragged(int dtype, const void* q, const void* k, co
                     void* k_cache, void* v_cache, long long cap, int B, int T, int Hq,
                     int Hkv, int d, int window, const long long* seq_pos_offsets,
                     const int* seq_lens, long long max_pos_offset, const void* rope_table,
-                    size_t rope_table_bytes, void* stream);
+                    size_t rope_table_bytes, int cache_order, void* stream);
 
 PLAMO_API int plamo_attn_prefill_ragged(int dtype, const void* q_rot, const void* k_rot,
                     const void* v_t, void* out, int B, int T, int Hq, int Hkv, int d,
@@ -232,7 +246,7 @@ PLAMO_API int plamo_attn_decode_ragged(int dtype, const void* q_rot, const void*
                     size_t workspace_bytes, int B, int Hq, int Hkv, int d, int window,
                     const long long* seq_pos_offsets, long long max_pos_offset,
                     const void* rope_table, size_t rope_table_bytes, float softmax_scale,
-                    void* stream);
+                    int cache_order, void* stream);
 
 /* Human-readable text for a status code (static storage). */
 PLAMO_API const char* plamo_status_str(int status);

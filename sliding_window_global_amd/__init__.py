@@ -19,6 +19,8 @@ from ._lib import PlamoRope
 
 PLAMO_F32 = 0
 PLAMO_BF16 = 1
+PLAMO_CACHE_PRE_ROPE = 0   # PLaMo 3's order: the cache holds K before RoPE
+PLAMO_CACHE_POST_ROPE = 1  # the cache holds K rotated at absolute positions
 HEAD_DIM = 128
 
 __all__ = [
@@ -83,6 +85,14 @@ def _dev(t: torch.Tensor | None, name: str, dtype=None) -> int | None:
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     return t.data_ptr()
+
+
+def _order(post_rope: bool) -> int:
+    return PLAMO_CACHE_POST_ROPE if post_rope else PLAMO_CACHE_PRE_ROPE
+
+
+def _nbytes(t: torch.Tensor | None) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _dtype_code(dt: torch.dtype) -> int:
@@ -152,7 +162,8 @@ def prefill_operand_shapes(B: int, T: int, Hkv: int, d: int, dtype, window: int 
 
 def plamo_kv_append(q, k, v, q_out, *, window: int, pos_offset: int, rope_table,
                     q_norm_w=None, k_norm_w=None, norm_offset: float = 1.0, norm_eps: float = 1e-6,
-                    k_rot_out=None, v_t_out=None, k_cache=None, v_cache=None, stream=None) -> None:
+                    k_rot_out=None, v_t_out=None, k_cache=None, v_cache=None, cache_post_rope: bool = False,
+                    stream=None) -> None:
     """q [B,T,Hq,d], k/v [B,T,Hkv,d]; outputs as documented in plamo_attn.h."""
     dt = q.dtype
     B, T, Hq, d = q.shape
@@ -177,7 +188,7 @@ def plamo_kv_append(q, k, v, q_out, *, window: int, pos_offset: int, rope_table,
         _dev(q_out, "q_out", dt), _dev(k_rot_out, "k_rot_out", dt), _dev(v_t_out, "v_t_out", dt),
         _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), int(cap), B, T, Hq, Hkv, d,
         int(window), int(pos_offset), _dev(rope_table, "rope_table", torch.float32),
-        rope_table.numel() * 4, _stream(stream))
+        rope_table.numel() * 4, _order(cache_post_rope), _stream(stream))
     _check(st, "plamo_kv_append")
 
 
@@ -205,7 +216,8 @@ def plamo_attn_decode_workspace_bytes(B: int, Hq: int, Hkv: int, window: int, po
 
 
 def plamo_attn_decode(q_rot, k_cache, v_cache, out, workspace, *, window: int, pos_offset: int,
-                      rope_table, softmax_scale: float | None = None, stream=None) -> None:
+                      rope_table, softmax_scale: float | None = None, cache_post_rope: bool = False,
+                      stream=None) -> None:
     """q_rot [B,1,Hq,d]; caches [B,Hkv,cap,d] (bf16) -> out [B,1,Hq,d]."""
     dt = q_rot.dtype
     B, T, Hq, d = q_rot.shape
@@ -219,8 +231,8 @@ def plamo_attn_decode(q_rot, k_cache, v_cache, out, workspace, *, window: int, p
     st = _lib.load().plamo_attn_decode(
         _dtype_code(dt), _dev(q_rot, "q_rot", dt), _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
         int(cap), _dev(out, "out", dt), _dev(workspace, "workspace"), ws_bytes, B, T, Hq, Hkv, d,
-        int(window), int(pos_offset), _dev(rope_table, "rope_table", torch.float32), rope_table.numel() * 4,
-        scale, _stream(stream))
+        int(window), int(pos_offset), _dev(rope_table, "rope_table", torch.float32), _nbytes(rope_table),
+        scale, _order(cache_post_rope), _stream(stream))
     _check(st, "plamo_attn_decode")
 
 
@@ -239,7 +251,7 @@ def _ragged_arrays(B: int, seq_pos_offsets, seq_lens):
 def plamo_kv_append_ragged(q, k, v, q_out, *, window: int, seq_pos_offsets, max_pos_offset: int,
                            rope_table, seq_lens=None, q_norm_w=None, k_norm_w=None,
                            norm_offset: float = 1.0, norm_eps: float = 1e-6, k_rot_out=None, v_t_out=None,
-                           k_cache=None, v_cache=None, stream=None) -> None:
+                           k_cache=None, v_cache=None, cache_post_rope: bool = False, stream=None) -> None:
     """plamo_kv_append with per-sequence positions seq_pos_offsets [B] (int64, GPU) bounded by
     max_pos_offset and token counts seq_lens [B] (int32, GPU; None = T each)."""
     dt = q.dtype
@@ -266,7 +278,7 @@ def plamo_kv_append_ragged(q, k, v, q_out, *, window: int, seq_pos_offsets, max_
         _dev(q_out, "q_out", dt), _dev(k_rot_out, "k_rot_out", dt), _dev(v_t_out, "v_t_out", dt),
         _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), int(cap), B, T, Hq, Hkv, d,
         int(window), pos_p, len_p, int(max_pos_offset), _dev(rope_table, "rope_table", torch.float32),
-        rope_table.numel() * 4, _stream(stream))
+        rope_table.numel() * 4, _order(cache_post_rope), _stream(stream))
     _check(st, "plamo_kv_append_ragged")
 
 
@@ -298,7 +310,7 @@ def plamo_attn_decode_ragged_workspace_bytes(B: int, Hq: int, Hkv: int, window: 
 
 def plamo_attn_decode_ragged(q_rot, k_cache, v_cache, out, workspace, *, window: int, seq_pos_offsets,
                              max_pos_offset: int, rope_table, softmax_scale: float | None = None,
-                             stream=None) -> None:
+                             cache_post_rope: bool = False, stream=None) -> None:
     """plamo_attn_decode with one position per sequence; workspace sized by
     plamo_attn_decode_ragged_workspace_bytes."""
     dt = q_rot.dtype
@@ -316,6 +328,6 @@ def plamo_attn_decode_ragged(q_rot, k_cache, v_cache, out, workspace, *, window:
     st = _lib.load().plamo_attn_decode_ragged(
         _dtype_code(dt), _dev(q_rot, "q_rot", dt), _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
         int(cap), _dev(out, "out", dt), _dev(workspace, "workspace"), ws_bytes, B, Hq, Hkv, d, int(window),
-        pos_p, int(max_pos_offset), _dev(rope_table, "rope_table", torch.float32), rope_table.numel() * 4,
-        scale, _stream(stream))
+        pos_p, int(max_pos_offset), _dev(rope_table, "rope_table", torch.float32), _nbytes(rope_table),
+        scale, _order(cache_post_rope), _stream(stream))
     _check(st, "plamo_attn_decode_ragged")

@@ -24,22 +24,23 @@ SIGNATURES = {
     "plamo_prefill_padded_len": (c_ll, [c_ll]),
     "plamo_kv_append": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_float,
                                 c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_ll, c_int, c_int, c_int,
-                                c_int, c_int, c_int, c_ll, c_void_p, c_size, c_void_p]),
+                                c_int, c_int, c_int, c_ll, c_void_p, c_size, c_int, c_void_p]),
     "plamo_attn_prefill": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                    c_int, c_int, c_ll, c_float, c_void_p]),
     "plamo_attn_decode_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int, c_ll]),
     "plamo_attn_decode": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_ll, c_void_p, c_void_p, c_size, c_int,
-                                  c_int, c_int, c_int, c_int, c_int, c_ll, c_void_p, c_size, c_float, c_void_p]),
+                                  c_int, c_int, c_int, c_int, c_int, c_ll, c_void_p, c_size, c_float, c_int,
+                                  c_void_p]),
     "plamo_kv_append_ragged": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_float,
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_ll, c_int, c_int,
                                        c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_ll, c_void_p, c_size,
-                                       c_void_p]),
+                                       c_int, c_void_p]),
     "plamo_attn_prefill_ragged": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
                                           c_int, c_int, c_int, c_void_p, c_void_p, c_ll, c_float, c_void_p]),
     "plamo_attn_decode_ragged_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int, c_ll]),
     "plamo_attn_decode_ragged": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_ll, c_void_p, c_void_p, c_size,
                                          c_int, c_int, c_int, c_int, c_int, c_void_p, c_ll, c_void_p, c_size,
-                                         c_float, c_void_p]),
+                                         c_float, c_int, c_void_p]),
     "plamo_status_str": (ctypes.c_char_p, [c_int]),
     "plamo_last_error": (ctypes.c_char_p, []),
 }

@@ -137,8 +137,10 @@ int kv_append_impl(int dtype, const void* q, const void* k, const void* v, const
                    void* k_rot_out, void* v_t_out, void* k_cache, void* v_cache, long long cap,
                    int B, int T, int Hq, int Hkv, int d, int window, long long pos_offset,
                    const long long* seq_pos, const int* seq_len, const void* rope_table,
-                   size_t rope_table_bytes, void* stream) {
+                   size_t rope_table_bytes, int cache_order, void* stream) {
   if (dtype != PLAMO_F32 && dtype != PLAMO_BF16) return fail(PLAMO_ERR_INVALID_ARG, "unknown dtype");
+  if (cache_order != PLAMO_CACHE_PRE_ROPE && cache_order != PLAMO_CACHE_POST_ROPE)
+    return fail(PLAMO_ERR_INVALID_ARG, "unknown cache_order");
   if (int st = check_heads(B, T, Hq, Hkv, d, window, pos_offset)) return st;
   if (B == 0 || T == 0) return ok();
   if (!q || !k || !v || !q_out) return fail(PLAMO_ERR_INVALID_ARG, "q, k, v and q_out must be non-NULL");
@@ -160,7 +162,10 @@ int kv_append_impl(int dtype, const void* q, const void* k, const void* v, const
   if (!rope_table) return fail(PLAMO_ERR_INVALID_ARG, "rope_table must be non-NULL");
   const long long covered = table_positions(rope_table_bytes);
   if (covered < 0) return fail(PLAMO_ERR_INVALID_ARG, "rope_table_bytes is not a whole number of rows");
-  if (covered < kept + T) return fail(PLAMO_ERR_WORKSPACE, "rope table does not cover positions < kept + T");
+  const bool post = cache_order == PLAMO_CACHE_POST_ROPE;
+  if (!post && covered < kept + T) return fail(PLAMO_ERR_WORKSPACE, "rope table does not cover positions < kept + T");
+  if (post && covered < pos_offset + T)
+    return fail(PLAMO_ERR_WORKSPACE, "post-RoPE cache: rope table does not cover positions < pos_offset + T");
 
   plamo::AppendArgs a;
   a.q = q; a.k = k; a.v = v; a.wq = q_norm_w; a.wk = k_norm_w;
@@ -172,6 +177,7 @@ int kv_append_impl(int dtype, const void* q, const void* k, const void* v, const
   a.pos_offset = pos_offset; a.kept = kept;
   a.seq_pos = seq_pos; a.seq_len = seq_len;
   a.ops_kernel = (k_rot_out || v_t_out) && (kept > 0 || seq_pos || seq_len);
+  a.post_rope = post;
   a.rope = static_cast<const float2*>(rope_table);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return launched(dtype == PLAMO_BF16 ? plamo::launch_kv_append_bf16(a, s) : plamo::launch_kv_append_f32(a, s));
@@ -212,13 +218,16 @@ int attn_decode_impl(int dtype, const void* q_rot, const void* k_cache, const vo
                      long long cap, void* out, void* workspace, size_t workspace_bytes, int B, int T,
                      int Hq, int Hkv, int d, int window, long long pos_offset, const long long* seq_pos,
                      const void* rope_table, size_t rope_table_bytes, float softmax_scale,
-                     void* stream) {
+                     int cache_order, void* stream) {
   if (dtype != PLAMO_BF16) return fail(dtype == PLAMO_F32 ? PLAMO_ERR_UNSUPPORTED : PLAMO_ERR_INVALID_ARG,
                                        "decode reads a bf16 cache");
   if (T != 1) return fail(T < 0 ? PLAMO_ERR_INVALID_ARG : PLAMO_ERR_UNSUPPORTED, "decode takes T = 1");
   if (int st = check_heads(B, T, Hq, Hkv, d, window, pos_offset)) return st;
+  if (cache_order != PLAMO_CACHE_PRE_ROPE && cache_order != PLAMO_CACHE_POST_ROPE)
+    return fail(PLAMO_ERR_INVALID_ARG, "unknown cache_order");
+  const bool post = cache_order == PLAMO_CACHE_POST_ROPE;
   if (B == 0) return ok();
-  if (!q_rot || !k_cache || !v_cache || !out || !rope_table)
+  if (!q_rot || !k_cache || !v_cache || !out || (!rope_table && !post))
     return fail(PLAMO_ERR_INVALID_ARG, "q_rot, caches, out and rope_table must be non-NULL");
   const void* ptrs[] = {q_rot, k_cache, v_cache, out, workspace, rope_table};
   for (const void* p : ptrs)
@@ -228,9 +237,11 @@ int attn_decode_impl(int dtype, const void* q_rot, const void* k_cache, const vo
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return fail(PLAMO_ERR_INVALID_ARG, "softmax_scale must be > 0");
   const long long kept = kept_tokens(window, pos_offset);
   const long long S = kept + 1;
-  const long long covered = table_positions(rope_table_bytes);
-  if (covered < 0) return fail(PLAMO_ERR_INVALID_ARG, "rope_table_bytes is not a whole number of rows");
-  if (covered < S) return fail(PLAMO_ERR_WORKSPACE, "rope table does not cover positions < kept + 1");
+  if (!post) {  // a post-RoPE cache is read as stored: no table
+    const long long covered = table_positions(rope_table_bytes);
+    if (covered < 0) return fail(PLAMO_ERR_INVALID_ARG, "rope_table_bytes is not a whole number of rows");
+    if (covered < S) return fail(PLAMO_ERR_WORKSPACE, "rope table does not cover positions < kept + 1");
+  }
   const plamo::DecodePlan plan = plamo::plan_decode(B, Hkv, S, seq_pos != nullptr);
   const size_t need = plamo::decode_workspace_bytes(B, Hq, plan);
   if (need > 0 && (!workspace || workspace_bytes < need)) return fail(PLAMO_ERR_WORKSPACE, "workspace too small");
@@ -242,6 +253,7 @@ int attn_decode_impl(int dtype, const void* q_rot, const void* k_cache, const vo
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.window = window;
   a.S = S; a.base = pos_offset - kept; a.plan = plan;
   a.pos_offset = pos_offset; a.seq_pos = seq_pos;
+  a.post_rope = post;
   a.rope = static_cast<const float2*>(rope_table);
   a.scale = softmax_scale;
   return launched(plamo::launch_decode_bf16(a, static_cast<hipStream_t>(stream)));
@@ -255,10 +267,10 @@ int plamo_kv_append(int dtype, const void* q, const void* k, const void* v, cons
                     const void* k_norm_w, float norm_offset, float norm_eps, void* q_out,
                     void* k_rot_out, void* v_t_out, void* k_cache, void* v_cache, long long cap,
                     int B, int T, int Hq, int Hkv, int d, int window, long long pos_offset,
-                    const void* rope_table, size_t rope_table_bytes, void* stream) {
+                    const void* rope_table, size_t rope_table_bytes, int cache_order, void* stream) {
   return kv_append_impl(dtype, q, k, v, q_norm_w, k_norm_w, norm_offset, norm_eps, q_out, k_rot_out,
                         v_t_out, k_cache, v_cache, cap, B, T, Hq, Hkv, d, window, pos_offset, nullptr,
-                        nullptr, rope_table, rope_table_bytes, stream);
+                        nullptr, rope_table, rope_table_bytes, cache_order, stream);
 }
 
 int plamo_kv_append_ragged(int dtype, const void* q, const void* k, const void* v, const void* q_norm_w,
@@ -267,12 +279,12 @@ int plamo_kv_append_ragged(int dtype, const void* q, const void* k, const void* 
                            int B, int T, int Hq, int Hkv, int d, int window,
                            const long long* seq_pos_offsets, const int* seq_lens,
                            long long max_pos_offset, const void* rope_table, size_t rope_table_bytes,
-                           void* stream) {
+                           int cache_order, void* stream) {
   if (B > 0 && T > 0)
     if (int st = check_ragged(seq_pos_offsets, seq_lens)) return st;
   return kv_append_impl(dtype, q, k, v, q_norm_w, k_norm_w, norm_offset, norm_eps, q_out, k_rot_out,
                         v_t_out, k_cache, v_cache, cap, B, T, Hq, Hkv, d, window, max_pos_offset,
-                        seq_pos_offsets, seq_lens, rope_table, rope_table_bytes, stream);
+                        seq_pos_offsets, seq_lens, rope_table, rope_table_bytes, cache_order, stream);
 }
 
 int plamo_attn_prefill(int dtype, const void* q_rot, const void* k_rot, const void* v_t, void* out,
@@ -311,22 +323,22 @@ int plamo_attn_decode(int dtype, const void* q_rot, const void* k_cache, const v
                       long long cap, void* out, void* workspace, size_t workspace_bytes, int B, int T,
                       int Hq, int Hkv, int d, int window, long long pos_offset,
                       const void* rope_table, size_t rope_table_bytes, float softmax_scale,
-                      void* stream) {
+                      int cache_order, void* stream) {
   return attn_decode_impl(dtype, q_rot, k_cache, v_cache, cap, out, workspace, workspace_bytes, B, T, Hq,
                           Hkv, d, window, pos_offset, nullptr, rope_table, rope_table_bytes,
-                          softmax_scale, stream);
+                          softmax_scale, cache_order, stream);
 }
 
 int plamo_attn_decode_ragged(int dtype, const void* q_rot, const void* k_cache, const void* v_cache,
                              long long cap, void* out, void* workspace, size_t workspace_bytes, int B,
                              int Hq, int Hkv, int d, int window, const long long* seq_pos_offsets,
                              long long max_pos_offset, const void* rope_table, size_t rope_table_bytes,
-                             float softmax_scale, void* stream) {
+                             float softmax_scale, int cache_order, void* stream) {
   if (B > 0)
     if (int st = check_ragged(seq_pos_offsets, nullptr)) return st;
   return attn_decode_impl(dtype, q_rot, k_cache, v_cache, cap, out, workspace, workspace_bytes, B, 1, Hq,
                           Hkv, d, window, max_pos_offset, seq_pos_offsets, rope_table, rope_table_bytes,
-                          softmax_scale, stream);
+                          softmax_scale, cache_order, stream);
 }
 
 }  // extern "C"

@@ -108,10 +108,12 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   const int n_tok = min(kTokBlock, sp.T - t0);  // may be <= 0 in the padding blocks
   if (n_tok <= 0 && (a.ops_kernel || !(k_rot || v_t))) return;  // block-uniform
 
-  // rotation factors of this block's renumbered positions kept + t
+  // rotation factors of this block's renumbered positions kept + t (post-RoPE cache:
+  // absolute positions pos + t)
+  const long long p_first = a.post_rope ? sp.pos : sp.kept;
   for (int i = threadIdx.x; i < kTokBlock * kHalf; i += kThreads) {
     const int r = i / kHalf, j = i % kHalf;
-    if (r < n_tok) zs[r][j] = rope_factor(a.rope, sp.kept + t0 + r, j);
+    if (r < n_tok) zs[r][j] = rope_factor(a.rope, p_first + t0 + r, j);
   }
   float gq[2 * kVec], gk[2 * kVec];  // gains c + w of this lane's dims (both halves)
 #pragma unroll
@@ -168,15 +170,19 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
 #pragma unroll
           for (int e = 0; e < 2 * kVec; ++e) x[u][e] *= inv * g[e];
         }
-        if (is_k) {
+        const bool to_cache = is_k && k_cache && (a.window == 0 || t >= sp.T - a.window);
+        E* cdst = nullptr;
+        if (to_cache) {
+          const long long n = sp.pos + t;
+          const long long s = a.window == 0 ? n : n % a.window;
+          cdst = k_cache + ((static_cast<long long>(b) * a.Hkv + kvh) * a.cap + s) * kHeadDim + c * kVec;
+        }
+        if (is_k && !a.post_rope) {  // the cache stores K before RoPE; RoPE acts on that value
 #pragma unroll
-          for (int e = 0; e < 2 * kVec; ++e) x[u][e] = Io<E>::rnd(x[u][e]);  // the cached value
-          if (k_cache && (a.window == 0 || t >= sp.T - a.window)) {
-            const long long n = sp.pos + t;
-            const long long s = a.window == 0 ? n : n % a.window;
-            E* dst = k_cache + ((static_cast<long long>(b) * a.Hkv + kvh) * a.cap + s) * kHeadDim + c * kVec;
-            *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(x[u]);
-            *reinterpret_cast<u32x4*>(dst + kHalf) = Io<E>::pack(x[u] + kVec);
+          for (int e = 0; e < 2 * kVec; ++e) x[u][e] = Io<E>::rnd(x[u][e]);
+          if (to_cache) {
+            *reinterpret_cast<u32x4*>(cdst) = Io<E>::pack(x[u]);
+            *reinterpret_cast<u32x4*>(cdst + kHalf) = Io<E>::pack(x[u] + kVec);
           }
           if (!k_rot) continue;
         }
@@ -187,6 +193,13 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
           const float x0 = x[u][e], x1 = x[u][kVec + e];
           y[e] = x0 * z.x - x1 * z.y;
           y[kVec + e] = x0 * z.y + x1 * z.x;
+        }
+        if (is_k && a.post_rope) {  // the cache stores K rotated at its absolute position
+          if (to_cache) {
+            *reinterpret_cast<u32x4*>(cdst) = Io<E>::pack(y);
+            *reinterpret_cast<u32x4*>(cdst + kHalf) = Io<E>::pack(y + kVec);
+          }
+          if (!k_rot) continue;
         }
         // the operand row of new token t follows the kept cached keys
         const long long R = sp.kept + t;
@@ -322,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a
   if (k_rot) {
     for (int i = threadIdx.x; i < kTokBlock * kHalf; i += kThreads) {
       const int r = i / kHalf, j = i % kHalf;
-      if (R0 + r < kept) zs[r][j] = rope_factor(a.rope, R0 + r, j);
+      if (R0 + r < kept && !a.post_rope) zs[r][j] = rope_factor(a.rope, R0 + r, j);
     }
     __syncthreads();
     for (int r = wave * kRowsPerPass + slot; r < kTokBlock; r += kWaves * kRowsPerPass) {
@@ -336,9 +349,14 @@ __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a
         Io<E>::unpack(*reinterpret_cast<const u32x4*>(src + kHalf), x + kVec);
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
-          const float2 z = zs[r][c * kVec + e];
-          y[e] = x[e] * z.x - x[kVec + e] * z.y;
-          y[kVec + e] = x[e] * z.y + x[kVec + e] * z.x;
+          if (a.post_rope) {  // already rotated (at its absolute position) in the cache
+            y[e] = x[e];
+            y[kVec + e] = x[kVec + e];
+          } else {
+            const float2 z = zs[r][c * kVec + e];
+            y[e] = x[e] * z.x - x[kVec + e] * z.y;
+            y[kVec + e] = x[e] * z.y + x[kVec + e] * z.x;
+          }
         }
       } else {
 #pragma unroll

@@ -43,7 +43,9 @@ constexpr int kVChunks = kSub * kVRow / 8; // 16-byte slots of one V sub-tile: 2
 constexpr int kVLoads = (kVChunks + 63) / 64;  // direct loads per V sub-tile: 5
 constexpr int kVSlot = kVLoads * 64 * 8;   // elements reserved per V sub-tile
 constexpr float kRescaleLog2 = 8.f;        // lazy-rescale threshold (log2 units)
-constexpr int kLoadsPerIssue = 4 + kVLoads + 1;  // K rows, V rows, coarse row
+// loads per tile issue: K rows, V rows and (when K is rotated here) the coarse rope row
+template <bool kRotate>
+constexpr int kLoadsPerIssue = 4 + kVLoads + (kRotate ? 1 : 0);
 
 // s_waitcnt vmcnt(n), expcnt / lgkmcnt left alone (gfx9 encoding: vmcnt bits 3:0, 15:14)
 constexpr unsigned wait_vmcnt(int n) { return 0x0F70u | (n & 15) | ((n >> 4) << 14); }
@@ -52,8 +54,11 @@ constexpr unsigned wait_vmcnt(int n) { return 0x0F70u | (n & 15) | ((n >> 4) << 
 // 64-key tile), ring of W < 64 slots.
 enum CacheMode { kContiguous = 0, kRing = 1, kSmallRing = 2 };
 
-template <int kMode>
+// kRotate: the cache holds K before RoPE (rotated here at renumbered positions); otherwise
+// it holds K already rotated at absolute positions and is used as stored.
+template <int kMode, bool kRotate>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a) {
+  constexpr int kLoads = kLoadsPerIssue<kRotate>;
   // three ring slots, separate LDS objects so that reads of one slot never wait for the
   // direct loads in flight into the others
   __shared__ __attribute__((aligned(16))) bf16_t vs0[kWaves][kVSlot];
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   const int key_in_tile = wave * kSub + m16;
   float2 fine[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) fine[e] = a.rope[key_in_tile * kHalf + g * 16 + e];
+  for (int e = 0; e < 16; ++e) fine[e] = kRotate ? a.rope[key_in_tile * kHalf + g * 16 + e] : float2{0.f, 0.f};
 
   // ---- per-lane pieces of the loads ---------------------------------------------------
   // V direct load i, lane l fills padded slot p = 64 i + l: row p / 17, chunk p % 17 (the
@@ -149,9 +154,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
       const bf16_t* src = vc + cache_row(wave * kSub + v_row[i]) * kHeadDim + v_col[i] * 8;
       __builtin_amdgcn_global_load_lds(src, vslot + i * 512, 16, 0, 0);
     }
-    // coarse row of the tile (64 pairs, 512 B), copied twice over the 64 lanes
-    const float2* crow = a.rope + (kRopeFine + (tb_issue >> 6)) * kHalf + (lane & 31) * 2;
-    __builtin_amdgcn_global_load_lds(crow, cslot, 16, 0, 0);
+    if (kRotate) {  // coarse row of the tile (64 pairs, 512 B), copied twice over the 64 lanes
+      const float2* crow = a.rope + (kRopeFine + (tb_issue >> 6)) * kHalf + (lane & 31) * 2;
+      __builtin_amdgcn_global_load_lds(crow, cslot, 16, 0, 0);
+    }
     if (t_issue + 1 < n_tiles) {
       ++t_issue;
       tb_issue += kTile;
@@ -174,10 +180,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
       __attribute__((always_inline)) {
     const long long key0 = s_begin + static_cast<long long>(t) * kTile + wave * kSub;
     if (key0 >= s_end) return;  // wave-uniform: no key of this wave in the tile
-    // K': rotate the lane's 16 pairs, pack to bf16 in the A-operand layout
+    // K': rotate the lane's 16 pairs, pack to bf16 in the A-operand layout (a post-RoPE
+    // cache row is already that operand)
     bf16x8 kf[4];
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs) {  // hs: slices (hs, hs+2) hold pairs 16g + 8hs + e
+    for (int hs = 0; hs < 2 && !kRotate; ++hs) {
+      kf[hs] = __builtin_bit_cast(bf16x8, kw[hs]);
+      kf[hs + 2] = __builtin_bit_cast(bf16x8, kw[hs + 2]);
+    }
+#pragma unroll
+    for (int hs = 0; hs < 2 && kRotate; ++hs) {  // hs: slices (hs, hs+2) hold pairs 16g + 8hs + e
       u32x4 lo_w, hi_w;
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
@@ -254,18 +266,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   // have landed; settle that here, once: a first use inside the loop would otherwise wait
   // for every load in flight.
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerIssue));
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoads));
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(qw[s]));
 #pragma unroll
-  for (int e = 0; e < 16; ++e) asm volatile("" : "+v"(fine[e].x), "+v"(fine[e].y));
+  for (int e = 0; e < 16 && kRotate; ++e) asm volatile("" : "+v"(fine[e].x), "+v"(fine[e].y));
 #pragma unroll
   for (int s = 0; s < 4; ++s) qf[s] = __builtin_bit_cast(bf16x8, q_ok ? qw[s] : u32x4{0, 0, 0, 0});
   // Before computing tile t, an explicit wait leaves the loads of the tiles issued after it
   // in flight (the compiler's own waits cannot follow the ring across loop iterations).
-  constexpr unsigned kTwoBehind = wait_vmcnt(2 * kLoadsPerIssue);
-  constexpr unsigned kOneBehind = wait_vmcnt(kLoadsPerIssue);
+  constexpr unsigned kTwoBehind = wait_vmcnt(2 * kLoads);
+  constexpr unsigned kOneBehind = wait_vmcnt(kLoads);
   int t = 0;
   for (; t + 3 <= n_tiles; t += 3) {
     issue(k2, v2, c2);  // tile t + 2
@@ -416,12 +428,21 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   // sequences have them) fill the slots as they free up, and the empty ranges of short
   // sequences come last.
   const dim3 grid = a.seq_pos ? dim3(a.Hkv, a.B, a.plan.n_split) : dim3(a.plan.n_split, a.Hkv, a.B);
-  if (a.window == 0)
-    hipLaunchKernelGGL(decode_split_kernel<kContiguous>, grid, dim3(kThreads), 0, stream, a);
-  else if (a.window >= kTile)
-    hipLaunchKernelGGL(decode_split_kernel<kRing>, grid, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_split_kernel<kSmallRing>, grid, dim3(kThreads), 0, stream, a);
+  if (!a.post_rope) {
+    if (a.window == 0)
+      hipLaunchKernelGGL((decode_split_kernel<kContiguous, true>), grid, dim3(kThreads), 0, stream, a);
+    else if (a.window >= kTile)
+      hipLaunchKernelGGL((decode_split_kernel<kRing, true>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<kSmallRing, true>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    if (a.window == 0)
+      hipLaunchKernelGGL((decode_split_kernel<kContiguous, false>), grid, dim3(kThreads), 0, stream, a);
+    else if (a.window >= kTile)
+      hipLaunchKernelGGL((decode_split_kernel<kRing, false>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<kSmallRing, false>), grid, dim3(kThreads), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.plan.n_split == 1) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.Hq), dim3(kHeadDim), 0, stream, a);

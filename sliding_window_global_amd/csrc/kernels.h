@@ -31,6 +31,7 @@ struct AppendArgs {
   const long long* seq_pos;  // ragged batch: per-sequence pos_offset (device), else NULL
   const int* seq_len;        // ragged batch: per-sequence new-token count (device), else NULL
   bool ops_kernel;           // the operand kernel writes every operand row outside the chunk
+  bool post_rope;            // the cache holds K rotated at absolute positions (else pre-RoPE)
   const float2* rope;
 };
 // Both launch, when prefill operands are requested after cached tokens or for a ragged
@@ -74,6 +75,7 @@ struct DecodeArgs {
   long long base;       // absolute position of renumbered key 0 (uniform batch)
   long long pos_offset; // position of the new token (ragged: the largest)
   const long long* seq_pos;  // ragged batch: per-sequence position (device), else NULL
+  bool post_rope;            // the cache holds K rotated at absolute positions: no rotation
   DecodePlan plan;
   const float2* rope;
   float scale;

@@ -31,7 +31,7 @@ class PrefillBuffers:
 
 def prefill(q, k, v, *, window, rope_table, q_norm_w=None, k_norm_w=None, norm_offset=1.0,
             norm_eps=1e-6, k_cache=None, v_cache=None, bufs: PrefillBuffers | None = None,
-            softmax_scale=None, stream=None, pos_offset=0) -> PrefillBuffers:
+            softmax_scale=None, stream=None, pos_offset=0, cache_post_rope=False) -> PrefillBuffers:
     """Prefill of a chunk q [B,T,Hq,d], k/v [B,T,Hkv,d] on the GPU whose first token sits at
     absolute position pos_offset. With pos_offset > 0 the caches must hold the earlier tokens
     (they are read for the chunk's attention, then updated with the chunk)."""
@@ -42,7 +42,7 @@ def prefill(q, k, v, *, window, rope_table, q_norm_w=None, k_norm_w=None, norm_o
     plamo_kv_append(q, k, v, bufs.q_rot, window=window, pos_offset=pos_offset, rope_table=rope_table,
                     q_norm_w=q_norm_w, k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps,
                     k_rot_out=bufs.k_rot, v_t_out=bufs.v_t, k_cache=k_cache, v_cache=v_cache,
-                    stream=stream)
+                    cache_post_rope=cache_post_rope, stream=stream)
     plamo_attn_prefill(bufs.q_rot, bufs.k_rot, bufs.v_t, bufs.out, window=window, pos_offset=pos_offset,
                        softmax_scale=softmax_scale, stream=stream)
     return bufs
@@ -62,7 +62,7 @@ class DecodeBuffers:
 
 def decode(q, k, v, k_cache, v_cache, *, window, pos_offset, rope_table, q_norm_w=None,
            k_norm_w=None, norm_offset=1.0, norm_eps=1e-6, bufs: DecodeBuffers | None = None,
-           softmax_scale=None, stream=None) -> DecodeBuffers:
+           softmax_scale=None, stream=None, cache_post_rope=False) -> DecodeBuffers:
     """One decode step at absolute position pos_offset: q [B,1,Hq,d], k/v [B,1,Hkv,d]."""
     B, _, Hq, d = q.shape
     Hkv = k.shape[2]
@@ -70,18 +70,18 @@ def decode(q, k, v, k_cache, v_cache, *, window, pos_offset, rope_table, q_norm_
         bufs = DecodeBuffers(B, Hq, Hkv, d, window, pos_offset, q.dtype, q.device)
     plamo_kv_append(q, k, v, bufs.q_rot, window=window, pos_offset=pos_offset, rope_table=rope_table,
                     q_norm_w=q_norm_w, k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps,
-                    k_cache=k_cache, v_cache=v_cache, stream=stream)
+                    k_cache=k_cache, v_cache=v_cache, cache_post_rope=cache_post_rope, stream=stream)
     plamo_attn_decode(bufs.q_rot, k_cache, v_cache, bufs.out, bufs.workspace, window=window,
                       pos_offset=pos_offset, rope_table=rope_table,
                       softmax_scale=1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale,
-                      stream=stream)
+                      cache_post_rope=cache_post_rope, stream=stream)
     return bufs
 
 
 def prefill_ragged(q, k, v, *, window, rope_table, seq_pos_offsets, max_pos_offset, seq_lens=None,
                    q_norm_w=None, k_norm_w=None, norm_offset=1.0, norm_eps=1e-6, k_cache=None,
                    v_cache=None, bufs: PrefillBuffers | None = None, softmax_scale=None,
-                   stream=None) -> PrefillBuffers:
+                   stream=None, cache_post_rope=False) -> PrefillBuffers:
     """Prefill of a ragged batch: sequence b's seq_lens[b] new tokens (rows of its [T] slab)
     start at absolute position seq_pos_offsets[b] <= max_pos_offset."""
     B, T, Hq, d = q.shape
@@ -92,7 +92,7 @@ def prefill_ragged(q, k, v, *, window, rope_table, seq_pos_offsets, max_pos_offs
                            max_pos_offset=max_pos_offset, seq_lens=seq_lens, rope_table=rope_table,
                            q_norm_w=q_norm_w, k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps,
                            k_rot_out=bufs.k_rot, v_t_out=bufs.v_t, k_cache=k_cache, v_cache=v_cache,
-                           stream=stream)
+                           cache_post_rope=cache_post_rope, stream=stream)
     plamo_attn_prefill_ragged(bufs.q_rot, bufs.k_rot, bufs.v_t, bufs.out, window=window,
                               seq_pos_offsets=seq_pos_offsets, max_pos_offset=max_pos_offset,
                               seq_lens=seq_lens, softmax_scale=softmax_scale, stream=stream)
@@ -101,7 +101,8 @@ def prefill_ragged(q, k, v, *, window, rope_table, seq_pos_offsets, max_pos_offs
 
 def decode_ragged(q, k, v, k_cache, v_cache, *, window, seq_pos_offsets, max_pos_offset, rope_table,
                   q_norm_w=None, k_norm_w=None, norm_offset=1.0, norm_eps=1e-6,
-                  bufs: DecodeBuffers | None = None, softmax_scale=None, stream=None) -> DecodeBuffers:
+                  bufs: DecodeBuffers | None = None, softmax_scale=None, stream=None,
+                  cache_post_rope=False) -> DecodeBuffers:
     """One decode step of a ragged batch: sequence b's new token sits at seq_pos_offsets[b]."""
     B, _, Hq, d = q.shape
     Hkv = k.shape[2]
@@ -110,8 +111,9 @@ def decode_ragged(q, k, v, k_cache, v_cache, *, window, seq_pos_offsets, max_pos
     plamo_kv_append_ragged(q, k, v, bufs.q_rot, window=window, seq_pos_offsets=seq_pos_offsets,
                            max_pos_offset=max_pos_offset, rope_table=rope_table, q_norm_w=q_norm_w,
                            k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps, k_cache=k_cache,
-                           v_cache=v_cache, stream=stream)
+                           v_cache=v_cache, cache_post_rope=cache_post_rope, stream=stream)
     plamo_attn_decode_ragged(bufs.q_rot, k_cache, v_cache, bufs.out, bufs.workspace, window=window,
                              seq_pos_offsets=seq_pos_offsets, max_pos_offset=max_pos_offset,
-                             rope_table=rope_table, softmax_scale=softmax_scale, stream=stream)
+                             rope_table=rope_table, softmax_scale=softmax_scale,
+                             cache_post_rope=cache_post_rope, stream=stream)
     return bufs

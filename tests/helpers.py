@@ -55,10 +55,10 @@ def oracle_prefill(q, k, v, *, window, rope, wq=None, wk=None, norm_offset=1.0, 
 
 
 def oracle_decode_one(q, k, v, prior_k, prior_v, pos_offset, *, window, rope, wq, wk,
-                      norm_offset=1.0, eps=1e-6, legacy_4k=False):
+                      norm_offset=1.0, eps=1e-6, legacy_4k=False, post_rope=False):
     """Oracle of one decode step of one sequence: q [1,Hq,d], k/v [1,Hkv,d]; prior_k/v are
     the kept tokens (normalised pre-RoPE K, raw V) in token order. Returns [1, Hq, d]."""
-    cache = LayerKVCache.with_prior(prior_k, prior_v, pos_offset, window, legacy_4k)
+    cache = LayerKVCache.with_prior(prior_k, prior_v, pos_offset, window, legacy_4k, post_rope)
     return attention_layer_step(
         q, k, v, cache, theta=rope.theta, yarn_factor=rope.yarn_factor, orig_ctx=rope.orig_ctx,
         beta_fast=rope.beta_fast, beta_slow=rope.beta_slow, q_norm_w=wq, k_norm_w=wk,
@@ -97,14 +97,16 @@ def untile_v_t(vt):
 
 
 def oracle_chunks(q, k, v, chunks, *, window, rope, wq=None, wk=None, norm_offset=1.0, eps=1e-6,
-                  rows_of=None, legacy_4k=False):
+                  rows_of=None, legacy_4k=False, post_rope=False, caches_out=None):
     """Oracle of a prefill in consecutive chunks (each chunk attends the cache the previous
     ones left, then updates it): q [B,n,Hq,d] etc., chunks = chunk lengths summing to n.
     rows_of(T) -> row indices kept per chunk (default all). Returns a list per chunk of
     [B, rows, Hq, d] float64."""
     B, n, Hq, d = q.shape
     Hkv = k.shape[2]
-    caches = [LayerKVCache(Hkv, d, window, legacy_4k) for _ in range(B)]
+    caches = [LayerKVCache(Hkv, d, window, legacy_4k, post_rope) for _ in range(B)]
+    if caches_out is not None:
+        caches_out.extend(caches)
     outs, p = [], 0
     for T in chunks:
         rows = None if rows_of is None else rows_of(T)

@@ -80,12 +80,12 @@ def test_decode_workspace_sizes(lib):
 def _append(lib, **over):
     a = dict(dtype=BF16, q=FAKE, k=FAKE, v=FAKE, wq=None, wk=None, c=1.0, eps=1e-6, q_out=FAKE,
              k_rot=None, v_t=None, kc=None, vc=None, cap=0, B=1, T=4, Hq=8, Hkv=2, d=128, window=16,
-             pos=0, table=FAKE, table_bytes=(64 + 1) * 512, stream=None)
+             pos=0, table=FAKE, table_bytes=(64 + 1) * 512, order=0, stream=None)
     a.update(over)
     return lib.plamo_kv_append(a["dtype"], a["q"], a["k"], a["v"], a["wq"], a["wk"], a["c"], a["eps"],
                                a["q_out"], a["k_rot"], a["v_t"], a["kc"], a["vc"], a["cap"], a["B"], a["T"],
                                a["Hq"], a["Hkv"], a["d"], a["window"], a["pos"], a["table"],
-                               a["table_bytes"], a["stream"])
+                               a["table_bytes"], a["order"], a["stream"])
 
 
 @pytest.mark.parametrize("over,status", [
@@ -109,6 +109,8 @@ def _append(lib, **over):
     (dict(pos=64, window=0, table_bytes=(64 + 1) * 512), WORKSPACE),  # table too short
     (dict(eps=-1.0), INVALID),
     (dict(pos=3, k_rot=FAKE), INVALID),             # operands after cached keys need the caches
+    (dict(order=2), INVALID),                        # unknown cache order
+    (dict(order=1, pos=62, window=16), WORKSPACE),   # post-RoPE: table covers absolute positions
 ])
 def test_kv_append_validation(lib, over, status):
     assert _append(lib, **over) == status
@@ -141,11 +143,11 @@ def test_prefill_validation(lib, over, status):
 def _decode(lib, **over):
     a = dict(dtype=BF16, q=FAKE, kc=FAKE, vc=FAKE, cap=2048, out=FAKE, ws=FAKE, ws_bytes=1 << 30, B=4, T=1,
              Hq=64, Hkv=8, d=128, window=2048, pos=5000, table=FAKE, table_bytes=(64 + 32) * 512,
-             scale=0.0884, stream=None)
+             scale=0.0884, order=0, stream=None)
     a.update(over)
     return lib.plamo_attn_decode(a["dtype"], a["q"], a["kc"], a["vc"], a["cap"], a["out"], a["ws"],
                                  a["ws_bytes"], a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], a["window"],
-                                 a["pos"], a["table"], a["table_bytes"], a["scale"], a["stream"])
+                                 a["pos"], a["table"], a["table_bytes"], a["scale"], a["order"], a["stream"])
 
 
 @pytest.mark.parametrize("over,status", [
@@ -153,7 +155,8 @@ def _decode(lib, **over):
     (dict(T=-1), INVALID), (dict(Hq=64, Hkv=2), UNSUPPORTED), (dict(cap=100), INVALID),
     (dict(window=0, cap=4000), INVALID), (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
     (dict(table_bytes=(64 + 31) * 512), WORKSPACE), (dict(kc=None), INVALID),
-    (dict(out=MISALIGNED), INVALID), (dict(scale=-1.0), INVALID),
+    (dict(out=MISALIGNED), INVALID), (dict(scale=-1.0), INVALID), (dict(order=-1), INVALID),
+    (dict(order=1, table=None, ws=None), WORKSPACE),  # post-RoPE needs no table; still a workspace
 ])
 def test_decode_validation(lib, over, status):
     assert _decode(lib, **over) == status
@@ -202,7 +205,7 @@ def test_ragged_entry_points_validate_their_arrays(lib):
         return lib.plamo_kv_append_ragged(a["dtype"], a["q"], a["k"], a["v"], a["wq"], a["wk"], a["c"], a["eps"],
                                           a["q_out"], a["k_rot"], a["v_t"], a["kc"], a["vc"], a["cap"], a["B"],
                                           a["T"], a["Hq"], a["Hkv"], a["d"], a["window"], seq_pos, seq_len,
-                                          max_pos, a["table"], a["table_bytes"], None)
+                                          max_pos, a["table"], a["table_bytes"], 0, None)
     assert append(None, None) == INVALID                  # positions are required
     assert append(ALIGNED4, None) == INVALID              # int64 array not 8-byte aligned
     assert append(FAKE, ctypes.c_void_p(0x7F0000000002)) == INVALID  # int32 array not 4-byte aligned
@@ -225,7 +228,7 @@ def test_ragged_entry_points_validate_their_arrays(lib):
         a.update(over)
         return lib.plamo_attn_decode_ragged(BF16, FAKE, FAKE, FAKE, a["cap"], FAKE, a["ws"], a["ws_bytes"], a["B"],
                                             64, 8, 128, a["window"], seq_pos, max_pos, FAKE, a["table_bytes"],
-                                            0.0884, None)
+                                            0.0884, 0, None)
     assert decode(None) == INVALID
     assert decode(ALIGNED4) == INVALID
     assert decode(FAKE, window=0, cap=4000) == INVALID     # global cap must exceed max_pos_offset

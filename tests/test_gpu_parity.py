@@ -254,7 +254,7 @@ def test_prefill_empty_is_noop():
 # decode
 # ----------------------------------------------------------------------------
 
-def _decode_case(B, Hq, Hkv, window, pos_offset, rope, seed, check_b, poison_future=True):
+def _decode_case(B, Hq, Hkv, window, pos_offset, rope, seed, check_b, poison_future=True, post_rope=False):
     d = 128
     cap = window if window else pos_offset + 1
     kc = device_normal_bf16((B, Hkv, cap, d), seed, "cuda")
@@ -273,12 +273,13 @@ def _decode_case(B, Hq, Hkv, window, pos_offset, rope, seed, check_b, poison_fut
     wq, wk = dr.normal((d,), 0.02), dr.normal((d,), 0.02)
     tab = rope_table(rope, max(pos_offset + 2, 64))
     bufs = layer.decode(dev(q), dev(k), dev(v), kc, vc, window=window, pos_offset=pos_offset,
-                        rope_table=tab, q_norm_w=dev(wq), k_norm_w=dev(wk), norm_offset=1.0)
+                        rope_table=tab, q_norm_w=dev(wq), k_norm_w=dev(wk), norm_offset=1.0,
+                        cache_post_rope=post_rope)
     torch.cuda.synchronize()
     out = host(bufs.out)
     for b in check_b:
         ref = oracle_decode_one(q[b], k[b], v[b], prior_k[b], prior_v[b], pos_offset, window=window,
-                                rope=rope, wq=wq, wk=wk)
+                                rope=rope, wq=wq, wk=wk, post_rope=post_rope)
         assert_parity(out[b], ref, TOL_BF16, f"decode b={b} W={window} p={pos_offset}")
     return bufs
 
@@ -306,6 +307,22 @@ def test_decode_batched_full_size(layer_idx):
     ly = wl.layers[layer_idx]
     _decode_case(wl.B, wl.Hq, wl.Hkv, ly.window, wl.pos_offset, ly.rope, wl.cache_seed(layer_idx),
                  check_b=[0, 31, 63], poison_future=False)
+
+
+def test_decode_batched_full_size_post_rope():
+    """The global batched-decode shape with a post-RoPE cache (the prior cache read as already
+    rotated K, the new token rotated at its absolute position): sampled sequences."""
+    wl = BATCHED_DECODE
+    ly = wl.layers[1]
+    _decode_case(wl.B, wl.Hq, wl.Hkv, ly.window, wl.pos_offset, ly.rope, wl.cache_seed(1),
+                 check_b=[0, 63], poison_future=False, post_rope=True)
+
+
+@pytest.mark.parametrize("window,pos_offset", [(2048, 100), (2048, 5000), (0, 5000), (16, 40)])
+def test_decode_small_batch_post_rope(window, pos_offset):
+    """Post-RoPE cache decode on ring fill-up, wrap and contiguous caches; dead slots NaN."""
+    rope = Rope(1e4) if window else Rope(1e6, 64.0)
+    _decode_case(3, 16, 2, window, pos_offset, rope, 300 + pos_offset + window, check_b=[0, 1, 2], post_rope=True)
 
 
 def test_decode_period_long_context_step():
@@ -484,9 +501,10 @@ def test_decode_ragged_full_size():
         assert_parity(out[b], ref, TOL_BF16, f"ragged decode b={b} p={pos[b]}")
 
 
-def _stream_case(window_arg, oracle_window, legacy_4k, rope, chunks, steps, seed):
+def _stream_case(window_arg, oracle_window, legacy_4k, rope, chunks, steps, seed, post_rope=False):
     """Prefill in chunks, then `steps` decode steps, on one token stream of B=2 sequences;
-    each call's output rows (sampled) against the oracle run on the same stream."""
+    each call's output rows (sampled) against the oracle run on the same stream. With a
+    post-RoPE cache, also the cache contents against the oracle's."""
     B, Hq, Hkv, d = 2, 8, 2, 128
     n = sum(chunks) + steps
     dr = Draw(seed, True)
@@ -500,23 +518,31 @@ def _stream_case(window_arg, oracle_window, legacy_4k, rope, chunks, steps, seed
     got, p = [], 0
     for T in chunks:
         bufs = layer.prefill(dev(q[:, p:p + T]), dev(k[:, p:p + T]), dev(v[:, p:p + T]), window=window_arg,
-                             rope_table=tab, k_cache=kc, v_cache=vc, pos_offset=p, **norm)
+                             rope_table=tab, k_cache=kc, v_cache=vc, pos_offset=p, cache_post_rope=post_rope,
+                             **norm)
         torch.cuda.synchronize()
         got.append(host(bufs.out))
         p += T
     for _ in range(steps):
         db = layer.decode(dev(q[:, p:p + 1]), dev(k[:, p:p + 1]), dev(v[:, p:p + 1]), kc, vc, window=window_arg,
-                          pos_offset=p, rope_table=tab, **norm)
+                          pos_offset=p, rope_table=tab, cache_post_rope=post_rope, **norm)
         torch.cuda.synchronize()
         got.append(host(db.out))
         p += 1
     all_chunks = list(chunks) + [1] * steps
     edges = [0, 1, 15, 16, 17, 2046, 2047, 2048, 2049, 2050]
     rows_of = lambda T: np.unique(np.array(edges + [T // 3, T // 2, T - 2, T - 1]).clip(0, T - 1))
+    caches = []
     ref = oracle_chunks(q, k, v, all_chunks, window=oracle_window, rope=rope, wq=wq, wk=wk, rows_of=rows_of,
-                        legacy_4k=legacy_4k)
+                        legacy_4k=legacy_4k, post_rope=post_rope, caches_out=caches)
     for i, (g, r) in enumerate(zip(got, ref)):
         assert_parity(g[:, rows_of(all_chunks[i])], r, TOL_BF16, f"call {i} (T={all_chunks[i]})")
+    if post_rope:  # the kept tokens, as stored: K rotated at absolute positions, in their slots
+        for b in range(B):
+            keep = caches[b].k.shape[0]
+            slots = np.arange(n - keep, n) if not window_arg else np.arange(n - keep, n) % window_arg
+            assert_parity(host(kc[b][:, torch.from_numpy(slots).cuda()]).transpose(1, 0, 2), caches[b].k, TOL_BF16,
+                          f"post-RoPE cache K, sequence {b}")
 
 
 @pytest.mark.parametrize("W,chunks", [(2048, [2500, 300]), (16, [40, 5])], ids=["W2048", "W16"])
@@ -531,3 +557,13 @@ def test_global_without_yarn():
     """A global layer without YaRN (the 4K release, 「PLaMo 3アーキテクチャ徹底解析」 §6.3): table
     built with yarn_factor 0; chunked prefill then decode against the oracle."""
     _stream_case(0, 0, False, Rope(1e6), [300, 200], 3, 5199)
+
+
+@pytest.mark.parametrize("window,chunks,rope", [(2048, [2500, 300], Rope(1e4)), (16, [40, 5], Rope(1e4)),
+                                                (0, [300, 200], Rope(1e6, 64.0))],
+                         ids=["W2048", "W16", "global_yarn64"])
+def test_post_rope_cache(window, chunks, rope):
+    """The post-RoPE cache order (「PLaMo 3アーキテクチャ徹底解析」 §4.4's other order: K rotated
+    at its absolute position before the store): chunked prefill then decode against the
+    oracle's post-RoPE layer, and the cache contents against the oracle's cache."""
+    _stream_case(window, window, False, rope, chunks, 3, 6100 + window, post_rope=True)
