@@ -10,6 +10,7 @@ from .oracle import (  # noqa: F401
     gqa_attention,
     kv_bytes,
     kv_head_of,
+    mixer_layer_step,
     offset_rms_norm,
     rope_frequencies,
     yarn_ramp_bounds,

@@ -277,6 +277,41 @@ def attention_layer_step(q, k, v, cache: LayerKVCache, *, theta: float,
 
 
 # ----------------------------------------------------------------------------
+# The attention sublayer around the hot path  [P3 §3.2, §4.1, §4.5]
+# ----------------------------------------------------------------------------
+
+def mixer_layer_step(x, cache: LayerKVCache, *, w_pre, w_qkv, w_o, w_post, Hq: int, Hkv: int,
+                     theta: float, yarn_factor: float = 0.0, q_norm_w=None, k_norm_w=None,
+                     pre_offset: float = 1.0, post_offset: float = 0.2, qk_offset: float = 1.0,
+                     eps: float = 1e-6, rows=None):
+    """One attention sublayer for one sequence: x [T, D] -> x + post(o_proj(attn(pre(x)))).
+
+    [P3 §3.2] pre_mixer_norm (offset 1) and post_mixer_norm (offset 0.2) over the D hidden
+    components; [P3 §4.1] one fused projection U W_qkv^T, W_qkv [(Hq + 2 Hkv) d, D], whose
+    output is split along its last axis into Q [0, Hq d), K [Hq d, (Hq + Hkv) d) and
+    V [(Hq + Hkv) d, (Hq + 2 Hkv) d), each reshaped to [T, H, d]; the attention layer step
+    of [P3 §4.4]; [P3 §4.5] the heads concatenated to [T, Hq d] and projected by
+    W_o [D, Hq d]. The normalised output is added to the residual stream x (reading: the
+    post norm acts on the sublayer output before the residual add). ``rows`` restricts
+    the returned rows (every token still enters the cache)."""
+    x = np.asarray(x, dtype=F64)
+    T, D = x.shape
+    w_qkv = np.asarray(w_qkv, dtype=F64)
+    d = w_qkv.shape[0] // (Hq + 2 * Hkv)
+    u = offset_rms_norm(x, w_pre, pre_offset, eps)
+    qkv = u @ w_qkv.T
+    q = qkv[:, :Hq * d].reshape(T, Hq, d)
+    k = qkv[:, Hq * d:(Hq + Hkv) * d].reshape(T, Hkv, d)
+    v = qkv[:, (Hq + Hkv) * d:].reshape(T, Hkv, d)
+    attn = attention_layer_step(q, k, v, cache, theta=theta, yarn_factor=yarn_factor,
+                                q_norm_w=q_norm_w, k_norm_w=k_norm_w, norm_offset=qk_offset,
+                                eps=eps, rows=rows)
+    o = attn.reshape(attn.shape[0], Hq * d) @ np.asarray(w_o, dtype=F64).T
+    xr = x if rows is None else x[np.asarray(rows)]
+    return xr + offset_rms_norm(o, w_post, post_offset, eps)
+
+
+# ----------------------------------------------------------------------------
 # Read volume and capacity accounting  [P3 §2.3, §5.2]
 # ----------------------------------------------------------------------------
 

@@ -496,11 +496,69 @@ def pin_post_rope_cache(o):
             assert np.max(np.abs(post.k - want)) < 1e-12
 
 
+def pin_mixer_bruteforce(o):
+    """「PLaMo 3アーキテクチャ徹底解析」 §3.2, §4.1, §4.5: the attention sublayer against scalar
+    loops (pre norm with offset 1, the fused projection split into Q | K | V along its output
+    axis, the attention step, heads concatenated, the output projection, post norm with
+    offset 0.2, residual add), with an empty and a populated cache."""
+    for (T, D, Hq, Hkv, d, W, prior, seed) in ((4, 6, 2, 1, 4, 3, 0, 31), (3, 5, 4, 2, 4, 0, 2, 32)):
+        x = _rand((T, D), seed)
+        w_pre, w_post = _rand((D,), seed + 1) * 0.2, _rand((D,), seed + 2) * 0.2
+        w_qkv = _rand(((Hq + 2 * Hkv) * d, D), seed + 3) * 0.5
+        w_o = _rand((D, Hq * d), seed + 4) * 0.5
+        wq, wk = _rand((d,), seed + 5) * 0.3, _rand((d,), seed + 6) * 0.3
+        pk, pv = _rand((prior, Hkv, d), seed + 7), _rand((prior, Hkv, d), seed + 8)
+        cache = o.LayerKVCache.with_prior(pk, pv, prior, W)
+        got = o.mixer_layer_step(x, cache, w_pre=w_pre, w_qkv=w_qkv, w_o=w_o, w_post=w_post, Hq=Hq, Hkv=Hkv,
+                                 theta=1e4, q_norm_w=wq, k_norm_w=wk)
+
+        def norm(vec, w, c):
+            r = 1.0 / math.sqrt(sum(e * e for e in vec) / len(vec) + 1e-6)
+            return [(c + w[i]) * vec[i] * r for i in range(len(vec))]
+
+        xs = x.tolist()
+        us = [norm(xs[t], w_pre.tolist(), 1.0) for t in range(T)]
+
+        def proj(row, first):  # output feature first + i of the fused projection
+            return [sum(w_qkv[first + i][j] * us[row][j] for j in range(D)) for i in range(d)]
+
+        q = [[proj(t, h * d) for h in range(Hq)] for t in range(T)]
+        k = [[proj(t, (Hq + g) * d) for g in range(Hkv)] for t in range(T)]
+        v = [[proj(t, (Hq + Hkv + g) * d) for g in range(Hkv)] for t in range(T)]
+        att = _brute_layer(q, k, v, pk.tolist(), pv.tolist(), W, 1e4, 0, wq.tolist(), wk.tolist(), 1.0, 1e-6)
+        for t in range(T):
+            flat = [att[t][h][r] for h in range(Hq) for r in range(d)]
+            ov = [sum(w_o[i][j] * flat[j] for j in range(Hq * d)) for i in range(D)]
+            want = [xs[t][i] + e for i, e in enumerate(norm(ov, w_post.tolist(), 0.2))]
+            assert np.max(np.abs(got[t] - np.array(want))) < 1e-11, (T, D, t)
+
+
+def pin_mixer_torch(o):
+    """Library cross-check of the projections and norms: torch float64 rms_norm (gain c + w)
+    and linear, the fused weight cut with torch.split at Hq d and Hkv d."""
+    T, D, Hq, Hkv, d = 7, 24, 4, 2, 8
+    x = _rand((T, D), 41)
+    w_pre, w_post = _rand((D,), 42) * 0.1, _rand((D,), 43) * 0.1
+    w_qkv, w_o = _rand(((Hq + 2 * Hkv) * d, D), 44) * 0.3, _rand((D, Hq * d), 45) * 0.3
+    got = o.mixer_layer_step(x, o.LayerKVCache(Hkv, d, 4), w_pre=w_pre, w_qkv=w_qkv, w_o=w_o, w_post=w_post,
+                             Hq=Hq, Hkv=Hkv, theta=1e4)
+    F = torch.nn.functional
+    xt = torch.from_numpy(x)
+    u = F.rms_norm(xt, (D,), torch.from_numpy(1.0 + w_pre), eps=1e-6)
+    qf, kf, vf = torch.split(F.linear(u, torch.from_numpy(w_qkv)), [Hq * d, Hkv * d, Hkv * d], dim=-1)
+    att = o.attention_layer_step(qf.reshape(T, Hq, d).numpy(), kf.reshape(T, Hkv, d).numpy(),
+                                 vf.reshape(T, Hkv, d).numpy(), o.LayerKVCache(Hkv, d, 4), theta=1e4)
+    oo = F.linear(torch.from_numpy(att.reshape(T, Hq * d)), torch.from_numpy(w_o))
+    want = xt + F.rms_norm(oo, (D,), torch.from_numpy(0.2 + w_post), eps=1e-6)
+    assert np.max(np.abs(got - want.numpy())) < 1e-12
+
+
 PINS = [pin_worked_example, pin_fig4_masks, pin_sdpa_float64, pin_bruteforce_layer,
         pin_rows_sum_to_one, pin_swa_equals_global_short, pin_uniform_closed_form,
         pin_gqa_grouping, pin_rope_library, pin_rope_complex, pin_rope_shift_invariance,
         pin_yarn_printed, pin_yarn_figure7, pin_rmsnorm, pin_cache_trim,
-        pin_decode_equivalence, pin_kv_accounting, pin_legacy_4k_band, pin_post_rope_cache]
+        pin_decode_equivalence, pin_kv_accounting, pin_legacy_4k_band, pin_post_rope_cache,
+        pin_mixer_bruteforce, pin_mixer_torch]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -546,6 +604,13 @@ MISTAKES = {
                                   "k_all, v_all = cache.update(apply_rope(k, np.arange(T), omega, amp), v)"),
     "post_rope_rotates_twice": ("k_rot = k_all if cache.post_rope else apply_rope(k_all, k_pos, omega, amp)",
                                 "k_rot = apply_rope(k_all, k_pos, omega, amp)"),
+    "mixer_k_v_swapped": ("k = qkv[:, Hq * d:(Hq + Hkv) * d].reshape(T, Hkv, d)",
+                          "k = qkv[:, (Hq + Hkv) * d:].reshape(T, Hkv, d)"),
+    "mixer_post_offset_one": ("return xr + offset_rms_norm(o, w_post, post_offset, eps)",
+                              "return xr + offset_rms_norm(o, w_post, pre_offset, eps)"),
+    "mixer_no_residual": ("return xr + offset_rms_norm(o, w_post, post_offset, eps)",
+                          "return offset_rms_norm(o, w_post, post_offset, eps)"),
+    "mixer_projection_untransposed": ("qkv = u @ w_qkv.T", "qkv = u @ w_qkv.reshape(w_qkv.shape[1], -1)"),
     "query_positions_from_zero": ("q_pos = np.arange(S - T, S)", "q_pos = np.arange(T)"),
     "default_scale_inverse_d": ("scale = 1.0 / math.sqrt(d)", "scale = 1.0 / d"),
     "weighted_sum_uses_keys": ("out[r0:r1, h, :] = a @ v[:, g, :]", "out[r0:r1, h, :] = a @ k_rot[:, g, :]"),
