@@ -7,7 +7,8 @@ is algorithmic prefill FLOP (4*d per attended (query, key) pair and query head) 
 second of that step. Also reported: the global-layer prefill (T=32768, YaRN), batched
 decode (B=64; ring W=2048 and global 32768) as KV-read GB/s, the same global decode with
 each sequence at its own position (ragged), both prefills fed in chunks (2048 local, 8192
-global) after cached tokens, the 8-layer period decode
+global) after cached tokens, the whole attention sublayer (projections and norms around the
+path, D = 5120), the 8-layer period decode
 at 131072 context, the roofline object of the prefill kernel, and the CPU oracle timed
 on a bounded sample of the headline workload.
 
@@ -240,6 +241,52 @@ def bench_decode_ragged(torch, swg, wl, layer_idx, steps, warmup):
                 frac_hbm=nbytes / ms / 1e6 / PEAK_HBM_GBS)
 
 
+def bench_mixer(torch, swg, wl, steps, warmup):
+    """The attention sublayer around the hot path (pre norm, QKV projection, append +
+    attention, output projection, post norm + residual) on a local-layer prefill at
+    D = 5120, random weights; times the whole sublayer and its three stages."""
+    from sliding_window_global_amd import layer
+    x, wdev = wl.draw_device("cuda")
+    wts = layer.MixerWeights(Hq=wl.Hq, Hkv=wl.Hkv, d=wl.d, **wdev)
+    kc = torch.empty((wl.B, wl.Hkv, wl.window, wl.d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    tab = swg.make_rope_table(wl.T + 64, rope_params(swg, wl.rope))
+    mb = layer.MixerBuffers(wl.B, wl.T, wl.D, wts)
+    ab = layer.PrefillBuffers(wl.B, wl.T, wl.Hq, wl.Hkv, wl.d, torch.bfloat16, window=wl.window)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        layer._mixer_in(x, wts, mb, None)
+        if ev:
+            ev[1].record()
+        layer.prefill(mb.q, mb.k, mb.v, window=wl.window, rope_table=tab, q_norm_w=wts.wq, k_norm_w=wts.wk,
+                      norm_offset=wts.qk_offset, k_cache=kc, v_cache=vc, bufs=ab)
+        if ev:
+            ev[2].record()
+        layer._mixer_out(x, ab.out, wts, mb, None)
+        if ev:
+            ev[3].record()
+
+    for _ in range(warmup):
+        step()
+    evs = []
+    for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        step(ev)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    part = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i in range(3)]
+    total = sum(part)
+    M = wl.B * wl.T
+    qkv_flops = 2.0 * M * wl.D * (wl.Hq + 2 * wl.Hkv) * wl.d
+    o_flops = 2.0 * M * wl.Hq * wl.d * wl.D
+    flops = wl.gemm_flops() + wl.attention_flops()
+    return dict(workload=wl.name, ms_per_step=total, ms_norm_qkv=part[0], ms_attention=part[1],
+                ms_oproj_norm=part[2], step_tflops=flops / total / 1e9,
+                qkv_proj_tflops=qkv_flops / part[0] / 1e9, o_proj_tflops=o_flops / part[2] / 1e9)
+
+
 def bench_period(torch, swg, wl, n_steps):
     """The 8-layer period (7 local W=2048 + 1 global), append + decode per layer per step,
     at 131072+k global context, batch 8."""
@@ -314,7 +361,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="", help="prefill_local|prefill_global|prefill_chunked|decode|period|copy_calibration")
+    ap.add_argument("--only", default="", help="prefill_local|prefill_global|prefill_chunked|mixer|decode|period|copy_calibration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--period-steps", type=int, default=128)
@@ -327,7 +374,8 @@ def main():
 
     import sliding_window_global_amd as swg
     from sliding_window_global_amd.profiling import read_traffic
-    from synthetic.workloads import BATCHED_DECODE, GLOBAL_PREFILL, LOCAL_PREFILL, PERIOD_DECODE
+    from synthetic.workloads import (BATCHED_DECODE, GLOBAL_PREFILL, LOCAL_PREFILL, MIXER_LOCAL_PREFILL,
+                                     PERIOD_DECODE)
 
     torch.cuda.set_device(0)
     swg._lib.load()
@@ -351,6 +399,11 @@ def main():
             r = bench_chunked_prefill(torch, swg, wl, chunk, n, max(1, args.warmup // 2))
             log(f"[bench]   {r}")
             extra[r["workload"]] = r
+    if only in ("", "mixer"):
+        log("[bench] attention sublayer, local prefill T=8192 D=5120")
+        r = bench_mixer(torch, swg, MIXER_LOCAL_PREFILL, args.steps, args.warmup)
+        log(f"[bench]   {r}")
+        extra[r["workload"]] = r
     if only in ("", "decode"):
         for li in (0, 1):
             log(f"[bench] batched decode layer {li}")

@@ -248,6 +248,31 @@ PLAMO_API int plamo_attn_decode_ragged(int dtype, const void* q_rot, const void*
                     const void* rope_table, size_t rope_table_bytes, float softmax_scale,
                     int cache_order, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * The attention sublayer around the hot path [P3 §3.2, §4.1, §4.5]
+ *
+ * x_out = x + N^(0.2)_{w_post}( O W_o^T ),  O = attention(split(N^(1)_{w_pre}(x) W_qkv^T))
+ * composed from plamo_rms_norm, plamo_linear and the attention calls above:
+ *   U = plamo_rms_norm(x, w_pre, offset 1)                 [B*T, D]
+ *   Q | K | V = plamo_linear(U, W_qkv rows [0, Hq d) | [Hq d, (Hq+Hkv) d) | the rest)
+ *   (the fused weight [(Hq + 2 Hkv) d, D] cut along its rows, [P3 §4.1])
+ *   O = plamo_kv_append + plamo_attn_prefill / plamo_attn_decode    [B*T, Hq d]
+ *   P = plamo_linear(O, W_o [D, Hq d])                     [B*T, D]
+ *   x_out = plamo_rms_norm(P, w_post, offset 0.2, residual x)
+ * ------------------------------------------------------------------------- */
+
+/* y[M, N] = x[M, K] W[N, K]^T, bf16 row-major, fp32 accumulation (the sublayer's
+ * projections [P3 §4.1, §4.5]). N % 8 == 0, K % 64 == 0 (PLAMO_ERR_UNSUPPORTED
+ * otherwise); y must not overlap x or W. */
+PLAMO_API int plamo_linear(const void* x, const void* w, void* y, long long M, int N, int K,
+                    void* stream);
+
+/* y = residual + (offset + w) * x / sqrt(mean(x^2) + eps) per row of n [P3 §3.2];
+ * residual NULL = no add. x, residual, y [rows, n], w [n], all of `dtype`, fp32 math;
+ * y may alias x or residual. n a multiple of 8 (bf16) or 4 (fp32). */
+PLAMO_API int plamo_rms_norm(int dtype, const void* x, const void* w, float offset, float eps,
+                    const void* residual, void* y, long long rows, int n, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 PLAMO_API const char* plamo_status_str(int status);
 

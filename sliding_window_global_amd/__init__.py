@@ -29,7 +29,7 @@ __all__ = [
     "plamo_prefill_padded_len", "legacy_4k_window", "plamo_kv_append", "plamo_attn_prefill",
     "plamo_attn_decode_workspace_bytes", "plamo_attn_decode", "plamo_kv_append_ragged",
     "plamo_attn_prefill_ragged", "plamo_attn_decode_ragged_workspace_bytes", "plamo_attn_decode_ragged",
-    "library_path",
+    "plamo_linear", "plamo_rms_norm", "library_path",
 ]
 
 
@@ -331,3 +331,31 @@ def plamo_attn_decode_ragged(q_rot, k_cache, v_cache, out, workspace, *, window:
         pos_p, int(max_pos_offset), _dev(rope_table, "rope_table", torch.float32), _nbytes(rope_table),
         scale, _order(cache_post_rope), _stream(stream))
     _check(st, "plamo_attn_decode_ragged")
+
+
+# ----------------------------------------------------------------------------
+# the attention sublayer around the hot path: projections and norms
+# ----------------------------------------------------------------------------
+
+def plamo_linear(x, w, y, *, stream=None) -> None:
+    """y[M, N] = x[M, K] w[N, K]^T (bf16); x may have leading batch axes."""
+    K = x.shape[-1]
+    M = x.numel() // K
+    N = w.shape[0]
+    if tuple(w.shape) != (N, K) or y.numel() != M * N or y.shape[-1] != N:
+        raise ValueError("need x [..., K], w [N, K], y [..., N]")
+    bf = torch.bfloat16
+    st = _lib.load().plamo_linear(_dev(x, "x", bf), _dev(w, "w", bf), _dev(y, "y", bf), M, N, K, _stream(stream))
+    _check(st, "plamo_linear")
+
+
+def plamo_rms_norm(x, w, y, *, offset: float, eps: float = 1e-6, residual=None, stream=None) -> None:
+    """y = residual + (offset + w) * x / rms(x) over the last axis."""
+    n = x.shape[-1]
+    rows = x.numel() // n
+    if tuple(w.shape) != (n,) or y.shape != x.shape or (residual is not None and residual.shape != x.shape):
+        raise ValueError("need x, y (and residual) of one shape and w [n]")
+    dt = x.dtype
+    st = _lib.load().plamo_rms_norm(_dtype_code(dt), _dev(x, "x", dt), _dev(w, "w", dt), float(offset), float(eps),
+                                    _dev(residual, "residual", dt), _dev(y, "y", dt), rows, n, _stream(stream))
+    _check(st, "plamo_rms_norm")

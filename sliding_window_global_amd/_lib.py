@@ -41,6 +41,9 @@ SIGNATURES = {
     "plamo_attn_decode_ragged": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_ll, c_void_p, c_void_p, c_size,
                                          c_int, c_int, c_int, c_int, c_int, c_void_p, c_ll, c_void_p, c_size,
                                          c_float, c_int, c_void_p]),
+    "plamo_linear": (c_int, [c_void_p, c_void_p, c_void_p, c_ll, c_int, c_int, c_void_p]),
+    "plamo_rms_norm": (c_int, [c_int, c_void_p, c_void_p, c_float, c_float, c_void_p, c_void_p, c_ll, c_int,
+                               c_void_p]),
     "plamo_status_str": (ctypes.c_char_p, [c_int]),
     "plamo_last_error": (ctypes.c_char_p, []),
 }

@@ -20,7 +20,9 @@ LIB_NAME = "libplamo_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["rope_table.hip", "append.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "abi.cpp"]
+SOURCES = ["rope_table.hip", "append.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "norm.hip",
+           "gemm.hip", "abi.cpp"]
+LINK_LIBS: list[str] = []
 # The bf16 prefill's softmax only ever sees finite or -inf scores: without NaN semantics
 # its running-max chain compiles to bare v_max3 (no input canonicalisation).
 EXTRA_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"]}
@@ -67,7 +69,7 @@ def build_library(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *LINK_LIBS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")

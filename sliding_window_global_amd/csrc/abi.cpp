@@ -341,4 +341,39 @@ int plamo_attn_decode_ragged(int dtype, const void* q_rot, const void* k_cache, 
                           softmax_scale, cache_order, stream);
 }
 
+/* ---- the sublayer around attention: projections and norms ---------------------- */
+
+int plamo_linear(const void* x, const void* w, void* y, long long M, int N, int K, void* stream) {
+  if (M < 0 || N < 1 || K < 1) return fail(PLAMO_ERR_INVALID_ARG, "need M >= 0, N >= 1, K >= 1");
+  if (N % 8 || K % 64) return fail(PLAMO_ERR_UNSUPPORTED, "need N % 8 == 0 and K % 64 == 0");
+  if (M > 65535LL * 128 || static_cast<long long>(K) * 256 * 2 > 0x7fffffffLL)
+    return fail(PLAMO_ERR_UNSUPPORTED, "M or K too large");
+  if (M == 0) return ok();
+  if (!x || !w || !y) return fail(PLAMO_ERR_INVALID_ARG, "x, w and y must be non-NULL");
+  const void* ptrs[] = {x, w, y};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  plamo::GemmArgs a;
+  a.x = x; a.w = w; a.y = y; a.M = M; a.N = N; a.K = K;
+  return launched(plamo::launch_gemm_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+int plamo_rms_norm(int dtype, const void* x, const void* w, float offset, float eps, const void* residual,
+                   void* y, long long rows, int n, void* stream) {
+  if (dtype != PLAMO_F32 && dtype != PLAMO_BF16) return fail(PLAMO_ERR_INVALID_ARG, "unknown dtype");
+  if (rows < 0 || n < 1) return fail(PLAMO_ERR_INVALID_ARG, "need rows >= 0 and n >= 1");
+  if (n % (dtype == PLAMO_BF16 ? 8 : 4)) return fail(PLAMO_ERR_UNSUPPORTED, "n must fill 16-byte chunks");
+  if (rows > (1LL << 33)) return fail(PLAMO_ERR_UNSUPPORTED, "too many rows");
+  if (!(eps >= 0.f) || !std::isfinite(offset)) return fail(PLAMO_ERR_INVALID_ARG, "bad offset/eps");
+  if (rows == 0) return ok();
+  if (!x || !w || !y) return fail(PLAMO_ERR_INVALID_ARG, "x, w and y must be non-NULL");
+  const void* ptrs[] = {x, w, y, residual};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  plamo::NormArgs a;
+  a.x = x; a.w = w; a.residual = residual; a.y = y; a.rows = rows; a.n = n; a.offset = offset; a.eps = eps;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launched(dtype == PLAMO_BF16 ? plamo::launch_rms_norm_bf16(a, s) : plamo::launch_rms_norm_f32(a, s));
+}
+
 }  // extern "C"

@@ -82,4 +82,25 @@ struct DecodeArgs {
 };
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
+struct GemmArgs {
+  const void* x;  // [M, K] bf16
+  const void* w;  // [N, K] bf16
+  void* y;        // [M, N] bf16
+  long long M, N;
+  int K;          // a multiple of 64
+};
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t stream);
+
+struct NormArgs {
+  const void* x;         // [rows, n]
+  const void* w;         // [n] stored gain weights (gain = offset + w)
+  const void* residual;  // [rows, n] or NULL
+  void* y;               // [rows, n]; may alias residual
+  long long rows;
+  int n;                 // a multiple of 8 (bf16) or 4 (fp32)
+  float offset, eps;
+};
+hipError_t launch_rms_norm_bf16(const NormArgs& a, hipStream_t stream);
+hipError_t launch_rms_norm_f32(const NormArgs& a, hipStream_t stream);
+
 }  // namespace plamo

@@ -11,7 +11,9 @@ import math
 
 import torch
 
-from . import (plamo_attn_decode, plamo_attn_decode_ragged, plamo_attn_decode_ragged_workspace_bytes,
+from dataclasses import dataclass
+
+from . import (plamo_linear, plamo_rms_norm, plamo_attn_decode, plamo_attn_decode_ragged, plamo_attn_decode_ragged_workspace_bytes,
                plamo_attn_decode_workspace_bytes,
                plamo_attn_prefill, plamo_attn_prefill_ragged, plamo_kv_append, plamo_kv_append_ragged,
                prefill_operand_shapes)
@@ -117,3 +119,81 @@ def decode_ragged(q, k, v, k_cache, v_cache, *, window, seq_pos_offsets, max_pos
                              rope_table=rope_table, softmax_scale=softmax_scale,
                              cache_post_rope=cache_post_rope, stream=stream)
     return bufs
+
+
+# ----------------------------------------------------------------------------
+# the attention sublayer: x -> x + post_norm(o_proj(attention(qkv_proj(pre_norm(x)))))
+# ----------------------------------------------------------------------------
+
+@dataclass
+class MixerWeights:
+    """Weights of one attention sublayer (bf16 GPU tensors): pre/post norm weights [D], the
+    fused projection w_qkv [(Hq + 2 Hkv) d, D], the output projection w_o [D, Hq d] and the
+    per-head Q/K norm weights [d]."""
+    w_pre: torch.Tensor
+    w_qkv: torch.Tensor
+    w_o: torch.Tensor
+    w_post: torch.Tensor
+    wq: torch.Tensor
+    wk: torch.Tensor
+    Hq: int
+    Hkv: int
+    d: int = 128
+    pre_offset: float = 1.0
+    post_offset: float = 0.2
+    qk_offset: float = 1.0
+
+    def qkv_slices(self):
+        """The fused weight cut along its rows into Q | K | V (contiguous views)."""
+        a, b = self.Hq * self.d, (self.Hq + self.Hkv) * self.d
+        return self.w_qkv[:a], self.w_qkv[a:b], self.w_qkv[b:]
+
+
+class MixerBuffers:
+    def __init__(self, B, T, D, wts: MixerWeights, device="cuda"):
+        bf = torch.bfloat16
+        self.u = torch.empty((B, T, D), dtype=bf, device=device)
+        self.q = torch.empty((B, T, wts.Hq, wts.d), dtype=bf, device=device)
+        self.k = torch.empty((B, T, wts.Hkv, wts.d), dtype=bf, device=device)
+        self.v = torch.empty((B, T, wts.Hkv, wts.d), dtype=bf, device=device)
+        self.p = torch.empty((B, T, D), dtype=bf, device=device)
+        self.out = torch.empty((B, T, D), dtype=bf, device=device)
+
+
+def _mixer_in(x, wts, bufs, stream):
+    plamo_rms_norm(x, wts.w_pre, bufs.u, offset=wts.pre_offset, stream=stream)
+    for w, y in zip(wts.qkv_slices(), (bufs.q, bufs.k, bufs.v)):  # [B, T, H, d] seen as [B, T, H d]
+        plamo_linear(bufs.u, w, y.view(*y.shape[:2], -1), stream=stream)
+
+
+def _mixer_out(x, attn_out, wts, bufs, stream):
+    plamo_linear(attn_out.view(*attn_out.shape[:2], -1), wts.w_o, bufs.p, stream=stream)  # heads concatenated
+    plamo_rms_norm(bufs.p, wts.w_post, bufs.out, offset=wts.post_offset, residual=x, stream=stream)
+
+
+def mixer_prefill(x, wts: MixerWeights, *, window, rope_table, k_cache=None, v_cache=None,
+                  pos_offset=0, bufs: MixerBuffers | None = None, attn_bufs: PrefillBuffers | None = None,
+                  stream=None):
+    """The attention sublayer over a chunk x [B, T, D] at pos_offset; returns (bufs, attn_bufs),
+    the new residual stream in bufs.out."""
+    B, T, D = x.shape
+    bufs = bufs or MixerBuffers(B, T, D, wts, x.device)
+    _mixer_in(x, wts, bufs, stream)
+    attn_bufs = prefill(bufs.q, bufs.k, bufs.v, window=window, rope_table=rope_table, q_norm_w=wts.wq,
+                        k_norm_w=wts.wk, norm_offset=wts.qk_offset, k_cache=k_cache, v_cache=v_cache,
+                        bufs=attn_bufs, stream=stream, pos_offset=pos_offset)
+    _mixer_out(x, attn_bufs.out, wts, bufs, stream)
+    return bufs, attn_bufs
+
+
+def mixer_decode(x, wts: MixerWeights, k_cache, v_cache, *, window, pos_offset, rope_table,
+                 bufs: MixerBuffers | None = None, attn_bufs: DecodeBuffers | None = None, stream=None):
+    """One decode step of the attention sublayer: x [B, 1, D]; returns (bufs, attn_bufs)."""
+    B, _, D = x.shape
+    bufs = bufs or MixerBuffers(B, 1, D, wts, x.device)
+    _mixer_in(x, wts, bufs, stream)
+    attn_bufs = decode(bufs.q, bufs.k, bufs.v, k_cache, v_cache, window=window, pos_offset=pos_offset,
+                       rope_table=rope_table, q_norm_w=wts.wq, k_norm_w=wts.wk, norm_offset=wts.qk_offset,
+                       bufs=attn_bufs, stream=stream)
+    _mixer_out(x, attn_bufs.out, wts, bufs, stream)
+    return bufs, attn_bufs

@@ -157,6 +157,56 @@ PERIOD_DECODE = DecodeWorkload(
     steps=128, seed=BASE_SEED + 5)
 
 
+@dataclass(frozen=True)
+class MixerWorkload:
+    """The attention sublayer around the hot path at PLaMo 3 31B's widths (hidden D = 5120,
+    「PLaMo 3アーキテクチャ徹底解析」 §2.1, §3.2, §4.1): random weights, projections scaled by
+    1/sqrt(fan-in) so that Q/K/V and the output projection stay O(1); norm weights N(0, 0.02);
+    residual input N(0, 1)."""
+    name: str
+    B: int
+    T: int
+    D: int
+    Hq: int
+    Hkv: int
+    d: int
+    window: int
+    rope: Rope
+    seed: int
+    norm_std: float = 0.02
+
+    def draw_device(self, device):
+        """(x [B, T, D], dict of bf16 weights) drawn on the device (synthetic.device_normal_bf16)."""
+        qkv_rows = (self.Hq + 2 * self.Hkv) * self.d
+        x = device_normal_bf16((self.B, self.T, self.D), self.seed, device)
+        w = dict(
+            w_pre=(device_normal_bf16((self.D,), self.seed + 1, device).float() * self.norm_std).bfloat16(),
+            w_qkv=(device_normal_bf16((qkv_rows, self.D), self.seed + 2, device).float()
+                   / math.sqrt(self.D)).bfloat16(),
+            w_o=(device_normal_bf16((self.D, self.Hq * self.d), self.seed + 3, device).float()
+                 / math.sqrt(self.Hq * self.d)).bfloat16(),
+            w_post=(device_normal_bf16((self.D,), self.seed + 4, device).float() * self.norm_std).bfloat16(),
+            wq=(device_normal_bf16((self.d,), self.seed + 5, device).float() * self.norm_std).bfloat16(),
+            wk=(device_normal_bf16((self.d,), self.seed + 6, device).float() * self.norm_std).bfloat16(),
+        )
+        return x, w
+
+    def gemm_flops(self) -> float:
+        """2 M N K for the fused QKV projection and the output projection."""
+        M = self.B * self.T
+        return 2.0 * M * self.D * (self.Hq + 2 * self.Hkv) * self.d + 2.0 * M * self.Hq * self.d * self.D
+
+    def attention_flops(self) -> float:
+        T, W = self.T, self.window
+        pairs = T * (T + 1) // 2 if W <= 0 or W >= T else W * (W + 1) // 2 + (T - W) * W
+        return 4.0 * self.d * self.Hq * self.B * pairs
+
+
+MIXER_LOCAL_PREFILL = MixerWorkload(
+    name="mixer_local_prefill_T8192_D5120", B=1, T=8192, D=5120, Hq=64, Hkv=8, d=128, window=2048,
+    rope=Rope(theta=1e4), seed=BASE_SEED + 7)
+
+
 def ragged_positions(B: int, max_pos: int, seed: int) -> np.ndarray:
     """Positions of the new token of each sequence of a ragged decode batch: independent
     uniform integers in [0, max_pos], the last one set to max_pos so that the batch's bound

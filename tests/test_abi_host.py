@@ -234,3 +234,20 @@ def test_ragged_entry_points_validate_their_arrays(lib):
     assert decode(FAKE, window=0, cap=4000) == INVALID     # global cap must exceed max_pos_offset
     assert decode(FAKE, ws=None) == WORKSPACE
     assert decode(FAKE, table_bytes=(64 + 31) * 512) == WORKSPACE
+
+
+def test_sublayer_entry_points_validate(lib):
+    assert lib.plamo_linear(FAKE, FAKE, FAKE, -1, 8, 64, None) == INVALID
+    assert lib.plamo_linear(FAKE, FAKE, FAKE, 4, 12, 64, None) == UNSUPPORTED   # N % 8
+    assert lib.plamo_linear(FAKE, FAKE, FAKE, 4, 8, 96, None) == UNSUPPORTED    # K % 64
+    assert lib.plamo_linear(None, FAKE, FAKE, 4, 8, 64, None) == INVALID
+    assert lib.plamo_linear(MISALIGNED, FAKE, FAKE, 4, 8, 64, None) == INVALID
+    assert lib.plamo_linear(FAKE, FAKE, FAKE, 0, 8, 64, None) == OK
+    norm = lambda **o: lib.plamo_rms_norm(o.get("dtype", BF16), o.get("x", FAKE), o.get("w", FAKE), 0.2, 1e-6,
+                                         o.get("r", None), o.get("y", FAKE), o.get("rows", 4), o.get("n", 64), None)
+    assert norm(dtype=5) == INVALID
+    assert norm(n=12) == UNSUPPORTED          # bf16 rows fill 16-byte chunks
+    assert norm(rows=-1) == INVALID
+    assert norm(x=MISALIGNED) == INVALID
+    assert norm(y=None) == INVALID
+    assert norm(rows=0) == OK
