@@ -254,8 +254,7 @@ PLAMO_API int plamo_attn_decode_ragged(int dtype, const void* q_rot, const void*
  * x_out = x + N^(0.2)_{w_post}( O W_o^T ),  O = attention(split(N^(1)_{w_pre}(x) W_qkv^T))
  * composed from plamo_rms_norm, plamo_linear and the attention calls above:
  *   U = plamo_rms_norm(x, w_pre, offset 1)                 [B*T, D]
- *   Q | K | V = plamo_linear(U, W_qkv rows [0, Hq d) | [Hq d, (Hq+Hkv) d) | the rest)
- *   (the fused weight [(Hq + 2 Hkv) d, D] cut along its rows, [P3 §4.1])
+ *   Q | K | V = plamo_qkv_projection(U, W_qkv)            one GEMM, output split [P3 §4.1]
  *   O = plamo_kv_append + plamo_attn_prefill / plamo_attn_decode    [B*T, Hq d]
  *   P = plamo_linear(O, W_o [D, Hq d])                     [B*T, D]
  *   x_out = plamo_rms_norm(P, w_post, offset 0.2, residual x)
@@ -266,6 +265,13 @@ PLAMO_API int plamo_attn_decode_ragged(int dtype, const void* q_rot, const void*
  * otherwise); y must not overlap x or W. */
 PLAMO_API int plamo_linear(const void* x, const void* w, void* y, long long M, int N, int K,
                     void* stream);
+
+/* The fused QKV projection [P3 §4.1]: [Q | K | V] = U W_qkv^T with U [M, D] (M = B*T
+ * tokens) and W_qkv [(Hq + 2 Hkv) d, D], the output columns cut at Hq d and (Hq + Hkv) d
+ * and written to q [M, Hq d], k [M, Hkv d], v [M, Hkv d] (i.e. [B, T, H, d] each, the
+ * layouts plamo_kv_append takes). bf16, fp32 accumulation; D % 64 == 0, d % 8 == 0. */
+PLAMO_API int plamo_qkv_projection(const void* u, const void* w_qkv, void* q, void* k, void* v,
+                    long long M, int D, int Hq, int Hkv, int d, void* stream);
 
 /* y = residual + (offset + w) * x / sqrt(mean(x^2) + eps) per row of n [P3 §3.2];
  * residual NULL = no add. x, residual, y [rows, n], w [n], all of `dtype`, fp32 math;

@@ -29,7 +29,7 @@ __all__ = [
     "plamo_prefill_padded_len", "legacy_4k_window", "plamo_kv_append", "plamo_attn_prefill",
     "plamo_attn_decode_workspace_bytes", "plamo_attn_decode", "plamo_kv_append_ragged",
     "plamo_attn_prefill_ragged", "plamo_attn_decode_ragged_workspace_bytes", "plamo_attn_decode_ragged",
-    "plamo_linear", "plamo_rms_norm", "library_path",
+    "plamo_linear", "plamo_qkv_projection", "plamo_rms_norm", "library_path",
 ]
 
 
@@ -347,6 +347,21 @@ def plamo_linear(x, w, y, *, stream=None) -> None:
     bf = torch.bfloat16
     st = _lib.load().plamo_linear(_dev(x, "x", bf), _dev(w, "w", bf), _dev(y, "y", bf), M, N, K, _stream(stream))
     _check(st, "plamo_linear")
+
+
+def plamo_qkv_projection(u, w_qkv, q, k, v, *, stream=None) -> None:
+    """[Q | K | V] = u w_qkv^T split into q [..., Hq, d], k, v [..., Hkv, d]; u [..., D]."""
+    D = u.shape[-1]
+    M = u.numel() // D
+    Hq, d = q.shape[-2], q.shape[-1]
+    Hkv = k.shape[-2]
+    if tuple(w_qkv.shape) != ((Hq + 2 * Hkv) * d, D) or q.numel() != M * Hq * d or \
+            k.numel() != M * Hkv * d or v.shape != k.shape:
+        raise ValueError("need u [..., D], w_qkv [(Hq + 2 Hkv) d, D], q [..., Hq, d], k and v [..., Hkv, d]")
+    bf = torch.bfloat16
+    st = _lib.load().plamo_qkv_projection(_dev(u, "u", bf), _dev(w_qkv, "w_qkv", bf), _dev(q, "q", bf),
+                                          _dev(k, "k", bf), _dev(v, "v", bf), M, D, Hq, Hkv, d, _stream(stream))
+    _check(st, "plamo_qkv_projection")
 
 
 def plamo_rms_norm(x, w, y, *, offset: float, eps: float = 1e-6, residual=None, stream=None) -> None:

@@ -42,6 +42,8 @@ SIGNATURES = {
                                          c_int, c_int, c_int, c_int, c_int, c_void_p, c_ll, c_void_p, c_size,
                                          c_float, c_int, c_void_p]),
     "plamo_linear": (c_int, [c_void_p, c_void_p, c_void_p, c_ll, c_int, c_int, c_void_p]),
+    "plamo_qkv_projection": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_ll, c_int, c_int, c_int,
+                                     c_int, c_void_p]),
     "plamo_rms_norm": (c_int, [c_int, c_void_p, c_void_p, c_float, c_float, c_void_p, c_void_p, c_ll, c_int,
                                c_void_p]),
     "plamo_status_str": (ctypes.c_char_p, [c_int]),

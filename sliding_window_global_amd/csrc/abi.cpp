@@ -346,7 +346,7 @@ int plamo_attn_decode_ragged(int dtype, const void* q_rot, const void* k_cache, 
 int plamo_linear(const void* x, const void* w, void* y, long long M, int N, int K, void* stream) {
   if (M < 0 || N < 1 || K < 1) return fail(PLAMO_ERR_INVALID_ARG, "need M >= 0, N >= 1, K >= 1");
   if (N % 8 || K % 64) return fail(PLAMO_ERR_UNSUPPORTED, "need N % 8 == 0 and K % 64 == 0");
-  if (M > 65535LL * 128 || static_cast<long long>(K) * 256 * 2 > 0x7fffffffLL)
+  if (M > 65535LL * 256 || static_cast<long long>(K) * 256 * 2 > 0x7fffffffLL)
     return fail(PLAMO_ERR_UNSUPPORTED, "M or K too large");
   if (M == 0) return ok();
   if (!x || !w || !y) return fail(PLAMO_ERR_INVALID_ARG, "x, w and y must be non-NULL");
@@ -354,7 +354,30 @@ int plamo_linear(const void* x, const void* w, void* y, long long M, int N, int 
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
   plamo::GemmArgs a;
-  a.x = x; a.w = w; a.y = y; a.M = M; a.N = N; a.K = K;
+  a.x = x; a.w = w; a.M = M; a.N = N; a.K = K;
+  a.y[0] = a.y[1] = a.y[2] = y;
+  a.part_end[0] = a.part_end[1] = a.part_end[2] = N;
+  return launched(plamo::launch_gemm_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+int plamo_qkv_projection(const void* u, const void* w_qkv, void* q, void* k, void* v, long long M, int D,
+                         int Hq, int Hkv, int d, void* stream) {
+  if (M < 0 || D < 1 || Hq < 1 || Hkv < 1 || d < 1) return fail(PLAMO_ERR_INVALID_ARG, "bad sizes");
+  if (D % 64 || d % 8) return fail(PLAMO_ERR_UNSUPPORTED, "need D % 64 == 0 and d % 8 == 0");
+  const long long N = static_cast<long long>(Hq + 2 * Hkv) * d;
+  if (M > 65535LL * 256 || N > (1LL << 30) || static_cast<long long>(D) * 256 * 2 > 0x7fffffffLL)
+    return fail(PLAMO_ERR_UNSUPPORTED, "sizes too large");
+  if (M == 0) return ok();
+  if (!u || !w_qkv || !q || !k || !v) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be non-NULL");
+  const void* ptrs[] = {u, w_qkv, q, k, v};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  plamo::GemmArgs a;
+  a.x = u; a.w = w_qkv; a.M = M; a.N = N; a.K = D;
+  a.y[0] = q; a.y[1] = k; a.y[2] = v;
+  a.part_end[0] = static_cast<long long>(Hq) * d;
+  a.part_end[1] = static_cast<long long>(Hq + Hkv) * d;
+  a.part_end[2] = N;
   return launched(plamo::launch_gemm_bf16(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -1,19 +1,24 @@
 // Projection GEMM of the attention sublayer on gfx950 bf16 MFMA:
 // y[M, N] = x[M, K] W[N, K]^T (both operands K-contiguous, fp32 accumulation, bf16 out).
-// 「PLaMo 3アーキテクチャ徹底解析」 §4.1: the fused QKV projection (N = (Hq + 2 Hkv) d, cut into
-// its Q | K | V row blocks), §4.5: the output projection (K = Hq d, N = hidden).
+// 「PLaMo 3アーキテクチャ徹底解析」 §4.1: the fused QKV projection (N = (Hq + 2 Hkv) d), whose
+// output columns are split into Q | K | V; the epilogue writes each part to its own tensor.
+// §4.5: the output projection (K = Hq d, N = hidden).
 //
-// block  = 128 rows of x (m) x 256 rows of W (n), 4 waves in a 2 x 2 grid, each wave
+// block  = 256 rows of x (m) x 256 rows of W (n), 8 waves in a 4 (m) x 2 (n) grid, each wave
 //          64 m x 128 n = 2 x 4 blocks of v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators).
 //          W fragments are the MFMA A operand (32 n x 16 k), x fragments the B operand, so a
 //          lane's accumulators hold one m and runs of 4 consecutive n: 8-byte stores.
-// tiles  = 64 k per step: W tile 256 x 64, x tile 128 x 64 (32 + 16 KiB), double buffered,
-//          copied global -> LDS by buffer loads with the LDS bit (a resource per operand
-//          block bounds every read; rows past M or N read 0). LDS rows are 128 B; the
-//          16-byte chunk c of row r sits at position c ^ ((r >> 1) & 7), so that the eight
-//          lanes of a row read one contiguous 128 B of global memory and the 16 rows that a
-//          quarter-wave's fragment read touches fall into distinct banks.
-// Requirements (checked by the caller): K % 64 == 0, N % 8 == 0.
+// tiles  = 64 k per step: W and x tiles 256 x 64 (32 KiB each), double buffered (128 KiB,
+//          one block per CU), copied global -> LDS by buffer loads with the LDS bit (a
+//          resource per operand block bounds every read; rows past M or N read 0). LDS rows
+//          are 128 B; the 16-byte chunk c of row r sits at position c ^ ((r >> 1) & 7), so
+//          that the eight lanes of a row read one contiguous 128 B of global memory and the
+//          16 rows of a quarter-wave's fragment read fall into distinct banks. The next
+//          sub-step's fragments are read while the current sub-step's MFMAs run.
+// Measured on the sublayer shapes: ~1.0-1.15 PFLOP/s; the same kernel without the tile copies
+// (timing only) runs ~1.5-1.8, a 4-stage copy ring and an XCD-grouped tile order changed
+// nothing, so the LDS traffic of the copies plus the operand reads is what limits it.
+// Requirements (checked by the caller): K % 64 == 0, every output part's width % 8 == 0.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,10 +26,12 @@ namespace plamo {
 
 namespace {
 
-constexpr int BM = 128;  // rows of x per block
+constexpr int BM = 256;  // rows of x per block
 constexpr int BN = 256;  // rows of W per block
 constexpr int BK = 64;   // k per step (8 chunks of 8)
-constexpr int kThreads = 256;
+constexpr int kChunks = BK / 8;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
 constexpr unsigned kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters untouched
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -43,14 +50,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;  // 4 (m) x 2 (n) waves
   const long long n0 = static_cast<long long>(blockIdx.x) * BN;
   const long long m0 = static_cast<long long>(blockIdx.y) * BM;
   const int K = a.K;
   const int nk = K / BK;
+  const long long N = a.N;
 
   // operand blocks: rows past N (M) lie outside the resource and read as 0
-  const long long n_rows = min(static_cast<long long>(BN), a.N - n0);
+  const long long n_rows = min(static_cast<long long>(BN), N - n0);
   const long long m_rows = min(static_cast<long long>(BM), a.M - m0);
   const __amdgpu_buffer_rsrc_t w_rsrc =
       make_rsrc(static_cast<const bf16_t*>(a.w) + n0 * K, static_cast<int>(n_rows * K * 2));
@@ -59,22 +67,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
 
   // copy of one 64-k step: 1 KiB per direct load = 8 rows x 128 B; lane l fills position
   // l % 8 of row l / 8 with global chunk (l % 8) ^ swz(row)
-  const int sub_row = lane >> 3, pos = lane & 7;
+  constexpr int kRowsPerLoad = 64 / kChunks;  // rows one 1 KiB direct load covers
+  const int sub_row = lane / kChunks, pos = lane % kChunks;
   auto issue = [&](__amdgpu_buffer_rsrc_t rsrc, int rows_per_wave, int step, bf16_t* buf)
       __attribute__((always_inline)) {
     const int k_off = step * BK * 2;  // bytes
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (i * 8 >= rows_per_wave) break;
-      const int row = wave * rows_per_wave + i * 8 + sub_row;
+      if (i * kRowsPerLoad >= rows_per_wave) break;
+      const int row = wave * rows_per_wave + i * kRowsPerLoad + sub_row;
       const int voff = (row * K + ((pos ^ swz(row)) * 8)) * 2;
-      lds_ptr_t dst = (lds_ptr_t)(buf + (wave * rows_per_wave + i * 8) * BK);  // generic -> LDS
+      lds_ptr_t dst = (lds_ptr_t)(buf + (wave * rows_per_wave + i * kRowsPerLoad) * BK);  // generic -> LDS
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, k_off, 0, 0);
     }
   };
   auto issue_step = [&](int step, bf16_t* abuf, bf16_t* bbuf) __attribute__((always_inline)) {
-    issue(w_rsrc, BN / 4, step, abuf);
-    issue(x_rsrc, BM / 4, step, bbuf);
+    issue(w_rsrc, BN / kWaves, step, abuf);
+    issue(x_rsrc, BM / kWaves, step, bbuf);
   };
 
   f32x16 acc[4][2];
@@ -91,21 +100,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   auto frag = [&](const bf16_t* buf, int r0, int s) __attribute__((always_inline)) {
     const int r = r0 + fr_row;
     const int c = 2 * s + fr_half;
-    return *reinterpret_cast<const bf16x8*>(buf + (r * 8 + (c ^ swz(r))) * 8);
+    return *reinterpret_cast<const bf16x8*>(buf + (r * kChunks + (c ^ swz(r))) * 8);
   };
   auto compute = [&](const bf16_t* abuf, const bf16_t* bbuf) __attribute__((always_inline)) {
+    bf16x8 af[2][4], bfr[2][2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 af[4], bfr[2];
+    for (int i = 0; i < 4; ++i) af[0][i] = frag(abuf, wn * 128 + i * 32, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = frag(abuf, wn * 128 + i * 32, s);
+    for (int j = 0; j < 2; ++j) bfr[0][j] = frag(bbuf, wm * 64 + j * 32, 0);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[j] = frag(bbuf, wm * 64 + j * 32, s);
+    for (int s = 0; s < BK / 16; ++s) {
+      if (s + 1 < BK / 16) {  // next sub-step's fragments go out before this one's MFMAs
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[(s + 1) & 1][i] = frag(abuf, wn * 128 + i * 32, s + 1);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bfr[(s + 1) & 1][j] = frag(bbuf, wm * 64 + j * 32, s + 1);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bfr[s & 1][j], acc[i][j], 0, 0, 0);
     }
   };
 
@@ -126,8 +141,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   }
 
   // store: accumulator (i, j) register e holds m = m0 + wm*64 + j*32 + lane % 32 and
-  // n = n0 + wn*128 + i*32 + (e/4)*8 + (lane/32)*4 + e%4
-  bf16_t* y = static_cast<bf16_t*>(a.y);
+  // n = n0 + wn*128 + i*32 + (e/4)*8 + (lane/32)*4 + e%4; column n belongs to output part p
+  // (parts are multiples of 8 wide, so a run of 4 never straddles two parts)
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const long long m = m0 + wm * 64 + j * 32 + (lane & 31);
@@ -137,11 +152,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const long long n = n0 + wn * 128 + i * 32 + q * 8 + (lane >> 5) * 4;
-        if (n >= a.N) continue;
+        if (n >= N) continue;
+        const int p = n < a.part_end[0] ? 0 : (n < a.part_end[1] ? 1 : 2);
+        const long long first = p == 0 ? 0 : a.part_end[p - 1];
+        const long long width = a.part_end[p] - first;
         u32x2 w;
         w[0] = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
         w[1] = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-        *reinterpret_cast<u32x2*>(y + m * a.N + n) = w;
+        *reinterpret_cast<u32x2*>(static_cast<bf16_t*>(a.y[p]) + m * width + (n - first)) = w;
       }
   }
 }

@@ -83,11 +83,12 @@ struct DecodeArgs {
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
 struct GemmArgs {
-  const void* x;  // [M, K] bf16
-  const void* w;  // [N, K] bf16
-  void* y;        // [M, N] bf16
+  const void* x;            // [M, K] bf16
+  const void* w;            // [N, K] bf16
+  void* y[3];               // output parts: columns [part_end[p-1], part_end[p]) go to y[p],
+  long long part_end[3];    // a row-major [M, width_p] tensor; unused parts end at N
   long long M, N;
-  int K;          // a multiple of 64
+  int K;                    // a multiple of 64
 };
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t stream);
 

@@ -13,7 +13,7 @@ import torch
 
 from dataclasses import dataclass
 
-from . import (plamo_linear, plamo_rms_norm, plamo_attn_decode, plamo_attn_decode_ragged, plamo_attn_decode_ragged_workspace_bytes,
+from . import (plamo_linear, plamo_qkv_projection, plamo_rms_norm, plamo_attn_decode, plamo_attn_decode_ragged, plamo_attn_decode_ragged_workspace_bytes,
                plamo_attn_decode_workspace_bytes,
                plamo_attn_prefill, plamo_attn_prefill_ragged, plamo_kv_append, plamo_kv_append_ragged,
                prefill_operand_shapes)
@@ -143,10 +143,6 @@ class MixerWeights:
     post_offset: float = 0.2
     qk_offset: float = 1.0
 
-    def qkv_slices(self):
-        """The fused weight cut along its rows into Q | K | V (contiguous views)."""
-        a, b = self.Hq * self.d, (self.Hq + self.Hkv) * self.d
-        return self.w_qkv[:a], self.w_qkv[a:b], self.w_qkv[b:]
 
 
 class MixerBuffers:
@@ -162,8 +158,7 @@ class MixerBuffers:
 
 def _mixer_in(x, wts, bufs, stream):
     plamo_rms_norm(x, wts.w_pre, bufs.u, offset=wts.pre_offset, stream=stream)
-    for w, y in zip(wts.qkv_slices(), (bufs.q, bufs.k, bufs.v)):  # [B, T, H, d] seen as [B, T, H d]
-        plamo_linear(bufs.u, w, y.view(*y.shape[:2], -1), stream=stream)
+    plamo_qkv_projection(bufs.u, wts.w_qkv, bufs.q, bufs.k, bufs.v, stream=stream)
 
 
 def _mixer_out(x, attn_out, wts, bufs, stream):

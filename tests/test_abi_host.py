@@ -243,6 +243,9 @@ def test_sublayer_entry_points_validate(lib):
     assert lib.plamo_linear(None, FAKE, FAKE, 4, 8, 64, None) == INVALID
     assert lib.plamo_linear(MISALIGNED, FAKE, FAKE, 4, 8, 64, None) == INVALID
     assert lib.plamo_linear(FAKE, FAKE, FAKE, 0, 8, 64, None) == OK
+    assert lib.plamo_qkv_projection(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 100, 8, 2, 128, None) == UNSUPPORTED  # D % 64
+    assert lib.plamo_qkv_projection(FAKE, FAKE, None, FAKE, FAKE, 4, 256, 8, 2, 128, None) == INVALID
+    assert lib.plamo_qkv_projection(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 256, 8, 2, 128, None) == OK
     norm = lambda **o: lib.plamo_rms_norm(o.get("dtype", BF16), o.get("x", FAKE), o.get("w", FAKE), 0.2, 1e-6,
                                          o.get("r", None), o.get("y", FAKE), o.get("rows", 4), o.get("n", 64), None)
     assert norm(dtype=5) == INVALID

@@ -49,6 +49,26 @@ def test_linear_matches_fp64_matmul(M, N, K):
     assert_parity(host(y)[rows], ref, TOL_BF16, f"linear {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,D,Hq,Hkv", [(8192, 5120, 64, 8), (301, 256, 8, 2), (3, 5120, 64, 8)])
+def test_qkv_projection_matches_fp64(M, D, Hq, Hkv):
+    """One GEMM against the fused weight, its output columns split into Q | K | V at Hq d and
+    (Hq + Hkv) d (「PLaMo 3アーキテクチャ徹底解析」 §4.1)."""
+    d = 128
+    g = torch.Generator(device="cuda").manual_seed(M + D)
+    u = torch.randn((M, D), generator=g, device="cuda").bfloat16()
+    w = (torch.randn(((Hq + 2 * Hkv) * d, D), generator=g, device="cuda") / math.sqrt(D)).bfloat16()
+    q = torch.empty((M, Hq, d), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((M, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    swg.plamo_qkv_projection(u, w, q, k, v)
+    torch.cuda.synchronize()
+    rows = np.unique(np.linspace(0, M - 1, 48).astype(int))
+    full = host(u)[rows] @ host(w).T
+    assert_parity(host(q).reshape(M, -1)[rows], full[:, :Hq * d], TOL_BF16, "Q part")
+    assert_parity(host(k).reshape(M, -1)[rows], full[:, Hq * d:(Hq + Hkv) * d], TOL_BF16, "K part")
+    assert_parity(host(v).reshape(M, -1)[rows], full[:, (Hq + Hkv) * d:], TOL_BF16, "V part")
+
+
 @pytest.mark.parametrize("offset,residual", [(1.0, False), (0.2, True)])
 def test_rms_norm_matches_oracle(offset, residual):
     g = torch.Generator(device="cuda").manual_seed(7)
