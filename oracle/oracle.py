@@ -16,7 +16,9 @@ Sources (page title, section):
        §4.2 GQA head sharing; §4.3 per-head Q/K norm; §4.4 order of cache update
        and RoPE, renumbered positions, local cache trimming; §4.5 attention
        equation; §5.1 causal and window masks; §5.2 KV capacity; §6.1 split-half
-       RoPE; §6.2 bases; §6.3 YaRN.
+       RoPE; §6.2 bases; §6.3 YaRN; §6.4 p-RoPE; §8 comparison table (the
+       Gemma-4-shaped layer: gain-only Q/K norm, gainless V norm, dot-product factor 1,
+       K stored after RoPE); §9.4 constant Q/K gains of that layer.
   [TR] 「Transformerと大規模言語モデル 技術解説」 (troy-technical.jp), §4 worked
        attention example (Fig. 3).
 
@@ -68,14 +70,23 @@ def yarn_ramp_bounds(d: int, theta: float, orig_ctx: float, beta_fast: float,
 
 def rope_frequencies(d: int, theta: float, yarn_factor: float = 0.0,
                      orig_ctx: float = 4096.0, beta_fast: float = 32.0,
-                     beta_slow: float = 1.0) -> tuple[np.ndarray, float]:
+                     beta_slow: float = 1.0, partial: float = 1.0) -> tuple[np.ndarray, float]:
     """Angular frequency per rotation pair and the amplitude factor.
 
     [P3 §6.1] omega_j = theta^(-2j/d), j = 0 .. d/2-1.
     [P3 §6.3] With YaRN factor s > 1: alpha_j = clip((j - j_low)/(j_high - j_low), 0, 1),
     omega~_j = omega_j * ((1 - alpha_j) + alpha_j / s), and cos and sin are both
-    scaled by 1 + 0.1 ln s. Without YaRN the amplitude is 1."""
+    scaled by 1 + 0.1 ln s. Without YaRN the amplitude is 1.
+    [P3 §6.4] p-RoPE (partial < 1): only the floor(p * d/2) highest-frequency pairs
+    turn, still with the exponent over the whole head dim d; the other pairs get
+    frequency 0 (cos 1, sin 0: left as they are). Not combined with YaRN."""
     j = np.arange(d // 2, dtype=F64)
+    if partial < 1.0:
+        if yarn_factor is not None and yarn_factor > 1.0:
+            raise ValueError("p-RoPE is not combined with YaRN")
+        n_rot = int(math.floor(partial * (d // 2)))
+        omega = np.where(j < n_rot, np.power(F64(theta), -2.0 * j / d), 0.0)
+        return omega, 1.0
     omega = np.power(F64(theta), -2.0 * j / d)
     if yarn_factor is None or yarn_factor <= 1.0:
         return omega, 1.0
@@ -226,11 +237,17 @@ def attention_layer_step(q, k, v, cache: LayerKVCache, *, theta: float,
                          beta_fast: float = 32.0, beta_slow: float = 1.0,
                          q_norm_w=None, k_norm_w=None, norm_offset: float = 1.0,
                          eps: float = 1e-6, scale: float | None = None,
-                         rows=None, return_intermediates: bool = False):
+                         rows=None, return_intermediates: bool = False,
+                         partial: float = 1.0, v_norm: bool = False):
     """One attention layer for one sequence, in the order of [P3 §4.4]:
     per-head Q/K RMSNorm -> cache update -> RoPE on the current Q and on every K the
     cache returns -> masked GQA attention. (A post_rope cache instead rotates K at its
     absolute position before the update and Q at its absolute position.)
+
+    The Gemma-4-shaped layer of [P3 §8] is this step with norm_offset 0 (the gain is the
+    stored weight itself), scale 1, a post_rope cache, p-RoPE on its global layer
+    (``partial``, [P3 §6.4]) and ``v_norm``: each new V head vector is divided by its
+    RMS (RMSNorm without gain, same eps) before it enters the cache.
 
     q [T, Hq, d]; k, v [T, Hkv, d] (projected, before norm). Positions are the
     internal running numbers of [P3 §4.4]: the S keys returned by the cache get
@@ -246,7 +263,9 @@ def attention_layer_step(q, k, v, cache: LayerKVCache, *, theta: float,
     if q_norm_w is not None:
         q = offset_rms_norm(q, q_norm_w, norm_offset, eps)
         k = offset_rms_norm(k, k_norm_w, norm_offset, eps)
-    omega, amp = rope_frequencies(d, theta, yarn_factor, orig_ctx, beta_fast, beta_slow)
+    if v_norm:
+        v = v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)
+    omega, amp = rope_frequencies(d, theta, yarn_factor, orig_ctx, beta_fast, beta_slow, partial)
     if cache.post_rope:
         # rotate the new K at its absolute positions, then store; the cache returns the
         # rotated K of the kept tokens and the new ones; queries at absolute positions

@@ -93,8 +93,11 @@ def pin_sdpa_float64(o):
             assert np.max(np.abs(got - ref)) < 1e-12
 
 
-def _brute_layer(q, k, v, prior_k, prior_v, W, theta, yarn, wq, wk, c, eps):
-    """Pure-Python scalar evaluation of one layer step: norm, cache, RoPE, attention."""
+def _brute_layer(q, k, v, prior_k, prior_v, W, theta, yarn, wq, wk, c, eps, n_rot=None,
+                 v_norm=False, scale=None):
+    """Pure-Python scalar evaluation of one layer step: norm, cache, RoPE, attention.
+    n_rot: only pairs j < n_rot turn (p-RoPE); v_norm: new V rows divided by their RMS;
+    scale: factor on the dot product (default 1/sqrt(d))."""
     T, Hq, d = len(q), len(q[0]), len(q[0][0])
     Hkv = len(k[0])
     half = d // 2
@@ -107,13 +110,17 @@ def _brute_layer(q, k, v, prior_k, prior_v, W, theta, yarn, wq, wk, c, eps):
     if wq is not None:
         q = [[norm(q[t][h], wq) for h in range(Hq)] for t in range(T)]
         k = [[norm(k[t][h], wk) for h in range(Hkv)] for t in range(T)]
+    if v_norm:
+        v = [[norm(v[t][h], [1.0 - c] * d) for h in range(Hkv)] for t in range(T)]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
     keys = [list(map(list, r)) for r in prior_k] + k
     vals = [list(map(list, r)) for r in prior_v] + v
     S = len(keys)
     omega = []
     amp = 1.0
     for j in range(half):
-        w0 = theta ** (-2.0 * j / d)
+        w0 = theta ** (-2.0 * j / d) if n_rot is None or j < n_rot else 0.0
         if yarn:
             lo = half * math.log(4096 / (2 * math.pi * 32)) / math.log(theta)
             hi = half * math.log(4096 / (2 * math.pi * 1)) / math.log(theta)
@@ -141,7 +148,7 @@ def _brute_layer(q, k, v, prior_k, prior_v, W, theta, yarn, wq, wk, c, eps):
             for s in range(S):
                 if s <= i and (W == 0 or i - s < W):
                     kr = rot(keys[s][g], s)
-                    sc.append((s, sum(qr[r] * kr[r] for r in range(d)) / math.sqrt(d)))
+                    sc.append((s, sum(qr[r] * kr[r] for r in range(d)) * scale))
             m = max(x for _, x in sc)
             e = [(s, math.exp(x - m)) for s, x in sc]
             z = sum(x for _, x in e)
@@ -553,12 +560,135 @@ def pin_mixer_torch(o):
     assert np.max(np.abs(got - want.numpy())) < 1e-12
 
 
+def pin_p_rope_page(o):
+    """「PLaMo 3アーキテクチャ徹底解析」 §6.4: p-RoPE of the Gemma-4-shaped global layer (d = 512,
+    p = 0.25, base 1e6): the printed frequency formula over the whole head dim for the 64
+    high-frequency pairs and frequency 0 for the other 192; pairs (j, j + 256); exactly the
+    printed components turn; it is not a 128-dim RoPE on the first 128 components."""
+    g = golden("p_rope_printed.json")
+    d, theta, p = g["d"], g["theta"], g["p"]
+    omega, amp = o.rope_frequencies(d, theta, partial=p)
+    assert amp == 1.0 and omega.shape == (g["pairs"],)
+    n_rot = g["rotated_pairs"]
+    for j in range(g["pairs"]):
+        want = math.exp(-2.0 * j / d * math.log(theta)) if j < n_rot else 0.0
+        assert abs(omega[j] - want) <= 1e-15 * max(1.0, want), (j, omega[j], want)
+    x = _rand((4, 3, d), 301)
+    pos = np.array([1, 7, 1000, 131071])
+    got = o.apply_rope(x, pos, omega, amp)
+    changed = np.any(got != x, axis=(0, 1))
+    want_set = np.zeros(d, dtype=bool)
+    for lo, hi in g["rotated_components"]:
+        want_set[lo:hi + 1] = True
+    assert np.array_equal(changed, want_set), np.nonzero(changed != want_set)
+    # each turning pair (j, j + 256) is a complex product with exp(i p w_j)
+    h = d // 2
+    z = (x[..., :n_rot] + 1j * x[..., h:h + n_rot]) * np.exp(1j * pos[:, None, None] * omega[None, None, :n_rot])
+    assert np.max(np.abs(got[..., :n_rot] - z.real)) < 1e-12
+    assert np.max(np.abs(got[..., h:h + n_rot] - z.imag)) < 1e-12
+    # the reading the page warns against: a 128-dim RoPE on components 0..127
+    w128 = np.exp(-2.0 * np.arange(64) / 128 * math.log(theta))
+    alt = x.copy()
+    a, b = x[..., :64], x[..., 64:128]
+    ang = pos[:, None, None] * w128[None, None, :]
+    alt[..., :64] = a * np.cos(ang) - b * np.sin(ang)
+    alt[..., 64:128] = a * np.sin(ang) + b * np.cos(ang)
+    assert np.max(np.abs(alt - got)) > 0.1
+    # scores still depend on the position difference only
+    q1, k1 = _rand((3, 1, d), 302), _rand((3, 1, d), 303)
+    qp, kp = np.array([5, 900, 3]), np.array([0, 899, 3])
+    base = np.sum(o.apply_rope(q1, qp, omega, amp) * o.apply_rope(k1, kp, omega, amp), -1)
+    for delta in (1, 4095, 262143):
+        sh = np.sum(o.apply_rope(q1, qp + delta, omega, amp) * o.apply_rope(k1, kp + delta, omega, amp), -1)
+        assert np.max(np.abs(sh - base)) < 1e-9 * max(1.0, np.max(np.abs(base)))
+
+
+def _gemma_kw(partial, wq, wk):
+    return dict(theta=1e6 if partial < 1.0 else 1e4, partial=partial, q_norm_w=wq, k_norm_w=wk,
+                norm_offset=0.0, scale=1.0, v_norm=True)
+
+
+def pin_gemma_layer_bruteforce(o):
+    """「PLaMo 3アーキテクチャ徹底解析」 §6.4 and the §8 comparison table: the Gemma-4-shaped layer
+    (gain = stored weight, offset 0; V divided by its RMS; dot-product factor 1; K stored
+    after RoPE at absolute positions; p-RoPE on the global layer) evaluated in chunks on a
+    post-RoPE cache, against scalar loops over the whole sequence at renumbered positions."""
+    cases = [dict(T=7, Hq=4, Hkv=2, d=8, W=3, partial=1.0, chunks=[3, 1, 3], seed=311),
+             dict(T=6, Hq=4, Hkv=1, d=16, W=0, partial=0.25, chunks=[2, 1, 1, 2], seed=312),
+             dict(T=5, Hq=2, Hkv=2, d=12, W=0, partial=0.5, chunks=[5], seed=313)]
+    for cs in cases:
+        T, Hq, Hkv, d, W = cs["T"], cs["Hq"], cs["Hkv"], cs["d"], cs["W"]
+        s = cs["seed"]
+        q, k, v = _rand((T, Hq, d), s), _rand((T, Hkv, d), s + 1), 3.0 * _rand((T, Hkv, d), s + 2)
+        wq, wk = 1.0 + 0.05 * _rand((d,), s + 3), 0.3 + 0.05 * _rand((d,), s + 4)
+        kw = _gemma_kw(cs["partial"], wq, wk)
+        cache = o.LayerKVCache(Hkv, d, W, post_rope=True)
+        outs, t0 = [], 0
+        for n in cs["chunks"]:
+            outs.append(o.attention_layer_step(q[t0:t0 + n], k[t0:t0 + n], v[t0:t0 + n], cache, **kw))
+            t0 += n
+        got = np.concatenate(outs)
+        n_rot = int(cs["partial"] * (d // 2))
+        want = _brute_layer(q.tolist(), k.tolist(), v.tolist(), [], [], W, kw["theta"], 0, wq.tolist(),
+                            wk.tolist(), 0.0, 1e-6, n_rot=n_rot, v_norm=True, scale=1.0)
+        assert np.max(np.abs(got - want)) < 1e-11, cs
+        # the post-RoPE cache holds V divided by its RMS
+        keep = cache.v.shape[0]
+        rms = np.sqrt(np.mean(cache.v ** 2, axis=-1))
+        assert np.max(np.abs(rms - 1.0)) < 1e-5 and keep == (T if W == 0 else min(T, W - 1))
+
+
+def pin_gemma_torch(o):
+    """The Gemma-4-shaped layers at their real head shapes (「PLaMo 3アーキテクチャ徹底解析」 §8
+    table: local d = 256, Hq = 32, Hkv = 16, W = 1024; global d = 512, Hkv = 4, p-RoPE
+    §6.4), a short sequence in two chunks, against torch float64: F.rms_norm for the Q/K
+    norms (weight = stored gain) and the gainless V norm, the rotation as a complex product
+    over pairs (j, j + d/2) with the frequencies written out, and scaled_dot_product_attention
+    with an explicit mask, scale 1 and enable_gqa. Also: scaling V leaves the output unchanged
+    (the V norm removes it, up to eps)."""
+    import torch.nn.functional as F
+    T = 40
+    for d, Hq, Hkv, W, partial, theta, seed in ((256, 32, 16, 24, 1.0, 1e4, 321),
+                                                 (512, 32, 4, 0, 0.25, 1e6, 322)):
+        q, k, v = _rand((T, Hq, d), seed), _rand((T, Hkv, d), seed + 1), _rand((T, Hkv, d), seed + 2)
+        wq = np.full(d, 1.02)
+        wk = np.full(d, 0.125 if W else 0.0625)
+        kw = _gemma_kw(partial, wq, wk)
+        kw["theta"] = theta
+        cache = o.LayerKVCache(Hkv, d, W, post_rope=True)
+        got = np.concatenate([o.attention_layer_step(q[:29], k[:29], v[:29], cache, **kw),
+                              o.attention_layer_step(q[29:], k[29:], v[29:], cache, **kw)])
+        qt = F.rms_norm(torch.from_numpy(q), (d,), torch.from_numpy(wq), eps=1e-6)
+        kt = F.rms_norm(torch.from_numpy(k), (d,), torch.from_numpy(wk), eps=1e-6)
+        vt = F.rms_norm(torch.from_numpy(v), (d,), None, eps=1e-6)
+        h = d // 2
+        n_rot = int(partial * h)
+        jj = np.arange(h)
+        om = np.where(jj < n_rot, np.exp(-2.0 * jj / d * math.log(theta)), 0.0)
+        rot = torch.from_numpy(np.exp(1j * np.arange(T)[:, None] * om[None, :]))[:, None, :]
+
+        def turn(x):
+            z = torch.complex(x[..., :h], x[..., h:]) * rot
+            return torch.cat([z.real, z.imag], -1)
+
+        mask = torch.ones(T, T, dtype=torch.bool).tril()
+        if W:
+            mask &= ~torch.ones(T, T, dtype=torch.bool).tril(-W)
+        ref = F.scaled_dot_product_attention(turn(qt).permute(1, 0, 2)[None], turn(kt).permute(1, 0, 2)[None],
+                                             vt.permute(1, 0, 2)[None], attn_mask=mask, scale=1.0,
+                                             enable_gqa=True)[0].permute(1, 0, 2).numpy()
+        assert np.max(np.abs(got - ref)) < 1e-11, (d, np.max(np.abs(got - ref)))
+        scaled = o.attention_layer_step(q, k, 7.5 * v, o.LayerKVCache(Hkv, d, W, post_rope=True), **kw)
+        assert np.max(np.abs(scaled - got)) < 1e-5
+
+
 PINS = [pin_worked_example, pin_fig4_masks, pin_sdpa_float64, pin_bruteforce_layer,
         pin_rows_sum_to_one, pin_swa_equals_global_short, pin_uniform_closed_form,
         pin_gqa_grouping, pin_rope_library, pin_rope_complex, pin_rope_shift_invariance,
         pin_yarn_printed, pin_yarn_figure7, pin_rmsnorm, pin_cache_trim,
         pin_decode_equivalence, pin_kv_accounting, pin_legacy_4k_band, pin_post_rope_cache,
-        pin_mixer_bruteforce, pin_mixer_torch]
+        pin_mixer_bruteforce, pin_mixer_torch, pin_p_rope_page, pin_gemma_layer_bruteforce,
+        pin_gemma_torch]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -611,6 +741,15 @@ MISTAKES = {
     "mixer_no_residual": ("return xr + offset_rms_norm(o, w_post, post_offset, eps)",
                           "return offset_rms_norm(o, w_post, post_offset, eps)"),
     "mixer_projection_untransposed": ("qkv = u @ w_qkv.T", "qkv = u @ w_qkv.reshape(w_qkv.shape[1], -1)"),
+    "p_rope_exponent_over_rotated_dims": ("np.power(F64(theta), -2.0 * j / d), 0.0)",
+                                          "np.power(F64(theta), -2.0 * j / (2 * n_rot)), 0.0)"),
+    "p_rope_low_frequency_pairs": ("omega = np.where(j < n_rot,", "omega = np.where(j >= d // 2 - n_rot,"),
+    "p_rope_count_over_head_dim": ("n_rot = int(math.floor(partial * (d // 2)))",
+                                   "n_rot = int(math.floor(partial * d))"),
+    "v_norm_with_k_gain": ("v = v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)",
+                           "v = offset_rms_norm(v, k_norm_w, norm_offset, eps)"),
+    "v_norm_sum_not_mean": ("v = v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)",
+                            "v = v / np.sqrt(np.sum(v * v, axis=-1, keepdims=True) + eps)"),
     "query_positions_from_zero": ("q_pos = np.arange(S - T, S)", "q_pos = np.arange(T)"),
     "default_scale_inverse_d": ("scale = 1.0 / math.sqrt(d)", "scale = 1.0 / d"),
     "weighted_sum_uses_keys": ("out[r0:r1, h, :] = a @ v[:, g, :]", "out[r0:r1, h, :] = a @ k_rot[:, g, :]"),
