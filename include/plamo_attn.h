@@ -28,8 +28,9 @@
  *     reported as PLAMO_ERR_HIP. No C++ exception crosses this boundary.
  *   - dtype PLAMO_BF16: bf16 tensors, fp32 arithmetic inside. PLAMO_F32: fp32
  *     tensors and arithmetic (prefill path only).
- *   - Head dimension d must be 128 (PLaMo 3's head_dim [P3 §2.1]); Hq must be a
- *     multiple of Hkv and Hq/Hkv <= 16.
+ *   - Head dimension d is 128 (PLaMo 3's head_dim [P3 §2.1]), or 256 / 512 for the
+ *     Gemma-4-shaped layers the page compares it with [P3 §8 table] (bf16 only; decode
+ *     then needs a post-RoPE cache). Hq must be a multiple of Hkv and Hq/Hkv <= 16.
  *   - Positions are 64-bit; one pos_offset serves every sequence of the batch
  *     (the *_ragged calls take one position per sequence).
  *   - Entry points hold no mutable global state and may be called from several
@@ -70,14 +71,19 @@ typedef enum { PLAMO_F32 = 0, PLAMO_BF16 = 1 } plamo_dtype;
  * one order only. */
 typedef enum { PLAMO_CACHE_PRE_ROPE = 0, PLAMO_CACHE_POST_ROPE = 1 } plamo_cache_order;
 
-/* RoPE parameters of one layer type [P3 §2.1, §6.2, §6.3].
- * Local layers: theta = 1e4, no YaRN. Global layers: theta = 1e6 with YaRN. */
+/* RoPE parameters of one layer type [P3 §2.1, §6.2, §6.3, §6.4].
+ * PLaMo 3: local layers theta = 1e4, no YaRN; global layers theta = 1e6 with YaRN.
+ * Gemma-4-shaped global layer: theta = 1e6, p-RoPE with partial = 0.25. */
 typedef struct {
   double theta;       /* RoPE base */
   double yarn_factor; /* YaRN factor s; <= 1 disables YaRN (amplitude 1) */
   double orig_ctx;    /* YaRN original context L0 (4096) */
   double beta_fast;   /* 32 */
   double beta_slow;   /* 1 */
+  double partial;     /* p-RoPE [P3 §6.4]: with 0 < p < 1 only the floor(p d/2)
+                         highest-frequency pairs turn (exponent still over d), the others
+                         keep frequency 0; 0 or >= 1 = every pair turns. Not with YaRN
+                         (PLAMO_ERR_UNSUPPORTED). */
 } plamo_rope;
 
 /* ---------------------------------------------------------------------------
@@ -110,7 +116,11 @@ PLAMO_API long long plamo_prefill_padded_len(long long S);
  * q        [B, T, Hq,  d]  projected queries                     (dtype)
  * k, v     [B, T, Hkv, d]  projected keys and values             (dtype)
  * q_norm_w, k_norm_w [d]   stored norm weights w (gain c + w); both NULL = no norm
- * norm_offset, norm_eps    c (1 for q_norm/k_norm [P3 §3.2]) and eps (1e-6)
+ * norm_offset, norm_eps    c (1 for q_norm/k_norm [P3 §3.2]; 0 where the gain is the
+ *                          weight itself, the Gemma-4-shaped layer [P3 §8]) and eps (1e-6)
+ * v_norm   1 = divide each new V head vector by its RMS (eps norm_eps, no gain) before it
+ *          is cached or used (the Gemma-4-shaped layer [P3 §8 table]); 0 = V as given.
+ *          k and v may be the same buffer (that layer's global K = V projection).
  * q_out    [B, T, Hq, d]   normalised and rotated Q                (dtype, required)
  * k_rot_out rotated K of the S = kept + T keys the chunk attends, Tp =
  *                          plamo_prefill_padded_len(S) rows per (b, KV head): rows
@@ -121,13 +131,13 @@ PLAMO_API long long plamo_prefill_padded_len(long long S);
  *                          written. (Prefill operand.) With kept > 0 the caches must be
  *                          given. Layout per (b, KV head):
  *                            fp32: [Tp][d];
- *                            bf16: Tp/64 tiles of 64 tokens, tile = [16][64][8]
- *                                  (dim / 8, token in tile, dim % 8), 16 KiB.
+ *                            bf16: Tp/64 tiles of 64 tokens, tile = [d/8][64][8]
+ *                                  (dim / 8, token in tile, dim % 8), 128 d bytes.
  * v_t_out  V of the same S keys (cached, then new) transposed, pad zeroed. NULL = not
  *                          written. (Prefill operand.) Layout
  *                          per (b, KV head):
  *                            fp32: [d][Tp] (token index fastest);
- *                            bf16: Tp/64 tiles, tile = [8][128][8]
+ *                            bf16: Tp/64 tiles, tile = [8][d][8]
  *                                  (token in tile / 8, dim, token % 8), 16 KiB.
  *                          Either operand occupies B*Hkv*Tp*d elements.
  * k_cache, v_cache [B, Hkv, cap, d]  normalised pre-RoPE K and raw V (dtype). NULL
@@ -145,7 +155,7 @@ PLAMO_API long long plamo_prefill_padded_len(long long S);
  * ------------------------------------------------------------------------- */
 PLAMO_API int plamo_kv_append(int dtype, const void* q, const void* k, const void* v,
                     const void* q_norm_w, const void* k_norm_w, float norm_offset,
-                    float norm_eps, void* q_out, void* k_rot_out, void* v_t_out,
+                    float norm_eps, int v_norm, void* q_out, void* k_rot_out, void* v_t_out,
                     void* k_cache, void* v_cache, long long cap, int B, int T, int Hq,
                     int Hkv, int d, int window, long long pos_offset,
                     const void* rope_table, size_t rope_table_bytes, int cache_order,
@@ -161,8 +171,9 @@ PLAMO_API int plamo_kv_append(int dtype, const void* q, const void* k, const voi
  * [P3 §4.5]). Query t (0..T-1) sits at renumbered position i = kept + t and
  * attends operand keys j <= i, and i - j < window when window > 0: a chunk after
  * pos_offset cached tokens sees the cached keys first, then its own causally.
- * softmax_scale is 1/sqrt(d) [P3 §4.5]; the YaRN amplitude is already in q_rot
- * and k_rot. bf16: kept + T <= 2^22 (PLAMO_ERR_UNSUPPORTED beyond).
+ * softmax_scale is 1/sqrt(d) [P3 §4.5] (1 for the Gemma-4-shaped layers [P3 §8
+ * table]); the YaRN amplitude is already in q_rot and k_rot. bf16: (kept + T) * d <=
+ * 2^29 (PLAMO_ERR_UNSUPPORTED beyond).
  * ------------------------------------------------------------------------- */
 PLAMO_API int plamo_attn_prefill(int dtype, const void* q_rot, const void* k_rot, const void* v_t,
                        void* out, int B, int T, int Hq, int Hkv, int d, int window,
@@ -230,7 +241,7 @@ PLAMO_API size_t plamo_attn_decode_ragged_workspace_bytes(int B, int Hq, int Hkv
 
 PLAMO_API int plamo_kv_append_ragged(int dtype, const void* q, const void* k, const void* v,
                     const void* q_norm_w, const void* k_norm_w, float norm_offset,
-                    float norm_eps, void* q_out, void* k_rot_out, void* v_t_out,
+                    float norm_eps, int v_norm, void* q_out, void* k_rot_out, void* v_t_out,
                     void* k_cache, void* v_cache, long long cap, int B, int T, int Hq,
                     int Hkv, int d, int window, const long long* seq_pos_offsets,
                     const int* seq_lens, long long max_pos_offset, const void* rope_table,

@@ -43,15 +43,19 @@ class PlamoError(RuntimeError):
 
 @dataclass(frozen=True)
 class RopeParams:
-    """RoPE of one layer type: base theta, YaRN factor (<= 1 = off), L0, beta_fast, beta_slow."""
+    """RoPE of one layer type: base theta, YaRN factor (<= 1 = off), L0, beta_fast, beta_slow, and
+    the p-RoPE fraction ``partial`` (0 < p < 1: only the floor(p d/2) highest-frequency pairs turn;
+    0 = all)."""
     theta: float
     yarn_factor: float = 0.0
     orig_ctx: float = 4096.0
     beta_fast: float = 32.0
     beta_slow: float = 1.0
+    partial: float = 0.0
 
     def c_struct(self) -> PlamoRope:
-        return PlamoRope(self.theta, self.yarn_factor, self.orig_ctx, self.beta_fast, self.beta_slow)
+        return PlamoRope(self.theta, self.yarn_factor, self.orig_ctx, self.beta_fast, self.beta_slow,
+                         self.partial)
 
 
 LOCAL_ROPE = RopeParams(theta=1e4)
@@ -115,13 +119,13 @@ def plamo_rope_table_init(table: torch.Tensor, max_pos: int, rope: RopeParams, d
     _check(st, "plamo_rope_table_init")
 
 
-def make_rope_table(max_pos: int, rope: RopeParams, device="cuda", stream=None) -> torch.Tensor:
-    """Allocate (torch) and fill a rope table covering positions [0, max_pos)."""
-    nbytes = plamo_rope_table_bytes(max_pos)
+def make_rope_table(max_pos: int, rope: RopeParams, device="cuda", stream=None, d: int = HEAD_DIM) -> torch.Tensor:
+    """Allocate (torch) and fill a rope table covering positions [0, max_pos) for head dim d."""
+    nbytes = plamo_rope_table_bytes(max_pos, d)
     if nbytes == 0:
-        raise ValueError("bad max_pos")
+        raise ValueError("bad max_pos or head dim")
     table = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
-    plamo_rope_table_init(table, max_pos, rope, stream=stream)
+    plamo_rope_table_init(table, max_pos, rope, d=d, stream=stream)
     return table
 
 
@@ -163,8 +167,9 @@ def prefill_operand_shapes(B: int, T: int, Hkv: int, d: int, dtype, window: int 
 def plamo_kv_append(q, k, v, q_out, *, window: int, pos_offset: int, rope_table,
                     q_norm_w=None, k_norm_w=None, norm_offset: float = 1.0, norm_eps: float = 1e-6,
                     k_rot_out=None, v_t_out=None, k_cache=None, v_cache=None, cache_post_rope: bool = False,
-                    stream=None) -> None:
-    """q [B,T,Hq,d], k/v [B,T,Hkv,d]; outputs as documented in plamo_attn.h."""
+                    v_norm: bool = False, stream=None) -> None:
+    """q [B,T,Hq,d], k/v [B,T,Hkv,d] (k and v may be one tensor); outputs as documented in
+    plamo_attn.h. v_norm: divide each V head vector by its RMS first."""
     dt = q.dtype
     B, T, Hq, d = q.shape
     Hkv = k.shape[2]
@@ -185,7 +190,7 @@ def plamo_kv_append(q, k, v, q_out, *, window: int, pos_offset: int, rope_table,
     st = _lib.load().plamo_kv_append(
         _dtype_code(dt), _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt),
         _dev(q_norm_w, "q_norm_w", dt), _dev(k_norm_w, "k_norm_w", dt), float(norm_offset), float(norm_eps),
-        _dev(q_out, "q_out", dt), _dev(k_rot_out, "k_rot_out", dt), _dev(v_t_out, "v_t_out", dt),
+        int(bool(v_norm)), _dev(q_out, "q_out", dt), _dev(k_rot_out, "k_rot_out", dt), _dev(v_t_out, "v_t_out", dt),
         _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), int(cap), B, T, Hq, Hkv, d,
         int(window), int(pos_offset), _dev(rope_table, "rope_table", torch.float32),
         rope_table.numel() * 4, _order(cache_post_rope), _stream(stream))
@@ -251,7 +256,8 @@ def _ragged_arrays(B: int, seq_pos_offsets, seq_lens):
 def plamo_kv_append_ragged(q, k, v, q_out, *, window: int, seq_pos_offsets, max_pos_offset: int,
                            rope_table, seq_lens=None, q_norm_w=None, k_norm_w=None,
                            norm_offset: float = 1.0, norm_eps: float = 1e-6, k_rot_out=None, v_t_out=None,
-                           k_cache=None, v_cache=None, cache_post_rope: bool = False, stream=None) -> None:
+                           k_cache=None, v_cache=None, cache_post_rope: bool = False, v_norm: bool = False,
+                           stream=None) -> None:
     """plamo_kv_append with per-sequence positions seq_pos_offsets [B] (int64, GPU) bounded by
     max_pos_offset and token counts seq_lens [B] (int32, GPU; None = T each)."""
     dt = q.dtype
@@ -275,7 +281,7 @@ def plamo_kv_append_ragged(q, k, v, q_out, *, window: int, seq_pos_offsets, max_
     st = _lib.load().plamo_kv_append_ragged(
         _dtype_code(dt), _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt),
         _dev(q_norm_w, "q_norm_w", dt), _dev(k_norm_w, "k_norm_w", dt), float(norm_offset), float(norm_eps),
-        _dev(q_out, "q_out", dt), _dev(k_rot_out, "k_rot_out", dt), _dev(v_t_out, "v_t_out", dt),
+        int(bool(v_norm)), _dev(q_out, "q_out", dt), _dev(k_rot_out, "k_rot_out", dt), _dev(v_t_out, "v_t_out", dt),
         _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), int(cap), B, T, Hq, Hkv, d,
         int(window), pos_p, len_p, int(max_pos_offset), _dev(rope_table, "rope_table", torch.float32),
         rope_table.numel() * 4, _order(cache_post_rope), _stream(stream))

@@ -14,7 +14,7 @@ c_int, c_ll, c_size, c_float, c_void_p = (ctypes.c_int, ctypes.c_longlong, ctype
 class PlamoRope(ctypes.Structure):
     _fields_ = [("theta", ctypes.c_double), ("yarn_factor", ctypes.c_double),
                 ("orig_ctx", ctypes.c_double), ("beta_fast", ctypes.c_double),
-                ("beta_slow", ctypes.c_double)]
+                ("beta_slow", ctypes.c_double), ("partial", ctypes.c_double)]
 
 
 # name -> (restype, argtypes), mirroring include/plamo_attn.h
@@ -23,7 +23,7 @@ SIGNATURES = {
     "plamo_rope_table_init": (c_int, [c_void_p, c_size, c_ll, c_int, ctypes.POINTER(PlamoRope), c_void_p]),
     "plamo_prefill_padded_len": (c_ll, [c_ll]),
     "plamo_kv_append": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_float,
-                                c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_ll, c_int, c_int, c_int,
+                                c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_ll, c_int, c_int, c_int,
                                 c_int, c_int, c_int, c_ll, c_void_p, c_size, c_int, c_void_p]),
     "plamo_attn_prefill": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                    c_int, c_int, c_ll, c_float, c_void_p]),
@@ -32,7 +32,7 @@ SIGNATURES = {
                                   c_int, c_int, c_int, c_int, c_int, c_ll, c_void_p, c_size, c_float, c_int,
                                   c_void_p]),
     "plamo_kv_append_ragged": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_float,
-                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_ll, c_int, c_int,
+                                       c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_ll, c_int, c_int,
                                        c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_ll, c_void_p, c_size,
                                        c_int, c_void_p]),
     "plamo_attn_prefill_ragged": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,

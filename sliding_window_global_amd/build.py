@@ -20,12 +20,12 @@ LIB_NAME = "libplamo_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["rope_table.hip", "append.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "norm.hip",
-           "gemm.hip", "abi.cpp"]
+SOURCES = ["rope_table.hip", "append.hip", "prefill_bf16.hip", "prefill_wide.hip", "prefill_f32.hip", "decode.hip",
+           "decode_wide.hip", "norm.hip", "gemm.hip", "abi.cpp"]
 LINK_LIBS: list[str] = []
 # The bf16 prefill's softmax only ever sees finite or -inf scores: without NaN semantics
 # its running-max chain compiles to bare v_max3 (no input canonicalisation).
-EXTRA_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"]}
+EXTRA_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"], "prefill_wide.hip": ["-fno-honor-nans"]}
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

@@ -29,12 +29,17 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int kHeadDim = 128;
 constexpr long long kFine = 64;
 constexpr long long kPad = 128;
-constexpr size_t kRowBytes = (kHeadDim / 2) * 2 * sizeof(float);  // one table row
+
+// Head dims with kernels: PLaMo 3's 128, and 256 / 512 (the Gemma-4-shaped layers, bf16).
+bool known_head_dim(int d) { return d == 128 || d == 256 || d == 512; }
+
+// Bytes of one rope-table row: d/2 (cos, sin) pairs.
+size_t row_bytes(int d) { return static_cast<size_t>(d / 2) * 2 * sizeof(float); }
 
 // Positions [0, covered) that a table of `bytes` bytes can rotate.
-long long table_positions(size_t bytes) {
-  if (bytes % kRowBytes) return -1;
-  const long long rows = static_cast<long long>(bytes / kRowBytes);
+long long table_positions(size_t bytes, int d) {
+  if (bytes % row_bytes(d)) return -1;
+  const long long rows = static_cast<long long>(bytes / row_bytes(d));
   if (rows <= kFine) return 0;
   return (rows - kFine) * kFine;
 }
@@ -42,7 +47,8 @@ long long table_positions(size_t bytes) {
 // Checks shared by every attention entry point; returns PLAMO_OK or an error status.
 int check_heads(int B, int T, int Hq, int Hkv, int d, int window, long long pos_offset) {
   if (B < 0 || T < 0) return fail(PLAMO_ERR_INVALID_ARG, "B and T must be >= 0");
-  if (d != kHeadDim) return fail(d > 0 ? PLAMO_ERR_UNSUPPORTED : PLAMO_ERR_INVALID_ARG, "head dim must be 128");
+  if (!known_head_dim(d))
+    return fail(d > 0 ? PLAMO_ERR_UNSUPPORTED : PLAMO_ERR_INVALID_ARG, "head dim must be 128, 256 or 512");
   if (Hq < 1 || Hkv < 1) return fail(PLAMO_ERR_INVALID_ARG, "Hq and Hkv must be >= 1");
   if (Hq % Hkv) return fail(PLAMO_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
   if (Hq / Hkv > 16) return fail(PLAMO_ERR_UNSUPPORTED, "Hq/Hkv must be <= 16");
@@ -87,14 +93,15 @@ long long plamo_prefill_padded_len(long long T) {
 }
 
 size_t plamo_rope_table_bytes(long long max_pos, int d) {
-  if (max_pos < 1 || d != kHeadDim || max_pos > (1LL << 40)) return 0;
+  if (max_pos < 1 || !known_head_dim(d) || max_pos > (1LL << 40)) return 0;
   const long long coarse = (max_pos + kFine - 1) / kFine;
-  return static_cast<size_t>(kFine + coarse) * kRowBytes;
+  return static_cast<size_t>(kFine + coarse) * row_bytes(d);
 }
 
 int plamo_rope_table_init(void* table, size_t table_bytes, long long max_pos, int d,
                           const plamo_rope* rope, void* stream) {
-  if (d != kHeadDim) return fail(d > 0 ? PLAMO_ERR_UNSUPPORTED : PLAMO_ERR_INVALID_ARG, "head dim must be 128");
+  if (!known_head_dim(d))
+    return fail(d > 0 ? PLAMO_ERR_UNSUPPORTED : PLAMO_ERR_INVALID_ARG, "head dim must be 128, 256 or 512");
   if (max_pos < 1 || max_pos > (1LL << 40)) return fail(PLAMO_ERR_INVALID_ARG, "max_pos must be in [1, 2^40]");
   if (!table || !rope) return fail(PLAMO_ERR_INVALID_ARG, "table and rope must be non-NULL");
   if (!aligned16(table)) return fail(PLAMO_ERR_INVALID_ARG, "table must be 16-byte aligned");
@@ -114,9 +121,17 @@ int plamo_rope_table_init(void* table, size_t table_bytes, long long max_pos, in
   } else {
     s = 0.0;
   }
+  // 「PLaMo 3アーキテクチャ徹底解析」 §6.4 (p-RoPE): floor(p d/2) pairs turn
+  int n_rot = d / 2;
+  const double p = rope->partial;
+  if (!(p >= 0.0) || !std::isfinite(p)) return fail(PLAMO_ERR_INVALID_ARG, "partial must be >= 0");
+  if (p > 0.0 && p < 1.0) {
+    if (s > 1.0) return fail(PLAMO_ERR_UNSUPPORTED, "p-RoPE is not combined with YaRN");
+    n_rot = static_cast<int>(std::floor(p * (d / 2)));
+  }
   const long long coarse = (max_pos + kFine - 1) / kFine;
   return launched(plamo::launch_rope_table(static_cast<float2*>(table), coarse, d, rope->theta, s,
-                                           j_low, j_high, amp, static_cast<hipStream_t>(stream)));
+                                           j_low, j_high, amp, n_rot, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"
@@ -133,7 +148,7 @@ int check_ragged(const long long* seq_pos, const int* seq_len) {
 
 // pos_offset is the batch's position (uniform) or the bound of every seq_pos entry (ragged).
 int kv_append_impl(int dtype, const void* q, const void* k, const void* v, const void* q_norm_w,
-                   const void* k_norm_w, float norm_offset, float norm_eps, void* q_out,
+                   const void* k_norm_w, float norm_offset, float norm_eps, int v_norm, void* q_out,
                    void* k_rot_out, void* v_t_out, void* k_cache, void* v_cache, long long cap,
                    int B, int T, int Hq, int Hkv, int d, int window, long long pos_offset,
                    const long long* seq_pos, const int* seq_len, const void* rope_table,
@@ -142,6 +157,8 @@ int kv_append_impl(int dtype, const void* q, const void* k, const void* v, const
   if (cache_order != PLAMO_CACHE_PRE_ROPE && cache_order != PLAMO_CACHE_POST_ROPE)
     return fail(PLAMO_ERR_INVALID_ARG, "unknown cache_order");
   if (int st = check_heads(B, T, Hq, Hkv, d, window, pos_offset)) return st;
+  if (d != kHeadDim && dtype != PLAMO_BF16) return fail(PLAMO_ERR_UNSUPPORTED, "head dims 256 and 512 are bf16 only");
+  if (v_norm != 0 && v_norm != 1) return fail(PLAMO_ERR_INVALID_ARG, "v_norm must be 0 or 1");
   if (B == 0 || T == 0) return ok();
   if (!q || !k || !v || !q_out) return fail(PLAMO_ERR_INVALID_ARG, "q, k, v and q_out must be non-NULL");
   if ((q_norm_w == nullptr) != (k_norm_w == nullptr))
@@ -160,7 +177,7 @@ int kv_append_impl(int dtype, const void* q, const void* k, const void* v, const
   if (kept > 0 && (k_rot_out || v_t_out) && !k_cache)
     return fail(PLAMO_ERR_INVALID_ARG, "prefill operands after cached tokens need the caches");
   if (!rope_table) return fail(PLAMO_ERR_INVALID_ARG, "rope_table must be non-NULL");
-  const long long covered = table_positions(rope_table_bytes);
+  const long long covered = table_positions(rope_table_bytes, d);
   if (covered < 0) return fail(PLAMO_ERR_INVALID_ARG, "rope_table_bytes is not a whole number of rows");
   const bool post = cache_order == PLAMO_CACHE_POST_ROPE;
   if (!post && covered < kept + T) return fail(PLAMO_ERR_WORKSPACE, "rope table does not cover positions < kept + T");
@@ -178,6 +195,8 @@ int kv_append_impl(int dtype, const void* q, const void* k, const void* v, const
   a.seq_pos = seq_pos; a.seq_len = seq_len;
   a.ops_kernel = (k_rot_out || v_t_out) && (kept > 0 || seq_pos || seq_len);
   a.post_rope = post;
+  a.v_norm = v_norm != 0;
+  a.d = d;
   a.rope = static_cast<const float2*>(rope_table);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return launched(dtype == PLAMO_BF16 ? plamo::launch_kv_append_bf16(a, s) : plamo::launch_kv_append_f32(a, s));
@@ -188,18 +207,20 @@ int attn_prefill_impl(int dtype, const void* q_rot, const void* k_rot, const voi
                       const long long* seq_pos, const int* seq_len, float softmax_scale, void* stream) {
   if (dtype != PLAMO_F32 && dtype != PLAMO_BF16) return fail(PLAMO_ERR_INVALID_ARG, "unknown dtype");
   if (int st = check_heads(B, T, Hq, Hkv, d, window, pos_offset)) return st;
+  if (d != kHeadDim && dtype != PLAMO_BF16) return fail(PLAMO_ERR_UNSUPPORTED, "head dims 256 and 512 are bf16 only");
   if (B == 0 || T == 0) return ok();
   const long long kept = kept_tokens(window, pos_offset);
   if (kept + T > (1LL << 30)) return fail(PLAMO_ERR_UNSUPPORTED, "kept + T must be <= 2^30");
   // bf16 operand tiles are addressed with 32-bit buffer offsets within one (b, KV head)
-  if (dtype == PLAMO_BF16 && kept + T > (1LL << 22))
-    return fail(PLAMO_ERR_UNSUPPORTED, "bf16 prefill needs kept + T <= 2^22");
+  if (dtype == PLAMO_BF16 && (kept + T) * d > (1LL << 29))
+    return fail(PLAMO_ERR_UNSUPPORTED, "bf16 prefill needs (kept + T) * d <= 2^29");
   if (!q_rot || !k_rot || !v_t || !out) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be non-NULL");
   const void* ptrs[] = {q_rot, k_rot, v_t, out};
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return fail(PLAMO_ERR_INVALID_ARG, "softmax_scale must be > 0");
-  const long long blocks = (static_cast<long long>(T) + 127) / 128 * Hq * static_cast<long long>(B);
+  const int rows_per_block = d == 512 ? 64 : 128;
+  const long long blocks = (static_cast<long long>(T) + rows_per_block - 1) / rows_per_block * Hq * static_cast<long long>(B);
   if (blocks > 0x7fffffffLL) return fail(PLAMO_ERR_UNSUPPORTED, "grid too large");
 
   plamo::PrefillArgs a;
@@ -210,7 +231,9 @@ int attn_prefill_impl(int dtype, const void* q_rot, const void* k_rot, const voi
   a.pos_offset = pos_offset;
   a.seq_pos = seq_pos; a.seq_len = seq_len;
   a.scale = softmax_scale;
+  a.d = d;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d != kHeadDim) return launched(plamo::launch_prefill_wide_bf16(a, s));
   return launched(dtype == PLAMO_BF16 ? plamo::launch_prefill_bf16(a, s) : plamo::launch_prefill_f32(a, s));
 }
 
@@ -226,6 +249,8 @@ int attn_decode_impl(int dtype, const void* q_rot, const void* k_cache, const vo
   if (cache_order != PLAMO_CACHE_PRE_ROPE && cache_order != PLAMO_CACHE_POST_ROPE)
     return fail(PLAMO_ERR_INVALID_ARG, "unknown cache_order");
   const bool post = cache_order == PLAMO_CACHE_POST_ROPE;
+  if (d != kHeadDim && !post)
+    return fail(PLAMO_ERR_UNSUPPORTED, "head dims 256 and 512 decode from a post-RoPE cache");
   if (B == 0) return ok();
   if (!q_rot || !k_cache || !v_cache || !out || (!rope_table && !post))
     return fail(PLAMO_ERR_INVALID_ARG, "q_rot, caches, out and rope_table must be non-NULL");
@@ -238,12 +263,12 @@ int attn_decode_impl(int dtype, const void* q_rot, const void* k_cache, const vo
   const long long kept = kept_tokens(window, pos_offset);
   const long long S = kept + 1;
   if (!post) {  // a post-RoPE cache is read as stored: no table
-    const long long covered = table_positions(rope_table_bytes);
+    const long long covered = table_positions(rope_table_bytes, d);
     if (covered < 0) return fail(PLAMO_ERR_INVALID_ARG, "rope_table_bytes is not a whole number of rows");
     if (covered < S) return fail(PLAMO_ERR_WORKSPACE, "rope table does not cover positions < kept + 1");
   }
   const plamo::DecodePlan plan = plamo::plan_decode(B, Hkv, S, seq_pos != nullptr);
-  const size_t need = plamo::decode_workspace_bytes(B, Hq, plan);
+  const size_t need = plamo::decode_workspace_bytes(B, Hq, d, plan);
   if (need > 0 && (!workspace || workspace_bytes < need)) return fail(PLAMO_ERR_WORKSPACE, "workspace too small");
   if (static_cast<long long>(B) * Hq > 0x7fffffffLL) return fail(PLAMO_ERR_UNSUPPORTED, "grid too large");
 
@@ -256,7 +281,9 @@ int attn_decode_impl(int dtype, const void* q_rot, const void* k_cache, const vo
   a.post_rope = post;
   a.rope = static_cast<const float2*>(rope_table);
   a.scale = softmax_scale;
-  return launched(plamo::launch_decode_bf16(a, static_cast<hipStream_t>(stream)));
+  a.d = d;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launched(d != kHeadDim ? plamo::launch_decode_wide_bf16(a, s) : plamo::launch_decode_bf16(a, s));
 }
 
 }  // namespace
@@ -264,17 +291,17 @@ int attn_decode_impl(int dtype, const void* q_rot, const void* k_cache, const vo
 extern "C" {
 
 int plamo_kv_append(int dtype, const void* q, const void* k, const void* v, const void* q_norm_w,
-                    const void* k_norm_w, float norm_offset, float norm_eps, void* q_out,
+                    const void* k_norm_w, float norm_offset, float norm_eps, int v_norm, void* q_out,
                     void* k_rot_out, void* v_t_out, void* k_cache, void* v_cache, long long cap,
                     int B, int T, int Hq, int Hkv, int d, int window, long long pos_offset,
                     const void* rope_table, size_t rope_table_bytes, int cache_order, void* stream) {
-  return kv_append_impl(dtype, q, k, v, q_norm_w, k_norm_w, norm_offset, norm_eps, q_out, k_rot_out,
+  return kv_append_impl(dtype, q, k, v, q_norm_w, k_norm_w, norm_offset, norm_eps, v_norm, q_out, k_rot_out,
                         v_t_out, k_cache, v_cache, cap, B, T, Hq, Hkv, d, window, pos_offset, nullptr,
                         nullptr, rope_table, rope_table_bytes, cache_order, stream);
 }
 
 int plamo_kv_append_ragged(int dtype, const void* q, const void* k, const void* v, const void* q_norm_w,
-                           const void* k_norm_w, float norm_offset, float norm_eps, void* q_out,
+                           const void* k_norm_w, float norm_offset, float norm_eps, int v_norm, void* q_out,
                            void* k_rot_out, void* v_t_out, void* k_cache, void* v_cache, long long cap,
                            int B, int T, int Hq, int Hkv, int d, int window,
                            const long long* seq_pos_offsets, const int* seq_lens,
@@ -282,7 +309,7 @@ int plamo_kv_append_ragged(int dtype, const void* q, const void* k, const void* 
                            int cache_order, void* stream) {
   if (B > 0 && T > 0)
     if (int st = check_ragged(seq_pos_offsets, seq_lens)) return st;
-  return kv_append_impl(dtype, q, k, v, q_norm_w, k_norm_w, norm_offset, norm_eps, q_out, k_rot_out,
+  return kv_append_impl(dtype, q, k, v, q_norm_w, k_norm_w, norm_offset, norm_eps, v_norm, q_out, k_rot_out,
                         v_t_out, k_cache, v_cache, cap, B, T, Hq, Hkv, d, window, max_pos_offset,
                         seq_pos_offsets, seq_lens, rope_table, rope_table_bytes, cache_order, stream);
 }
@@ -308,7 +335,7 @@ size_t plamo_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int wind
   if (check_heads(B, 1, Hq, Hkv, d, window, pos_offset) != PLAMO_OK) return 0;
   if (B == 0) return 0;
   const long long S = kept_tokens(window, pos_offset) + 1;
-  return plamo::decode_workspace_bytes(B, Hq, plamo::plan_decode(B, Hkv, S, false));
+  return plamo::decode_workspace_bytes(B, Hq, d, plamo::plan_decode(B, Hkv, S, false));
 }
 
 size_t plamo_attn_decode_ragged_workspace_bytes(int B, int Hq, int Hkv, int d, int window,
@@ -316,7 +343,7 @@ size_t plamo_attn_decode_ragged_workspace_bytes(int B, int Hq, int Hkv, int d, i
   if (check_heads(B, 1, Hq, Hkv, d, window, max_pos_offset) != PLAMO_OK) return 0;
   if (B == 0) return 0;
   const long long S = kept_tokens(window, max_pos_offset) + 1;
-  return plamo::decode_workspace_bytes(B, Hq, plamo::plan_decode(B, Hkv, S, true));
+  return plamo::decode_workspace_bytes(B, Hq, d, plamo::plan_decode(B, Hkv, S, true));
 }
 
 int plamo_attn_decode(int dtype, const void* q_rot, const void* k_cache, const void* v_cache,

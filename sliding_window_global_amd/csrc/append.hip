@@ -8,17 +8,22 @@
 //              current Q and the K the cache returns, at renumbered positions.
 //   §6.1/§6.3  split-half pairs (j, j + 64); rotation factors from the two-level table.
 //
-// One block = 64 tokens of one sequence and one KV head: its G = Hq/Hkv query heads,
-// the K head and the V head. The block first forms the rotation factors of its 64
-// positions in LDS. A row (one token of one head) is handled by a group of lanes, each
-// holding one 16-byte chunk of the first half and the matching chunk of the second
-// half, so every rotation pair is lane-local and the norm is a reduction over the
-// group. V is staged through LDS to write the transposed prefill operand with
-// full rows.
+// Head dims 256 and 512 (the Gemma-4-shaped layers of the same page's §8 table) run the
+// same code: gain-only norms are offset 0, p-RoPE (§6.4) is a table whose idle pairs
+// hold (1, 0), and the optional V norm divides each V head vector by its RMS before it
+// is cached or used.
 //
-// bf16 prefill operands are tiled by 64 keys, each tile 16 KiB in the order the prefill
-// kernel copies straight into LDS: K' tile = [16 dim chunks][64 keys][8 dims], V^T tile =
-// [8 key chunks][128 dims][8 keys]. fp32 operands are plain [Tp][d] and [d][Tp].
+// One block = 64 tokens of one sequence and one KV head: its G = Hq/Hkv query heads,
+// the K head and the V head. With d = 128 the block first forms the rotation factors of
+// its 64 positions in LDS; wider heads read them from the table as they go (64 positions
+// of 256 pairs would not fit). A row (one token of one head) is handled by a group of
+// lanes, each holding one 16-byte chunk of the first half and the matching chunk of the
+// second half, so every rotation pair is lane-local and the norm is a reduction over the
+// group. V is staged through LDS to write the transposed prefill operand with full rows.
+//
+// bf16 prefill operands are tiled by 64 keys, each tile 64 d bf16 in the order the prefill
+// kernels copy straight into LDS: K' tile = [d/8 dim chunks][64 keys][8 dims], V^T tile =
+// [8 key chunks][d dims][8 keys]. fp32 operands are plain [Tp][d] and [d][Tp].
 #include "common.h"
 #include "kernels.h"
 
@@ -31,15 +36,17 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
 // One LDS area per block, used first for the rotation factors of the block's 64 positions
-// ([64][64] float2, 32 KiB) and afterwards, behind a barrier, for the V^T staging tile
-// ([128 dims][64 + 16/sizeof(E) tokens]). Sharing it keeps a block within 36 KiB, so that
-// four blocks (all of a 64-token x 8-KV-head step) fit on a CU.
+// (d = 128 only: [64][64] float2, 32 KiB) and afterwards, behind a barrier, for the V^T
+// staging tile ([d dims][64 + 16/sizeof(E) tokens]). Sharing it keeps a d = 128 block
+// within 36 KiB, so that four blocks (all of a 64-token x 8-KV-head step) fit on a CU.
 template <typename E>
 constexpr int kTileStride = kTokBlock + 16 / static_cast<int>(sizeof(E));  // tokens, 16-byte rows
-template <typename E>
-constexpr int kSmemBytes = kTokBlock * kHalf * 8 > kHeadDim * kTileStride<E> * static_cast<int>(sizeof(E))
-                               ? kTokBlock * kHalf * 8
-                               : kHeadDim * kTileStride<E> * static_cast<int>(sizeof(E));
+template <int D>
+constexpr bool kStageRope = D == kHeadDim;
+template <typename E, int D>
+constexpr int kSmemBytes = (kStageRope<D> ? kTokBlock * (D / 2) * 8 : 0) > D * kTileStride<E> * static_cast<int>(sizeof(E))
+                               ? kTokBlock * (D / 2) * 8
+                               : D * kTileStride<E> * static_cast<int>(sizeof(E));
 
 template <typename E>
 struct Io;
@@ -74,15 +81,46 @@ struct Io<bf16_t> {
   }
 };
 
+// A 16-byte chunk of one V row times s (the inverse RMS of the row, V norm), rounded back
+// to the storage type.
 template <typename E>
+__device__ __forceinline__ u32x4 scaled_chunk(u32x4 w, float s) {
+  float x[16 / sizeof(E)];
+  Io<E>::unpack(w, x);
+#pragma unroll
+  for (int e = 0; e < static_cast<int>(16 / sizeof(E)); ++e) x[e] *= s;
+  return Io<E>::pack(x);
+}
+
+// V norm: v_inv[r] = 1 / sqrt(mean(V_r^2) + eps) for rows r < n of `src` (row r at
+// src + r * stride), one wave per row.
+template <typename E, int D>
+__device__ __forceinline__ void v_row_inv_rms(const E* __restrict__ src, long long stride, int n, float eps,
+                                              float* v_inv, int wave, int lane) {
+  for (int r = wave; r < n; r += kWaves) {
+    const E* row = src + r * stride;
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) {
+      const float x = Io<E>::ld(row + e * 64 + lane);
+      s += x * x;
+    }
+    s = wave_sum(s);
+    if (lane == 0) v_inv[r] = rsqrtf(s * (1.f / D) + eps);
+  }
+}
+
+template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
+  constexpr int kH = D / 2;                     // rotation pairs
   constexpr int kVec = 16 / sizeof(E);          // elements per 16-byte chunk
-  constexpr int kLanesPerRow = kHalf / kVec;    // 8 (bf16) or 16 (fp32)
+  constexpr int kLanesPerRow = kH / kVec;       // d = 128: 8 (bf16) or 16 (fp32)
   constexpr int kRowsPerPass = 64 / kLanesPerRow;
   constexpr int kUnroll = 2;
   constexpr bool kTiled = sizeof(E) == 2;      // bf16 prefill operands are tiled
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes<E>];
-  float2 (*zs)[kHalf] = reinterpret_cast<float2 (*)[kHalf]>(smem);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes<E, D>];
+  __shared__ float v_inv[kTokBlock];
+  float2 (*zs)[kH] = reinterpret_cast<float2 (*)[kH]>(smem);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -111,16 +149,21 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   // rotation factors of this block's renumbered positions kept + t (post-RoPE cache:
   // absolute positions pos + t)
   const long long p_first = a.post_rope ? sp.pos : sp.kept;
-  for (int i = threadIdx.x; i < kTokBlock * kHalf; i += kThreads) {
-    const int r = i / kHalf, j = i % kHalf;
-    if (r < n_tok) zs[r][j] = rope_factor(a.rope, p_first + t0 + r, j);
+  if (kStageRope<D>) {
+    for (int i = threadIdx.x; i < kTokBlock * kH; i += kThreads) {
+      const int r = i / kH, j = i % kH;
+      if (r < n_tok) zs[r][j] = rope_factor<kH>(a.rope, p_first + t0 + r, j);
+    }
   }
+  if (a.v_norm && n_tok > 0)
+    v_row_inv_rms<E, D>(v + ((static_cast<long long>(b) * a.T + t0) * a.Hkv + kvh) * D,
+                        static_cast<long long>(a.Hkv) * D, n_tok, a.eps, v_inv, wave, lane);
   float gq[2 * kVec], gk[2 * kVec];  // gains c + w of this lane's dims (both halves)
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int e = 0; e < kVec; ++e) {
-      const int dim = h * kHalf + c * kVec + e;
+      const int dim = h * kH + c * kVec + e;
       gq[h * kVec + e] = norm ? a.norm_offset + Io<E>::ld(wq + dim) : 1.f;
       gk[h * kVec + e] = norm ? a.norm_offset + Io<E>::ld(wk + dim) : 1.f;
     }
@@ -144,9 +187,9 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
         tt[u] = is_k ? r : r / G;
         const int head = is_k ? kvh : kvh * G + r % G;
         const int H = is_k ? a.Hkv : a.Hq;
-        off[u] = ((static_cast<long long>(b) * a.T + t0 + tt[u]) * H + head) * kHeadDim + c * kVec;
+        off[u] = ((static_cast<long long>(b) * a.T + t0 + tt[u]) * H + head) * D + c * kVec;
         const u32x4 w0 = *reinterpret_cast<const u32x4*>(src + off[u]);
-        const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + off[u] + kHalf);
+        const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + off[u] + kH);
         Io<E>::unpack(w0, x[u]);
         Io<E>::unpack(w1, x[u] + kVec);
         float s = 0.f;
@@ -166,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
         if (r >= n_rows) continue;
         const int t = t0 + tt[u];
         if (norm) {
-          const float inv = rsqrtf(ss[u] * (1.f / kHeadDim) + a.eps);
+          const float inv = rsqrtf(ss[u] * (1.f / D) + a.eps);
 #pragma unroll
           for (int e = 0; e < 2 * kVec; ++e) x[u][e] *= inv * g[e];
         }
@@ -175,21 +218,22 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
         if (to_cache) {
           const long long n = sp.pos + t;
           const long long s = a.window == 0 ? n : n % a.window;
-          cdst = k_cache + ((static_cast<long long>(b) * a.Hkv + kvh) * a.cap + s) * kHeadDim + c * kVec;
+          cdst = k_cache + ((static_cast<long long>(b) * a.Hkv + kvh) * a.cap + s) * D + c * kVec;
         }
         if (is_k && !a.post_rope) {  // the cache stores K before RoPE; RoPE acts on that value
 #pragma unroll
           for (int e = 0; e < 2 * kVec; ++e) x[u][e] = Io<E>::rnd(x[u][e]);
           if (to_cache) {
             *reinterpret_cast<u32x4*>(cdst) = Io<E>::pack(x[u]);
-            *reinterpret_cast<u32x4*>(cdst + kHalf) = Io<E>::pack(x[u] + kVec);
+            *reinterpret_cast<u32x4*>(cdst + kH) = Io<E>::pack(x[u] + kVec);
           }
           if (!k_rot) continue;
         }
         float y[2 * kVec];
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
-          const float2 z = zs[tt[u]][c * kVec + e];
+          const float2 z = kStageRope<D> ? zs[tt[u]][c * kVec + e]
+                                         : rope_factor<kH>(a.rope, p_first + t, c * kVec + e);
           const float x0 = x[u][e], x1 = x[u][kVec + e];
           y[e] = x0 * z.x - x1 * z.y;
           y[kVec + e] = x0 * z.y + x1 * z.x;
@@ -197,22 +241,22 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
         if (is_k && a.post_rope) {  // the cache stores K rotated at its absolute position
           if (to_cache) {
             *reinterpret_cast<u32x4*>(cdst) = Io<E>::pack(y);
-            *reinterpret_cast<u32x4*>(cdst + kHalf) = Io<E>::pack(y + kVec);
+            *reinterpret_cast<u32x4*>(cdst + kH) = Io<E>::pack(y + kVec);
           }
           if (!k_rot) continue;
         }
         // the operand row of new token t follows the kept cached keys
         const long long R = sp.kept + t;
-        if (kTiled && is_k) {  // chunks c and c + 8 of key R within its tile
-          E* dst = k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + (R & ~63LL)) * kHeadDim +
+        if (kTiled && is_k) {  // chunks c and c + d/16 of key R within its tile
+          E* dst = k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + (R & ~63LL)) * D +
                    (c * kTokBlock + (R & 63)) * kVec;
           *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(y);
-          *reinterpret_cast<u32x4*>(dst + 8 * kTokBlock * kVec) = Io<E>::pack(y + kVec);
+          *reinterpret_cast<u32x4*>(dst + kLanesPerRow * kTokBlock * kVec) = Io<E>::pack(y + kVec);
         } else {
-          E* dst = is_k ? k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + R) * kHeadDim + c * kVec
+          E* dst = is_k ? k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + R) * D + c * kVec
                         : q_out + off[u];
           *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(y);
-          *reinterpret_cast<u32x4*>(dst + kHalf) = Io<E>::pack(y + kVec);
+          *reinterpret_cast<u32x4*>(dst + kH) = Io<E>::pack(y + kVec);
         }
       }
     }
@@ -221,23 +265,24 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   rows(k, n_tok, true, 1);
 
   if (k_rot && !a.ops_kernel) {  // zero the padding rows T .. Tp-1 of this block
-    for (int i = threadIdx.x; i < kTokBlock * (kHeadDim / kVec); i += kThreads) {
+    for (int i = threadIdx.x; i < kTokBlock * (D / kVec); i += kThreads) {
       if (kTiled) {  // i = chunk * 64 + key in tile
         const long long t = t0 + i % kTokBlock;
         if (t >= sp.T && t < a.Tp)
-          reinterpret_cast<u32x4*>(k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t0) * kHeadDim)[i] =
+          reinterpret_cast<u32x4*>(k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t0) * D)[i] =
               u32x4{0, 0, 0, 0};
       } else {
-        const long long t = t0 + i / (kHeadDim / kVec);
+        const long long t = t0 + i / (D / kVec);
         if (t >= sp.T && t < a.Tp)
-          reinterpret_cast<u32x4*>(k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t) * kHeadDim)
-              [i % (kHeadDim / kVec)] = u32x4{0, 0, 0, 0};
+          reinterpret_cast<u32x4*>(k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t) * D)
+              [i % (D / kVec)] = u32x4{0, 0, 0, 0};
       }
     }
   }
 
-  // --- values: raw copy into the cache (16-byte chunks), transposed prefill operand ----
-  constexpr int kChunks = kHeadDim / kVec;  // 16-byte chunks per row
+  // --- values: copy into the cache (16-byte chunks), transposed prefill operand --------
+  // (V norm: every chunk scaled by its row's inverse RMS, rounded once)
+  constexpr int kChunks = D / kVec;  // 16-byte chunks per row
   if (v_cache) {
     for (int i = (threadIdx.x + kThreads - 128) % kThreads; i < n_tok * kChunks; i += kThreads) {  // from wave 2
       const int t = t0 + i / kChunks;
@@ -245,9 +290,11 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
       const long long n = sp.pos + t;
       const long long s = a.window == 0 ? n : n % a.window;
       const int cidx = i % kChunks;
-      const long long row = ((static_cast<long long>(b) * a.T + t) * a.Hkv + kvh) * kHeadDim;
-      const long long crow = ((static_cast<long long>(b) * a.Hkv + kvh) * a.cap + s) * kHeadDim;
-      reinterpret_cast<u32x4*>(v_cache + crow)[cidx] = reinterpret_cast<const u32x4*>(v + row)[cidx];
+      const long long row = ((static_cast<long long>(b) * a.T + t) * a.Hkv + kvh) * D;
+      const long long crow = ((static_cast<long long>(b) * a.Hkv + kvh) * a.cap + s) * D;
+      u32x4 w = reinterpret_cast<const u32x4*>(v + row)[cidx];
+      if (a.v_norm) w = scaled_chunk<E>(w, v_inv[t - t0]);
+      reinterpret_cast<u32x4*>(v_cache + crow)[cidx] = w;
     }
   }
   if (v_t && !a.ops_kernel) {  // (otherwise the operand kernel writes all of V^T)
@@ -259,7 +306,8 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
       const int t = t0 + r;
       E x[kVec];
       if (t < sp.T) {
-        const u32x4 w = reinterpret_cast<const u32x4*>(v + ((static_cast<long long>(b) * a.T + t) * a.Hkv + kvh) * kHeadDim)[cidx];
+        u32x4 w = reinterpret_cast<const u32x4*>(v + ((static_cast<long long>(b) * a.T + t) * a.Hkv + kvh) * D)[cidx];
+        if (a.v_norm) w = scaled_chunk<E>(w, v_inv[r]);
         __builtin_memcpy(x, &w, 16);
       } else {
 #pragma unroll
@@ -272,19 +320,19 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
     constexpr int kTokChunks = kTokBlock / kVec;
     if (kTiled) {
       if (t0 < a.Tp) {  // Tp is a multiple of 128, so a tile is wholly inside or outside
-        u32x4* dst = reinterpret_cast<u32x4*>(v_t + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t0) * kHeadDim);
-        for (int i = threadIdx.x; i < kHeadDim * kTokChunks; i += kThreads) {  // i = key chunk * 128 + dim
-          const int cc = i % kHeadDim, tc = i / kHeadDim;
+        u32x4* dst = reinterpret_cast<u32x4*>(v_t + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t0) * D);
+        for (int i = threadIdx.x; i < D * kTokChunks; i += kThreads) {  // i = key chunk * d + dim
+          const int cc = i % D, tc = i / D;
           dst[i] = *reinterpret_cast<const u32x4*>(&tile[cc * kTS + tc * kVec]);
         }
       }
     } else {
-      for (int i = threadIdx.x; i < kHeadDim * kTokChunks; i += kThreads) {
+      for (int i = threadIdx.x; i < D * kTokChunks; i += kThreads) {
         const int cc = i / kTokChunks, tc = i % kTokChunks;
         const long long t = t0 + tc * kVec;
         if (t < a.Tp) {  // Tp is a multiple of 128, so a chunk is wholly inside or outside
           const u32x4 w = *reinterpret_cast<const u32x4*>(&tile[cc * kTS + tc * kVec]);
-          *reinterpret_cast<u32x4*>(v_t + ((static_cast<long long>(b) * a.Hkv + kvh) * kHeadDim + cc) * a.Tp + t) = w;
+          *reinterpret_cast<u32x4*>(v_t + ((static_cast<long long>(b) * a.Hkv + kvh) * D + cc) * a.Tp + t) = w;
         }
       }
     }
@@ -298,16 +346,18 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
 // all kept + T keys (cached V, then the chunk's own V), zeros past kept + T, with kept and
 // T those of the block's sequence. Runs before the append kernel, which may overwrite
 // ring slots these keys still occupy and writes the chunk's own K' rows.
-template <typename E>
+template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a) {
+  constexpr int kH = D / 2;
   constexpr int kVec = 16 / sizeof(E);
-  constexpr int kLanesPerRow = kHalf / kVec;
+  constexpr int kLanesPerRow = kH / kVec;
   constexpr int kRowsPerPass = 64 / kLanesPerRow;
   constexpr bool kTiled = sizeof(E) == 2;
-  constexpr int kChunks = kHeadDim / kVec;
+  constexpr int kChunks = D / kVec;
   constexpr int kTS = kTileStride<E>;  // LDS row stride (tokens) of the V^T staging tile
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes<E>];
-  float2 (*zs)[kHalf] = reinterpret_cast<float2 (*)[kHalf]>(smem);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes<E, D>];
+  __shared__ float v_inv[kTokBlock];
+  float2 (*zs)[kH] = reinterpret_cast<float2 (*)[kH]>(smem);
   E* tile = reinterpret_cast<E*>(smem);
 
   const int lane = threadIdx.x & 63;
@@ -322,22 +372,24 @@ __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a
   const long long S = kept + sp.T;
   const long long base = sp.pos - kept;  // absolute position of renumbered key 0
   const long long bh = static_cast<long long>(b) * a.Hkv + kvh;
-  const E* __restrict__ kc = static_cast<const E*>(a.k_cache) + bh * a.cap * kHeadDim;
-  const E* __restrict__ vc = static_cast<const E*>(a.v_cache) + bh * a.cap * kHeadDim;
+  const E* __restrict__ kc = static_cast<const E*>(a.k_cache) + bh * a.cap * D;
+  const E* __restrict__ vc = static_cast<const E*>(a.v_cache) + bh * a.cap * D;
   const E* __restrict__ v = static_cast<const E*>(a.v);
   E* __restrict__ k_rot = static_cast<E*>(a.k_rot_out);
   E* __restrict__ v_t = static_cast<E*>(a.v_t_out);
   auto cache_row = [&](long long R) {
     const long long n = base + R;
-    return (a.window == 0 ? n : n % a.window) * kHeadDim;
+    return (a.window == 0 ? n : n % a.window) * D;
   };
 
   if (k_rot) {
-    for (int i = threadIdx.x; i < kTokBlock * kHalf; i += kThreads) {
-      const int r = i / kHalf, j = i % kHalf;
-      if (R0 + r < kept && !a.post_rope) zs[r][j] = rope_factor(a.rope, R0 + r, j);
+    if (kStageRope<D>) {
+      for (int i = threadIdx.x; i < kTokBlock * kH; i += kThreads) {
+        const int r = i / kH, j = i % kH;
+        if (R0 + r < kept && !a.post_rope) zs[r][j] = rope_factor<kH>(a.rope, R0 + r, j);
+      }
+      __syncthreads();
     }
-    __syncthreads();
     for (int r = wave * kRowsPerPass + slot; r < kTokBlock; r += kWaves * kRowsPerPass) {
       const long long R = R0 + r;
       if (R >= kept && R < S) continue;  // the chunk's own keys: the append kernel
@@ -346,14 +398,14 @@ __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a
         float x[2 * kVec];
         const E* src = kc + cache_row(R) + c * kVec;
         Io<E>::unpack(*reinterpret_cast<const u32x4*>(src), x);
-        Io<E>::unpack(*reinterpret_cast<const u32x4*>(src + kHalf), x + kVec);
+        Io<E>::unpack(*reinterpret_cast<const u32x4*>(src + kH), x + kVec);
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
           if (a.post_rope) {  // already rotated (at its absolute position) in the cache
             y[e] = x[e];
             y[kVec + e] = x[kVec + e];
           } else {
-            const float2 z = zs[r][c * kVec + e];
+            const float2 z = kStageRope<D> ? zs[r][c * kVec + e] : rope_factor<kH>(a.rope, R, c * kVec + e);
             y[e] = x[e] * z.x - x[kVec + e] * z.y;
             y[kVec + e] = x[e] * z.y + x[kVec + e] * z.x;
           }
@@ -363,27 +415,36 @@ __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a
         for (int e = 0; e < 2 * kVec; ++e) y[e] = 0.f;
       }
       if (kTiled) {
-        E* dst = k_rot + (bh * a.Tp + R0) * kHeadDim + (c * kTokBlock + r) * kVec;
+        E* dst = k_rot + (bh * a.Tp + R0) * D + (c * kTokBlock + r) * kVec;
         *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(y);
-        *reinterpret_cast<u32x4*>(dst + 8 * kTokBlock * kVec) = Io<E>::pack(y + kVec);
+        *reinterpret_cast<u32x4*>(dst + kLanesPerRow * kTokBlock * kVec) = Io<E>::pack(y + kVec);
       } else {
-        E* dst = k_rot + (bh * a.Tp + R) * kHeadDim + c * kVec;
+        E* dst = k_rot + (bh * a.Tp + R) * D + c * kVec;
         *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(y);
-        *reinterpret_cast<u32x4*>(dst + kHalf) = Io<E>::pack(y + kVec);
+        *reinterpret_cast<u32x4*>(dst + kH) = Io<E>::pack(y + kVec);
       }
     }
   }
 
   if (v_t) {
-    __syncthreads();  // every wave is done with the rotation factors
+    // V norm: the chunk's own rows (R in [kept, S)) come raw from v; cached rows were
+    // normalised when they were appended
+    const long long r_new = kept > R0 ? kept - R0 : 0;  // first tile row holding a new token
+    const long long r_end = S - R0 < kTokBlock ? S - R0 : kTokBlock;
+    if (a.v_norm && r_end > r_new)
+      v_row_inv_rms<E, D>(v + ((static_cast<long long>(b) * a.T + (R0 + r_new - kept)) * a.Hkv + kvh) * D,
+                          static_cast<long long>(a.Hkv) * D, static_cast<int>(r_end - r_new), a.eps,
+                          v_inv + r_new, wave, lane);
+    __syncthreads();  // every wave is done with the rotation factors; v_inv is complete
     for (int i = threadIdx.x; i < kTokBlock * kChunks; i += kThreads) {
       const int r = i / kChunks, cidx = i % kChunks;
       const long long R = R0 + r;
       E x[kVec];
       if (R < S) {
         const E* src = R < kept ? vc + cache_row(R)
-                                : v + ((static_cast<long long>(b) * a.T + (R - kept)) * a.Hkv + kvh) * kHeadDim;
-        const u32x4 w = reinterpret_cast<const u32x4*>(src)[cidx];
+                                : v + ((static_cast<long long>(b) * a.T + (R - kept)) * a.Hkv + kvh) * D;
+        u32x4 w = reinterpret_cast<const u32x4*>(src)[cidx];
+        if (a.v_norm && R >= kept) w = scaled_chunk<E>(w, v_inv[r]);
         __builtin_memcpy(x, &w, 16);
       } else {
 #pragma unroll
@@ -395,44 +456,48 @@ __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a
     __syncthreads();
     constexpr int kTokChunks = kTokBlock / kVec;
     if (kTiled) {
-      u32x4* dst = reinterpret_cast<u32x4*>(v_t + (bh * a.Tp + R0) * kHeadDim);
-      for (int i = threadIdx.x; i < kHeadDim * kTokChunks; i += kThreads) {  // i = key chunk * 128 + dim
-        const int cc = i % kHeadDim, tc = i / kHeadDim;
+      u32x4* dst = reinterpret_cast<u32x4*>(v_t + (bh * a.Tp + R0) * D);
+      for (int i = threadIdx.x; i < D * kTokChunks; i += kThreads) {  // i = key chunk * d + dim
+        const int cc = i % D, tc = i / D;
         dst[i] = *reinterpret_cast<const u32x4*>(&tile[cc * kTS + tc * kVec]);
       }
     } else {
-      for (int i = threadIdx.x; i < kHeadDim * kTokChunks; i += kThreads) {
+      for (int i = threadIdx.x; i < D * kTokChunks; i += kThreads) {
         const int cc = i / kTokChunks, tc = i % kTokChunks;
         const u32x4 w = *reinterpret_cast<const u32x4*>(&tile[cc * kTS + tc * kVec]);
-        *reinterpret_cast<u32x4*>(v_t + (bh * kHeadDim + cc) * a.Tp + R0 + tc * kVec) = w;
+        *reinterpret_cast<u32x4*>(v_t + (bh * D + cc) * a.Tp + R0 + tc * kVec) = w;
       }
     }
   }
 }
 
-template <typename E>
+template <typename E, int D>
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   const bool operands = a.k_rot_out || a.v_t_out;
   if (operands && a.ops_kernel) {
     const unsigned tiles = static_cast<unsigned>(a.Tp / kTokBlock);
-    hipLaunchKernelGGL(prefill_operands_kernel<E>, dim3(tiles, a.Hkv, a.B), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_operands_kernel<E, D>), dim3(tiles, a.Hkv, a.B), dim3(kThreads), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   // without the operand kernel the append kernel also covers the padding tokens T .. Tp-1
   const long long tokens = (operands && !a.ops_kernel) ? a.Tp : a.T;
   const unsigned gx = static_cast<unsigned>((tokens + kTokBlock - 1) / kTokBlock);
-  hipLaunchKernelGGL(kv_append_kernel<E>, dim3(gx, a.Hkv, a.B), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((kv_append_kernel<E, D>), dim3(gx, a.Hkv, a.B), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_kv_append_bf16(const AppendArgs& a, hipStream_t stream) {
-  return launch_append<bf16_t>(a, stream);
+  switch (a.d) {
+    case 256: return launch_append<bf16_t, 256>(a, stream);
+    case 512: return launch_append<bf16_t, 512>(a, stream);
+    default: return launch_append<bf16_t, kHeadDim>(a, stream);
+  }
 }
 hipError_t launch_kv_append_f32(const AppendArgs& a, hipStream_t stream) {
-  return launch_append<float>(a, stream);
+  return launch_append<float, kHeadDim>(a, stream);
 }
 
 }  // namespace plamo

@@ -54,9 +54,11 @@ __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w 
 // Rotation factor amp * exp(i p w_j) from the two-level table: coarse row p >> 6 times
 // fine row p & 63 (complex product, fp32). Layout: fine [64][d/2] float2 first, then
 // coarse [n_coarse][d/2] float2.
+// kH = d/2 pairs per table row.
+template <int kH = kHalf>
 __device__ __forceinline__ float2 rope_factor(const float2* __restrict__ table, long long p, int j) {
-  const float2 f = table[(p & (kRopeFine - 1)) * kHalf + j];
-  const float2 c = table[(kRopeFine + (p >> 6)) * kHalf + j];
+  const float2 f = table[(p & (kRopeFine - 1)) * kH + j];
+  const float2 c = table[(kRopeFine + (p >> 6)) * kH + j];
   return make_float2(c.x * f.x - c.y * f.y, c.x * f.y + c.y * f.x);
 }
 

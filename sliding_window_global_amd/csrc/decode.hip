@@ -416,10 +416,10 @@ DecodePlan plan_decode(int B, int Hkv, long long S, bool ragged) {
   return p;
 }
 
-size_t decode_workspace_bytes(int B, int Hq, const DecodePlan& plan) {
-  // one split writes the output directly
+size_t decode_workspace_bytes(int B, int Hq, int d, const DecodePlan& plan) {
+  // one split writes the output directly; a split's partial state is acc[d], m, l
   if (plan.n_split == 1) return 0;
-  return static_cast<size_t>(B) * Hq * plan.n_split * kPartial * sizeof(float);
+  return static_cast<size_t>(B) * Hq * plan.n_split * (d + 2) * sizeof(float);
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {

@@ -6,9 +6,10 @@
 
 namespace plamo {
 
+// n_rot: pairs j < n_rot turn; the others get frequency 0 (p-RoPE); n_rot = d/2 for all.
 hipError_t launch_rope_table(float2* table, long long n_coarse, int d, double theta,
                              double yarn_factor, double j_low, double j_high,
-                             double amplitude, hipStream_t stream);
+                             double amplitude, int n_rot, hipStream_t stream);
 
 struct AppendArgs {
   const void* q;
@@ -32,6 +33,8 @@ struct AppendArgs {
   const int* seq_len;        // ragged batch: per-sequence new-token count (device), else NULL
   bool ops_kernel;           // the operand kernel writes every operand row outside the chunk
   bool post_rope;            // the cache holds K rotated at absolute positions (else pre-RoPE)
+  bool v_norm;               // divide each new V head vector by its RMS before use
+  int d;                     // head dim: 128 (fp32 and bf16), 256 or 512 (bf16)
   const float2* rope;
 };
 // Both launch, when prefill operands are requested after cached tokens or for a ragged
@@ -52,8 +55,11 @@ struct PrefillArgs {
   const long long* seq_pos;  // ragged batch: per-sequence pos_offset (device), else NULL
   const int* seq_len;        // ragged batch: per-sequence token count (device), else NULL
   float scale;
+  int d;                     // head dim: 128, 256 or 512 (bf16)
 };
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+// Head dims 256 and 512 (bf16).
+hipError_t launch_prefill_wide_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 
 struct DecodePlan {
@@ -61,7 +67,7 @@ struct DecodePlan {
   long long chunk;     // keys per range, a multiple of the key tile
 };
 DecodePlan plan_decode(int B, int Hkv, long long S, bool ragged);
-size_t decode_workspace_bytes(int B, int Hq, const DecodePlan& plan);
+size_t decode_workspace_bytes(int B, int Hq, int d, const DecodePlan& plan);
 
 struct DecodeArgs {
   const void* q_rot;    // [B, 1, Hq, d]
@@ -79,8 +85,11 @@ struct DecodeArgs {
   DecodePlan plan;
   const float2* rope;
   float scale;
+  int d;                     // head dim: 128; 256 or 512 with a post-RoPE cache
 };
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+// Head dims 256 and 512, post-RoPE cache.
+hipError_t launch_decode_wide_bf16(const DecodeArgs& a, hipStream_t stream);
 
 struct GemmArgs {
   const void* x;            // [M, K] bf16

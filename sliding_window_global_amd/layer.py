@@ -33,10 +33,11 @@ class PrefillBuffers:
 
 def prefill(q, k, v, *, window, rope_table, q_norm_w=None, k_norm_w=None, norm_offset=1.0,
             norm_eps=1e-6, k_cache=None, v_cache=None, bufs: PrefillBuffers | None = None,
-            softmax_scale=None, stream=None, pos_offset=0, cache_post_rope=False) -> PrefillBuffers:
+            softmax_scale=None, stream=None, pos_offset=0, cache_post_rope=False, v_norm=False) -> PrefillBuffers:
     """Prefill of a chunk q [B,T,Hq,d], k/v [B,T,Hkv,d] on the GPU whose first token sits at
     absolute position pos_offset. With pos_offset > 0 the caches must hold the earlier tokens
-    (they are read for the chunk's attention, then updated with the chunk)."""
+    (they are read for the chunk's attention, then updated with the chunk). v_norm: V divided
+    by its RMS per head vector (the Gemma-4-shaped layer)."""
     B, T, Hq, d = q.shape
     Hkv = k.shape[2]
     if bufs is None:
@@ -44,7 +45,7 @@ def prefill(q, k, v, *, window, rope_table, q_norm_w=None, k_norm_w=None, norm_o
     plamo_kv_append(q, k, v, bufs.q_rot, window=window, pos_offset=pos_offset, rope_table=rope_table,
                     q_norm_w=q_norm_w, k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps,
                     k_rot_out=bufs.k_rot, v_t_out=bufs.v_t, k_cache=k_cache, v_cache=v_cache,
-                    cache_post_rope=cache_post_rope, stream=stream)
+                    cache_post_rope=cache_post_rope, v_norm=v_norm, stream=stream)
     plamo_attn_prefill(bufs.q_rot, bufs.k_rot, bufs.v_t, bufs.out, window=window, pos_offset=pos_offset,
                        softmax_scale=softmax_scale, stream=stream)
     return bufs
@@ -64,7 +65,7 @@ class DecodeBuffers:
 
 def decode(q, k, v, k_cache, v_cache, *, window, pos_offset, rope_table, q_norm_w=None,
            k_norm_w=None, norm_offset=1.0, norm_eps=1e-6, bufs: DecodeBuffers | None = None,
-           softmax_scale=None, stream=None, cache_post_rope=False) -> DecodeBuffers:
+           softmax_scale=None, stream=None, cache_post_rope=False, v_norm=False) -> DecodeBuffers:
     """One decode step at absolute position pos_offset: q [B,1,Hq,d], k/v [B,1,Hkv,d]."""
     B, _, Hq, d = q.shape
     Hkv = k.shape[2]
@@ -72,7 +73,8 @@ def decode(q, k, v, k_cache, v_cache, *, window, pos_offset, rope_table, q_norm_
         bufs = DecodeBuffers(B, Hq, Hkv, d, window, pos_offset, q.dtype, q.device)
     plamo_kv_append(q, k, v, bufs.q_rot, window=window, pos_offset=pos_offset, rope_table=rope_table,
                     q_norm_w=q_norm_w, k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps,
-                    k_cache=k_cache, v_cache=v_cache, cache_post_rope=cache_post_rope, stream=stream)
+                    k_cache=k_cache, v_cache=v_cache, cache_post_rope=cache_post_rope, v_norm=v_norm,
+                    stream=stream)
     plamo_attn_decode(bufs.q_rot, k_cache, v_cache, bufs.out, bufs.workspace, window=window,
                       pos_offset=pos_offset, rope_table=rope_table,
                       softmax_scale=1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale,
@@ -83,7 +85,7 @@ def decode(q, k, v, k_cache, v_cache, *, window, pos_offset, rope_table, q_norm_
 def prefill_ragged(q, k, v, *, window, rope_table, seq_pos_offsets, max_pos_offset, seq_lens=None,
                    q_norm_w=None, k_norm_w=None, norm_offset=1.0, norm_eps=1e-6, k_cache=None,
                    v_cache=None, bufs: PrefillBuffers | None = None, softmax_scale=None,
-                   stream=None, cache_post_rope=False) -> PrefillBuffers:
+                   stream=None, cache_post_rope=False, v_norm=False) -> PrefillBuffers:
     """Prefill of a ragged batch: sequence b's seq_lens[b] new tokens (rows of its [T] slab)
     start at absolute position seq_pos_offsets[b] <= max_pos_offset."""
     B, T, Hq, d = q.shape
@@ -94,7 +96,7 @@ def prefill_ragged(q, k, v, *, window, rope_table, seq_pos_offsets, max_pos_offs
                            max_pos_offset=max_pos_offset, seq_lens=seq_lens, rope_table=rope_table,
                            q_norm_w=q_norm_w, k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps,
                            k_rot_out=bufs.k_rot, v_t_out=bufs.v_t, k_cache=k_cache, v_cache=v_cache,
-                           cache_post_rope=cache_post_rope, stream=stream)
+                           cache_post_rope=cache_post_rope, v_norm=v_norm, stream=stream)
     plamo_attn_prefill_ragged(bufs.q_rot, bufs.k_rot, bufs.v_t, bufs.out, window=window,
                               seq_pos_offsets=seq_pos_offsets, max_pos_offset=max_pos_offset,
                               seq_lens=seq_lens, softmax_scale=softmax_scale, stream=stream)
@@ -104,7 +106,7 @@ def prefill_ragged(q, k, v, *, window, rope_table, seq_pos_offsets, max_pos_offs
 def decode_ragged(q, k, v, k_cache, v_cache, *, window, seq_pos_offsets, max_pos_offset, rope_table,
                   q_norm_w=None, k_norm_w=None, norm_offset=1.0, norm_eps=1e-6,
                   bufs: DecodeBuffers | None = None, softmax_scale=None, stream=None,
-                  cache_post_rope=False) -> DecodeBuffers:
+                  cache_post_rope=False, v_norm=False) -> DecodeBuffers:
     """One decode step of a ragged batch: sequence b's new token sits at seq_pos_offsets[b]."""
     B, _, Hq, d = q.shape
     Hkv = k.shape[2]
@@ -113,7 +115,7 @@ def decode_ragged(q, k, v, k_cache, v_cache, *, window, seq_pos_offsets, max_pos
     plamo_kv_append_ragged(q, k, v, bufs.q_rot, window=window, seq_pos_offsets=seq_pos_offsets,
                            max_pos_offset=max_pos_offset, rope_table=rope_table, q_norm_w=q_norm_w,
                            k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps, k_cache=k_cache,
-                           v_cache=v_cache, cache_post_rope=cache_post_rope, stream=stream)
+                           v_cache=v_cache, cache_post_rope=cache_post_rope, v_norm=v_norm, stream=stream)
     plamo_attn_decode_ragged(bufs.q_rot, k_cache, v_cache, bufs.out, bufs.workspace, window=window,
                              seq_pos_offsets=seq_pos_offsets, max_pos_offset=max_pos_offset,
                              rope_table=rope_table, softmax_scale=softmax_scale,

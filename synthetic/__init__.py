@@ -57,3 +57,8 @@ class Draw:
     def normal(self, shape, std: float = 1.0) -> np.ndarray:
         x = normal_f32(self.gen, shape, std)
         return bf16_round(x) if self.bf16 else x
+
+    def uniform(self, lo: float, hi: float) -> float:
+        """One float32 value uniform in [lo, hi) (bf16-rounded when ``bf16``)."""
+        x = np.float32(self.gen.uniform(lo, hi))
+        return float(bf16_round(np.array([x]))[0]) if self.bf16 else float(x)

@@ -230,3 +230,111 @@ def device_normal_bf16(shape, seed: int, device):
     g.manual_seed(seed)
     x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
     return x.to(torch.bfloat16)
+
+
+# ----------------------------------------------------------------------------
+# The Gemma-4-shaped second workload (「PLaMo 3アーキテクチャ徹底解析」 §8 comparison table,
+# §6.4 p-RoPE, §9.4 gains): local layers d = 256, Hq = 32, Hkv = 16, window 1024, RoPE base
+# 1e4 on every pair; global layers d = 512, Hq = 32, Hkv = 4, p-RoPE (p = 0.25, base 1e6),
+# V taken from the K projection. Q/K norm gain = the stored weight (offset 0), constant
+# within each vector as the page reports for the released weights: Q in [0.95, 1.05], K in
+# [0.120, 0.132] (local) or [0.060, 0.065] (global); V divided by its RMS; dot-product
+# factor 1; K cached after RoPE.
+# ----------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class GemmaLayer:
+    kind: str          # "local" or "global"
+    d: int
+    Hq: int
+    Hkv: int
+    window: int        # 0 = global causal layer
+    theta: float
+    partial: float     # p-RoPE fraction of pairs that turn; 0 = all
+    k_gain: tuple      # range of the constant K gain
+    kv_shared: bool    # V is the K projection output
+    q_gain: tuple = (0.95, 1.05)
+    scale: float = 1.0
+    norm_offset: float = 0.0
+    eps: float = 1e-6
+
+    def draw_gains(self, dr: Draw):
+        """(wq, wk): constant vectors [d] (the gain itself, offset 0)."""
+        gq = dr.uniform(*self.q_gain)
+        gk = dr.uniform(*self.k_gain)
+        return np.full(self.d, gq, dtype=np.float32), np.full(self.d, gk, dtype=np.float32)
+
+    def draw_tokens(self, dr: Draw, B: int, T: int):
+        """q [B,T,Hq,d], k [B,T,Hkv,d], v (the same array as k when shared), bf16-exact."""
+        q = dr.normal((B, T, self.Hq, self.d))
+        k = dr.normal((B, T, self.Hkv, self.d))
+        v = k if self.kv_shared else dr.normal((B, T, self.Hkv, self.d))
+        return q, k, v
+
+
+GEMMA_LOCAL_LAYER = GemmaLayer("local", 256, 32, 16, 1024, 1e4, 0.0, (0.120, 0.132), False)
+GEMMA_GLOBAL_LAYER = GemmaLayer("global", 512, 32, 4, 0, 1e6, 0.25, (0.060, 0.065), True)
+
+
+@dataclass(frozen=True)
+class GemmaPrefill:
+    name: str
+    layer: GemmaLayer
+    B: int
+    T: int
+    seed: int
+
+    def draw(self):
+        dr = Draw(self.seed, True)
+        q, k, v = self.layer.draw_tokens(dr, self.B, self.T)
+        wq, wk = self.layer.draw_gains(dr)
+        return dict(q=q, k=k, v=v, wq=wq, wk=wk)
+
+    def attended_pairs_per_head(self) -> int:
+        T, W = self.T, self.layer.window
+        if W <= 0 or W >= T:
+            return T * (T + 1) // 2
+        return W * (W + 1) // 2 + (T - W) * W
+
+    def flops(self) -> float:
+        return 4.0 * self.layer.d * self.layer.Hq * self.B * self.attended_pairs_per_head()
+
+
+@dataclass(frozen=True)
+class GemmaDecode:
+    """Batched decode of one Gemma-shaped layer: B sequences whose new token sits at
+    pos_offset; the cache holds the kept earlier tokens (K after RoPE, scaled to the layer's
+    K gain; V of unit RMS), drawn on the device."""
+    name: str
+    layer: GemmaLayer
+    B: int
+    pos_offset: int
+    seed: int
+
+    def keys_attended(self) -> int:
+        W = self.layer.window
+        return (self.pos_offset if W == 0 else min(self.pos_offset, W - 1)) + 1
+
+    def cache_cap(self) -> int:
+        return self.layer.window if self.layer.window else self.pos_offset + 1
+
+    def kv_bytes(self) -> int:
+        return 2 * 2 * self.B * self.layer.Hkv * self.layer.d * self.keys_attended()
+
+    def draw_new_tokens(self):
+        dr = Draw(self.seed, True)
+        q, k, v = self.layer.draw_tokens(dr, self.B, 1)
+        wq, wk = self.layer.draw_gains(dr)
+        return dict(q=q, k=k, v=v, wq=wq, wk=wk)
+
+    def cache_seed(self) -> int:
+        return self.seed * 7919
+
+
+GEMMA_LOCAL_PREFILL = GemmaPrefill("gemma_local_prefill_T8192_d256_W1024", GEMMA_LOCAL_LAYER, 1, 8192,
+                                   BASE_SEED + 8)
+GEMMA_GLOBAL_PREFILL = GemmaPrefill("gemma_global_prefill_T32768_d512_p0.25", GEMMA_GLOBAL_LAYER, 1, 32768,
+                                    BASE_SEED + 9)
+GEMMA_LOCAL_DECODE = GemmaDecode("gemma_local_decode_B64_ring1024", GEMMA_LOCAL_LAYER, 64, 32767, BASE_SEED + 10)
+GEMMA_GLOBAL_DECODE = GemmaDecode("gemma_global_decode_B64_ctx32768", GEMMA_GLOBAL_LAYER, 64, 32767,
+                                  BASE_SEED + 11)

@@ -62,6 +62,9 @@ def test_pure_host_helpers(lib):
     assert lib.plamo_rope_table_bytes(131200, 128) == (64 + 2050) * 512
     assert lib.plamo_rope_table_bytes(0, 128) == 0
     assert lib.plamo_rope_table_bytes(100, 64) == 0
+    # wider heads: d/2 pairs per row
+    assert lib.plamo_rope_table_bytes(1, 256) == (64 + 1) * 1024
+    assert lib.plamo_rope_table_bytes(131072, 512) == (64 + 2048) * 2048
 
 
 def test_decode_workspace_sizes(lib):
@@ -75,15 +78,18 @@ def test_decode_workspace_sizes(lib):
     # a ragged batch cuts its key ranges finer than the uniform plan of its longest sequence
     n = lib.plamo_attn_decode_ragged_workspace_bytes(64, 64, 8, 128, 0, 32767)
     assert n > 0 and n % (130 * 4 * 64 * 64) == 0 and n // (130 * 4 * 64 * 64) > 1
+    # wide heads: (acc[d], m, l) per split
+    n = lib.plamo_attn_decode_workspace_bytes(8, 32, 4, 512, 0, 131071)
+    assert n > 0 and n % (514 * 4 * 8 * 32) == 0 and n // (514 * 4 * 8 * 32) > 1
 
 
 def _append(lib, **over):
-    a = dict(dtype=BF16, q=FAKE, k=FAKE, v=FAKE, wq=None, wk=None, c=1.0, eps=1e-6, q_out=FAKE,
+    a = dict(dtype=BF16, q=FAKE, k=FAKE, v=FAKE, wq=None, wk=None, c=1.0, eps=1e-6, v_norm=0, q_out=FAKE,
              k_rot=None, v_t=None, kc=None, vc=None, cap=0, B=1, T=4, Hq=8, Hkv=2, d=128, window=16,
              pos=0, table=FAKE, table_bytes=(64 + 1) * 512, order=0, stream=None)
     a.update(over)
     return lib.plamo_kv_append(a["dtype"], a["q"], a["k"], a["v"], a["wq"], a["wk"], a["c"], a["eps"],
-                               a["q_out"], a["k_rot"], a["v_t"], a["kc"], a["vc"], a["cap"], a["B"], a["T"],
+                               a["v_norm"], a["q_out"], a["k_rot"], a["v_t"], a["kc"], a["vc"], a["cap"], a["B"], a["T"],
                                a["Hq"], a["Hkv"], a["d"], a["window"], a["pos"], a["table"],
                                a["table_bytes"], a["order"], a["stream"])
 
@@ -111,6 +117,10 @@ def _append(lib, **over):
     (dict(pos=3, k_rot=FAKE), INVALID),             # operands after cached keys need the caches
     (dict(order=2), INVALID),                        # unknown cache order
     (dict(order=1, pos=62, window=16), WORKSPACE),   # post-RoPE: table covers absolute positions
+    (dict(v_norm=2), INVALID),
+    (dict(d=256, dtype=F32), UNSUPPORTED),           # wide heads are bf16 only
+    (dict(d=512, table_bytes=(64 + 1) * 512 + 512), INVALID),  # d = 512 rows are 2 KiB
+    (dict(d=512, pos=64, window=0, table_bytes=(64 + 1) * 2048), WORKSPACE),
 ])
 def test_kv_append_validation(lib, over, status):
     assert _append(lib, **over) == status
@@ -135,6 +145,8 @@ def _prefill(lib, **over):
     (dict(out=None), INVALID), (dict(k=MISALIGNED), INVALID),
     (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID), (dict(T=-3), INVALID),
     (dict(T=(1 << 22) + 1), UNSUPPORTED),            # bf16 operands use 32-bit buffer offsets
+    (dict(d=512, T=(1 << 20) + 1), UNSUPPORTED),     # the same bound, (kept + T) * d <= 2^29
+    (dict(d=256, dtype=F32), UNSUPPORTED), (dict(d=384), UNSUPPORTED),
 ])
 def test_prefill_validation(lib, over, status):
     assert _prefill(lib, **over) == status
@@ -157,6 +169,9 @@ def _decode(lib, **over):
     (dict(table_bytes=(64 + 31) * 512), WORKSPACE), (dict(kc=None), INVALID),
     (dict(out=MISALIGNED), INVALID), (dict(scale=-1.0), INVALID), (dict(order=-1), INVALID),
     (dict(order=1, table=None, ws=None), WORKSPACE),  # post-RoPE needs no table; still a workspace
+    (dict(d=256), UNSUPPORTED),                       # wide heads decode from a post-RoPE cache
+    (dict(d=512, order=1, table=None, ws=None), WORKSPACE),
+    (dict(d=512, order=1, ws_bytes=16), WORKSPACE),
 ])
 def test_decode_validation(lib, over, status):
     assert _decode(lib, **over) == status
@@ -173,6 +188,13 @@ def test_rope_init_validation(lib):
     assert lib.plamo_rope_table_init(FAKE, need, 1000, 128, ctypes.byref(bad_beta), None) == INVALID
     assert lib.plamo_rope_table_init(FAKE, need, 1000, 128, ctypes.byref(bad_theta), None) == INVALID
     assert lib.plamo_rope_table_init(FAKE, need, 0, 128, ctypes.byref(r), None) == INVALID
+    # p-RoPE: not with YaRN, and a fraction must be >= 0
+    p_yarn = _lib.PlamoRope(1e6, 256.0, 4096.0, 32.0, 1.0, 0.25)
+    p_neg = _lib.PlamoRope(1e6, 0.0, 4096.0, 32.0, 1.0, -0.25)
+    need512 = lib.plamo_rope_table_bytes(1000, 512)
+    assert lib.plamo_rope_table_init(FAKE, need512, 1000, 512, ctypes.byref(p_yarn), None) == UNSUPPORTED
+    assert lib.plamo_rope_table_init(FAKE, need512, 1000, 512, ctypes.byref(p_neg), None) == INVALID
+    assert lib.plamo_rope_table_init(FAKE, need512 - 2048, 1000, 512, ctypes.byref(p_neg), None) == WORKSPACE
 
 
 def test_tiled_operand_helpers_invert_documented_layout():
@@ -203,7 +225,7 @@ def test_ragged_entry_points_validate_their_arrays(lib):
     def append(seq_pos, seq_len, max_pos=0, **over):
         a = dict(base, **over)
         return lib.plamo_kv_append_ragged(a["dtype"], a["q"], a["k"], a["v"], a["wq"], a["wk"], a["c"], a["eps"],
-                                          a["q_out"], a["k_rot"], a["v_t"], a["kc"], a["vc"], a["cap"], a["B"],
+                                          0, a["q_out"], a["k_rot"], a["v_t"], a["kc"], a["vc"], a["cap"], a["B"],
                                           a["T"], a["Hq"], a["Hkv"], a["d"], a["window"], seq_pos, seq_len,
                                           max_pos, a["table"], a["table_bytes"], 0, None)
     assert append(None, None) == INVALID                  # positions are required
