@@ -8,7 +8,8 @@ second of that step. Also reported: the global-layer prefill (T=32768, YaRN), ba
 decode (B=64; ring W=2048 and global 32768) as KV-read GB/s, the same global decode with
 each sequence at its own position (ragged), both prefills fed in chunks (2048 local, 8192
 global) after cached tokens, the whole attention sublayer (projections and norms around the
-path, D = 5120), the 8-layer period decode
+path, D = 5120), the Gemma-4-shaped layers (d = 256 local, d = 512 global with p-RoPE: prefill
+and B = 64 decode), the 8-layer period decode
 at 131072 context, the roofline object of the prefill kernel, and the CPU oracle timed
 on a bounded sample of the headline workload.
 
@@ -241,6 +242,94 @@ def bench_decode_ragged(torch, swg, wl, layer_idx, steps, warmup):
                 frac_hbm=nbytes / ms / 1e6 / PEAK_HBM_GBS)
 
 
+# ----------------------------------------------------------------------------
+# the Gemma-4-shaped second workload (head dims 256 / 512, p-RoPE, V norm, factor 1)
+# ----------------------------------------------------------------------------
+
+def gemma_table(swg, L, max_pos):
+    return swg.make_rope_table(max_pos, swg.RopeParams(L.theta, partial=L.partial), d=L.d)
+
+
+def gemma_kw(torch, L, wq, wk):
+    return dict(q_norm_w=dev_bf16(torch, wq), k_norm_w=dev_bf16(torch, wk), norm_offset=L.norm_offset,
+                norm_eps=L.eps, cache_post_rope=True, v_norm=True)
+
+
+def bench_gemma_prefill(torch, swg, wl, steps, warmup):
+    """kv_append (gain-only QK norm, V norm, p-RoPE or RoPE, post-RoPE cache, operands) +
+    attn_prefill (factor 1) of one Gemma-shaped layer from an empty cache."""
+    from sliding_window_global_amd import layer
+    L = wl.layer
+    inp = wl.draw()
+    q, k = dev_bf16(torch, inp["q"]), dev_bf16(torch, inp["k"])
+    v = k if L.kv_shared else dev_bf16(torch, inp["v"])
+    tab = gemma_table(swg, L, wl.T + 64)
+    cap = L.window if L.window else wl.T
+    kc = torch.empty((wl.B, L.Hkv, cap, L.d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    bufs = layer.PrefillBuffers(wl.B, wl.T, L.Hq, L.Hkv, L.d, torch.bfloat16)
+    kw = gemma_kw(torch, L, inp["wq"], inp["wk"])
+
+    def step(t_step=None, t_attn=None):
+        t_step[0].record() if t_step else None
+        swg.plamo_kv_append(q, k, v, bufs.q_rot, window=L.window, pos_offset=0, rope_table=tab,
+                            k_rot_out=bufs.k_rot, v_t_out=bufs.v_t, k_cache=kc, v_cache=vc, **kw)
+        t_attn[0].record() if t_attn else None
+        swg.plamo_attn_prefill(bufs.q_rot, bufs.k_rot, bufs.v_t, bufs.out, window=L.window,
+                               softmax_scale=L.scale)
+        t_attn[1].record() if t_attn else None
+        t_step[1].record() if t_step else None
+
+    for _ in range(warmup):
+        step()
+    ts, ta = Timer(torch), Timer(torch)
+    for _ in range(steps):
+        step(ts.span(), ta.span())
+    ms_step, ms_attn = ts.mean_ms(), ta.mean_ms()
+    flops = wl.flops()
+    return dict(workload=wl.name, flops=flops, ms_per_step=ms_step, ms_attn=ms_attn,
+                step_tflops=flops / ms_step / 1e9, attn_tflops=flops / ms_attn / 1e9,
+                frac_mfma=flops / ms_attn / 1e9 / PEAK_BF16_TFLOPS)
+
+
+def bench_gemma_decode(torch, swg, wl, steps, warmup):
+    """attn_decode of one Gemma-shaped layer (B = 64, post-RoPE cache read as stored) at its real
+    cache size; KV-read GB/s over the attended keys."""
+    from sliding_window_global_amd import layer
+    from synthetic.workloads import device_normal_bf16
+    L = wl.layer
+    p = wl.pos_offset
+    cap = wl.cache_cap()
+    kc = device_normal_bf16((wl.B, L.Hkv, cap, L.d), wl.cache_seed(), "cuda")
+    vc = device_normal_bf16((wl.B, L.Hkv, cap, L.d), wl.cache_seed() + 1, "cuda")
+    new = wl.draw_new_tokens()
+    tab = gemma_table(swg, L, p + 64)
+    bufs = layer.DecodeBuffers(wl.B, L.Hq, L.Hkv, L.d, L.window, p)
+    k1 = dev_bf16(torch, new["k"])
+    v1 = k1 if L.kv_shared else dev_bf16(torch, new["v"])
+    swg.plamo_kv_append(dev_bf16(torch, new["q"]), k1, v1, bufs.q_rot, window=L.window, pos_offset=p,
+                        rope_table=tab, k_cache=kc, v_cache=vc, **gemma_kw(torch, L, new["wq"], new["wk"]))
+
+    def run():
+        swg.plamo_attn_decode(bufs.q_rot, kc, vc, bufs.out, bufs.workspace, window=L.window, pos_offset=p,
+                              rope_table=None, softmax_scale=L.scale, cache_post_rope=True)
+
+    for _ in range(warmup):
+        run()
+    t = Timer(torch)
+    for _ in range(steps):
+        a, b = t.span()
+        a.record()
+        run()
+        b.record()
+    ms = t.mean_ms()
+    nbytes = wl.kv_bytes()
+    del kc, vc
+    torch.cuda.empty_cache()
+    return dict(workload=wl.name, kv_bytes=nbytes, keys=wl.keys_attended(), ms=ms, gbs=nbytes / ms / 1e6,
+                frac_hbm=nbytes / ms / 1e6 / PEAK_HBM_GBS)
+
+
 def bench_mixer(torch, swg, wl, steps, warmup):
     """The attention sublayer around the hot path (pre norm, QKV projection, append +
     attention, output projection, post norm + residual) on a local-layer prefill at
@@ -361,7 +450,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="", help="prefill_local|prefill_global|prefill_chunked|mixer|decode|period|copy_calibration")
+    ap.add_argument("--only", default="",
+                    help="prefill_local|prefill_global|prefill_chunked|mixer|decode|period|gemma|copy_calibration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--period-steps", type=int, default=128)
@@ -374,8 +464,9 @@ def main():
 
     import sliding_window_global_amd as swg
     from sliding_window_global_amd.profiling import read_traffic
-    from synthetic.workloads import (BATCHED_DECODE, GLOBAL_PREFILL, LOCAL_PREFILL, MIXER_LOCAL_PREFILL,
-                                     PERIOD_DECODE)
+    from synthetic.workloads import (BATCHED_DECODE, GEMMA_GLOBAL_DECODE, GEMMA_GLOBAL_PREFILL,
+                                     GEMMA_LOCAL_DECODE, GEMMA_LOCAL_PREFILL, GLOBAL_PREFILL, LOCAL_PREFILL,
+                                     MIXER_LOCAL_PREFILL, PERIOD_DECODE)
 
     torch.cuda.set_device(0)
     swg._lib.load()
@@ -418,6 +509,17 @@ def main():
         r = bench_decode_ragged(torch, swg, BATCHED_DECODE, 1, args.steps, args.warmup)
         log(f"[bench]   {r}")
         extra[r["workload"]] = r
+    if only in ("", "gemma"):
+        for wl, n in ((GEMMA_LOCAL_PREFILL, args.steps), (GEMMA_GLOBAL_PREFILL, max(3, args.steps // 4))):
+            log(f"[bench] Gemma-shaped prefill {wl.name}")
+            r = bench_gemma_prefill(torch, swg, wl, n, max(1, args.warmup // 2))
+            log(f"[bench]   {r}")
+            extra[r["workload"]] = r
+        for wl in (GEMMA_LOCAL_DECODE, GEMMA_GLOBAL_DECODE):
+            log(f"[bench] Gemma-shaped decode {wl.name}")
+            r = bench_gemma_decode(torch, swg, wl, args.steps, args.warmup)
+            log(f"[bench]   {r}")
+            extra[r["workload"]] = r
     if only in ("", "period"):
         log("[bench] 8-layer period decode")
         r = bench_period(torch, swg, PERIOD_DECODE, args.period_steps)

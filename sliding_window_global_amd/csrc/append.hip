@@ -35,17 +35,20 @@ constexpr int kTokBlock = 64;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
-// One LDS area per block, used first for the rotation factors of the block's 64 positions
-// (d = 128 only: [64][64] float2, 32 KiB) and afterwards, behind a barrier, for the V^T
-// staging tile ([d dims][64 + 16/sizeof(E) tokens]). Sharing it keeps a d = 128 block
-// within 36 KiB, so that four blocks (all of a 64-token x 8-KV-head step) fit on a CU.
+// One LDS area per block, used first for the rotation factors of kRopeTok positions at a
+// time ([kRopeTok][d/2] float2, 32 KiB: all 64 positions at d = 128, 32 or 16 of them at
+// d = 256 or 512) and afterwards, behind a barrier, for the V^T staging tile ([d dims][64 +
+// 16/sizeof(E) tokens]). Sharing it keeps a d = 128 block within 36 KiB, so that four
+// blocks (all of a 64-token x 8-KV-head step) fit on a CU.
 template <typename E>
 constexpr int kTileStride = kTokBlock + 16 / static_cast<int>(sizeof(E));  // tokens, 16-byte rows
 template <int D>
-constexpr bool kStageRope = D == kHeadDim;
+constexpr int kRopeTok = kTokBlock * kHeadDim / D;
+template <int D>
+constexpr bool kStageRope = D == kHeadDim;  // the operand kernel stages its factors at d = 128 only
 template <typename E, int D>
-constexpr int kSmemBytes = (kStageRope<D> ? kTokBlock * (D / 2) * 8 : 0) > D * kTileStride<E> * static_cast<int>(sizeof(E))
-                               ? kTokBlock * (D / 2) * 8
+constexpr int kSmemBytes = kRopeTok<D> * (D / 2) * 8 > D * kTileStride<E> * static_cast<int>(sizeof(E))
+                               ? kRopeTok<D> * (D / 2) * 8
                                : D * kTileStride<E> * static_cast<int>(sizeof(E));
 
 template <typename E>
@@ -146,15 +149,16 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   const int n_tok = min(kTokBlock, sp.T - t0);  // may be <= 0 in the padding blocks
   if (n_tok <= 0 && (a.ops_kernel || !(k_rot || v_t))) return;  // block-uniform
 
-  // rotation factors of this block's renumbered positions kept + t (post-RoPE cache:
-  // absolute positions pos + t)
+  // rotation factors of the block's renumbered positions kept + t (post-RoPE cache:
+  // absolute positions pos + t), kRopeTok tokens from token ts on
   const long long p_first = a.post_rope ? sp.pos : sp.kept;
-  if (kStageRope<D>) {
-    for (int i = threadIdx.x; i < kTokBlock * kH; i += kThreads) {
+  auto stage = [&](int ts) {
+    for (int i = threadIdx.x; i < kRopeTok<D> * kH; i += kThreads) {
       const int r = i / kH, j = i % kH;
-      if (r < n_tok) zs[r][j] = rope_factor<kH>(a.rope, p_first + t0 + r, j);
+      if (ts + r < n_tok) zs[r][j] = rope_factor<kH>(a.rope, p_first + t0 + ts + r, j);
     }
-  }
+  };
+  stage(0);
   if (a.v_norm && n_tok > 0)
     v_row_inv_rms<E, D>(v + ((static_cast<long long>(b) * a.T + t0) * a.Hkv + kvh) * D,
                         static_cast<long long>(a.Hkv) * D, n_tok, a.eps, v_inv, wave, lane);
@@ -170,21 +174,23 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   __syncthreads();
 
   // One pass normalises and rotates kRowsPerPass rows per wave (kUnroll passes in flight).
-  // is_k: row r is token t0 + r of the K head; else row r is (token r / G, head r % G).
-  // Row passes start at wave `first`, so that with few rows (a decode step) the Q rows, the
-  // K rows and the V copy below run on different waves at the same time.
-  auto rows = [&](const E* __restrict__ src, int n_rows, bool is_k, int first) {
+  // is_k: row r is token t0 + ts + r of the K head; else row r is (token ts + r / G, head
+  // r % G), ts the first token whose factors are staged. Row passes start at wave `first`,
+  // so that with few rows (a decode step) the Q rows, the K rows and the V copy below run
+  // on different waves at the same time.
+  auto rows = [&](const E* __restrict__ src, int n_rows, bool is_k, int first, int ts) {
     const float* g = is_k ? gk : gq;
     const int w = (wave + kWaves - first) % kWaves;
     for (int base = w * kRowsPerPass * kUnroll; base < n_rows; base += kWaves * kRowsPerPass * kUnroll) {
       float x[kUnroll][2 * kVec];
       float ss[kUnroll];
       long long off[kUnroll];
-      int tt[kUnroll];
+      int tt[kUnroll], zr[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int r = min(base + u * kRowsPerPass + slot, n_rows - 1);
-        tt[u] = is_k ? r : r / G;
+        zr[u] = is_k ? r : r / G;
+        tt[u] = ts + zr[u];
         const int head = is_k ? kvh : kvh * G + r % G;
         const int H = is_k ? a.Hkv : a.Hq;
         off[u] = ((static_cast<long long>(b) * a.T + t0 + tt[u]) * H + head) * D + c * kVec;
@@ -232,8 +238,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
         float y[2 * kVec];
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
-          const float2 z = kStageRope<D> ? zs[tt[u]][c * kVec + e]
-                                         : rope_factor<kH>(a.rope, p_first + t, c * kVec + e);
+          const float2 z = zs[zr[u]][c * kVec + e];
           const float x0 = x[u][e], x1 = x[u][kVec + e];
           y[e] = x0 * z.x - x1 * z.y;
           y[kVec + e] = x0 * z.y + x1 * z.x;
@@ -261,8 +266,16 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
       }
     }
   };
-  rows(q, n_tok * G, false, 0);
-  rows(k, n_tok, true, 1);
+  for (int ts = 0; ts < n_tok; ts += kRopeTok<D>) {  // one pass at d = 128
+    if (ts > 0) {
+      __syncthreads();  // every wave is done with the previous factors
+      stage(ts);
+      __syncthreads();
+    }
+    const int nt = min(kRopeTok<D>, n_tok - ts);
+    rows(q, nt * G, false, 0, ts);
+    rows(k, nt, true, 1, ts);
+  }
 
   if (k_rot && !a.ops_kernel) {  // zero the padding rows T .. Tp-1 of this block
     for (int i = threadIdx.x; i < kTokBlock * (D / kVec); i += kThreads) {

@@ -12,13 +12,16 @@
 // Here a wave holds NB blocks of 16 rows and uses v_mfma_f32_16x16x32_bf16.
 //
 // Work decomposition
-//   block  = 4 waves x 16 NB query rows of one (sequence, query head). Query row t sits
+//   block  = 8 waves x 16 NB query rows of one (sequence, query head), NB = 2 at d = 256
+//            and 1 at d = 512: two waves per SIMD, each within 256 registers (with one wave
+//            per SIMD the LDS reads and the step barrier are not hidden). Query row t sits
 //            at renumbered position kept + t and attends operand keys 0 .. kept + t.
 //   step   = 32 keys, one half of a 64-key operand tile (K' tile [d/8][64][8], V^T tile
 //            [8][d][8], both written by the append kernel). Each half is one set of
 //            1 KiB direct copies into LDS (buffer loads with the LDS bit: the K' half is
 //            512-byte runs of each dim chunk, the V^T half is contiguous), double
-//            buffered over four LDS objects, steps from the diagonal downwards.
+//            buffered over four LDS objects, one barrier per step, steps from the
+//            diagonal downwards.
 //   math   = S^T[32 keys][16 rows] = K' Q'^T as two 16-key blocks, then
 //            O^T[d][16 rows] += V^T[d][32 keys] P^T. The query index is the MFMA column,
 //            so each lane owns one row (of each of its NB blocks) and the 16 lanes of a
@@ -38,8 +41,6 @@ namespace plamo {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr int kBN = 32;                // keys per step
 constexpr float kRescaleLog2 = 8.f;    // lazy-rescale threshold (log2 units)
 
@@ -70,8 +71,10 @@ __device__ __forceinline__ void block_barrier() {
 // kb: keys 8g .. 8g+7 over both blocks, in the order of the P^T operand.
 __device__ __forceinline__ int key_of(int m, int kb) { return ((m >> 2) << 3) | (kb << 2) | (m & 3); }
 
-template <int D, int NB, bool kLocal>
-__global__ __launch_bounds__(kThreads, 1) void prefill_wide_kernel(PrefillArgs a) {
+// D: head dim; NB: 16-row blocks per wave; kWaves: waves per block; kOcc: blocks per CU the
+// register budget is cut for.
+template <int D, int NB, int kWaves, int kOcc, bool kLocal>
+__global__ __launch_bounds__(kWaves * 64, kOcc) void prefill_wide_kernel(PrefillArgs a) {
   constexpr int kRowsW = 16 * NB;         // query rows per wave
   constexpr int BM = kWaves * kRowsW;     // query rows per block
   constexpr int kKS = D / 32;             // k-steps of S^T over the head dim
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wide_kernel(PrefillArgs a
   const int op_bytes = static_cast<int>(a.Tp * D * 2);
   const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(static_cast<const bf16_t*>(a.k_rot) + bh * a.Tp * D, op_bytes);
   const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(static_cast<const bf16_t*>(a.v_t) + bh * a.Tp * D, op_bytes);
-  // Copy i (0 .. 4 kLoads - 1) of a half tile fills LDS bytes 1024 i .. +1023. K': dim chunks
+  // Copy i (0 .. kWaves kLoads - 1) of a half tile fills LDS bytes 1024 i .. +1023. K': dim chunks
   // 2i and 2i+1, 32 keys each, from 512-byte runs 1 KiB apart in the 64-key tile; V^T: the
   // half's bytes in order. The half (0 or 1) goes in the scalar offset with the tile.
   const uint32_t k_off = static_cast<uint32_t>((2 * wave * kLoads + (lane >> 5)) * 1024 + (lane & 31) * 16);
@@ -238,20 +241,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wide_kernel(PrefillArgs a
     }
   };
 
-  // One step: copy the next half tile into the other buffers, wait for this one's copies
-  // (the next ones stay in flight), compute, and let every wave finish reading before the
-  // buffers are refilled one step later.
+  // One step, one barrier: each wave waits for its own copies of this step, and the barrier
+  // then says both that every copy of the step has landed and that every wave is done
+  // reading the other buffers (the previous step), which are refilled with the next half
+  // tile while this one is computed.
   auto run_step = [&](int step, const bf16_t* kbuf, const bf16_t* vbuf, bf16_t* k_next, bf16_t* v_next)
       __attribute__((always_inline)) {
-    if (step + 1 < n_steps) {
-      issue(step + 1, k_next, v_next);
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoads));
-    } else {
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
     block_barrier();
+    if (step + 1 < n_steps) issue(step + 1, k_next, v_next);
     compute(step, kbuf, vbuf);
-    block_barrier();
   };
 
   issue(0, ks0, vs0);
@@ -281,24 +280,30 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wide_kernel(PrefillArgs a
   }
 }
 
-template <int D, int NB>
+template <int D, int NB, int kWaves, int kOcc>
 hipError_t launch_wide(const PrefillArgs& a, hipStream_t stream) {
   constexpr int BM = kWaves * 16 * NB;
   const long long blocks = (a.T + BM - 1) / BM * static_cast<long long>(a.Hq) * a.B;
   if (a.window > 0)
-    hipLaunchKernelGGL((prefill_wide_kernel<D, NB, true>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((prefill_wide_kernel<D, NB, kWaves, kOcc, true>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kWaves * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_wide_kernel<D, NB, false>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((prefill_wide_kernel<D, NB, kWaves, kOcc, false>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
+#ifndef WIDE_CFG256
+#define WIDE_CFG256 2, 8, 1
+#endif
+#ifndef WIDE_CFG512
+#define WIDE_CFG512 1, 8, 1
+#endif
 hipError_t launch_prefill_wide_bf16(const PrefillArgs& a, hipStream_t stream) {
-  if (a.d == 256) return launch_wide<256, 2>(a, stream);
-  return launch_wide<512, 1>(a, stream);
+  if (a.d == 256) return launch_wide<256, WIDE_CFG256>(a, stream);
+  return launch_wide<512, WIDE_CFG512>(a, stream);
 }
 
 }  // namespace plamo
