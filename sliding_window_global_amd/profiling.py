@@ -21,7 +21,9 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 PREFILL_SOURCES = [os.path.join(PKG, "csrc", "prefill_bf16.hip"), os.path.join(PKG, "csrc", "common.h")]
 DECODE_SOURCES = [os.path.join(PKG, "csrc", "decode.hip"), os.path.join(PKG, "csrc", "common.h")]
-SOURCES = {"prefill": PREFILL_SOURCES, "decode": DECODE_SOURCES}
+SOURCES = {"prefill": PREFILL_SOURCES, "decode": DECODE_SOURCES,
+           "prefill_wide": [os.path.join(PKG, "csrc", "prefill_wide.hip"), os.path.join(PKG, "csrc", "common.h")],
+           "decode_wide": [os.path.join(PKG, "csrc", "decode_wide.hip"), os.path.join(PKG, "csrc", "common.h")]}
 
 
 def sources_sha256(paths) -> str:
