@@ -121,7 +121,8 @@ PLAMO_API long long plamo_prefill_padded_len(long long S);
  * v_norm   1 = divide each new V head vector by its RMS (eps norm_eps, no gain) before it
  *          is cached or used (the Gemma-4-shaped layer [P3 §8 table]); 0 = V as given.
  *          k and v may be the same buffer (that layer's global K = V projection).
- * q_out    [B, T, Hq, d]   normalised and rotated Q                (dtype, required)
+ * q_out    [B, T, Hq, d]   normalised and rotated Q (dtype). q and q_out both NULL: the
+ *                          queries are left to plamo_attn_prefill_fused_q.
  * k_rot_out rotated K of the S = kept + T keys the chunk attends, Tp =
  *                          plamo_prefill_padded_len(S) rows per (b, KV head): rows
  *                          0..kept-1 the cached (pre-RoPE) keys read from k_cache before
@@ -178,6 +179,26 @@ PLAMO_API int plamo_kv_append(int dtype, const void* q, const void* k, const voi
 PLAMO_API int plamo_attn_prefill(int dtype, const void* q_rot, const void* k_rot, const void* v_t,
                        void* out, int B, int T, int Hq, int Hkv, int d, int window,
                        long long pos_offset, float softmax_scale, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * plamo_attn_prefill_fused_q -- plamo_attn_prefill that applies steps 1 and 3 to the
+ * queries itself [P3 §4.3, §4.4, §6.1]
+ *
+ * q [B, T, Hq, d] are the projected queries as plamo_kv_append takes them; each query
+ * row is normalised (gain norm_offset + q_norm_w, eps norm_eps; q_norm_w NULL = no norm)
+ * and rotated with `rope_table` at the position plamo_kv_append would give it (renumbered
+ * kept + t, or absolute pos_offset + t with cache_order PLAMO_CACHE_POST_ROPE), in fp32,
+ * then rounded once to bf16 for the MFMA. Call plamo_kv_append with q = q_out = NULL
+ * first (it then writes only the K/V side: cache, k_rot, v_t), so Q' never goes through
+ * HBM. k_rot, v_t, out and the mask as for plamo_attn_prefill. bf16 and d = 128 only
+ * (PLAMO_ERR_UNSUPPORTED otherwise); the table must cover the queries' positions
+ * (PLAMO_ERR_WORKSPACE otherwise).
+ * ------------------------------------------------------------------------- */
+PLAMO_API int plamo_attn_prefill_fused_q(int dtype, const void* q, const void* q_norm_w,
+                       float norm_offset, float norm_eps, const void* k_rot, const void* v_t,
+                       void* out, int B, int T, int Hq, int Hkv, int d, int window,
+                       long long pos_offset, const void* rope_table, size_t rope_table_bytes,
+                       int cache_order, float softmax_scale, void* stream);
 
 /* ---------------------------------------------------------------------------
  * plamo_attn_decode -- step 4 for one new token per sequence, read from the cache
@@ -251,6 +272,13 @@ PLAMO_API int plamo_attn_prefill_ragged(int dtype, const void* q_rot, const void
                     const void* v_t, void* out, int B, int T, int Hq, int Hkv, int d,
                     int window, const long long* seq_pos_offsets, const int* seq_lens,
                     long long max_pos_offset, float softmax_scale, void* stream);
+
+PLAMO_API int plamo_attn_prefill_fused_q_ragged(int dtype, const void* q, const void* q_norm_w,
+                    float norm_offset, float norm_eps, const void* k_rot, const void* v_t,
+                    void* out, int B, int T, int Hq, int Hkv, int d, int window,
+                    const long long* seq_pos_offsets, const int* seq_lens, long long max_pos_offset,
+                    const void* rope_table, size_t rope_table_bytes, int cache_order,
+                    float softmax_scale, void* stream);
 
 PLAMO_API int plamo_attn_decode_ragged(int dtype, const void* q_rot, const void* k_cache,
                     const void* v_cache, long long cap, void* out, void* workspace,

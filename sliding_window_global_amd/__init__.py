@@ -30,6 +30,7 @@ __all__ = [
     "plamo_attn_decode_workspace_bytes", "plamo_attn_decode", "plamo_kv_append_ragged",
     "plamo_attn_prefill_ragged", "plamo_attn_decode_ragged_workspace_bytes", "plamo_attn_decode_ragged",
     "plamo_linear", "plamo_qkv_projection", "plamo_rms_norm", "library_path",
+    "plamo_attn_prefill_fused_q", "plamo_attn_prefill_fused_q_ragged",
 ]
 
 
@@ -170,13 +171,18 @@ def plamo_kv_append(q, k, v, q_out, *, window: int, pos_offset: int, rope_table,
                     v_norm: bool = False, stream=None) -> None:
     """q [B,T,Hq,d], k/v [B,T,Hkv,d] (k and v may be one tensor); outputs as documented in
     plamo_attn.h. v_norm: divide each V head vector by its RMS first."""
-    dt = q.dtype
-    B, T, Hq, d = q.shape
-    Hkv = k.shape[2]
-    if tuple(k.shape) != (B, T, Hkv, d) or tuple(v.shape) != (B, T, Hkv, d):
-        raise ValueError("k and v must be [B, T, Hkv, d] matching q")
-    if tuple(q_out.shape) != (B, T, Hq, d):
-        raise ValueError("q_out must match q")
+    dt = k.dtype
+    B, T, Hkv, d = k.shape
+    if q is None:  # K/V side only: the queries go to plamo_attn_prefill_fused_q
+        if q_out is not None:
+            raise ValueError("give q and q_out, or neither")
+        Hq = 0
+    else:
+        Hq = q.shape[2]
+        if tuple(q.shape) != (B, T, Hq, d) or tuple(q_out.shape) != (B, T, Hq, d):
+            raise ValueError("q and q_out must be [B, T, Hq, d] matching k")
+    if tuple(v.shape) != (B, T, Hkv, d):
+        raise ValueError("v must be [B, T, Hkv, d] matching k")
     k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dt, window, pos_offset)
     if k_rot_out is not None and tuple(k_rot_out.shape) != k_shape:
         raise ValueError(f"k_rot_out must be {list(k_shape)}")
@@ -191,7 +197,7 @@ def plamo_kv_append(q, k, v, q_out, *, window: int, pos_offset: int, rope_table,
         _dtype_code(dt), _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt),
         _dev(q_norm_w, "q_norm_w", dt), _dev(k_norm_w, "k_norm_w", dt), float(norm_offset), float(norm_eps),
         int(bool(v_norm)), _dev(q_out, "q_out", dt), _dev(k_rot_out, "k_rot_out", dt), _dev(v_t_out, "v_t_out", dt),
-        _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), int(cap), B, T, Hq, Hkv, d,
+        _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), int(cap), B, T, Hq or Hkv, Hkv, d,
         int(window), int(pos_offset), _dev(rope_table, "rope_table", torch.float32),
         rope_table.numel() * 4, _order(cache_post_rope), _stream(stream))
     _check(st, "plamo_kv_append")
@@ -213,6 +219,29 @@ def plamo_attn_prefill(q_rot, k_rot, v_t, out, *, window: int, pos_offset: int =
         _dtype_code(dt), _dev(q_rot, "q_rot", dt), _dev(k_rot, "k_rot", dt), _dev(v_t, "v_t", dt),
         _dev(out, "out", dt), B, T, Hq, Hkv, d, int(window), int(pos_offset), scale, _stream(stream))
     _check(st, "plamo_attn_prefill")
+
+
+def plamo_attn_prefill_fused_q(q, k_rot, v_t, out, *, window: int, rope_table, pos_offset: int = 0,
+                               q_norm_w=None, norm_offset: float = 1.0, norm_eps: float = 1e-6,
+                               cache_post_rope: bool = False, softmax_scale: float | None = None,
+                               stream=None) -> None:
+    """plamo_attn_prefill on the projected queries q [B,T,Hq,d] (bf16, d = 128): the kernel
+    normalises and rotates them itself; call plamo_kv_append with q = q_out = None first."""
+    dt = q.dtype
+    B, T, Hq, d = q.shape
+    Hkv = k_rot.shape[1]
+    k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dt, window, pos_offset)
+    if tuple(k_rot.shape) != k_shape or tuple(v_t.shape) != v_shape:
+        raise ValueError(f"k_rot must be {list(k_shape)} and v_t {list(v_shape)}")
+    if tuple(out.shape) != (B, T, Hq, d):
+        raise ValueError("out must match q")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    st = _lib.load().plamo_attn_prefill_fused_q(
+        _dtype_code(dt), _dev(q, "q", dt), _dev(q_norm_w, "q_norm_w", dt), float(norm_offset), float(norm_eps),
+        _dev(k_rot, "k_rot", dt), _dev(v_t, "v_t", dt), _dev(out, "out", dt), B, T, Hq, Hkv, d, int(window),
+        int(pos_offset), _dev(rope_table, "rope_table", torch.float32), _nbytes(rope_table),
+        _order(cache_post_rope), scale, _stream(stream))
+    _check(st, "plamo_attn_prefill_fused_q")
 
 
 def plamo_attn_decode_workspace_bytes(B: int, Hq: int, Hkv: int, window: int, pos_offset: int,
@@ -260,13 +289,18 @@ def plamo_kv_append_ragged(q, k, v, q_out, *, window: int, seq_pos_offsets, max_
                            stream=None) -> None:
     """plamo_kv_append with per-sequence positions seq_pos_offsets [B] (int64, GPU) bounded by
     max_pos_offset and token counts seq_lens [B] (int32, GPU; None = T each)."""
-    dt = q.dtype
-    B, T, Hq, d = q.shape
-    Hkv = k.shape[2]
-    if tuple(k.shape) != (B, T, Hkv, d) or tuple(v.shape) != (B, T, Hkv, d):
-        raise ValueError("k and v must be [B, T, Hkv, d] matching q")
-    if tuple(q_out.shape) != (B, T, Hq, d):
-        raise ValueError("q_out must match q")
+    dt = k.dtype
+    B, T, Hkv, d = k.shape
+    if q is None:  # K/V side only: the queries go to plamo_attn_prefill_fused_q_ragged
+        if q_out is not None:
+            raise ValueError("give q and q_out, or neither")
+        Hq = 0
+    else:
+        Hq = q.shape[2]
+        if tuple(q.shape) != (B, T, Hq, d) or tuple(q_out.shape) != (B, T, Hq, d):
+            raise ValueError("q and q_out must be [B, T, Hq, d] matching k")
+    if tuple(v.shape) != (B, T, Hkv, d):
+        raise ValueError("v must be [B, T, Hkv, d] matching k")
     k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dt, window, max_pos_offset)
     if k_rot_out is not None and tuple(k_rot_out.shape) != k_shape:
         raise ValueError(f"k_rot_out must be {list(k_shape)}")
@@ -282,7 +316,7 @@ def plamo_kv_append_ragged(q, k, v, q_out, *, window: int, seq_pos_offsets, max_
         _dtype_code(dt), _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt),
         _dev(q_norm_w, "q_norm_w", dt), _dev(k_norm_w, "k_norm_w", dt), float(norm_offset), float(norm_eps),
         int(bool(v_norm)), _dev(q_out, "q_out", dt), _dev(k_rot_out, "k_rot_out", dt), _dev(v_t_out, "v_t_out", dt),
-        _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), int(cap), B, T, Hq, Hkv, d,
+        _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), int(cap), B, T, Hq or Hkv, Hkv, d,
         int(window), pos_p, len_p, int(max_pos_offset), _dev(rope_table, "rope_table", torch.float32),
         rope_table.numel() * 4, _order(cache_post_rope), _stream(stream))
     _check(st, "plamo_kv_append_ragged")
@@ -306,6 +340,29 @@ def plamo_attn_prefill_ragged(q_rot, k_rot, v_t, out, *, window: int, seq_pos_of
         _dev(out, "out", dt), B, T, Hq, Hkv, d, int(window), pos_p, len_p, int(max_pos_offset), scale,
         _stream(stream))
     _check(st, "plamo_attn_prefill_ragged")
+
+
+def plamo_attn_prefill_fused_q_ragged(q, k_rot, v_t, out, *, window: int, seq_pos_offsets, max_pos_offset: int,
+                                      rope_table, seq_lens=None, q_norm_w=None, norm_offset: float = 1.0,
+                                      norm_eps: float = 1e-6, cache_post_rope: bool = False,
+                                      softmax_scale: float | None = None, stream=None) -> None:
+    """plamo_attn_prefill_fused_q with per-sequence positions and token counts."""
+    dt = q.dtype
+    B, T, Hq, d = q.shape
+    Hkv = k_rot.shape[1]
+    k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dt, window, max_pos_offset)
+    if tuple(k_rot.shape) != k_shape or tuple(v_t.shape) != v_shape:
+        raise ValueError(f"k_rot must be {list(k_shape)} and v_t {list(v_shape)}")
+    if tuple(out.shape) != (B, T, Hq, d):
+        raise ValueError("out must match q")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    pos_p, len_p = _ragged_arrays(B, seq_pos_offsets, seq_lens)
+    st = _lib.load().plamo_attn_prefill_fused_q_ragged(
+        _dtype_code(dt), _dev(q, "q", dt), _dev(q_norm_w, "q_norm_w", dt), float(norm_offset), float(norm_eps),
+        _dev(k_rot, "k_rot", dt), _dev(v_t, "v_t", dt), _dev(out, "out", dt), B, T, Hq, Hkv, d, int(window),
+        pos_p, len_p, int(max_pos_offset), _dev(rope_table, "rope_table", torch.float32), _nbytes(rope_table),
+        _order(cache_post_rope), scale, _stream(stream))
+    _check(st, "plamo_attn_prefill_fused_q_ragged")
 
 
 def plamo_attn_decode_ragged_workspace_bytes(B: int, Hq: int, Hkv: int, window: int, max_pos_offset: int,

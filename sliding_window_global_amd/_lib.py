@@ -27,6 +27,13 @@ SIGNATURES = {
                                 c_int, c_int, c_int, c_ll, c_void_p, c_size, c_int, c_void_p]),
     "plamo_attn_prefill": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                    c_int, c_int, c_ll, c_float, c_void_p]),
+    "plamo_attn_prefill_fused_q": (c_int, [c_int, c_void_p, c_void_p, c_float, c_float, c_void_p, c_void_p,
+                                           c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_ll, c_void_p,
+                                           c_size, c_int, c_float, c_void_p]),
+    "plamo_attn_prefill_fused_q_ragged": (c_int, [c_int, c_void_p, c_void_p, c_float, c_float, c_void_p,
+                                                  c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
+                                                  c_void_p, c_void_p, c_ll, c_void_p, c_size, c_int, c_float,
+                                                  c_void_p]),
     "plamo_attn_decode_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int, c_ll]),
     "plamo_attn_decode": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_ll, c_void_p, c_void_p, c_size, c_int,
                                   c_int, c_int, c_int, c_int, c_int, c_ll, c_void_p, c_size, c_float, c_int,

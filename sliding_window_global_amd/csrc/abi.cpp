@@ -160,7 +160,8 @@ int kv_append_impl(int dtype, const void* q, const void* k, const void* v, const
   if (d != kHeadDim && dtype != PLAMO_BF16) return fail(PLAMO_ERR_UNSUPPORTED, "head dims 256 and 512 are bf16 only");
   if (v_norm != 0 && v_norm != 1) return fail(PLAMO_ERR_INVALID_ARG, "v_norm must be 0 or 1");
   if (B == 0 || T == 0) return ok();
-  if (!q || !k || !v || !q_out) return fail(PLAMO_ERR_INVALID_ARG, "q, k, v and q_out must be non-NULL");
+  if (!k || !v) return fail(PLAMO_ERR_INVALID_ARG, "k and v must be non-NULL");
+  if ((q == nullptr) != (q_out == nullptr)) return fail(PLAMO_ERR_INVALID_ARG, "give q and q_out, or neither");
   if ((q_norm_w == nullptr) != (k_norm_w == nullptr))
     return fail(PLAMO_ERR_INVALID_ARG, "give both norm weights or neither");
   if ((k_cache == nullptr) != (v_cache == nullptr))
@@ -184,7 +185,7 @@ int kv_append_impl(int dtype, const void* q, const void* k, const void* v, const
   if (post && covered < pos_offset + T)
     return fail(PLAMO_ERR_WORKSPACE, "post-RoPE cache: rope table does not cover positions < pos_offset + T");
 
-  plamo::AppendArgs a;
+  plamo::AppendArgs a{};
   a.q = q; a.k = k; a.v = v; a.wq = q_norm_w; a.wk = k_norm_w;
   a.norm_offset = norm_offset; a.eps = norm_eps;
   a.q_out = q_out; a.k_rot_out = k_rot_out; a.v_t_out = v_t_out;
@@ -202,9 +203,19 @@ int kv_append_impl(int dtype, const void* q, const void* k, const void* v, const
   return launched(dtype == PLAMO_BF16 ? plamo::launch_kv_append_bf16(a, s) : plamo::launch_kv_append_f32(a, s));
 }
 
+// Steps 1 and 3 for Q done inside the prefill (plamo_attn_prefill_fused_q).
+struct FusedQ {
+  const void* q_norm_w;
+  float norm_offset, norm_eps;
+  const void* rope_table;
+  size_t rope_table_bytes;
+  int cache_order;
+};
+
 int attn_prefill_impl(int dtype, const void* q_rot, const void* k_rot, const void* v_t, void* out,
                       int B, int T, int Hq, int Hkv, int d, int window, long long pos_offset,
-                      const long long* seq_pos, const int* seq_len, float softmax_scale, void* stream) {
+                      const long long* seq_pos, const int* seq_len, float softmax_scale, void* stream,
+                      const FusedQ* fq = nullptr) {
   if (dtype != PLAMO_F32 && dtype != PLAMO_BF16) return fail(PLAMO_ERR_INVALID_ARG, "unknown dtype");
   if (int st = check_heads(B, T, Hq, Hkv, d, window, pos_offset)) return st;
   if (d != kHeadDim && dtype != PLAMO_BF16) return fail(PLAMO_ERR_UNSUPPORTED, "head dims 256 and 512 are bf16 only");
@@ -219,11 +230,27 @@ int attn_prefill_impl(int dtype, const void* q_rot, const void* k_rot, const voi
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return fail(PLAMO_ERR_INVALID_ARG, "softmax_scale must be > 0");
+  if (fq) {
+    if (dtype != PLAMO_BF16 || d != kHeadDim)
+      return fail(PLAMO_ERR_UNSUPPORTED, "the fused-Q prefill is bf16 with d = 128");
+    if (fq->cache_order != PLAMO_CACHE_PRE_ROPE && fq->cache_order != PLAMO_CACHE_POST_ROPE)
+      return fail(PLAMO_ERR_INVALID_ARG, "unknown cache_order");
+    if (!(fq->norm_eps >= 0.f) || !std::isfinite(fq->norm_offset))
+      return fail(PLAMO_ERR_INVALID_ARG, "bad norm offset/eps");
+    if (!fq->rope_table) return fail(PLAMO_ERR_INVALID_ARG, "rope_table must be non-NULL");
+    if ((fq->q_norm_w && !aligned16(fq->q_norm_w)) || !aligned16(fq->rope_table))
+      return fail(PLAMO_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    const long long covered = table_positions(fq->rope_table_bytes, d);
+    if (covered < 0) return fail(PLAMO_ERR_INVALID_ARG, "rope_table_bytes is not a whole number of rows");
+    const bool post = fq->cache_order == PLAMO_CACHE_POST_ROPE;
+    if (covered < (post ? pos_offset : kept) + T)
+      return fail(PLAMO_ERR_WORKSPACE, "rope table does not cover the queries' positions");
+  }
   const int rows_per_block = d == 512 ? 64 : 128;
   const long long blocks = (static_cast<long long>(T) + rows_per_block - 1) / rows_per_block * Hq * static_cast<long long>(B);
   if (blocks > 0x7fffffffLL) return fail(PLAMO_ERR_UNSUPPORTED, "grid too large");
 
-  plamo::PrefillArgs a;
+  plamo::PrefillArgs a{};
   a.q_rot = q_rot; a.k_rot = k_rot; a.v_t = v_t; a.out = out;
   a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.window = window;
   a.Tp = plamo_prefill_padded_len(kept + T);
@@ -232,6 +259,14 @@ int attn_prefill_impl(int dtype, const void* q_rot, const void* k_rot, const voi
   a.seq_pos = seq_pos; a.seq_len = seq_len;
   a.scale = softmax_scale;
   a.d = d;
+  if (fq) {
+    a.fuse_q = true;
+    a.post_rope = fq->cache_order == PLAMO_CACHE_POST_ROPE;
+    a.wq = fq->q_norm_w;
+    a.norm_offset = fq->norm_offset;
+    a.eps = fq->norm_eps;
+    a.rope = static_cast<const float2*>(fq->rope_table);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d != kHeadDim) return launched(plamo::launch_prefill_wide_bf16(a, s));
   return launched(dtype == PLAMO_BF16 ? plamo::launch_prefill_bf16(a, s) : plamo::launch_prefill_f32(a, s));
@@ -272,7 +307,7 @@ int attn_decode_impl(int dtype, const void* q_rot, const void* k_cache, const vo
   if (need > 0 && (!workspace || workspace_bytes < need)) return fail(PLAMO_ERR_WORKSPACE, "workspace too small");
   if (static_cast<long long>(B) * Hq > 0x7fffffffLL) return fail(PLAMO_ERR_UNSUPPORTED, "grid too large");
 
-  plamo::DecodeArgs a;
+  plamo::DecodeArgs a{};
   a.q_rot = q_rot; a.k_cache = k_cache; a.v_cache = v_cache; a.cap = cap; a.out = out;
   a.ws = static_cast<float*>(workspace);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.window = window;
@@ -329,6 +364,30 @@ int plamo_attn_prefill_ragged(int dtype, const void* q_rot, const void* k_rot, c
     if (int st = check_ragged(seq_pos_offsets, seq_lens)) return st;
   return attn_prefill_impl(dtype, q_rot, k_rot, v_t, out, B, T, Hq, Hkv, d, window, max_pos_offset,
                            seq_pos_offsets, seq_lens, softmax_scale, stream);
+}
+
+int plamo_attn_prefill_fused_q(int dtype, const void* q, const void* q_norm_w, float norm_offset,
+                               float norm_eps, const void* k_rot, const void* v_t, void* out, int B, int T,
+                               int Hq, int Hkv, int d, int window, long long pos_offset,
+                               const void* rope_table, size_t rope_table_bytes, int cache_order,
+                               float softmax_scale, void* stream) {
+  const FusedQ fq{q_norm_w, norm_offset, norm_eps, rope_table, rope_table_bytes, cache_order};
+  return attn_prefill_impl(dtype, q, k_rot, v_t, out, B, T, Hq, Hkv, d, window, pos_offset, nullptr, nullptr,
+                           softmax_scale, stream, &fq);
+}
+
+int plamo_attn_prefill_fused_q_ragged(int dtype, const void* q, const void* q_norm_w, float norm_offset,
+                                      float norm_eps, const void* k_rot, const void* v_t, void* out, int B,
+                                      int T, int Hq, int Hkv, int d, int window,
+                                      const long long* seq_pos_offsets, const int* seq_lens,
+                                      long long max_pos_offset, const void* rope_table,
+                                      size_t rope_table_bytes, int cache_order, float softmax_scale,
+                                      void* stream) {
+  if (B > 0 && T > 0)
+    if (int st = check_ragged(seq_pos_offsets, seq_lens)) return st;
+  const FusedQ fq{q_norm_w, norm_offset, norm_eps, rope_table, rope_table_bytes, cache_order};
+  return attn_prefill_impl(dtype, q, k_rot, v_t, out, B, T, Hq, Hkv, d, window, max_pos_offset, seq_pos_offsets,
+                           seq_lens, softmax_scale, stream, &fq);
 }
 
 size_t plamo_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int window, long long pos_offset) {

@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
       __syncthreads();
     }
     const int nt = min(kRopeTok<D>, n_tok - ts);
-    rows(q, nt * G, false, 0, ts);
+    if (q_out) rows(q, nt * G, false, 0, ts);  // (no Q: the prefill normalises and rotates it)
     rows(k, nt, true, 1, ts);
   }
 

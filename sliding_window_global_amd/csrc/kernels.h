@@ -56,6 +56,13 @@ struct PrefillArgs {
   const int* seq_len;        // ragged batch: per-sequence token count (device), else NULL
   float scale;
   int d;                     // head dim: 128, 256 or 512 (bf16)
+  // Fused Q (bf16, d = 128): q_rot then holds the projected queries, normalised (when wq is
+  // given: gain norm_offset + w, eps) and rotated here at the positions the append uses.
+  bool fuse_q;
+  bool post_rope;            // (fused Q) rotate at absolute positions
+  const void* wq;
+  float norm_offset, eps;
+  const float2* rope;
 };
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 // Head dims 256 and 512 (bf16).

@@ -74,7 +74,9 @@ __device__ __forceinline__ int k_chunk(int r, int c) { return (c * BN + r) * 8; 
 __device__ __forceinline__ int v_chunk(int d, int c) { return (c * kHeadDim + d) * 8; }
 
 // kLocal: sliding-window layer (window > 0); otherwise the global causal layer.
-template <bool kLocal>
+// kFuseQ: q_rot holds the projected queries; the block normalises and rotates its rows
+// itself (steps 1 and 3 of §4.4 for Q), so that the append need not write Q' to HBM.
+template <bool kLocal, bool kFuseQ>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // Four separate LDS objects (not one indexed array): with the loop unrolled by two,
   // every LDS read names a buffer that no in-flight direct load targets, so the
@@ -148,6 +150,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   auto issue_k = [&](int step, bf16_t* buf) __attribute__((always_inline)) { issue(k_rsrc, step, buf); };
   auto issue_v = [&](int step, bf16_t* buf) __attribute__((always_inline)) { issue(v_rsrc, step, buf); };
 
+  // K'(0) is copied while the Q' fragments below are loaded (and, fused, formed): the two
+  // latencies overlap instead of adding up.
+  issue_k(0, ks0);
+
   // ---- Q' fragment (MFMA B operand): lane holds dims s*16 + hl*8 .. +7 of its row ----
   // Pre-multiplied by scale * log2(e), so that S comes out of the MFMA in exp2 units.
   const float c = a.scale * 1.4426950408889634f;
@@ -159,13 +165,66 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     const bool ok = qrow < n_rows;
     const bf16_t* src = q + (static_cast<long long>(b) * a.T + (ok ? qrow : 0)) * a.Hq * kHeadDim +
                         static_cast<long long>(hq) * kHeadDim + hl * 8;
+    if (!kFuseQ) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      u32x4 w = ok ? *reinterpret_cast<const u32x4*>(src + s * 16) : u32x4{0, 0, 0, 0};
+      for (int s = 0; s < 8; ++s) {
+        u32x4 w = ok ? *reinterpret_cast<const u32x4*>(src + s * 16) : u32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = pack_bf16x2(lo_bf16(w[i]) * c, hi_bf16(w[i]) * c);
-      qf[s] = __builtin_bit_cast(bf16x8, w);
+        for (int i = 0; i < 4; ++i)
+          w[i] = pack_bf16x2(lo_bf16(w[i]) * c, hi_bf16(w[i]) * c);
+        qf[s] = __builtin_bit_cast(bf16x8, w);
+      }
+    } else {
+      // §3.2 / §4.3: x (c' + w) / sqrt(mean(x^2) + eps) over the row's 128 dims (the other 64
+      // sit in lane n ^ 32); §6.1: pair j (dims j, j + 64) turns by the angle of position
+      // kept + qrow (post-RoPE cache: pos + qrow), factor amp exp(i p w_j) from the table. The
+      // lane's pairs are j = s*16 + hl*8 + e, s < 4, partners in slice s + 4: all lane-local.
+      float x[8][8];
+      float ss = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const u32x4 w = ok ? *reinterpret_cast<const u32x4*>(src + s * 16) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[s][2 * i] = lo_bf16(w[i]);
+          x[s][2 * i + 1] = hi_bf16(w[i]);
+          ss += x[s][2 * i] * x[s][2 * i] + x[s][2 * i + 1] * x[s][2 * i + 1];
+        }
+      }
+      if (a.wq) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+        const float inv = rsqrtf((__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * (1.f / kHeadDim) + a.eps);
+        const bf16_t* wq = static_cast<const bf16_t*>(a.wq) + hl * 8;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const u32x4 gw = *reinterpret_cast<const u32x4*>(wq + s * 16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[s][2 * i] *= inv * (a.norm_offset + lo_bf16(gw[i]));
+            x[s][2 * i + 1] *= inv * (a.norm_offset + hi_bf16(gw[i]));
+          }
+        }
+      }
+      const long long pos = (a.post_rope ? sp.pos : sp.kept) + (ok ? qrow : 0);
+      const float2* fine = a.rope + (pos & (kRopeFine - 1)) * kHalf + hl * 8;
+      const float2* coarse = a.rope + (kRopeFine + (pos >> 6)) * kHalf + hl * 8;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 f = fine[s * 16 + e], cz = coarse[s * 16 + e];
+          const float zx = cz.x * f.x - cz.y * f.y, zy = cz.x * f.y + cz.y * f.x;
+          const float x0 = x[s][e], x1 = x[s + 4][e];
+          x[s][e] = x0 * zx - x1 * zy;
+          x[s + 4][e] = x0 * zy + x1 * zx;
+        }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(x[s][2 * i] * c, x[s][2 * i + 1] * c);
+        qf[s] = __builtin_bit_cast(bf16x8, w);
+      }
     }
   }
 
@@ -332,7 +391,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   };
 
   // ---- K'(0) in LDS; S^T(0) while K'(1) and V^T(0) arrive; then steps 0 .. n_tiles-1 ----
-  issue_k(0, ks0);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   f32x16 s_a[2], s_b[2];  // S^T of the current and of the next tile, roles alternating
@@ -371,13 +429,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   const long long nqb = (a.T + BM - 1) / BM;
-  const long long blocks = nqb * a.Hq * a.B;
-  if (a.window > 0)
-    hipLaunchKernelGGL(prefill_bf16_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL(prefill_bf16_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       stream, a);
+  const dim3 grid(static_cast<unsigned>(nqb * a.Hq * a.B));
+  if (a.window > 0) {
+    if (a.fuse_q)
+      hipLaunchKernelGGL((prefill_bf16_kernel<true, true>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_bf16_kernel<true, false>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    if (a.fuse_q)
+      hipLaunchKernelGGL((prefill_bf16_kernel<false, true>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_bf16_kernel<false, false>), grid, dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

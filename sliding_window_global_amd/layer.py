@@ -13,9 +13,10 @@ import torch
 
 from dataclasses import dataclass
 
-from . import (plamo_linear, plamo_qkv_projection, plamo_rms_norm, plamo_attn_decode, plamo_attn_decode_ragged, plamo_attn_decode_ragged_workspace_bytes,
-               plamo_attn_decode_workspace_bytes,
-               plamo_attn_prefill, plamo_attn_prefill_ragged, plamo_kv_append, plamo_kv_append_ragged,
+from . import (plamo_attn_decode, plamo_attn_decode_ragged, plamo_attn_decode_ragged_workspace_bytes,
+               plamo_attn_decode_workspace_bytes, plamo_attn_prefill, plamo_attn_prefill_fused_q,
+               plamo_attn_prefill_fused_q_ragged, plamo_attn_prefill_ragged, plamo_kv_append,
+               plamo_kv_append_ragged, plamo_linear, plamo_qkv_projection, plamo_rms_norm,
                prefill_operand_shapes)
 
 
@@ -33,15 +34,27 @@ class PrefillBuffers:
 
 def prefill(q, k, v, *, window, rope_table, q_norm_w=None, k_norm_w=None, norm_offset=1.0,
             norm_eps=1e-6, k_cache=None, v_cache=None, bufs: PrefillBuffers | None = None,
-            softmax_scale=None, stream=None, pos_offset=0, cache_post_rope=False, v_norm=False) -> PrefillBuffers:
+            softmax_scale=None, stream=None, pos_offset=0, cache_post_rope=False, v_norm=False,
+            fuse_q=False) -> PrefillBuffers:
     """Prefill of a chunk q [B,T,Hq,d], k/v [B,T,Hkv,d] on the GPU whose first token sits at
     absolute position pos_offset. With pos_offset > 0 the caches must hold the earlier tokens
     (they are read for the chunk's attention, then updated with the chunk). v_norm: V divided
-    by its RMS per head vector (the Gemma-4-shaped layer)."""
+    by its RMS per head vector (the Gemma-4-shaped layer). fuse_q (bf16, d = 128): the append
+    handles K and V only and the prefill kernel normalises and rotates Q itself."""
     B, T, Hq, d = q.shape
     Hkv = k.shape[2]
     if bufs is None:
         bufs = PrefillBuffers(B, T, Hq, Hkv, d, q.dtype, q.device, window, pos_offset)
+    if fuse_q:
+        plamo_kv_append(None, k, v, None, window=window, pos_offset=pos_offset, rope_table=rope_table,
+                        q_norm_w=q_norm_w, k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps,
+                        k_rot_out=bufs.k_rot, v_t_out=bufs.v_t, k_cache=k_cache, v_cache=v_cache,
+                        cache_post_rope=cache_post_rope, v_norm=v_norm, stream=stream)
+        plamo_attn_prefill_fused_q(q, bufs.k_rot, bufs.v_t, bufs.out, window=window, rope_table=rope_table,
+                                   pos_offset=pos_offset, q_norm_w=q_norm_w, norm_offset=norm_offset,
+                                   norm_eps=norm_eps, cache_post_rope=cache_post_rope,
+                                   softmax_scale=softmax_scale, stream=stream)
+        return bufs
     plamo_kv_append(q, k, v, bufs.q_rot, window=window, pos_offset=pos_offset, rope_table=rope_table,
                     q_norm_w=q_norm_w, k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps,
                     k_rot_out=bufs.k_rot, v_t_out=bufs.v_t, k_cache=k_cache, v_cache=v_cache,
@@ -85,13 +98,26 @@ def decode(q, k, v, k_cache, v_cache, *, window, pos_offset, rope_table, q_norm_
 def prefill_ragged(q, k, v, *, window, rope_table, seq_pos_offsets, max_pos_offset, seq_lens=None,
                    q_norm_w=None, k_norm_w=None, norm_offset=1.0, norm_eps=1e-6, k_cache=None,
                    v_cache=None, bufs: PrefillBuffers | None = None, softmax_scale=None,
-                   stream=None, cache_post_rope=False, v_norm=False) -> PrefillBuffers:
+                   stream=None, cache_post_rope=False, v_norm=False, fuse_q=False) -> PrefillBuffers:
     """Prefill of a ragged batch: sequence b's seq_lens[b] new tokens (rows of its [T] slab)
     start at absolute position seq_pos_offsets[b] <= max_pos_offset."""
     B, T, Hq, d = q.shape
     Hkv = k.shape[2]
     if bufs is None:
         bufs = PrefillBuffers(B, T, Hq, Hkv, d, q.dtype, q.device, window, max_pos_offset)
+    if fuse_q:
+        plamo_kv_append_ragged(None, k, v, None, window=window, seq_pos_offsets=seq_pos_offsets,
+                               max_pos_offset=max_pos_offset, seq_lens=seq_lens, rope_table=rope_table,
+                               q_norm_w=q_norm_w, k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps,
+                               k_rot_out=bufs.k_rot, v_t_out=bufs.v_t, k_cache=k_cache, v_cache=v_cache,
+                               cache_post_rope=cache_post_rope, v_norm=v_norm, stream=stream)
+        plamo_attn_prefill_fused_q_ragged(q, bufs.k_rot, bufs.v_t, bufs.out, window=window,
+                                          seq_pos_offsets=seq_pos_offsets, max_pos_offset=max_pos_offset,
+                                          rope_table=rope_table, seq_lens=seq_lens, q_norm_w=q_norm_w,
+                                          norm_offset=norm_offset, norm_eps=norm_eps,
+                                          cache_post_rope=cache_post_rope, softmax_scale=softmax_scale,
+                                          stream=stream)
+        return bufs
     plamo_kv_append_ragged(q, k, v, bufs.q_rot, window=window, seq_pos_offsets=seq_pos_offsets,
                            max_pos_offset=max_pos_offset, seq_lens=seq_lens, rope_table=rope_table,
                            q_norm_w=q_norm_w, k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps,

@@ -127,6 +127,33 @@ def test_kv_append_validation(lib, over, status):
     assert lib.plamo_last_error()
 
 
+def test_kv_append_without_queries(lib):
+    # q and q_out both NULL: the K/V side only (for the fused-Q prefill); one of them alone is an error
+    assert _append(lib, q=None) == INVALID
+    assert _append(lib, q_out=None) == INVALID
+    assert _append(lib, q=None, q_out=None, k=None) == INVALID
+
+
+def test_prefill_fused_q_validation(lib):
+    def fused(**over):
+        a = dict(dtype=BF16, q=FAKE, wq=FAKE, c=1.0, eps=1e-6, k=FAKE, v=FAKE, out=FAKE, B=1, T=100, Hq=8, Hkv=2,
+                 d=128, window=0, pos=0, table=FAKE, table_bytes=(64 + 2) * 512, order=0, scale=0.0884)
+        a.update(over)
+        return lib.plamo_attn_prefill_fused_q(a["dtype"], a["q"], a["wq"], a["c"], a["eps"], a["k"], a["v"], a["out"],
+                                              a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], a["window"], a["pos"],
+                                              a["table"], a["table_bytes"], a["order"], a["scale"], None)
+    assert fused(dtype=F32) == UNSUPPORTED
+    assert fused(d=256) == UNSUPPORTED
+    assert fused(table=None) == INVALID
+    assert fused(table_bytes=100) == INVALID
+    assert fused(T=200) == WORKSPACE                  # the table covers positions < 128 only
+    assert fused(order=1, pos=40, window=16, T=100) == WORKSPACE  # post-RoPE: absolute positions 40 .. 139
+    assert fused(order=3) == INVALID
+    assert fused(wq=MISALIGNED) == INVALID
+    assert fused(eps=-1.0) == INVALID
+    assert fused(T=0, q=None) == OK
+
+
 def test_kv_append_empty_is_ok(lib):
     assert _append(lib, T=0, q=None, k=None, v=None, q_out=None) == OK
     assert _append(lib, B=0, q=None, k=None, v=None, q_out=None) == OK
