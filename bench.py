@@ -1,10 +1,10 @@
 """Benchmark of the PLaMo 3 hybrid attention hot path on one MI355X.
 
 One JSON line on stdout. The headline step is one local-layer prefill at the PLaMo 3
-shape (B=1, T=8192, Hq=64, Hkv=8, d=128, W=2048): plamo_kv_append (K norm, cache
-write, K RoPE, prefill operands) + plamo_attn_prefill_fused_q (Q norm and RoPE inside the
-attention kernel), inputs resident in HBM; the same step with Q' written and read back
-through HBM is reported in ``extra``. ``value``
+shape (B=1, T=8192, Hq=64, Hkv=8, d=128, W=2048): plamo_kv_append (QK norm, cache
+write, RoPE, prefill operands) + plamo_attn_prefill, inputs resident in HBM; the same step
+with the queries normalised and rotated inside the attention kernel
+(plamo_attn_prefill_fused_q) is reported in ``extra``. ``value``
 is algorithmic prefill FLOP (4*d per attended (query, key) pair and query head) per
 second of that step. Also reported: the global-layer prefill (T=32768, YaRN), batched
 decode (B=64; ring W=2048 and global 32768) as KV-read GB/s, the same global decode with
@@ -74,7 +74,7 @@ def rope_params(swg, r):
 # prefill
 # ----------------------------------------------------------------------------
 
-def bench_prefill(torch, swg, wl, steps, warmup, norm_offset, fuse_q=True):
+def bench_prefill(torch, swg, wl, steps, warmup, norm_offset, fuse_q=False):
     """One prefill step: plamo_kv_append + the attention. fuse_q: the append writes only the K/V
     side and plamo_attn_prefill_fused_q normalises and rotates Q inside the attention kernel
     (Q' never goes through HBM); otherwise the append writes Q' and plamo_attn_prefill reads it."""
@@ -487,12 +487,12 @@ def main():
         log("[bench] local prefill T=8192 W=2048")
         local = bench_prefill(torch, swg, LOCAL_PREFILL, args.steps, args.warmup, LOCAL_PREFILL.norm_offset)
         log(f"[bench]   {local}")
-        log("[bench] local prefill, Q' through HBM (append writes it, the attention reads it)")
+        log("[bench] local prefill, Q normalised and rotated inside the attention kernel")
         u = bench_prefill(torch, swg, LOCAL_PREFILL, args.steps, args.warmup, LOCAL_PREFILL.norm_offset,
-                          fuse_q=False)
+                          fuse_q=True)
         log(f"[bench]   {u}")
-        extra["prefill_local_unfused_q"] = {k: u[k] for k in ("workload", "ms_per_step", "ms_attn", "step_tflops",
-                                                               "attn_tflops")}
+        extra["prefill_local_fused_q"] = {k: u[k] for k in ("workload", "ms_per_step", "ms_attn", "step_tflops",
+                                                             "attn_tflops")}
     if only in ("", "prefill_global"):
         log("[bench] global prefill T=32768 YaRN")
         g = bench_prefill(torch, swg, GLOBAL_PREFILL, max(3, args.steps // 4), max(1, args.warmup // 2),
@@ -574,12 +574,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": LOCAL_PREFILL.name, "B": 1, "T": 8192, "Hq": 64, "Hkv": 8, "d": 128,
                    "window": 2048,
-                   "step": "kv_append (K, V: norm, cache, RoPE, operands) + attn_prefill_fused_q (Q norm, RoPE, attention)"},
+                   "step": "kv_append + attn_prefill"},
         "roofline": {"bound": "mfma", "achieved": round(local["attn_tflops"], 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(local["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
                      "traffic": read_traffic(os.path.join(ROOT, "profiles", "prefill_local_T8192_hbm_traffic.txt")),
-                     "kernel": "prefill_bf16_kernel<true, true>", "flop_per_launch": LOCAL_PREFILL.flops()},
+                     "kernel": "prefill_bf16_kernel<true, false>", "flop_per_launch": LOCAL_PREFILL.flops()},
         "cpu_baseline": cpu,
         "extra": extra,
     }
