@@ -195,3 +195,72 @@ def test_gemma_decode_full_size(wl):
         cache = LayerKVCache.with_prior(prior[b][0], prior[b][1], p, W, post_rope=True)
         ref = oracle_step(L, x["q"][b], x["k"][b], x["v"][b], cache, x["wq"], x["wk"])
         assert_parity(out[b], ref, TOL_BF16, f"{wl.name}, sequence {b}")
+
+
+@pytest.mark.parametrize("L,window", [(GEMMA_LOCAL_LAYER, 100), (GEMMA_GLOBAL_LAYER, 0)], ids=["d256_W100", "d512"])
+def test_gemma_ragged_batch(L, window):
+    """A ragged batch of the Gemma-shaped layers: each step gives every sequence its own
+    position and token count (0 = it sits the step out), then one ragged decode step; input
+    rows past a sequence's count are NaN (never read), output rows past it keep a sentinel
+    (never written). Every sequence against the oracle run on its own stream in the same chunks."""
+    import dataclasses
+    Hq, Hkv = (4, 2) if window else (8, 1)
+    L = dataclasses.replace(L, Hq=Hq, Hkv=Hkv, window=window)
+    B, d = 3, L.d
+    lens = np.array([[150, 37, 90], [70, 130, 0]], dtype=np.int64)
+    n_tot = lens.sum(0) + 1
+    dr = Draw(7300 + window, True)
+    streams = [L.draw_tokens(dr, 1, int(n)) for n in n_tot]
+    wq, wk = L.draw_gains(dr)
+    cap = window if window else int(n_tot.sum())
+    kc = torch.zeros((B, Hkv, cap, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    tab = table_for(L, int(n_tot.sum()) + 64)
+    kw = gpu_kw(L, wq, wk)
+    pos = np.zeros(B, np.int64)
+    got = [[] for _ in range(B)]
+    sentinel = 123.0
+
+    def slabs(L_, T):
+        out = []
+        for i in range(3):
+            x = np.full((B, T) + streams[0][i].shape[2:], np.nan, np.float32)
+            for b in range(B):
+                x[b, :L_[b]] = streams[b][i][0, pos[b]:pos[b] + L_[b]]
+            out.append(dev(x))
+        if L.kv_shared:  # one tensor for K and V, as the layer's projection gives them
+            out[2] = out[1]
+        return out
+
+    for Ls in lens:
+        T = int(Ls.max())
+        maxp = int(pos.max())
+        bufs = layer.PrefillBuffers(B, T, Hq, Hkv, d, torch.bfloat16, "cuda", window, maxp)
+        bufs.out.fill_(sentinel)
+        layer.prefill_ragged(*slabs(Ls, T), window=window, rope_table=tab,
+                             seq_pos_offsets=torch.tensor(pos, device="cuda"), max_pos_offset=maxp,
+                             seq_lens=torch.tensor(Ls, dtype=torch.int32, device="cuda"), k_cache=kc, v_cache=vc,
+                             bufs=bufs, **kw)
+        torch.cuda.synchronize()
+        out = host(bufs.out)
+        for b in range(B):
+            assert np.all(out[b, Ls[b]:] == sentinel), f"rows past sequence {b}'s count were written"
+            if Ls[b]:
+                got[b].append(out[b, :Ls[b]])
+        pos += Ls
+    one = np.ones(B, np.int64)
+    db = layer.decode_ragged(*slabs(one, 1), kc, vc, window=window, seq_pos_offsets=torch.tensor(pos, device="cuda"),
+                             max_pos_offset=int(pos.max()), rope_table=tab, **kw)
+    torch.cuda.synchronize()
+    out = host(db.out)
+    for b in range(B):
+        got[b].append(out[b])
+    for b in range(B):
+        chunks = [int(Ls[b]) for Ls in lens if Ls[b]] + [1]
+        q, k, v = streams[b]
+        cache = LayerKVCache(Hkv, d, window, post_rope=True)
+        p = 0
+        for i, T in enumerate(chunks):
+            ref = oracle_step(L, q[0, p:p + T], k[0, p:p + T], v[0, p:p + T], cache, wq, wk)
+            assert_parity(got[b][i], ref, TOL_BF16, f"sequence {b}, call {i} (T={T})")
+            p += T
