@@ -95,18 +95,29 @@ __device__ __forceinline__ u32x4 scaled_chunk(u32x4 w, float s) {
   return Io<E>::pack(x);
 }
 
-// V norm: v_inv[r] = 1 / sqrt(mean(V_r^2) + eps) for rows r < n of `src` (row r at
-// src + r * stride), one wave per row.
+// V norm: v_inv[r] = 1 / sqrt(mean(V_r^2) + eps) for rows r < n <= 64 of `src` (row r at
+// src + r * stride): wave w takes rows w, w + 4, ..., each lane reading its D/64 consecutive
+// elements of a row at once; all of a wave's loads are issued before the first reduction.
 template <typename E, int D>
 __device__ __forceinline__ void v_row_inv_rms(const E* __restrict__ src, long long stride, int n, float eps,
                                               float* v_inv, int wave, int lane) {
-  for (int r = wave; r < n; r += kWaves) {
-    const E* row = src + r * stride;
+  constexpr int kPer = D / 64;
+  constexpr int kRows = kTokBlock / kWaves;
+  E x[kRows][kPer];
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) {
+    const int r = wave + k * kWaves;
+    if (r < n) __builtin_memcpy(x[k], src + r * stride + lane * kPer, sizeof(x[k]));
+  }
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) {
+    const int r = wave + k * kWaves;
+    if (r >= n) break;  // wave-uniform
     float s = 0.f;
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) {
-      const float x = Io<E>::ld(row + e * 64 + lane);
-      s += x * x;
+    for (int e = 0; e < kPer; ++e) {
+      const float f = Io<E>::ld(&x[k][e]);
+      s += f * f;
     }
     s = wave_sum(s);
     if (lane == 0) v_inv[r] = rsqrtf(s * (1.f / D) + eps);
@@ -119,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   constexpr int kVec = 16 / sizeof(E);          // elements per 16-byte chunk
   constexpr int kLanesPerRow = kH / kVec;       // d = 128: 8 (bf16) or 16 (fp32)
   constexpr int kRowsPerPass = 64 / kLanesPerRow;
-  constexpr int kUnroll = 2;
+  constexpr int kUnroll = 2;  // rows in flight per lane (4 measured slower at every head dim: fewer resident waves)
   constexpr bool kTiled = sizeof(E) == 2;      // bf16 prefill operands are tiled
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes<E, D>];
   __shared__ float v_inv[kTokBlock];
@@ -164,13 +175,19 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
                         static_cast<long long>(a.Hkv) * D, n_tok, a.eps, v_inv, wave, lane);
   float gq[2 * kVec], gk[2 * kVec];  // gains c + w of this lane's dims (both halves)
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int e = 0; e < 2 * kVec; ++e) gq[e] = gk[e] = 1.f;
+  if (norm) {
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) {
-      const int dim = h * kH + c * kVec + e;
-      gq[h * kVec + e] = norm ? a.norm_offset + Io<E>::ld(wq + dim) : 1.f;
-      gk[h * kVec + e] = norm ? a.norm_offset + Io<E>::ld(wk + dim) : 1.f;
+    for (int h = 0; h < 2; ++h) {
+      Io<E>::unpack(*reinterpret_cast<const u32x4*>(wq + h * kH + c * kVec), gq + h * kVec);
+      Io<E>::unpack(*reinterpret_cast<const u32x4*>(wk + h * kH + c * kVec), gk + h * kVec);
     }
+#pragma unroll
+    for (int e = 0; e < 2 * kVec; ++e) {
+      gq[e] += a.norm_offset;
+      gk[e] += a.norm_offset;
+    }
+  }
   __syncthreads();
 
   // One pass normalises and rotates kRowsPerPass rows per wave (kUnroll passes in flight).
