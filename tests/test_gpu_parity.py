@@ -15,7 +15,7 @@ import torch
 
 from helpers import (TOL_BF16, TOL_F32, assert_parity, kept_slots, oracle_chunks, oracle_decode_one,
                      oracle_prefill, window_mean_closed_form, untile_k_rot, untile_v_t)
-from oracle import apply_rope, offset_rms_norm, rope_frequencies
+from oracle import LayerKVCache, apply_rope, attention_layer_step, offset_rms_norm, rope_frequencies
 from synthetic import Draw
 from synthetic.workloads import (BATCHED_DECODE, GLOBAL_PREFILL, LOCAL_PREFILL, PERIOD_DECODE,
                                  TINY_SWA_FP32, Rope, device_normal_bf16)
@@ -333,6 +333,42 @@ def test_decode_period_long_context_step():
         ly = wl.layers[li]
         _decode_case(wl.B, wl.Hq, wl.Hkv, ly.window, wl.pos_offset, ly.rope, wl.cache_seed(li),
                      check_b=[0, 7], poison_future=False)
+
+
+@pytest.mark.parametrize("li", [0, 7], ids=["local_ring2048", "global131072"])
+def test_decode_period_128_steps(li):
+    """The 8-layer period's 128 consecutive decode steps (append + decode per step) on one
+    local and the global layer at B = 8 from 131071 kept tokens; steps 0, 63 and 127 of two
+    sequences against the oracle run on the same token stream (its cache takes every step's
+    normalised K and V, attention is evaluated at the checked steps)."""
+    wl = PERIOD_DECODE
+    ly = wl.layers[li]
+    B, Hq, Hkv, d, W = wl.B, wl.Hq, wl.Hkv, wl.d, ly.window
+    p0, steps, c = wl.pos_offset, wl.steps, wl.norm_offset
+    cap = wl.cache_cap(ly)
+    kc = device_normal_bf16((B, Hkv, cap, d), wl.cache_seed(li), "cuda")
+    vc = device_normal_bf16((B, Hkv, cap, d), wl.cache_seed(li) + 1, "cuda")
+    check_b, check_k = [0, 5], (0, 63, 127)
+    sl = torch.from_numpy(kept_slots(p0, W)).cuda()
+    caches = {b: LayerKVCache.with_prior(host(kc[b][:, sl]).transpose(1, 0, 2), host(vc[b][:, sl]).transpose(1, 0, 2),
+                                         p0, W) for b in check_b}
+    tab = rope_table(ly.rope, p0 + steps + 64)
+    omega_kw = dict(theta=ly.rope.theta, yarn_factor=ly.rope.yarn_factor, orig_ctx=ly.rope.orig_ctx,
+                    beta_fast=ly.rope.beta_fast, beta_slow=ly.rope.beta_slow)
+    for k in range(steps):
+        x = wl.draw_new_tokens(k, li)
+        db = layer.decode(dev(x["q"]), dev(x["k"]), dev(x["v"]), kc, vc, window=W, pos_offset=p0 + k, rope_table=tab,
+                          q_norm_w=dev(x["wq"]), k_norm_w=dev(x["wk"]), norm_offset=c)
+        if k in check_k:
+            torch.cuda.synchronize()
+            out = host(db.out)
+        for b in check_b:
+            if k in check_k:
+                ref = attention_layer_step(x["q"][b], x["k"][b], x["v"][b], caches[b], q_norm_w=x["wq"],
+                                           k_norm_w=x["wk"], norm_offset=c, scale=1.0 / math.sqrt(d), **omega_kw)
+                assert_parity(out[b], ref, TOL_BF16, f"layer {li} step {k} sequence {b}")
+            else:  # the oracle's cache takes the step's normalised K and raw V
+                caches[b].update(offset_rms_norm(x["k"][b], x["wk"], c), x["v"][b])
 
 
 @pytest.mark.parametrize("window", [0, 16, 2048])
