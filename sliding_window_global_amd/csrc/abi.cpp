@@ -246,7 +246,7 @@ int attn_prefill_impl(int dtype, const void* q_rot, const void* k_rot, const voi
     if (covered < (post ? pos_offset : kept) + T)
       return fail(PLAMO_ERR_WORKSPACE, "rope table does not cover the queries' positions");
   }
-  const int rows_per_block = d == 512 ? 64 : 128;
+  const int rows_per_block = 128;  // every prefill kernel takes 128 query rows per block
   const long long blocks = (static_cast<long long>(T) + rows_per_block - 1) / rows_per_block * Hq * static_cast<long long>(B);
   if (blocks > 0x7fffffffLL) return fail(PLAMO_ERR_UNSUPPORTED, "grid too large");
 

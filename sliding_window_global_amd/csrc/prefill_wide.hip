@@ -12,10 +12,12 @@
 // Here a wave holds NB blocks of 16 rows and uses v_mfma_f32_16x16x32_bf16.
 //
 // Work decomposition
-//   block  = 8 waves x 16 NB query rows of one (sequence, query head), NB = 2 at d = 256
-//            and 1 at d = 512: two waves per SIMD, each within 256 registers (with one wave
-//            per SIMD the LDS reads and the step barrier are not hidden). Query row t sits
-//            at renumbered position kept + t and attends operand keys 0 .. kept + t.
+//   block  = waves x 16 NB query rows of one (sequence, query head): at d = 256 4 waves x
+//            32 rows, two blocks per CU (128-row blocks waste fewer masked pairs at the window
+//            edge than 256-row ones); at d = 512 8 waves x 16 rows (the 128 KiB of buffers
+//            allow one block). Either way two waves per SIMD, each within 256 registers (with
+//            one wave per SIMD the LDS reads and the step barrier are not hidden). Query row t
+//            sits at renumbered position kept + t and attends operand keys 0 .. kept + t.
 //   step   = 32 keys, one half of a 64-key operand tile (K' tile [d/8][64][8], V^T tile
 //            [8][d][8], both written by the append kernel). Each half is one set of
 //            1 KiB direct copies into LDS (buffer loads with the LDS bit: the K' half is
@@ -296,7 +298,7 @@ hipError_t launch_wide(const PrefillArgs& a, hipStream_t stream) {
 }  // namespace
 
 #ifndef WIDE_CFG256
-#define WIDE_CFG256 2, 8, 1
+#define WIDE_CFG256 2, 4, 2
 #endif
 #ifndef WIDE_CFG512
 #define WIDE_CFG512 1, 8, 1
