@@ -14,12 +14,14 @@
 // is cached or used.
 //
 // One block = 64 tokens of one sequence and one KV head: its G = Hq/Hkv query heads,
-// the K head and the V head. With d = 128 the block first forms the rotation factors of
-// its 64 positions in LDS; wider heads read them from the table as they go (64 positions
-// of 256 pairs would not fit). A row (one token of one head) is handled by a group of
+// the K head and the V head. The block forms the rotation factors of its positions in
+// LDS, 32 KiB at a time: all 64 positions at d = 128, 32 or 16 of them at d = 256 or 512.
+// A row (one token of one head) is handled by a group of
 // lanes, each holding one 16-byte chunk of the first half and the matching chunk of the
 // second half, so every rotation pair is lane-local and the norm is a reduction over the
-// group. V is staged through LDS to write the transposed prefill operand with full rows.
+// group. bf16 V is read once, into registers: a lane holds one dim chunk of 8 keys, which
+// it writes to the cache as it is and to the transposed prefill operand after an 8 x 8
+// transpose in registers; fp32 V is staged through LDS for the transpose.
 //
 // bf16 prefill operands are tiled by 64 keys, each tile 64 d bf16 in the order the prefill
 // kernels copy straight into LDS: K' tile = [d/8 dim chunks][64 keys][8 dims], V^T tile =
@@ -37,9 +39,9 @@ constexpr int kWaves = kThreads / 64;
 
 // One LDS area per block, used first for the rotation factors of kRopeTok positions at a
 // time ([kRopeTok][d/2] float2, 32 KiB: all 64 positions at d = 128, 32 or 16 of them at
-// d = 256 or 512) and afterwards, behind a barrier, for the V^T staging tile ([d dims][64 +
-// 16/sizeof(E) tokens]). Sharing it keeps a d = 128 block within 36 KiB, so that four
-// blocks (all of a 64-token x 8-KV-head step) fit on a CU.
+// d = 256 or 512) and afterwards, behind a barrier, for the fp32 V^T staging tile ([d dims]
+// [64 + 4 tokens]). bf16 blocks need no staging tile, so every head dim takes 32 KiB and
+// five blocks fit on a CU.
 template <typename E>
 constexpr int kTileStride = kTokBlock + 16 / static_cast<int>(sizeof(E));  // tokens, 16-byte rows
 template <int D>
@@ -47,7 +49,7 @@ constexpr int kRopeTok = kTokBlock * kHeadDim / D;
 template <int D>
 constexpr bool kStageRope = D == kHeadDim;  // the operand kernel stages its factors at d = 128 only
 template <typename E, int D>
-constexpr int kSmemBytes = kRopeTok<D> * (D / 2) * 8 > D * kTileStride<E> * static_cast<int>(sizeof(E))
+constexpr int kSmemBytes = sizeof(E) == 2 || kRopeTok<D> * (D / 2) * 8 > D * kTileStride<E> * static_cast<int>(sizeof(E))
                                ? kRopeTok<D> * (D / 2) * 8
                                : D * kTileStride<E> * static_cast<int>(sizeof(E));
 
@@ -124,6 +126,49 @@ __device__ __forceinline__ void v_row_inv_rms(const E* __restrict__ src, long lo
   }
 }
 
+// bf16 V of one 8-key chunk of a 64-key operand tile, in registers: the lane's dims
+// 8 cidx .. 8 cidx + 7 of keys r = 0 .. 7, w[r] as 4 packed pairs. src(r) is key r's row
+// (nullptr: a zero row); with the V norm, rows for which scaled(r) holds are divided by
+// their RMS (rows that were normalised before they were cached are not). The row sums of
+// squares are reduced over the d/8 lanes that hold the other dim chunks of the same keys,
+// adjacent lanes of one wave that all take this call together.
+template <int D, typename Src, typename Scaled>
+__device__ __forceinline__ void v_key_chunk(Src src, Scaled scaled, bool v_norm, float eps, int cidx, u32x4 (&w)[8]) {
+  constexpr int kChunks = D / 8;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const bf16_t* p = src(r);
+    w[r] = p ? reinterpret_cast<const u32x4*>(p)[cidx] : u32x4{0, 0, 0, 0};
+  }
+  if (!v_norm) return;
+  float s[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    s[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[r] += lo_bf16(w[r][e]) * lo_bf16(w[r][e]) + hi_bf16(w[r][e]) * hi_bf16(w[r][e]);
+  }
+#pragma unroll
+  for (int m = 1; m < kChunks; m <<= 1)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) s[r] += __shfl_xor(s[r], m, 64);
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+    if (scaled(r)) w[r] = scaled_chunk<bf16_t>(w[r], rsqrtf(s[r] * (1.f / D) + eps));
+}
+
+// 8 x 8 bf16 transpose: o[e] = dim e of keys 0 .. 7, key 2q in the low half of word q (the
+// V^T tile's 8-key runs).
+__device__ __forceinline__ void transpose8x8_bf16(const u32x4 (&w)[8], u32x4 (&o)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t x = w[2 * q][e >> 1], y = w[2 * q + 1][e >> 1];
+      o[e][q] = (e & 1) ? (x >> 16) | (y & 0xFFFF0000u) : (x & 0xFFFFu) | (y << 16);
+    }
+}
+
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   constexpr int kH = D / 2;                     // rotation pairs
@@ -170,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
     }
   };
   stage(0);
-  if (a.v_norm && n_tok > 0)
+  if (!kTiled && a.v_norm && n_tok > 0)
     v_row_inv_rms<E, D>(v + ((static_cast<long long>(b) * a.T + t0) * a.Hkv + kvh) * D,
                         static_cast<long long>(a.Hkv) * D, n_tok, a.eps, v_inv, wave, lane);
   float gq[2 * kVec], gk[2 * kVec];  // gains c + w of this lane's dims (both halves)
@@ -313,50 +358,76 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   // --- values: copy into the cache (16-byte chunks), transposed prefill operand --------
   // (V norm: every chunk scaled by its row's inverse RMS, rounded once)
   constexpr int kChunks = D / kVec;  // 16-byte chunks per row
-  if (v_cache) {
-    for (int i = (threadIdx.x + kThreads - 128) % kThreads; i < n_tok * kChunks; i += kThreads) {  // from wave 2
-      const int t = t0 + i / kChunks;
-      if (!(a.window == 0 || t >= sp.T - a.window)) continue;
-      const long long n = sp.pos + t;
-      const long long s = a.window == 0 ? n : n % a.window;
-      const int cidx = i % kChunks;
-      const long long row = ((static_cast<long long>(b) * a.T + t) * a.Hkv + kvh) * D;
-      const long long crow = ((static_cast<long long>(b) * a.Hkv + kvh) * a.cap + s) * D;
-      u32x4 w = reinterpret_cast<const u32x4*>(v + row)[cidx];
-      if (a.v_norm) w = scaled_chunk<E>(w, v_inv[t - t0]);
-      reinterpret_cast<u32x4*>(v_cache + crow)[cidx] = w;
-    }
-  }
-  if (v_t && !a.ops_kernel) {  // (otherwise the operand kernel writes all of V^T)
-    constexpr int kTS = kTileStride<E>;
-    E* tile = reinterpret_cast<E*>(smem);
-    __syncthreads();  // every wave is done with the rotation factors
-    for (int i = threadIdx.x; i < kTokBlock * kChunks; i += kThreads) {
-      const int r = i / kChunks, cidx = i % kChunks;
-      const int t = t0 + r;
-      E x[kVec];
-      if (t < sp.T) {
-        u32x4 w = reinterpret_cast<const u32x4*>(v + ((static_cast<long long>(b) * a.T + t) * a.Hkv + kvh) * D)[cidx];
-        if (a.v_norm) w = scaled_chunk<E>(w, v_inv[r]);
-        __builtin_memcpy(x, &w, 16);
-      } else {
+  if constexpr (kTiled) {
+    const bool vt_here = v_t && !a.ops_kernel && t0 < a.Tp;  // Tp: a multiple of 128, so whole tiles
+    if (v_cache || vt_here) {
+      // lane task i = key chunk kc (8 tokens) x dim chunk cidx; from wave 2, as above
+      for (int i = (threadIdx.x + kThreads - 128) % kThreads; i < 8 * kChunks; i += kThreads) {
+        const int kc = i / kChunks, cidx = i % kChunks;
+        const int tk = t0 + kc * 8;
+        if (tk >= sp.T && !vt_here) continue;  // uniform over the lanes of one key chunk
+        u32x4 w[8];
+        v_key_chunk<D>(
+            [&](int r) -> const bf16_t* {
+              return tk + r < sp.T ? v + ((static_cast<long long>(b) * a.T + tk + r) * a.Hkv + kvh) * D : nullptr;
+            },
+            [](int) { return true; }, a.v_norm, a.eps, cidx, w);
+        if (v_cache) {
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) x[e] = E(0);
-      }
+          for (int r = 0; r < 8; ++r) {
+            const int t = tk + r;
+            if (t >= sp.T || !(a.window == 0 || t >= sp.T - a.window)) continue;
+            const long long n = sp.pos + t;
+            const long long s = a.window == 0 ? n : n % a.window;
+            reinterpret_cast<u32x4*>(v_cache + ((static_cast<long long>(b) * a.Hkv + kvh) * a.cap + s) * D)[cidx] = w[r];
+          }
+        }
+        if (vt_here) {  // tile [8 key chunks][d dims][8 keys]: dims 8 cidx .. +7 of key chunk kc
+          u32x4 o[8];
+          transpose8x8_bf16(w, o);
+          u32x4* dst = reinterpret_cast<u32x4*>(v_t + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t0) * D) +
+                       kc * D + cidx * 8;
 #pragma unroll
-      for (int e = 0; e < kVec; ++e) tile[(cidx * kVec + e) * kTS + r] = x[e];
-    }
-    __syncthreads();
-    constexpr int kTokChunks = kTokBlock / kVec;
-    if (kTiled) {
-      if (t0 < a.Tp) {  // Tp is a multiple of 128, so a tile is wholly inside or outside
-        u32x4* dst = reinterpret_cast<u32x4*>(v_t + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + t0) * D);
-        for (int i = threadIdx.x; i < D * kTokChunks; i += kThreads) {  // i = key chunk * d + dim
-          const int cc = i % D, tc = i / D;
-          dst[i] = *reinterpret_cast<const u32x4*>(&tile[cc * kTS + tc * kVec]);
+          for (int e = 0; e < 8; ++e) dst[e] = o[e];
         }
       }
-    } else {
+    }
+  } else {
+    if (v_cache) {
+      for (int i = (threadIdx.x + kThreads - 128) % kThreads; i < n_tok * kChunks; i += kThreads) {  // from wave 2
+        const int t = t0 + i / kChunks;
+        if (!(a.window == 0 || t >= sp.T - a.window)) continue;
+        const long long n = sp.pos + t;
+        const long long s = a.window == 0 ? n : n % a.window;
+        const int cidx = i % kChunks;
+        const long long row = ((static_cast<long long>(b) * a.T + t) * a.Hkv + kvh) * D;
+        const long long crow = ((static_cast<long long>(b) * a.Hkv + kvh) * a.cap + s) * D;
+        u32x4 w = reinterpret_cast<const u32x4*>(v + row)[cidx];
+        if (a.v_norm) w = scaled_chunk<E>(w, v_inv[t - t0]);
+        reinterpret_cast<u32x4*>(v_cache + crow)[cidx] = w;
+      }
+    }
+    if (v_t && !a.ops_kernel) {  // (otherwise the operand kernel writes all of V^T)
+      constexpr int kTS = kTileStride<E>;
+      E* tile = reinterpret_cast<E*>(smem);
+      __syncthreads();  // every wave is done with the rotation factors
+      for (int i = threadIdx.x; i < kTokBlock * kChunks; i += kThreads) {
+        const int r = i / kChunks, cidx = i % kChunks;
+        const int t = t0 + r;
+        E x[kVec];
+        if (t < sp.T) {
+          u32x4 w = reinterpret_cast<const u32x4*>(v + ((static_cast<long long>(b) * a.T + t) * a.Hkv + kvh) * D)[cidx];
+          if (a.v_norm) w = scaled_chunk<E>(w, v_inv[r]);
+          __builtin_memcpy(x, &w, 16);
+        } else {
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) x[e] = E(0);
+        }
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) tile[(cidx * kVec + e) * kTS + r] = x[e];
+      }
+      __syncthreads();
+      constexpr int kTokChunks = kTokBlock / kVec;
       for (int i = threadIdx.x; i < D * kTokChunks; i += kThreads) {
         const int cc = i / kTokChunks, tc = i % kTokChunks;
         const long long t = t0 + tc * kVec;
@@ -456,42 +527,59 @@ __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a
     }
   }
 
-  if (v_t) {
-    // V norm: the chunk's own rows (R in [kept, S)) come raw from v; cached rows were
-    // normalised when they were appended
-    const long long r_new = kept > R0 ? kept - R0 : 0;  // first tile row holding a new token
-    const long long r_end = S - R0 < kTokBlock ? S - R0 : kTokBlock;
-    if (a.v_norm && r_end > r_new)
-      v_row_inv_rms<E, D>(v + ((static_cast<long long>(b) * a.T + (R0 + r_new - kept)) * a.Hkv + kvh) * D,
-                          static_cast<long long>(a.Hkv) * D, static_cast<int>(r_end - r_new), a.eps,
-                          v_inv + r_new, wave, lane);
-    __syncthreads();  // every wave is done with the rotation factors; v_inv is complete
-    for (int i = threadIdx.x; i < kTokBlock * kChunks; i += kThreads) {
-      const int r = i / kChunks, cidx = i % kChunks;
-      const long long R = R0 + r;
-      E x[kVec];
-      if (R < S) {
-        const E* src = R < kept ? vc + cache_row(R)
-                                : v + ((static_cast<long long>(b) * a.T + (R - kept)) * a.Hkv + kvh) * D;
-        u32x4 w = reinterpret_cast<const u32x4*>(src)[cidx];
-        if (a.v_norm && R >= kept) w = scaled_chunk<E>(w, v_inv[r]);
-        __builtin_memcpy(x, &w, 16);
-      } else {
+  if constexpr (kTiled) {
+    if (v_t) {
+      // V norm: the chunk's own rows (R in [kept, S)) come raw from v; cached rows were
+      // normalised when they were appended
+      for (int i = threadIdx.x; i < 8 * kChunks; i += kThreads) {
+        const int kc = i / kChunks, cidx = i % kChunks;
+        const long long Rk = R0 + kc * 8;
+        u32x4 w[8];
+        v_key_chunk<D>(
+            [&](int r) -> const bf16_t* {
+              const long long R = Rk + r;
+              if (R < kept) return reinterpret_cast<const bf16_t*>(vc + cache_row(R));
+              if (R < S) return reinterpret_cast<const bf16_t*>(v + ((static_cast<long long>(b) * a.T + (R - kept)) * a.Hkv + kvh) * D);
+              return nullptr;
+            },
+            [&](int r) { return Rk + r >= kept; }, a.v_norm, a.eps, cidx, w);
+        u32x4 o[8];
+        transpose8x8_bf16(w, o);
+        u32x4* dst = reinterpret_cast<u32x4*>(v_t + (bh * a.Tp + R0) * D) + kc * D + cidx * 8;
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) x[e] = E(0);
+        for (int e = 0; e < 8; ++e) dst[e] = o[e];
       }
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) tile[(cidx * kVec + e) * kTS + r] = x[e];
     }
-    __syncthreads();
-    constexpr int kTokChunks = kTokBlock / kVec;
-    if (kTiled) {
-      u32x4* dst = reinterpret_cast<u32x4*>(v_t + (bh * a.Tp + R0) * D);
-      for (int i = threadIdx.x; i < D * kTokChunks; i += kThreads) {  // i = key chunk * d + dim
-        const int cc = i % D, tc = i / D;
-        dst[i] = *reinterpret_cast<const u32x4*>(&tile[cc * kTS + tc * kVec]);
+  } else {
+    if (v_t) {
+      // V norm: the chunk's own rows (R in [kept, S)) come raw from v; cached rows were
+      // normalised when they were appended
+      const long long r_new = kept > R0 ? kept - R0 : 0;  // first tile row holding a new token
+      const long long r_end = S - R0 < kTokBlock ? S - R0 : kTokBlock;
+      if (a.v_norm && r_end > r_new)
+        v_row_inv_rms<E, D>(v + ((static_cast<long long>(b) * a.T + (R0 + r_new - kept)) * a.Hkv + kvh) * D,
+                            static_cast<long long>(a.Hkv) * D, static_cast<int>(r_end - r_new), a.eps,
+                            v_inv + r_new, wave, lane);
+      __syncthreads();  // every wave is done with the rotation factors; v_inv is complete
+      for (int i = threadIdx.x; i < kTokBlock * kChunks; i += kThreads) {
+        const int r = i / kChunks, cidx = i % kChunks;
+        const long long R = R0 + r;
+        E x[kVec];
+        if (R < S) {
+          const E* src = R < kept ? vc + cache_row(R)
+                                  : v + ((static_cast<long long>(b) * a.T + (R - kept)) * a.Hkv + kvh) * D;
+          u32x4 w = reinterpret_cast<const u32x4*>(src)[cidx];
+          if (a.v_norm && R >= kept) w = scaled_chunk<E>(w, v_inv[r]);
+          __builtin_memcpy(x, &w, 16);
+        } else {
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) x[e] = E(0);
+        }
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) tile[(cidx * kVec + e) * kTS + r] = x[e];
       }
-    } else {
+      __syncthreads();
+      constexpr int kTokChunks = kTokBlock / kVec;
       for (int i = threadIdx.x; i < D * kTokChunks; i += kThreads) {
         const int cc = i / kTokChunks, tc = i % kTokChunks;
         const u32x4 w = *reinterpret_cast<const u32x4*>(&tile[cc * kTS + tc * kVec]);
