@@ -313,6 +313,24 @@ def pin_rope_shift_invariance(o):
             assert np.max(np.abs(sh - base)) < 1e-9 * max(1.0, np.max(np.abs(base)))
 
 
+def pin_local_window_slice(o):
+    """「PLaMo 3アーキテクチャ徹底解析」 §4.4, §5.1, §6.1: on a local layer, a one-shot prefill's
+    row r attends keys r - W + 1 .. r only, and RoPE scores depend on positions through their
+    difference, so the layer run on those W tokens alone (positions 0 .. W - 1) gives the same
+    row (the full-size GPU checks rely on this to run the oracle on windows)."""
+    T, Hq, Hkv, d, W = 300, 4, 2, 32, 64
+    q, k, v = _rand((T, Hq, d), 301), _rand((T, Hkv, d), 302), _rand((T, Hkv, d), 303)
+    wq, wk = _rand((d,), 304) * 0.1, _rand((d,), 305) * 0.1
+    kw = dict(theta=1e4, yarn_factor=0.0, q_norm_w=wq, k_norm_w=wk, norm_offset=1.0)
+    rows = np.array([0, 10, 63, 64, 200, 299])
+    full = o.attention_layer_step(q, k, v, o.LayerKVCache(Hkv, d, W), rows=rows, **kw)
+    for i, r in enumerate(rows):
+        s0 = max(0, r - W + 1)
+        sl = slice(s0, r + 1)
+        one = o.attention_layer_step(q[sl], k[sl], v[sl], o.LayerKVCache(Hkv, d, W), rows=np.array([r - s0]), **kw)
+        assert np.max(np.abs(one[0] - full[i])) < 1e-12, r
+
+
 def pin_yarn_printed(o):
     """「PLaMo 3アーキテクチャ徹底解析」 §6.3: the printed ramp bounds and amplitude figures."""
     g = golden("yarn_printed.json")
@@ -684,7 +702,7 @@ def pin_gemma_torch(o):
 
 PINS = [pin_worked_example, pin_fig4_masks, pin_sdpa_float64, pin_bruteforce_layer,
         pin_rows_sum_to_one, pin_swa_equals_global_short, pin_uniform_closed_form,
-        pin_gqa_grouping, pin_rope_library, pin_rope_complex, pin_rope_shift_invariance,
+        pin_gqa_grouping, pin_rope_library, pin_rope_complex, pin_rope_shift_invariance, pin_local_window_slice,
         pin_yarn_printed, pin_yarn_figure7, pin_rmsnorm, pin_cache_trim,
         pin_decode_equivalence, pin_kv_accounting, pin_legacy_4k_band, pin_post_rope_cache,
         pin_mixer_bruteforce, pin_mixer_torch, pin_p_rope_page, pin_gemma_layer_bruteforce,
