@@ -85,7 +85,8 @@ def test_wide_rope_table(L):
 
 def _small_stream(L: GemmaLayer, Hq, Hkv, window, chunks, steps, seed):
     """Chunked prefill then decode steps of B = 2 sequences on one token stream; every output
-    row and the final cache contents (K after RoPE, V of unit RMS) against the oracle."""
+    row and the final cache contents (K after RoPE, V of unit RMS) against the oracle. The
+    caches start as NaN: a slot that holds no kept token must never be read."""
     import dataclasses
     L = dataclasses.replace(L, Hq=Hq, Hkv=Hkv, window=window)
     B, d = 2, L.d
@@ -94,8 +95,8 @@ def _small_stream(L: GemmaLayer, Hq, Hkv, window, chunks, steps, seed):
     q, k, v = L.draw_tokens(dr, B, n)
     wq, wk = L.draw_gains(dr)
     cap = window if window else n
-    kc = torch.zeros((B, Hkv, cap, d), dtype=torch.bfloat16, device="cuda")
-    vc = torch.zeros_like(kc)
+    kc = torch.full((B, Hkv, cap, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
     tab = table_for(L, n + 64)
     kw = gpu_kw(L, wq, wk)
 
@@ -145,6 +146,40 @@ def test_gemma_local_small_window_edges():
     """d = 256 with windows around the 32-key step and the 64-key tile: 31, 33, 65."""
     for w in (31, 33, 65):
         _small_stream(GEMMA_LOCAL_LAYER, 4, 2, w, [97, 70], 2, 7200 + w)
+
+
+def test_gemma_partly_filled_caches():
+    """Rings that never fill (window 100 after 40 + 7 tokens and 3 decodes) and a global cache
+    whose later slots are still unwritten: the NaN in those slots must not reach an output."""
+    _small_stream(GEMMA_LOCAL_LAYER, 4, 2, 100, [40, 7], 3, 7301)
+    _small_stream(GEMMA_GLOBAL_LAYER, 8, 1, 0, [30, 20], 2, 7302)
+
+
+def test_gemma_wide_kernels_deterministic():
+    """Repeated calls give bit-identical outputs: the d = 256 prefill at full size and the
+    d = 512 split decode (fixed merge order, no atomics)."""
+    wl = GEMMA_LOCAL_PREFILL
+    L = wl.layer
+    x = wl.draw()
+    tab = table_for(L, wl.T + 64)
+    qd, kd, vd = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    outs = [layer.prefill(qd, kd, vd, window=L.window, rope_table=tab, **gpu_kw(L, x["wq"], x["wk"])).out.clone()
+            for _ in range(2)]
+    assert torch.equal(outs[0], outs[1])
+    G = GEMMA_GLOBAL_LAYER
+    B, p = 4, 5000
+    kc = device_normal_bf16((B, G.Hkv, p + 1, G.d), 7401, "cuda")
+    vc = device_normal_bf16((B, G.Hkv, p + 1, G.d), 7402, "cuda")
+    dr = Draw(7403, True)
+    q, k, _ = G.draw_tokens(dr, B, 1)
+    wq, wk = G.draw_gains(dr)
+    tab = table_for(G, p + 64)
+    outs = []
+    for _ in range(2):
+        kd = dev(k)
+        outs.append(layer.decode(dev(q), kd, kd, kc, vc, window=0, pos_offset=p, rope_table=tab,
+                                 **gpu_kw(G, wq, wk)).out.clone())
+    assert torch.equal(outs[0], outs[1])
 
 
 @pytest.mark.parametrize("wl", [GEMMA_LOCAL_PREFILL, GEMMA_GLOBAL_PREFILL], ids=["local_T8192", "global_T32768"])
