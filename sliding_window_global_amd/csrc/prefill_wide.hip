@@ -29,8 +29,9 @@
 //            so each lane owns one row (of each of its NB blocks) and the 16 lanes of a
 //            row group share it: row maxima and sums reduce over lanes l, l^16, l^32, l^48.
 //            K' rows are read in the order that gives each lane eight consecutive keys
-//            across the two S^T blocks, exactly the P^T operand of the P V MFMA; V^T is
-//            read in natural key order. Each K' fragment feeds NB MFMAs.
+//            across the two S^T blocks, exactly the P^T operand of the P V MFMA (the copy
+//            into LDS already places them in that order, so each fragment read is
+//            contiguous); V^T is read in natural key order. Each K' fragment feeds NB MFMAs.
 //   softmax = exp2 domain (Q' pre-scaled by scale * log2 e); lazy rescaling: the
 //            reference of a row moves only when a score exceeds it by 2^8; row sums from
 //            the same bf16-rounded P as P V.
@@ -125,9 +126,12 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void prefill_wide_kernel(Prefill
   const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(static_cast<const bf16_t*>(a.k_rot) + bh * a.Tp * D, op_bytes);
   const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(static_cast<const bf16_t*>(a.v_t) + bh * a.Tp * D, op_bytes);
   // Copy i (0 .. kWaves kLoads - 1) of a half tile fills LDS bytes 1024 i .. +1023. K': dim chunks
-  // 2i and 2i+1, 32 keys each, from 512-byte runs 1 KiB apart in the 64-key tile; V^T: the
-  // half's bytes in order. The half (0 or 1) goes in the scalar offset with the tile.
-  const uint32_t k_off = static_cast<uint32_t>((2 * wave * kLoads + (lane >> 5)) * 1024 + (lane & 31) * 16);
+  // 2i and 2i+1, 32 keys each, from 512-byte runs 1 KiB apart in the 64-key tile, slot
+  // 16 kb + m of a run taking key key_of(m, kb) (each lane fetches the key its LDS slot
+  // holds), so that the 16 keys one S^T fragment read needs are 256 contiguous bytes; V^T:
+  // the half's bytes in order. The half (0 or 1) goes in the scalar offset with the tile.
+  const uint32_t k_off = static_cast<uint32_t>((2 * wave * kLoads + (lane >> 5)) * 1024 +
+                                               key_of(lane & 15, (lane >> 4) & 1) * 16);
   const uint32_t v_off = static_cast<uint32_t>(wave * kLoads * 1024 + lane * 16);
   auto issue = [&](int step, bf16_t* kbuf, bf16_t* vbuf) __attribute__((always_inline)) {
     const int key32 = kt_hi - step;
@@ -184,12 +188,13 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void prefill_wide_kernel(Prefill
     f32x4 sacc[NB][2];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) sacc[nb][0] = sacc[nb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // K' in LDS: [d/8 chunks][32 keys][8]; k-step s reads chunk 4s + g
+    // K' in LDS: [d/8 chunks][32 slots][8], slot 16 kb + n holding key key_of(n, kb); k-step s
+    // reads chunk 4s + g
 #pragma unroll
     for (int s = 0; s < kKS; ++s)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kbuf + ((4 * s + g) * kBN + key_of(n, kb)) * 8);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kbuf + ((4 * s + g) * kBN + kb * 16 + n) * 8);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) sacc[nb][kb] = mfma16(kf, qf[nb][s], sacc[nb][kb]);
       }
