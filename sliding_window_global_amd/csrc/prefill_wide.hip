@@ -12,12 +12,14 @@
 // Here a wave holds NB blocks of 16 rows and uses v_mfma_f32_16x16x32_bf16.
 //
 // Work decomposition
-//   block  = waves x 16 NB query rows of one (sequence, query head): at d = 256 4 waves x
-//            32 rows, two blocks per CU (128-row blocks waste fewer masked pairs at the window
-//            edge than 256-row ones); at d = 512 8 waves x 16 rows (the 128 KiB of buffers
-//            allow one block). Either way two waves per SIMD, each within 256 registers (with
-//            one wave per SIMD the LDS reads and the step barrier are not hidden). Query row t
-//            sits at renumbered position kept + t and attends operand keys 0 .. kept + t.
+//   block  = waves x 16 NB query rows of one sequence, for kHeads query heads of one KV
+//            group: at d = 256 8 waves, two query heads x 4 waves x 32 rows sharing every
+//            K'/V^T copy (128-row blocks waste fewer masked pairs at the window edge than
+//            256-row ones; the two heads halve the copies per row); at d = 512 8 waves x 16
+//            rows of one head (the 128 KiB of buffers allow one block). Either way two waves
+//            per SIMD, each within 256 registers (with one wave per SIMD the LDS reads and the
+//            step barrier are not hidden). Query row t sits at renumbered position kept + t and
+//            attends operand keys 0 .. kept + t.
 //   step   = 32 keys, one half of a 64-key operand tile (K' tile [d/8][64][8], V^T tile
 //            [8][d][8], both written by the append kernel). Each half is one set of
 //            1 KiB direct copies into LDS (buffer loads with the LDS bit: the K' half is
@@ -75,11 +77,13 @@ __device__ __forceinline__ void block_barrier() {
 __device__ __forceinline__ int key_of(int m, int kb) { return ((m >> 2) << 3) | (kb << 2) | (m & 3); }
 
 // D: head dim; NB: 16-row blocks per wave; kWaves: waves per block; kOcc: blocks per CU the
-// register budget is cut for.
-template <int D, int NB, int kWaves, int kOcc, bool kLocal>
+// register budget is cut for; kHeads: query heads of one KV group per block (its waves split
+// into kHeads row groups of the same query rows, sharing every K'/V^T copy).
+template <int D, int NB, int kWaves, int kOcc, bool kLocal, int kHeads>
 __global__ __launch_bounds__(kWaves * 64, kOcc) void prefill_wide_kernel(PrefillArgs a) {
   constexpr int kRowsW = 16 * NB;         // query rows per wave
-  constexpr int BM = kWaves * kRowsW;     // query rows per block
+  constexpr int kWavesH = kWaves / kHeads;  // waves per query head
+  constexpr int BM = kWavesH * kRowsW;    // query rows per block
   constexpr int kKS = D / 32;             // k-steps of S^T over the head dim
   constexpr int kDT = D / 16;             // 16-dim blocks of O^T
   constexpr int kSub = kBN * D;           // bf16 elements of a K' or V^T half tile
@@ -96,19 +100,20 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void prefill_wide_kernel(Prefill
   const int n = lane & 15;  // MFMA column = query row within a 16-row block
   const int g = lane >> 4;  // lane group
 
-  // ---- block -> (b, kv head, query block, query head in group), XCD-aware ----------
+  // ---- block -> (b, kv head, query block, query heads in group), XCD-aware ---------
   const int G = a.Hq / a.Hkv;
+  const int GH = G / kHeads;  // blocks per (query block, KV head)
   const int nqb = (a.T + BM - 1) / BM;
   const unsigned total = gridDim.x;
   unsigned logical = blockIdx.x;
   if ((total & 7u) == 0) logical = (blockIdx.x & 7u) * (total >> 3) + (blockIdx.x >> 3);
-  const int g_in = logical % G;
-  unsigned rest = logical / G;
+  const int g_in = logical % GH;
+  unsigned rest = logical / GH;
   const int qb_order = rest % nqb;
   rest /= nqb;
   const int kvh = rest % a.Hkv;
   const int b = rest / a.Hkv;
-  const int hq = kvh * G + g_in;
+  const int hq = kvh * G + g_in * kHeads + wave / kWavesH;  // the wave's query head
   const int qb = kLocal ? qb_order : nqb - 1 - qb_order;
   const int i0 = qb * BM;
 
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void prefill_wide_kernel(Prefill
 
   // ---- Q' fragments (B operand of S^T): block nb, row n, dims 32 s + 8 g .. +7 -------
   const float c = a.scale * 1.4426950408889634f;
-  const int r0 = i0 + wave * kRowsW;  // first row of the wave
+  const int r0 = i0 + (wave % kWavesH) * kRowsW;  // first row of the wave
   const int p0 = kept + r0;           // its position
   bf16x8 qf[NB][kKS];
 #pragma unroll
@@ -287,15 +292,18 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void prefill_wide_kernel(Prefill
   }
 }
 
-template <int D, int NB, int kWaves, int kOcc>
+template <int D, int NB, int kWaves, int kOcc, int kHeads>
 hipError_t launch_wide(const PrefillArgs& a, hipStream_t stream) {
-  constexpr int BM = kWaves * 16 * NB;
-  const long long blocks = (a.T + BM - 1) / BM * static_cast<long long>(a.Hq) * a.B;
+  if constexpr (kHeads > 1) {  // a group size kHeads does not divide: one head per block
+    if ((a.Hq / a.Hkv) % kHeads != 0) return launch_wide<D, NB, kWaves / kHeads, kOcc * kHeads, 1>(a, stream);
+  }
+  constexpr int BM = kWaves / kHeads * 16 * NB;
+  const long long blocks = (a.T + BM - 1) / BM * static_cast<long long>(a.Hq / kHeads) * a.B;
   if (a.window > 0)
-    hipLaunchKernelGGL((prefill_wide_kernel<D, NB, kWaves, kOcc, true>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((prefill_wide_kernel<D, NB, kWaves, kOcc, true, kHeads>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kWaves * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_wide_kernel<D, NB, kWaves, kOcc, false>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((prefill_wide_kernel<D, NB, kWaves, kOcc, false, kHeads>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
@@ -303,10 +311,10 @@ hipError_t launch_wide(const PrefillArgs& a, hipStream_t stream) {
 }  // namespace
 
 #ifndef WIDE_CFG256
-#define WIDE_CFG256 2, 4, 2
+#define WIDE_CFG256 2, 8, 1, 2
 #endif
 #ifndef WIDE_CFG512
-#define WIDE_CFG512 1, 8, 1
+#define WIDE_CFG512 1, 8, 1, 1
 #endif
 hipError_t launch_prefill_wide_bf16(const PrefillArgs& a, hipStream_t stream) {
   if (a.d == 256) return launch_wide<256, WIDE_CFG256>(a, stream);
