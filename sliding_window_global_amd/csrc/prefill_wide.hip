@@ -47,6 +47,7 @@ namespace plamo {
 namespace {
 
 constexpr int kBN = 32;                // keys per step
+constexpr int kRing = 3;               // LDS operand fragments in flight per wave (2 and 4 measured no better)
 constexpr float kRescaleLog2 = 8.f;    // lazy-rescale threshold (log2 units)
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -193,16 +194,30 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void prefill_wide_kernel(Prefill
     f32x4 sacc[NB][2];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) sacc[nb][0] = sacc[nb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // K' in LDS: [d/8 chunks][32 slots][8], slot 16 kb + n holding key key_of(n, kb); k-step s
-    // reads chunk 4s + g
+    // K' in LDS: [d/8 chunks][32 slots][8], slot 16 kb + n holding key key_of(n, kb); fragment
+    // i = 2s + kb (k-step s) reads chunk 4s + g. V^T in LDS: [4 key chunks][d][8]; dim block dt
+    // reads chunk g, dim 16 dt + n. Both go through a ring of kRing registers: fragment i + kRing
+    // is read as soon as fragment i has been issued to the MFMAs, so each LDS read has kRing
+    // MFMA groups to land (read one at a time, the wave stalled on every read).
+    auto kread = [&](int i) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8*>(kbuf + ((4 * (i >> 1) + g) * kBN + (i & 1) * 16 + n) * 8);
+    };
+    auto vread = [&](int dt) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8*>(vbuf + (g * D + dt * 16 + n) * 8);
+    };
+    bf16x8 kr[kRing];
 #pragma unroll
-    for (int s = 0; s < kKS; ++s)
+    for (int i = 0; i < kRing; ++i) kr[i] = kread(i);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kbuf + ((4 * s + g) * kBN + kb * 16 + n) * 8);
+    for (int i = 0; i < 2 * kKS; ++i) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) sacc[nb][kb] = mfma16(kf, qf[nb][s], sacc[nb][kb]);
-      }
+      for (int nb = 0; nb < NB; ++nb) sacc[nb][i & 1] = mfma16(kr[i % kRing], qf[nb][i >> 1], sacc[nb][i & 1]);
+      if (i + kRing < 2 * kKS) kr[i % kRing] = kread(i + kRing);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bf16x8 vr[kRing];  // the first V^T fragments land during the softmax below
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) vr[i] = vread(i);
 
     // P^T: lane (n, g) of block nb holds keys key0 + 8g + j, j = 4 kb + e
     const bool mask = needs_mask(key0);
@@ -244,12 +259,12 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void prefill_wide_kernel(Prefill
       pf[nb] = __builtin_bit_cast(bf16x8, w);
     }
 
-    // V^T in LDS: [4 key chunks][d][8]; dim block dt reads chunk g, dim 16 dt + n
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt) {
-      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vbuf + (g * D + dt * 16 + n) * 8);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) oacc[nb][dt] = mfma16(vf, pf[nb], oacc[nb][dt]);
+      for (int nb = 0; nb < NB; ++nb) oacc[nb][dt] = mfma16(vr[dt % kRing], pf[nb], oacc[nb][dt]);
+      if (dt + kRing < kDT) vr[dt % kRing] = vread(dt + kRing);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
