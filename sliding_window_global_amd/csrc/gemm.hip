@@ -15,7 +15,7 @@
 //          that the eight lanes of a row read one contiguous 128 B of global memory and the
 //          16 rows of a quarter-wave's fragment read fall into distinct banks. The next
 //          sub-step's fragments are read while the current sub-step's MFMAs run.
-// Measured on the sublayer shapes: ~1.0-1.15 PFLOP/s; the same kernel without the tile copies
+// Measured on the sublayer shapes: ~1.0-1.1 PFLOP/s; the same kernel without the tile copies
 // (timing only) runs ~1.5-1.8, a 4-stage copy ring and an XCD-grouped tile order changed
 // nothing, so the LDS traffic of the copies plus the operand reads is what limits it.
 // Requirements (checked by the caller): K % 64 == 0, every output part's width % 8 == 0.
@@ -116,11 +116,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) bfr[(s + 1) & 1][j] = frag(bbuf, wm * 64 + j * 32, s + 1);
       }
+      // (without these the scheduler moves each read back next to its use, and every MFMA
+      // group waits for its own fragments)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bfr[s & 1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
