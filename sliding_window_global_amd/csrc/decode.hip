@@ -11,8 +11,9 @@
 // range of renumbered keys, a multiple of 64 long, cut into 64-key tiles. Wave w owns
 // keys 16w .. 16w+15 of every tile and streams them on its own, without block barriers:
 //   K rows   global -> registers, already in the MFMA operand layout (4 x 16 B per lane),
-//   V rows   global -> LDS by direct loads (rows padded to 272 B: the transposed operand
-//            reads below are free of bank conflicts),
+//   V rows   global -> LDS by direct loads (rows padded to 288 B, so that the transposing
+//            operand reads below, four rows of 32 B per lane group, are free of bank
+//            conflicts),
 //   rope     the tile's coarse factor row global -> LDS by one direct load,
 // three sub-tiles per wave in flight or in use (a ring unrolled by three).
 //   S^T[16 keys][16 heads] = K'[16][128] Q'^T  (v_mfma_f32_16x16x32_bf16; heads padded to 16)
@@ -38,14 +39,17 @@ constexpr int kMaxGroup = 16;
 constexpr int kPartial = kHeadDim + 2;     // acc[128], m, l
 constexpr int kMaxSplit = 256;             // key ranges per (sequence, KV head)
 constexpr long long kMinChunk = 256;       // keys per range, at least
-constexpr int kVRow = kHeadDim + 8;        // padded V row in LDS (elements): 272 B
-constexpr int kVChunks = kSub * kVRow / 8; // 16-byte slots of one V sub-tile: 272
+constexpr int kVRow = kHeadDim + 16;       // padded V row in LDS (elements): 288 B
+constexpr int kVChunks = kSub * kVRow / 8; // 16-byte slots of one V sub-tile: 288
 constexpr int kVLoads = (kVChunks + 63) / 64;  // direct loads per V sub-tile: 5
 constexpr int kVSlot = kVLoads * 64 * 8;   // elements reserved per V sub-tile
 constexpr float kRescaleLog2 = 8.f;        // lazy-rescale threshold (log2 units)
 // loads per tile issue: K rows, V rows and (when K is rotated here) the coarse rope row
 template <bool kRotate>
 constexpr int kLoadsPerIssue = 4 + kVLoads + (kRotate ? 1 : 0);
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 // s_waitcnt vmcnt(n), expcnt / lgkmcnt left alone (gfx9 encoding: vmcnt bits 3:0, 15:14)
 constexpr unsigned wait_vmcnt(int n) { return 0x0F70u | (n & 15) | ((n >> 4) << 14); }
@@ -115,14 +119,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   for (int e = 0; e < 16; ++e) fine[e] = kRotate ? a.rope[key_in_tile * kHalf + g * 16 + e] : float2{0.f, 0.f};
 
   // ---- per-lane pieces of the loads ---------------------------------------------------
-  // V direct load i, lane l fills padded slot p = 64 i + l: row p / 17, chunk p % 17 (the
-  // pad chunk 16 and the slots past 16 rows copy a chunk of the last row, never read).
+  // V direct load i, lane l fills padded slot p = 64 i + l: row p / 18, chunk p % 18 (the
+  // pad chunks 16, 17 and the slots past 16 rows copy a chunk of the last row, never read).
   int v_row[kVLoads], v_col[kVLoads];
 #pragma unroll
   for (int i = 0; i < kVLoads; ++i) {
     const int p = 64 * i + lane;
-    v_row[i] = min(p / 17, kSub - 1);
-    v_col[i] = min(p % 17, 15);
+    v_row[i] = min(p / (kVRow / 8), kSub - 1);
+    v_col[i] = min(p % (kVRow / 8), 15);
   }
   // Issue the loads of this wave's keys of the next tile into a K register set, a V slot
   // and a coarse-row slot. Tiles are issued in order 0, 1, 2, ...; past the end the last
@@ -241,13 +245,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
     l_run = add_bf16x2(pw[1], add_bf16x2(pw[0], l_run));  // the same bf16 p as P V
     const s16x4 pb = __builtin_bit_cast(s16x4, pw);
 
-    // V^T fragments: d = 16dt + m16, keys 4g + i of the sub-tile (padded rows in LDS)
-    const bf16_t* vrow = vslot + (4 * g) * kVRow + m16;
+    // V^T fragments: d = 16dt + m16, keys 4g + i of the sub-tile, one transposing LDS read
+    // each: lane 4r + q of lane group g addresses key 4g + r, dims 16dt + 4q .. +3, and the
+    // read hands lane m16 of the group dim 16dt + m16 of the four keys (key 4g + i in i).
+    const bf16_t* vrow = vslot + (4 * g + (m16 >> 2)) * kVRow + (m16 & 3) * 4;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      s16x4 va;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) va[i] = static_cast<short>(vrow[i * kVRow + dt * 16]);
+      const s16x4 va = __builtin_bit_cast(s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                     (lds_v4i16_t*)(vrow + dt * 16)));
       oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[dt], 0, 0, 0);
     }
   };
