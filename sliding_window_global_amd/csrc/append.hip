@@ -186,9 +186,16 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   const int c = lane % kLanesPerRow;  // chunk index within a half row: pairs c*kVec ..
   const int slot = lane / kLanesPerRow;
   const int t0 = blockIdx.x * kTokBlock;
-  const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
+  // A short chunk's few token blocks are spread wider: n_qs blocks share one (token block,
+  // KV head), block qs normalising and rotating query heads qs Gs .. qs Gs + Gs - 1; the first
+  // of them also handles K, V and the operand padding.
+  const int n_qs = a.q_split > 1 ? a.q_split : 1;
+  const int kvh = blockIdx.y / n_qs;
+  const int qs = blockIdx.y % n_qs;
+  const int Gs = G / n_qs;
+  const bool kv_part = qs == 0;
   const E* __restrict__ q = static_cast<const E*>(a.q);
   const E* __restrict__ k = static_cast<const E*>(a.k);
   const E* __restrict__ v = static_cast<const E*>(a.v);
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   // this sequence's first position, kept keys and token count (a.T is the row stride)
   const SeqPos sp = seq_pos_of(a.seq_pos, a.seq_len, a.pos_offset, a.T, a.window, b);
   const int n_tok = min(kTokBlock, sp.T - t0);  // may be <= 0 in the padding blocks
-  if (n_tok <= 0 && (a.ops_kernel || !(k_rot || v_t))) return;  // block-uniform
+  if (n_tok <= 0 && (a.ops_kernel || !(k_rot || v_t) || !kv_part)) return;  // block-uniform
 
   // rotation factors of the block's renumbered positions kept + t (post-RoPE cache:
   // absolute positions pos + t), kRopeTok tokens from token ts on
@@ -236,8 +243,8 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   __syncthreads();
 
   // One pass normalises and rotates kRowsPerPass rows per wave (kUnroll passes in flight).
-  // is_k: row r is token t0 + ts + r of the K head; else row r is (token ts + r / G, head
-  // r % G), ts the first token whose factors are staged. Row passes start at wave `first`,
+  // is_k: row r is token t0 + ts + r of the K head; else row r is (token ts + r / Gs, head
+  // qs Gs + r % Gs of the group), ts the first token whose factors are staged. Row passes start at wave `first`,
   // so that with few rows (a decode step) the Q rows, the K rows and the V copy below run
   // on different waves at the same time.
   auto rows = [&](const E* __restrict__ src, int n_rows, bool is_k, int first, int ts) {
@@ -251,9 +258,9 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int r = min(base + u * kRowsPerPass + slot, n_rows - 1);
-        zr[u] = is_k ? r : r / G;
+        zr[u] = is_k ? r : r / Gs;
         tt[u] = ts + zr[u];
-        const int head = is_k ? kvh : kvh * G + r % G;
+        const int head = is_k ? kvh : kvh * G + qs * Gs + r % Gs;
         const int H = is_k ? a.Hkv : a.Hq;
         off[u] = ((static_cast<long long>(b) * a.T + t0 + tt[u]) * H + head) * D + c * kVec;
         const u32x4 w0 = *reinterpret_cast<const u32x4*>(src + off[u]);
@@ -335,11 +342,11 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
       __syncthreads();
     }
     const int nt = min(kRopeTok<D>, n_tok - ts);
-    if (q_out) rows(q, nt * G, false, 0, ts);  // (no Q: the prefill normalises and rotates it)
-    rows(k, nt, true, 1, ts);
+    if (q_out) rows(q, nt * Gs, false, 0, ts);  // (no Q: the prefill normalises and rotates it)
+    if (kv_part) rows(k, nt, true, 1, ts);
   }
 
-  if (k_rot && !a.ops_kernel) {  // zero the padding rows T .. Tp-1 of this block
+  if (kv_part && k_rot && !a.ops_kernel) {  // zero the padding rows T .. Tp-1 of this block
     for (int i = threadIdx.x; i < kTokBlock * (D / kVec); i += kThreads) {
       if (kTiled) {  // i = chunk * 64 + key in tile
         const long long t = t0 + i % kTokBlock;
@@ -359,8 +366,8 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   // (V norm: every chunk scaled by its row's inverse RMS, rounded once)
   constexpr int kChunks = D / kVec;  // 16-byte chunks per row
   if constexpr (kTiled) {
-    const bool vt_here = v_t && !a.ops_kernel && t0 < a.Tp;  // Tp: a multiple of 128, so whole tiles
-    if (v_cache || vt_here) {
+    const bool vt_here = kv_part && v_t && !a.ops_kernel && t0 < a.Tp;  // Tp: a multiple of 128, so whole tiles
+    if ((kv_part && v_cache) || vt_here) {
       // lane task i = key chunk kc (8 tokens) x dim chunk cidx; from wave 2, as above
       for (int i = (threadIdx.x + kThreads - 128) % kThreads; i < 8 * kChunks; i += kThreads) {
         const int kc = i / kChunks, cidx = i % kChunks;
@@ -601,7 +608,16 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   // without the operand kernel the append kernel also covers the padding tokens T .. Tp-1
   const long long tokens = (operands && !a.ops_kernel) ? a.Tp : a.T;
   const unsigned gx = static_cast<unsigned>((tokens + kTokBlock - 1) / kTokBlock);
-  hipLaunchKernelGGL((kv_append_kernel<E, D>), dim3(gx, a.Hkv, a.B), dim3(kThreads), 0, stream, a);
+  // a bf16 chunk of a few token blocks: split the query heads over up to 2^k blocks until
+  // about 1024 blocks are in flight (single-token steps keep one block per KV head)
+  AppendArgs b = a;
+  b.q_split = 1;
+  if (sizeof(E) == 2 && a.q_out && a.T >= kTokBlock) {
+    const long long blocks = static_cast<long long>(gx) * a.Hkv * a.B;
+    const int G = a.Hq / a.Hkv;
+    while (blocks * b.q_split < 1024 && G % (2 * b.q_split) == 0) b.q_split *= 2;
+  }
+  hipLaunchKernelGGL((kv_append_kernel<E, D>), dim3(gx, a.Hkv * b.q_split, a.B), dim3(kThreads), 0, stream, b);
   return hipGetLastError();
 }
 

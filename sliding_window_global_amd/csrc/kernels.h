@@ -36,6 +36,7 @@ struct AppendArgs {
   bool v_norm;               // divide each new V head vector by its RMS before use
   int d;                     // head dim: 128 (fp32 and bf16), 256 or 512 (bf16)
   const float2* rope;
+  int q_split;               // (set by the launch) blocks sharing one token block's query heads
 };
 // Both launch, when prefill operands are requested after cached tokens or for a ragged
 // batch, first the operand kernel (the kept keys from the cache, all of V^T and the
