@@ -287,7 +287,8 @@ def _decode_case(B, Hq, Hkv, window, pos_offset, rope, seed, check_b, poison_fut
 @pytest.mark.parametrize("window,pos_offset", [(2048, 0), (2048, 1), (2048, 100), (2048, 2046),
                                                (2048, 2047), (2048, 2048), (2048, 32767),
                                                (2048, 32767 + 1000), (0, 0), (0, 63), (0, 64),
-                                               (0, 5000), (16, 3), (16, 40)])
+                                               (0, 5000), (16, 3), (16, 40), (1, 0), (1, 50),
+                                               (2, 7), (2, 8)])
 def test_decode_small_batch(window, pos_offset):
     """Ring fill-up and wrap, contiguous growth, tile edges; dead slots hold NaN."""
     rope = Rope(1e4) if window else Rope(1e6, 64.0)
