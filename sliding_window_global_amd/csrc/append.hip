@@ -215,10 +215,17 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   // rotation factors of the block's renumbered positions kept + t (post-RoPE cache:
   // absolute positions pos + t), kRopeTok tokens from token ts on
   const long long p_first = a.post_rope ? sp.pos : sp.kept;
+  // (two adjacent pairs per step: 16-byte table reads and LDS writes; the product of each
+  // pair is the one rope_factor forms)
   auto stage = [&](int ts) {
-    for (int i = threadIdx.x; i < kRopeTok<D> * kH; i += kThreads) {
-      const int r = i / kH, j = i % kH;
-      if (ts + r < n_tok) zs[r][j] = rope_factor<kH>(a.rope, p_first + t0 + ts + r, j);
+    for (int i = threadIdx.x; i < kRopeTok<D> * (kH / 2); i += kThreads) {
+      const int r = i / (kH / 2), j = 2 * (i % (kH / 2));
+      if (ts + r >= n_tok) continue;
+      const long long p = p_first + t0 + ts + r;
+      const float4 f = *reinterpret_cast<const float4*>(a.rope + (p & (kRopeFine - 1)) * kH + j);
+      const float4 cz = *reinterpret_cast<const float4*>(a.rope + (kRopeFine + (p >> 6)) * kH + j);
+      *reinterpret_cast<float4*>(&zs[r][j]) = make_float4(cz.x * f.x - cz.y * f.y, cz.x * f.y + cz.y * f.x,
+                                                          cz.z * f.z - cz.w * f.w, cz.z * f.w + cz.w * f.z);
     }
   };
   stage(0);
