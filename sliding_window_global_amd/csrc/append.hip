@@ -498,10 +498,15 @@ __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a
   };
 
   if (k_rot) {
-    if (kStageRope<D>) {
-      for (int i = threadIdx.x; i < kTokBlock * kH; i += kThreads) {
-        const int r = i / kH, j = i % kH;
-        if (R0 + r < kept && !a.post_rope) zs[r][j] = rope_factor<kH>(a.rope, R0 + r, j);
+    if (kStageRope<D>) {  // (two adjacent pairs per step, as in the append kernel)
+      for (int i = threadIdx.x; i < kTokBlock * (kH / 2); i += kThreads) {
+        const int r = i / (kH / 2), j = 2 * (i % (kH / 2));
+        if (R0 + r >= kept || a.post_rope) continue;
+        const long long p = R0 + r;
+        const float4 f = *reinterpret_cast<const float4*>(a.rope + (p & (kRopeFine - 1)) * kH + j);
+        const float4 cz = *reinterpret_cast<const float4*>(a.rope + (kRopeFine + (p >> 6)) * kH + j);
+        *reinterpret_cast<float4*>(&zs[r][j]) = make_float4(cz.x * f.x - cz.y * f.y, cz.x * f.y + cz.y * f.x,
+                                                            cz.z * f.z - cz.w * f.w, cz.z * f.w + cz.w * f.z);
       }
       __syncthreads();
     }
