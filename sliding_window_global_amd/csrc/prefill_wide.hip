@@ -34,6 +34,8 @@
 //            across the two S^T blocks, exactly the P^T operand of the P V MFMA (the copy
 //            into LDS already places them in that order, so each fragment read is
 //            contiguous); V^T is read in natural key order. Each K' fragment feeds NB MFMAs.
+//            Fragments come from LDS through a 3-deep register ring, so a read has three
+//            MFMA groups to land before its own.
 //   softmax = exp2 domain (Q' pre-scaled by scale * log2 e); lazy rescaling: the
 //            reference of a row moves only when a score exceeds it by 2^8; row sums from
 //            the same bf16-rounded P as P V.
