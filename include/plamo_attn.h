@@ -26,8 +26,15 @@
  *   - Arguments are checked before anything is launched; on failure the call
  *     returns a negative plamo_status and enqueues nothing. A launch error is
  *     reported as PLAMO_ERR_HIP. No C++ exception crosses this boundary.
- *   - dtype PLAMO_BF16: bf16 tensors, fp32 arithmetic inside. PLAMO_F32: fp32
- *     tensors and arithmetic (prefill path only).
+ *   - dtype PLAMO_BF16: bf16 tensors, fp32 arithmetic inside, except the two score
+ *     operands Q' (q_out / q_rot) and K' (k_rot_out / k_rot), which are IEEE half (fp16):
+ *     each is rounded once from its fp32 normalised and rotated value, and the score
+ *     product runs on fp16 MFMA (same rate as bf16, three more mantissa bits; V, P and the
+ *     outputs stay bf16). Range: these operands are RMS-normalised, so with the norm they
+ *     stay inside the half range for gains |c + w_r| <= 512 at any head dim and RoPE
+ *     amplitude here; without the norm the inputs must satisfy |q|, |k| <= 8192 (not
+ *     checked: a larger value would overflow to inf). PLAMO_F32: fp32 tensors and
+ *     arithmetic (prefill path only).
  *   - Head dimension d is 128 (PLaMo 3's head_dim [P3 §2.1]), or 256 / 512 for the
  *     Gemma-4-shaped layers the page compares it with [P3 §8 table] (bf16 only; decode
  *     then needs a post-RoPE cache). Hq must be a multiple of Hkv and Hq/Hkv <= 16.
@@ -121,18 +128,19 @@ PLAMO_API long long plamo_prefill_padded_len(long long S);
  * v_norm   1 = divide each new V head vector by its RMS (eps norm_eps, no gain) before it
  *          is cached or used (the Gemma-4-shaped layer [P3 §8 table]); 0 = V as given.
  *          k and v may be the same buffer (that layer's global K = V projection).
- * q_out    [B, T, Hq, d]   normalised and rotated Q (dtype). q and q_out both NULL: the
- *                          queries are left to plamo_attn_prefill_fused_q.
+ * q_out    [B, T, Hq, d]   normalised and rotated Q (fp16 for PLAMO_BF16, fp32 for
+ *                          PLAMO_F32). q and q_out both NULL: the queries are left to
+ *                          plamo_attn_prefill_fused_q.
  * k_rot_out rotated K of the S = kept + T keys the chunk attends, Tp =
  *                          plamo_prefill_padded_len(S) rows per (b, KV head): rows
  *                          0..kept-1 the cached (pre-RoPE) keys read from k_cache before
  *                          this call updates it, rotated at renumbered positions
- *                          0..kept-1; rows kept..S-1 the new tokens (normalised,
- *                          cache-rounded, rotated); rows S..Tp-1 zero. NULL = not
+ *                          0..kept-1; rows kept..S-1 the new tokens (normalised and
+ *                          rotated in fp32, rounded once); rows S..Tp-1 zero. NULL = not
  *                          written. (Prefill operand.) With kept > 0 the caches must be
  *                          given. Layout per (b, KV head):
- *                            fp32: [Tp][d];
- *                            bf16: Tp/64 tiles of 64 tokens, tile = [d/8][64][8]
+ *                            PLAMO_F32: fp32 [Tp][d];
+ *                            PLAMO_BF16: fp16, Tp/64 tiles of 64 tokens, tile = [d/8][64][8]
  *                                  (dim / 8, token in tile, dim % 8), 128 d bytes.
  * v_t_out  V of the same S keys (cached, then new) transposed, pad zeroed. NULL = not
  *                          written. (Prefill operand.) Layout
@@ -165,7 +173,7 @@ PLAMO_API int plamo_kv_append(int dtype, const void* q, const void* k, const voi
 /* ---------------------------------------------------------------------------
  * plamo_attn_prefill -- step 4 for a prefill of T tokens [P3 §4.5, §5.1]
  *
- * q_rot [B, T, Hq, d]; k_rot and v_t in the dtype's layout written by
+ * q_rot [B, T, Hq, d] (fp16 for PLAMO_BF16); k_rot and v_t in the dtype's layout written by
  * plamo_kv_append with the same window and pos_offset (Tp =
  * plamo_prefill_padded_len(kept + T), kept as for plamo_kv_append); out
  * [B, T, Hq, d] (token major, i.e. [B, T, Hq*d] ready for the output projection
@@ -188,7 +196,7 @@ PLAMO_API int plamo_attn_prefill(int dtype, const void* q_rot, const void* k_rot
  * row is normalised (gain norm_offset + q_norm_w, eps norm_eps; q_norm_w NULL = no norm)
  * and rotated with `rope_table` at the position plamo_kv_append would give it (renumbered
  * kept + t, or absolute pos_offset + t with cache_order PLAMO_CACHE_POST_ROPE), in fp32,
- * then rounded once to bf16 for the MFMA. Call plamo_kv_append with q = q_out = NULL
+ * then scaled and rounded once to fp16 for the MFMA. Call plamo_kv_append with q = q_out = NULL
  * first (it then writes only the K/V side: cache, k_rot, v_t), so Q' never goes through
  * HBM. k_rot, v_t, out and the mask as for plamo_attn_prefill. bf16 and d = 128 only
  * (PLAMO_ERR_UNSUPPORTED otherwise); the table must cover the queries' positions
@@ -209,7 +217,9 @@ PLAMO_API int plamo_attn_prefill_fused_q(int dtype, const void* q, const void* q
  * their renumbered positions 0 .. S-1 rotate the pre-RoPE K on the fly with
  * `rope_table`; q_rot carries position S-1.
  *
- * q_rot [B, 1, Hq, d]; k_cache, v_cache [B, Hkv, cap, d] (bf16); out [B, 1, Hq, d].
+ * q_rot [B, 1, Hq, d] (fp16, as plamo_kv_append writes it); k_cache, v_cache [B, Hkv, cap,
+ * d] (bf16); out [B, 1, Hq, d] (bf16). Cached K is rotated in fp32 and rounded to fp16 for
+ * the score product.
  * workspace: device scratch of at least plamo_attn_decode_workspace_bytes(...)
  * bytes (split-K partial results); contents on entry do not matter. When that
  * size is 0 (one key range per sequence and KV head) workspace may be NULL.

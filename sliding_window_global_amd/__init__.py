@@ -100,6 +100,12 @@ def _nbytes(t: torch.Tensor | None) -> int:
     return 0 if t is None else t.numel() * t.element_size()
 
 
+def score_dtype(dt: torch.dtype) -> torch.dtype:
+    """Storage type of the score operands Q' (q_out / q_rot) and K' (k_rot) of a layer of
+    dtype dt: IEEE half on bf16 layers (include/plamo_attn.h), fp32 on fp32 ones."""
+    return torch.float16 if dt == torch.bfloat16 else dt
+
+
 def _dtype_code(dt: torch.dtype) -> int:
     if dt == torch.bfloat16:
         return PLAMO_BF16
@@ -196,7 +202,8 @@ def plamo_kv_append(q, k, v, q_out, *, window: int, pos_offset: int, rope_table,
     st = _lib.load().plamo_kv_append(
         _dtype_code(dt), _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt),
         _dev(q_norm_w, "q_norm_w", dt), _dev(k_norm_w, "k_norm_w", dt), float(norm_offset), float(norm_eps),
-        int(bool(v_norm)), _dev(q_out, "q_out", dt), _dev(k_rot_out, "k_rot_out", dt), _dev(v_t_out, "v_t_out", dt),
+        int(bool(v_norm)), _dev(q_out, "q_out", score_dtype(dt)), _dev(k_rot_out, "k_rot_out", score_dtype(dt)),
+        _dev(v_t_out, "v_t_out", dt),
         _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), int(cap), B, T, Hq or Hkv, Hkv, d,
         int(window), int(pos_offset), _dev(rope_table, "rope_table", torch.float32),
         rope_table.numel() * 4, _order(cache_post_rope), _stream(stream))
@@ -205,8 +212,9 @@ def plamo_kv_append(q, k, v, q_out, *, window: int, pos_offset: int, rope_table,
 
 def plamo_attn_prefill(q_rot, k_rot, v_t, out, *, window: int, pos_offset: int = 0,
                        softmax_scale: float | None = None, stream=None) -> None:
-    """q_rot [B,T,Hq,d], k_rot / v_t as prefill_operand_shapes -> out [B,T,Hq,d]."""
-    dt = q_rot.dtype
+    """q_rot [B,T,Hq,d], k_rot / v_t as prefill_operand_shapes -> out [B,T,Hq,d] (q_rot and
+    k_rot in score_dtype of the layer's dtype, v_t and out in the layer's dtype)."""
+    dt = v_t.dtype
     B, T, Hq, d = q_rot.shape
     Hkv = k_rot.shape[1]
     k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dt, window, pos_offset)
@@ -216,8 +224,8 @@ def plamo_attn_prefill(q_rot, k_rot, v_t, out, *, window: int, pos_offset: int =
         raise ValueError("out must match q_rot")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     st = _lib.load().plamo_attn_prefill(
-        _dtype_code(dt), _dev(q_rot, "q_rot", dt), _dev(k_rot, "k_rot", dt), _dev(v_t, "v_t", dt),
-        _dev(out, "out", dt), B, T, Hq, Hkv, d, int(window), int(pos_offset), scale, _stream(stream))
+        _dtype_code(dt), _dev(q_rot, "q_rot", score_dtype(dt)), _dev(k_rot, "k_rot", score_dtype(dt)),
+        _dev(v_t, "v_t", dt), _dev(out, "out", dt), B, T, Hq, Hkv, d, int(window), int(pos_offset), scale, _stream(stream))
     _check(st, "plamo_attn_prefill")
 
 
@@ -238,7 +246,8 @@ def plamo_attn_prefill_fused_q(q, k_rot, v_t, out, *, window: int, rope_table, p
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     st = _lib.load().plamo_attn_prefill_fused_q(
         _dtype_code(dt), _dev(q, "q", dt), _dev(q_norm_w, "q_norm_w", dt), float(norm_offset), float(norm_eps),
-        _dev(k_rot, "k_rot", dt), _dev(v_t, "v_t", dt), _dev(out, "out", dt), B, T, Hq, Hkv, d, int(window),
+        _dev(k_rot, "k_rot", score_dtype(dt)), _dev(v_t, "v_t", dt), _dev(out, "out", dt), B, T, Hq, Hkv, d,
+        int(window),
         int(pos_offset), _dev(rope_table, "rope_table", torch.float32), _nbytes(rope_table),
         _order(cache_post_rope), scale, _stream(stream))
     _check(st, "plamo_attn_prefill_fused_q")
@@ -252,8 +261,8 @@ def plamo_attn_decode_workspace_bytes(B: int, Hq: int, Hkv: int, window: int, po
 def plamo_attn_decode(q_rot, k_cache, v_cache, out, workspace, *, window: int, pos_offset: int,
                       rope_table, softmax_scale: float | None = None, cache_post_rope: bool = False,
                       stream=None) -> None:
-    """q_rot [B,1,Hq,d]; caches [B,Hkv,cap,d] (bf16) -> out [B,1,Hq,d]."""
-    dt = q_rot.dtype
+    """q_rot [B,1,Hq,d] (fp16); caches [B,Hkv,cap,d] (bf16) -> out [B,1,Hq,d] (bf16)."""
+    dt = out.dtype
     B, T, Hq, d = q_rot.shape
     Hkv, cap = k_cache.shape[1], k_cache.shape[2]
     if tuple(k_cache.shape) != (B, Hkv, cap, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
@@ -263,7 +272,8 @@ def plamo_attn_decode(q_rot, k_cache, v_cache, out, workspace, *, window: int, p
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _lib.load().plamo_attn_decode(
-        _dtype_code(dt), _dev(q_rot, "q_rot", dt), _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        _dtype_code(dt), _dev(q_rot, "q_rot", score_dtype(dt)), _dev(k_cache, "k_cache", dt),
+        _dev(v_cache, "v_cache", dt),
         int(cap), _dev(out, "out", dt), _dev(workspace, "workspace"), ws_bytes, B, T, Hq, Hkv, d,
         int(window), int(pos_offset), _dev(rope_table, "rope_table", torch.float32), _nbytes(rope_table),
         scale, _order(cache_post_rope), _stream(stream))
@@ -315,7 +325,8 @@ def plamo_kv_append_ragged(q, k, v, q_out, *, window: int, seq_pos_offsets, max_
     st = _lib.load().plamo_kv_append_ragged(
         _dtype_code(dt), _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt),
         _dev(q_norm_w, "q_norm_w", dt), _dev(k_norm_w, "k_norm_w", dt), float(norm_offset), float(norm_eps),
-        int(bool(v_norm)), _dev(q_out, "q_out", dt), _dev(k_rot_out, "k_rot_out", dt), _dev(v_t_out, "v_t_out", dt),
+        int(bool(v_norm)), _dev(q_out, "q_out", score_dtype(dt)), _dev(k_rot_out, "k_rot_out", score_dtype(dt)),
+        _dev(v_t_out, "v_t_out", dt),
         _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), int(cap), B, T, Hq or Hkv, Hkv, d,
         int(window), pos_p, len_p, int(max_pos_offset), _dev(rope_table, "rope_table", torch.float32),
         rope_table.numel() * 4, _order(cache_post_rope), _stream(stream))
@@ -325,7 +336,7 @@ def plamo_kv_append_ragged(q, k, v, q_out, *, window: int, seq_pos_offsets, max_
 def plamo_attn_prefill_ragged(q_rot, k_rot, v_t, out, *, window: int, seq_pos_offsets, max_pos_offset: int,
                               seq_lens=None, softmax_scale: float | None = None, stream=None) -> None:
     """plamo_attn_prefill with per-sequence positions and token counts (as plamo_kv_append_ragged)."""
-    dt = q_rot.dtype
+    dt = v_t.dtype
     B, T, Hq, d = q_rot.shape
     Hkv = k_rot.shape[1]
     k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dt, window, max_pos_offset)
@@ -336,8 +347,8 @@ def plamo_attn_prefill_ragged(q_rot, k_rot, v_t, out, *, window: int, seq_pos_of
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     pos_p, len_p = _ragged_arrays(B, seq_pos_offsets, seq_lens)
     st = _lib.load().plamo_attn_prefill_ragged(
-        _dtype_code(dt), _dev(q_rot, "q_rot", dt), _dev(k_rot, "k_rot", dt), _dev(v_t, "v_t", dt),
-        _dev(out, "out", dt), B, T, Hq, Hkv, d, int(window), pos_p, len_p, int(max_pos_offset), scale,
+        _dtype_code(dt), _dev(q_rot, "q_rot", score_dtype(dt)), _dev(k_rot, "k_rot", score_dtype(dt)),
+        _dev(v_t, "v_t", dt), _dev(out, "out", dt), B, T, Hq, Hkv, d, int(window), pos_p, len_p, int(max_pos_offset), scale,
         _stream(stream))
     _check(st, "plamo_attn_prefill_ragged")
 
@@ -359,7 +370,8 @@ def plamo_attn_prefill_fused_q_ragged(q, k_rot, v_t, out, *, window: int, seq_po
     pos_p, len_p = _ragged_arrays(B, seq_pos_offsets, seq_lens)
     st = _lib.load().plamo_attn_prefill_fused_q_ragged(
         _dtype_code(dt), _dev(q, "q", dt), _dev(q_norm_w, "q_norm_w", dt), float(norm_offset), float(norm_eps),
-        _dev(k_rot, "k_rot", dt), _dev(v_t, "v_t", dt), _dev(out, "out", dt), B, T, Hq, Hkv, d, int(window),
+        _dev(k_rot, "k_rot", score_dtype(dt)), _dev(v_t, "v_t", dt), _dev(out, "out", dt), B, T, Hq, Hkv, d,
+        int(window),
         pos_p, len_p, int(max_pos_offset), _dev(rope_table, "rope_table", torch.float32), _nbytes(rope_table),
         _order(cache_post_rope), scale, _stream(stream))
     _check(st, "plamo_attn_prefill_fused_q_ragged")
@@ -376,7 +388,7 @@ def plamo_attn_decode_ragged(q_rot, k_cache, v_cache, out, workspace, *, window:
                              cache_post_rope: bool = False, stream=None) -> None:
     """plamo_attn_decode with one position per sequence; workspace sized by
     plamo_attn_decode_ragged_workspace_bytes."""
-    dt = q_rot.dtype
+    dt = out.dtype
     B, T, Hq, d = q_rot.shape
     if T != 1:
         raise ValueError("decode takes one token per sequence")
@@ -389,7 +401,8 @@ def plamo_attn_decode_ragged(q_rot, k_cache, v_cache, out, workspace, *, window:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     pos_p, _ = _ragged_arrays(B, seq_pos_offsets, None)
     st = _lib.load().plamo_attn_decode_ragged(
-        _dtype_code(dt), _dev(q_rot, "q_rot", dt), _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        _dtype_code(dt), _dev(q_rot, "q_rot", score_dtype(dt)), _dev(k_cache, "k_cache", dt),
+        _dev(v_cache, "v_cache", dt),
         int(cap), _dev(out, "out", dt), _dev(workspace, "workspace"), ws_bytes, B, Hq, Hkv, d, int(window),
         pos_p, int(max_pos_offset), _dev(rope_table, "rope_table", torch.float32), _nbytes(rope_table),
         scale, _order(cache_post_rope), _stream(stream))

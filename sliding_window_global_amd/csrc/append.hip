@@ -23,9 +23,12 @@
 // it writes to the cache as it is and to the transposed prefill operand after an 8 x 8
 // transpose in registers; fp32 V is staged through LDS for the transpose.
 //
-// bf16 prefill operands are tiled by 64 keys, each tile 64 d bf16 in the order the prefill
-// kernels copy straight into LDS: K' tile = [d/8 dim chunks][64 keys][8 dims], V^T tile =
-// [8 key chunks][d dims][8 keys]. fp32 operands are plain [Tp][d] and [d][Tp].
+// bf16 prefill operands are tiled by 64 keys, each tile 64 d elements in the order the
+// prefill kernels copy straight into LDS: K' tile = [d/8 dim chunks][64 keys][8 dims], V^T
+// tile = [8 key chunks][d dims][8 keys]. fp32 operands are plain [Tp][d] and [d][Tp].
+// On a bf16 layer the score operands Q' and K' are written as IEEE halves, each rounded once
+// from the fp32 normalised and rotated value (a new key is rotated before the cache rounds
+// it); the cache and V^T stay bf16.
 #include "common.h"
 #include "kernels.h"
 
@@ -59,7 +62,6 @@ struct Io;
 template <>
 struct Io<float> {
   static __device__ __forceinline__ float ld(const float* p) { return *p; }
-  static __device__ __forceinline__ float rnd(float x) { return x; }
   static __device__ __forceinline__ void unpack(const u32x4& w, float* x) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e]);
@@ -67,12 +69,13 @@ struct Io<float> {
   static __device__ __forceinline__ u32x4 pack(const float* x) {
     return u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
   }
+  // score operands (Q', K') keep the storage type
+  static __device__ __forceinline__ u32x4 pack_op(const float* x) { return pack(x); }
 };
 
 template <>
 struct Io<bf16_t> {
   static __device__ __forceinline__ float ld(const bf16_t* p) { return bf16_to_f32(*p); }
-  static __device__ __forceinline__ float rnd(float x) { return bf16_to_f32(f32_to_bf16(x)); }
   static __device__ __forceinline__ void unpack(const u32x4& w, float* x) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -83,6 +86,12 @@ struct Io<bf16_t> {
   static __device__ __forceinline__ u32x4 pack(const float* x) {
     return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
                  pack_bf16x2(x[6], x[7])};
+  }
+  // score operands (Q', K') of a bf16 layer are IEEE halves: one rounding of the fp32
+  // normalised and rotated value, with three more mantissa bits than bf16
+  static __device__ __forceinline__ u32x4 pack_op(const float* x) {
+    return u32x4{pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3]), pack_f16x2(x[4], x[5]),
+                 pack_f16x2(x[6], x[7])};
   }
 };
 
@@ -302,9 +311,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
           const long long s = a.window == 0 ? n : n % a.window;
           cdst = k_cache + ((static_cast<long long>(b) * a.Hkv + kvh) * a.cap + s) * D + c * kVec;
         }
-        if (is_k && !a.post_rope) {  // the cache stores K before RoPE; RoPE acts on that value
-#pragma unroll
-          for (int e = 0; e < 2 * kVec; ++e) x[u][e] = Io<E>::rnd(x[u][e]);
+        if (is_k && !a.post_rope) {  // the cache stores K before RoPE (rounded to the cache type)
           if (to_cache) {
             *reinterpret_cast<u32x4*>(cdst) = Io<E>::pack(x[u]);
             *reinterpret_cast<u32x4*>(cdst + kH) = Io<E>::pack(x[u] + kVec);
@@ -331,13 +338,13 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
         if (kTiled && is_k) {  // chunks c and c + d/16 of key R within its tile
           E* dst = k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + (R & ~63LL)) * D +
                    (c * kTokBlock + (R & 63)) * kVec;
-          *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(y);
-          *reinterpret_cast<u32x4*>(dst + kLanesPerRow * kTokBlock * kVec) = Io<E>::pack(y + kVec);
+          *reinterpret_cast<u32x4*>(dst) = Io<E>::pack_op(y);
+          *reinterpret_cast<u32x4*>(dst + kLanesPerRow * kTokBlock * kVec) = Io<E>::pack_op(y + kVec);
         } else {
           E* dst = is_k ? k_rot + ((static_cast<long long>(b) * a.Hkv + kvh) * a.Tp + R) * D + c * kVec
                         : q_out + off[u];
-          *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(y);
-          *reinterpret_cast<u32x4*>(dst + kH) = Io<E>::pack(y + kVec);
+          *reinterpret_cast<u32x4*>(dst) = Io<E>::pack_op(y);
+          *reinterpret_cast<u32x4*>(dst + kH) = Io<E>::pack_op(y + kVec);
         }
       }
     }
@@ -536,12 +543,12 @@ __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a
       }
       if (kTiled) {
         E* dst = k_rot + (bh * a.Tp + R0) * D + (c * kTokBlock + r) * kVec;
-        *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(y);
-        *reinterpret_cast<u32x4*>(dst + kLanesPerRow * kTokBlock * kVec) = Io<E>::pack(y + kVec);
+        *reinterpret_cast<u32x4*>(dst) = Io<E>::pack_op(y);
+        *reinterpret_cast<u32x4*>(dst + kLanesPerRow * kTokBlock * kVec) = Io<E>::pack_op(y + kVec);
       } else {
         E* dst = k_rot + (bh * a.Tp + R) * D + c * kVec;
-        *reinterpret_cast<u32x4*>(dst) = Io<E>::pack(y);
-        *reinterpret_cast<u32x4*>(dst + kH) = Io<E>::pack(y + kVec);
+        *reinterpret_cast<u32x4*>(dst) = Io<E>::pack_op(y);
+        *reinterpret_cast<u32x4*>(dst + kH) = Io<E>::pack_op(y + kVec);
       }
     }
   }

@@ -13,9 +13,11 @@ constexpr int kRopeFine = 64;      // positions per coarse rope-table row
 constexpr int kPadT = 128;         // prefill operand padding of the token axis
 
 typedef uint16_t bf16_t;  // raw bfloat16 bits in memory
+typedef uint16_t f16_t;   // raw IEEE half bits in memory (the Q' and K' score operands)
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
@@ -42,6 +44,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
 
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+
+// Pack two floats into one dword of two IEEE halves (lo in the low half), round to nearest
+// even: one v_cvt_pk_f16_f32. The score operands Q' and K' are stored and multiplied in
+// this format: they are RMS-normalised (bounded by |gain| sqrt(d) times the RoPE amplitude),
+// so the three extra mantissa bits over bf16 come at no range cost.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f32x2v f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2v));
+}
+
+__device__ __forceinline__ float lo_f16(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(f16x2v, w).x);
+}
+__device__ __forceinline__ float hi_f16(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(f16x2v, w).y);
+}
+
 // acc + lo(w) + hi(w) for a dword of two bf16 (v_dot2c_f32_bf16 against (1, 1)).
 __device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
   const bf16x2v one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
@@ -50,6 +70,9 @@ __device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// bf16 pair -> IEEE half pair (exact for |x| in [2^-14, 65504], the range of normalised K).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) { return pack_f16x2(lo_bf16(w), hi_bf16(w)); }
 
 // Rotation factor amp * exp(i p w_j) from the two-level table: coarse row p >> 6 times
 // fine row p & 63 (complex product, fp32). Layout: fine [64][d/2] float2 first, then

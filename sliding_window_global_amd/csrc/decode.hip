@@ -16,7 +16,9 @@
 //            conflicts),
 //   rope     the tile's coarse factor row global -> LDS by one direct load,
 // three sub-tiles per wave in flight or in use (a ring unrolled by three).
-//   S^T[16 keys][16 heads] = K'[16][128] Q'^T  (v_mfma_f32_16x16x32_bf16; heads padded to 16)
+//   S^T[16 keys][16 heads] = K'[16][128] Q'^T  (v_mfma_f32_16x16x32_f16: Q' arrives as IEEE
+//                                              halves, K' is rotated in fp32 and rounded to
+//                                              half; heads padded to 16)
 //   O^T[128 d][16 heads]  += V^T[128][16] P^T   (v_mfma_f32_16x16x16_bf16)
 // Each lane rotates its key's 16 pairs in registers: the fine rope factor of its key is
 // fixed for the whole loop (tile starts are multiples of 64), the coarse row comes with
@@ -104,10 +106,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   // (loaded here, zeroed for the padding heads once the loads have landed, below)
   const bool q_ok = m16 < G;
   u32x4 qw[4];
-  bf16x8 qf[4];
+  f16x8 qf[4];
   {
-    const bf16_t* src = static_cast<const bf16_t*>(a.q_rot) +
-                        (static_cast<long long>(b) * a.Hq + kvh * G + (q_ok ? m16 : 0)) * kHeadDim;
+    const f16_t* src = static_cast<const f16_t*>(a.q_rot) +
+                       (static_cast<long long>(b) * a.Hq + kvh * G + (q_ok ? m16 : 0)) * kHeadDim;
 #pragma unroll
     for (int s = 0; s < 4; ++s) qw[s] = *reinterpret_cast<const u32x4*>(src + (s >> 1) * kHalf + g * 16 + (s & 1) * 8);
   }
@@ -184,13 +186,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
       __attribute__((always_inline)) {
     const long long key0 = s_begin + static_cast<long long>(t) * kTile + wave * kSub;
     if (key0 >= s_end) return;  // wave-uniform: no key of this wave in the tile
-    // K': rotate the lane's 16 pairs, pack to bf16 in the A-operand layout (a post-RoPE
-    // cache row is already that operand)
-    bf16x8 kf[4];
+    // K': rotate the lane's 16 pairs, pack to half in the A-operand layout (a post-RoPE
+    // cache row is already that operand, converted bf16 -> half exactly)
+    f16x8 kf[4];
 #pragma unroll
-    for (int hs = 0; hs < 2 && !kRotate; ++hs) {
-      kf[hs] = __builtin_bit_cast(bf16x8, kw[hs]);
-      kf[hs + 2] = __builtin_bit_cast(bf16x8, kw[hs + 2]);
+    for (int s = 0; s < 4 && !kRotate; ++s) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = bf16x2_to_f16x2(kw[s][i]);
+      kf[s] = __builtin_bit_cast(f16x8, w);
     }
 #pragma unroll
     for (int hs = 0; hs < 2 && kRotate; ++hs) {  // hs: slices (hs, hs+2) hold pairs 16g + 8hs + e
@@ -210,15 +214,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
           ra[u] = x0 * zx - x1 * zy;
           rb[u] = x0 * zy + x1 * zx;
         }
-        lo_w[e2] = pack_bf16x2(ra[0], ra[1]);
-        hi_w[e2] = pack_bf16x2(rb[0], rb[1]);
+        lo_w[e2] = pack_f16x2(ra[0], ra[1]);
+        hi_w[e2] = pack_f16x2(rb[0], rb[1]);
       }
-      kf[hs] = __builtin_bit_cast(bf16x8, lo_w);
-      kf[hs + 2] = __builtin_bit_cast(bf16x8, hi_w);
+      kf[hs] = __builtin_bit_cast(f16x8, lo_w);
+      kf[hs + 2] = __builtin_bit_cast(f16x8, hi_w);
     }
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], sacc, 0, 0, 0);
+    for (int s = 0; s < 4; ++s) sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[s], qf[s], sacc, 0, 0, 0);
 
     // S^T layout: lane holds head m16, keys key0 + 4g + i
     float mx = -INFINITY;
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
 #pragma unroll
   for (int e = 0; e < 16 && kRotate; ++e) asm volatile("" : "+v"(fine[e].x), "+v"(fine[e].y));
 #pragma unroll
-  for (int s = 0; s < 4; ++s) qf[s] = __builtin_bit_cast(bf16x8, q_ok ? qw[s] : u32x4{0, 0, 0, 0});
+  for (int s = 0; s < 4; ++s) qf[s] = __builtin_bit_cast(f16x8, q_ok ? qw[s] : u32x4{0, 0, 0, 0});
   // Before computing tile t, an explicit wait leaves the loads of the tiles issued after it
   // in flight (the compiler's own waits cannot follow the ring across loop iterations).
   constexpr unsigned kTwoBehind = wait_vmcnt(2 * kLoads);

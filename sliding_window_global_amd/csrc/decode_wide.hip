@@ -13,7 +13,9 @@
 // (d/32 x 16 B per lane), V rows global -> LDS by direct loads (rows padded by 16 bytes, so
 // the transposed operand reads are free of bank conflicts), two sub-tiles per wave in
 // flight or in use.
-//   S^T[16 keys][16 heads] = K'[16][d] Q'^T     (v_mfma_f32_16x16x32_bf16; heads padded to 16)
+//   S^T[16 keys][16 heads] = K'[16][d] Q'^T     (v_mfma_f32_16x16x32_f16: Q' arrives as IEEE
+//                                               halves, the bf16 cache rows convert exactly;
+//                                               heads padded to 16)
 //   O^T[d][16 heads]      += V^T[d][16] P^T     (v_mfma_f32_16x16x16_bf16)
 // The softmax reference moves lazily (only when a head's score exceeds it by 2^8). The 4
 // waves' states merge in LDS; with one split the block writes the output, otherwise a
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 2 : 1) void decode_wide_kernel
   __shared__ __attribute__((aligned(16))) bf16_t vs0[kWaves][W::kVSlot];
   __shared__ __attribute__((aligned(16))) bf16_t vs1[kWaves][W::kVSlot];
   __shared__ float red_m[kWaves * kMaxGroup], red_l[kWaves * kMaxGroup];
-  __shared__ __attribute__((aligned(16))) bf16_t q_s[W::kQLds ? kMaxGroup * W::kQRow : 8];
+  __shared__ __attribute__((aligned(16))) f16_t q_s[W::kQLds ? kMaxGroup * W::kQRow : 8];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -87,9 +89,9 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 2 : 1) void decode_wide_kernel
   // ---- Q' fragment (B operand of S^T): head m16, dims 32 s + 8 g .. +7 ----------------
   const bool q_ok = m16 < G;
   u32x4 qw[W::kQLds ? 1 : W::kKC];
-  bf16x8 qf[W::kQLds ? 1 : W::kKC];
+  f16x8 qf[W::kQLds ? 1 : W::kKC];
   if (W::kQLds) {  // the block's G heads into LDS, padding heads zero
-    const bf16_t* src = static_cast<const bf16_t*>(a.q_rot) + (static_cast<long long>(b) * a.Hq + kvh * G) * D;
+    const f16_t* src = static_cast<const f16_t*>(a.q_rot) + (static_cast<long long>(b) * a.Hq + kvh * G) * D;
     for (int i = threadIdx.x; i < kMaxGroup * (D / 8); i += kThreads) {
       const int h = i / (D / 8), cc = i % (D / 8);
       const u32x4 w = h < G ? reinterpret_cast<const u32x4*>(src + h * D)[cc] : u32x4{0, 0, 0, 0};
@@ -97,13 +99,13 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 2 : 1) void decode_wide_kernel
     }
     __syncthreads();
   } else {
-    const bf16_t* src = static_cast<const bf16_t*>(a.q_rot) +
-                        (static_cast<long long>(b) * a.Hq + kvh * G + (q_ok ? m16 : 0)) * D + g * 8;
+    const f16_t* src = static_cast<const f16_t*>(a.q_rot) +
+                       (static_cast<long long>(b) * a.Hq + kvh * G + (q_ok ? m16 : 0)) * D + g * 8;
 #pragma unroll
     for (int s = 0; s < (W::kQLds ? 1 : W::kKC); ++s) qw[s] = *reinterpret_cast<const u32x4*>(src + s * 32);
   }
   auto q_frag = [&](int s) __attribute__((always_inline)) {
-    if (W::kQLds) return *reinterpret_cast<const bf16x8*>(q_s + m16 * W::kQRow + s * 32 + g * 8);
+    if (W::kQLds) return *reinterpret_cast<const f16x8*>(q_s + m16 * W::kQRow + s * 32 + g * 8);
     return qf[W::kQLds ? 0 : s];
   };
 
@@ -160,8 +162,12 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 2 : 1) void decode_wide_kernel
     if (key0 >= s_end) return;  // wave-uniform
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < W::kKC; ++s)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw[s]), q_frag(s), sacc, 0, 0, 0);
+    for (int s = 0; s < W::kKC; ++s) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = bf16x2_to_f16x2(kw[s][i]);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, w), q_frag(s), sacc, 0, 0, 0);
+    }
     // S^T layout: lane holds head m16, keys key0 + 4g + i
     float mx = -INFINITY;
 #pragma unroll
@@ -208,7 +214,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 2 : 1) void decode_wide_kernel
 #pragma unroll
   for (int s = 0; s < (W::kQLds ? 0 : W::kKC); ++s) asm volatile("" : "+v"(qw[s]));
 #pragma unroll
-  for (int s = 0; s < (W::kQLds ? 0 : W::kKC); ++s) qf[s] = __builtin_bit_cast(bf16x8, q_ok ? qw[s] : u32x4{0, 0, 0, 0});
+  for (int s = 0; s < (W::kQLds ? 0 : W::kKC); ++s) qf[s] = __builtin_bit_cast(f16x8, q_ok ? qw[s] : u32x4{0, 0, 0, 0});
   constexpr unsigned kOneBehind = wait_vmcnt(W::kLoads);
   int t = 0;
   for (; t + 2 <= n_tiles; t += 2) {

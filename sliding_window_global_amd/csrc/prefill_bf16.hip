@@ -17,7 +17,8 @@
 //            conflicts) and the reads of different chunks differ by constant offsets.
 //   order  = key tiles from the diagonal downwards. A row with no visible key in the
 //            first tiles keeps a -inf reference until its first visible key.
-//   math   = S^T = K' Q'^T and O^T = V^T P^T with v_mfma_f32_32x32x16_bf16: the query
+//   math   = S^T = K' Q'^T on v_mfma_f32_32x32x16_f16 (Q' and K' are IEEE halves) and
+//            O^T = V^T P^T on v_mfma_f32_32x32x16_bf16 (V and P bf16): the query
 //            index is the MFMA column in both, so each lane owns one query row for the
 //            online softmax and for the rescaling of its O^T accumulators. K' rows are
 //            read in the order that makes each lane's eight consecutive S^T entries
@@ -58,6 +59,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// the score product: Q' and K' are IEEE halves (same MFMA rate as bf16, three more bits)
+__device__ __forceinline__ f32x16 mfma32_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Key (within a 32-key block) whose K' row feeds MFMA row m: swaps bits 2 and 3, so that
@@ -155,12 +160,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   issue_k(0, ks0);
 
   // ---- Q' fragment (MFMA B operand): lane holds dims s*16 + hl*8 .. +7 of its row ----
-  // Pre-multiplied by scale * log2(e), so that S comes out of the MFMA in exp2 units.
+  // Pre-multiplied by scale * log2(e), so that S comes out of the MFMA in exp2 units, and
+  // rounded to IEEE half (Q' arrives as halves from the append, or is formed here in fp32).
   const float c = a.scale * 1.4426950408889634f;
   const int r0 = i0 + wave * 32;
   const int qrow = r0 + n;
   const int p0 = kept + r0;  // position of the wave's first row
-  bf16x8 qf[8];
+  f16x8 qf[8];
   {
     const bool ok = qrow < n_rows;
     const bf16_t* src = q + (static_cast<long long>(b) * a.T + (ok ? qrow : 0)) * a.Hq * kHeadDim +
@@ -171,8 +177,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
         u32x4 w = ok ? *reinterpret_cast<const u32x4*>(src + s * 16) : u32x4{0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          w[i] = pack_bf16x2(lo_bf16(w[i]) * c, hi_bf16(w[i]) * c);
-        qf[s] = __builtin_bit_cast(bf16x8, w);
+          w[i] = pack_f16x2(lo_f16(w[i]) * c, hi_f16(w[i]) * c);
+        qf[s] = __builtin_bit_cast(f16x8, w);
       }
     } else {
       // §3.2 / §4.3: x (c' + w) / sqrt(mean(x^2) + eps) over the row's 128 dims (the other 64
@@ -222,8 +228,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
       for (int s = 0; s < 8; ++s) {
         u32x4 w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(x[s][2 * i] * c, x[s][2 * i + 1] * c);
-        qf[s] = __builtin_bit_cast(bf16x8, w);
+        for (int i = 0; i < 4; ++i) w[i] = pack_f16x2(x[s][2 * i] * c, x[s][2 * i + 1] * c);
+        qf[s] = __builtin_bit_cast(f16x8, w);
       }
     }
   }
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     for (int i = 0; i < 16; ++i) {
       if (kQK) {
         const int kb = i & 1, s = i >> 1;
-        s_next[kb] = mfma32(__builtin_bit_cast(bf16x8, fr[i % kDepth]), qf[s], s == 0 ? neg_m : s_next[kb]);
+        s_next[kb] = mfma32_f16(__builtin_bit_cast(f16x8, fr[i % kDepth]), qf[s], s == 0 ? neg_m : s_next[kb]);
         if (i + kDepth < i_last) fr[i % kDepth] = frag(i + kDepth, kbuf, vbuf);
       }
       if (kPV) {
@@ -310,9 +316,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
       asm volatile("" : "+v"(l_run));
     }
 
-    // the last step has no next tile: its S^T is never used
-    const bool real_next = step + 1 < n_tiles;
-    if (kQK && real_next && needs_mask(step + 1)) {
+    // (kQK: a next tile exists; the last step is run without the QK half)
+    if (kQK && needs_mask(step + 1)) {
       // key k of the tile is visible to the row at position kept + qrow iff
       // k <= kept + qrow - j0 and, on local layers, k > kept + qrow - j0 - window
       const int dq = kept + qrow - (kt_hi - step - 1) * BN - hl * 8;
@@ -356,7 +361,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
       // Lazy rescaling: the reference max only moves (and O, l are only rescaled) when some
       // row of the wave gains more than 2^8 over it, or on a row's first tile.
       const bool first = m_run == -INFINITY;
-      if (real_next && __builtin_amdgcn_ballot_w64(mx > kRescaleLog2 || first) != 0) {  // wave-uniform
+      if (__builtin_amdgcn_ballot_w64(mx > kRescaleLog2 || first) != 0) {  // wave-uniform
         // first tile: the reference becomes the row max (a row with no visible key yet
         // keeps -inf); later: it moves up by the gain, if any
         const float bump = first ? (mx == -INFINITY ? 0.f : mx) : fmaxf(mx, 0.f);
@@ -381,13 +386,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   using T0 = std::integral_constant<bool, false>;
   // `k_fill`, `v_fill` receive K'(step+2) and V^T(step+1); `kbuf` holds K'(step+1) and
   // `vbuf` V^T(step). The buffers refilled here were last read before the previous barrier.
-  auto run_step = [&](int step, const bf16_t* kbuf, const bf16_t* vbuf, bf16_t* k_fill, bf16_t* v_fill,
+  // QK: whether a next tile exists (the last step only multiplies P V).
+  auto run_step = [&](auto QK, int step, const bf16_t* kbuf, const bf16_t* vbuf, bf16_t* k_fill, bf16_t* v_fill,
                       f32x16* s_cur, f32x16* s_next) __attribute__((always_inline)) {
     if (step + 2 < n_tiles) issue_k(step + 2, k_fill);
     if (step + 1 < n_tiles) issue_v(step + 1, v_fill);
-    step_body(T1{}, T1{}, step, kbuf, vbuf, s_cur, s_next);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
+    step_body(QK, T1{}, step, kbuf, vbuf, s_cur, s_next);
+    if (decltype(QK)::value) {  // (after the last step nothing is read from LDS again)
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+    }
   };
 
   // ---- K'(0) in LDS; S^T(0) while K'(1) and V^T(0) arrive; then steps 0 .. n_tiles-1 ----
@@ -399,9 +407,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   step_body(T1{}, T0{}, -1, ks0, vs1, s_b, s_a);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  for (int step = 0; step < n_tiles; step += 2) {
-    run_step(step, ks1, vs0, ks0, vs1, s_a, s_b);
-    if (step + 1 < n_tiles) run_step(step + 1, ks0, vs1, ks1, vs0, s_b, s_a);
+  int step = 0;
+  for (; step + 2 < n_tiles; step += 2) {
+    run_step(T1{}, step, ks1, vs0, ks0, vs1, s_a, s_b);
+    run_step(T1{}, step + 1, ks0, vs1, ks1, vs0, s_b, s_a);
+  }
+  if (step + 1 < n_tiles) {
+    run_step(T1{}, step, ks1, vs0, ks0, vs1, s_a, s_b);
+    run_step(T0{}, step + 1, ks0, vs1, ks1, vs0, s_b, s_a);
+  } else {
+    run_step(T0{}, step, ks1, vs0, ks0, vs1, s_a, s_b);
   }
 
   // ---- normalise and store: lane writes d = dt*32 + i*8 + hl*4 + 0..3 of its row ----

@@ -9,7 +9,8 @@
 //
 // Why not the d = 128 kernel widened: its wave holds 32 query rows, i.e. Q' and O^T of
 // 32 x d each in registers, which at d = 512 is 384 of the 512 registers a lane can have.
-// Here a wave holds NB blocks of 16 rows and uses v_mfma_f32_16x16x32_bf16.
+// Here a wave holds NB blocks of 16 rows and uses the 16x16x32 MFMAs: f16 for the scores
+// (Q' and K' are IEEE halves), bf16 for P V.
 //
 // Work decomposition
 //   block  = waves x 16 NB query rows of one sequence, for kHeads query heads of one KV
@@ -36,7 +37,7 @@
 //            contiguous); V^T is read in natural key order. Each K' fragment feeds NB MFMAs.
 //            Fragments come from LDS through a 3-deep register ring, so a read has three
 //            MFMA groups to land before its own.
-//   softmax = exp2 domain (Q' pre-scaled by scale * log2 e); lazy rescaling: the
+//   softmax = exp2 domain (Q' pre-scaled by scale * log2 e, rounded to half); lazy rescaling: the
 //            reference of a row moves only when a score exceeds it by 2^8; row sums from
 //            the same bf16-rounded P as P V.
 //   launch = 1-D grid remapped so that the query heads sharing a KV head and neighbouring
@@ -64,6 +65,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// the score product: Q' and K' are IEEE halves (same MFMA rate as bf16, three more bits)
+__device__ __forceinline__ f32x4 mfma16_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // Barrier without the memory fence of __syncthreads (which would also wait for the copies
@@ -158,19 +163,19 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void prefill_wide_kernel(Prefill
   const float c = a.scale * 1.4426950408889634f;
   const int r0 = i0 + (wave % kWavesH) * kRowsW;  // first row of the wave
   const int p0 = kept + r0;           // its position
-  bf16x8 qf[NB][kKS];
+  f16x8 qf[NB][kKS];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int row = r0 + nb * 16 + n;
     const bool ok = row < n_rows;
-    const bf16_t* src = static_cast<const bf16_t*>(a.q_rot) +
-                        ((static_cast<long long>(b) * a.T + (ok ? row : 0)) * a.Hq + hq) * D + g * 8;
+    const f16_t* src = static_cast<const f16_t*>(a.q_rot) +
+                       ((static_cast<long long>(b) * a.T + (ok ? row : 0)) * a.Hq + hq) * D + g * 8;
 #pragma unroll
     for (int s = 0; s < kKS; ++s) {
       u32x4 w = ok ? *reinterpret_cast<const u32x4*>(src + s * 32) : u32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(lo_bf16(w[i]) * c, hi_bf16(w[i]) * c);
-      qf[nb][s] = __builtin_bit_cast(bf16x8, w);
+      for (int i = 0; i < 4; ++i) w[i] = pack_f16x2(lo_f16(w[i]) * c, hi_f16(w[i]) * c);
+      qf[nb][s] = __builtin_bit_cast(f16x8, w);
     }
   }
 
@@ -202,18 +207,18 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void prefill_wide_kernel(Prefill
     // is read as soon as fragment i has been issued to the MFMAs, so each LDS read has kRing
     // MFMA groups to land (read one at a time, the wave stalled on every read).
     auto kread = [&](int i) __attribute__((always_inline)) {
-      return *reinterpret_cast<const bf16x8*>(kbuf + ((4 * (i >> 1) + g) * kBN + (i & 1) * 16 + n) * 8);
+      return *reinterpret_cast<const f16x8*>(kbuf + ((4 * (i >> 1) + g) * kBN + (i & 1) * 16 + n) * 8);
     };
     auto vread = [&](int dt) __attribute__((always_inline)) {
       return *reinterpret_cast<const bf16x8*>(vbuf + (g * D + dt * 16 + n) * 8);
     };
-    bf16x8 kr[kRing];
+    f16x8 kr[kRing];
 #pragma unroll
     for (int i = 0; i < kRing; ++i) kr[i] = kread(i);
 #pragma unroll
     for (int i = 0; i < 2 * kKS; ++i) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sacc[nb][i & 1] = mfma16(kr[i % kRing], qf[nb][i >> 1], sacc[nb][i & 1]);
+      for (int nb = 0; nb < NB; ++nb) sacc[nb][i & 1] = mfma16_f16(kr[i % kRing], qf[nb][i >> 1], sacc[nb][i & 1]);
       if (i + kRing < 2 * kKS) kr[i % kRing] = kread(i + kRing);
       __builtin_amdgcn_sched_barrier(0);
     }

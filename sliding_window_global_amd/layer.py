@@ -17,17 +17,17 @@ from . import (plamo_attn_decode, plamo_attn_decode_ragged, plamo_attn_decode_ra
                plamo_attn_decode_workspace_bytes, plamo_attn_prefill, plamo_attn_prefill_fused_q,
                plamo_attn_prefill_fused_q_ragged, plamo_attn_prefill_ragged, plamo_kv_append,
                plamo_kv_append_ragged, plamo_linear, plamo_qkv_projection, plamo_rms_norm,
-               prefill_operand_shapes)
+               prefill_operand_shapes, score_dtype)
 
 
 class PrefillBuffers:
     """Operands of one prefill chunk: normalised/rotated Q, rotated K and transposed V of the
-    kept + T keys it attends."""
+    kept + T keys it attends (Q' and K' in score_dtype: fp16 on a bf16 layer)."""
 
     def __init__(self, B, T, Hq, Hkv, d, dtype, device="cuda", window=0, pos_offset=0):
         k_shape, v_shape = prefill_operand_shapes(B, T, Hkv, d, dtype, window, pos_offset)
-        self.q_rot = torch.empty((B, T, Hq, d), dtype=dtype, device=device)
-        self.k_rot = torch.empty(k_shape, dtype=dtype, device=device)
+        self.q_rot = torch.empty((B, T, Hq, d), dtype=score_dtype(dtype), device=device)
+        self.k_rot = torch.empty(k_shape, dtype=score_dtype(dtype), device=device)
         self.v_t = torch.empty(v_shape, dtype=dtype, device=device)
         self.out = torch.empty((B, T, Hq, d), dtype=dtype, device=device)
 
@@ -69,7 +69,7 @@ class DecodeBuffers:
     whose positions are at most pos_offset)."""
 
     def __init__(self, B, Hq, Hkv, d, window, pos_offset, dtype=torch.bfloat16, device="cuda", ragged=False):
-        self.q_rot = torch.empty((B, 1, Hq, d), dtype=dtype, device=device)
+        self.q_rot = torch.empty((B, 1, Hq, d), dtype=score_dtype(dtype), device=device)
         self.out = torch.empty((B, 1, Hq, d), dtype=dtype, device=device)
         size = plamo_attn_decode_ragged_workspace_bytes if ragged else plamo_attn_decode_workspace_bytes
         nbytes = size(B, Hq, Hkv, window, pos_offset, d)

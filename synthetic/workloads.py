@@ -18,7 +18,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import BASE_SEED, Draw
+from . import BASE_SEED, Draw, bf16_round
 
 
 @dataclass(frozen=True)
@@ -236,10 +236,11 @@ def device_normal_bf16(shape, seed: int, device):
 # The Gemma-4-shaped second workload (「PLaMo 3アーキテクチャ徹底解析」 §8 comparison table,
 # §6.4 p-RoPE, §9.4 gains): local layers d = 256, Hq = 32, Hkv = 16, window 1024, RoPE base
 # 1e4 on every pair; global layers d = 512, Hq = 32, Hkv = 4, p-RoPE (p = 0.25, base 1e6),
-# V taken from the K projection. Q/K norm gain = the stored weight (offset 0), constant
-# within each vector as the page reports for the released weights: Q in [0.95, 1.05], K in
-# [0.120, 0.132] (local) or [0.060, 0.065] (global); V divided by its RMS; dot-product
-# factor 1; K cached after RoPE.
+# V taken from the K projection. Q/K norm gain = the stored weight (offset 0): a level
+# drawn in the ranges the page reports for the released weights (Q in [0.95, 1.05], K in
+# [0.120, 0.132] local or [0.060, 0.065] global; constant within each vector there) plus
+# independent per-component N(0, 0.02) noise, so that each component of the gain differs;
+# V divided by its RMS; dot-product factor 1; K cached after RoPE.
 # ----------------------------------------------------------------------------
 
 @dataclass(frozen=True)
@@ -258,11 +259,16 @@ class GemmaLayer:
     norm_offset: float = 0.0
     eps: float = 1e-6
 
+    gain_noise_std: float = 0.02
+
     def draw_gains(self, dr: Draw):
-        """(wq, wk): constant vectors [d] (the gain itself, offset 0)."""
+        """(wq, wk) [d] (the gain itself, offset 0): the level of each vector uniform in its
+        range, plus per-component N(0, gain_noise_std) noise; stored as bf16."""
         gq = dr.uniform(*self.q_gain)
         gk = dr.uniform(*self.k_gain)
-        return np.full(self.d, gq, dtype=np.float32), np.full(self.d, gk, dtype=np.float32)
+        nq = dr.normal((self.d,), self.gain_noise_std)
+        nk = dr.normal((self.d,), self.gain_noise_std)
+        return (bf16_round(np.float32(gq) + nq), bf16_round(np.float32(gk) + nk))
 
     def draw_tokens(self, dr: Draw, B: int, T: int):
         """q [B,T,Hq,d], k [B,T,Hkv,d], v (the same array as k when shared), bf16-exact."""

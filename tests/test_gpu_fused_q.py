@@ -42,11 +42,9 @@ def table(rope: Rope, max_pos: int):
                                                        rope.beta_fast, rope.beta_slow))
 
 
-# Norm offsets: the pages' q/k value 1 on local layers; the global workload's 5^-1.5 on YaRN
-# layers (with offset 1 the YaRN amplitude squared, 2.0 - 2.4, sharpens the synthetic scores
-# until bf16 rounding of Q', K' and P alone reaches ~2.3e-2 on rows with few keys, on the
-# unfused path as well).
-C_GLOBAL = GLOBAL_PREFILL.norm_offset
+# Norm offsets: the pages' q/k value 1 on every layer, the YaRN layers included (there the
+# amplitude squared, 2.0 - 2.4, sharpens the scores the most).
+C_GLOBAL = 1.0
 
 
 @pytest.mark.parametrize("window,chunks,rope,post_rope,c", [

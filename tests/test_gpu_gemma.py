@@ -150,17 +150,11 @@ def test_gemma_local_small_window_edges():
 
 def test_gemma_local_group_sizes():
     """d = 256 with query-head groups of 3 (not a multiple of the heads a prefill block takes)
-    and 4 (two blocks per KV head).
-
-    The seeds tried first (7103 and 7104) each put one element past the bar: 0.0229 where it
-    is 0.0208 (row 3, 4 keys) and 0.0347 (row 67, 64 keys). A float64 replay of the kernels'
-    bf16 rounding points (Q', Q' x scale, K', V, P, O) gives those same two values; switching
-    off the rounding of the cached K' alone takes the second one to 0.009. With dot-product
-    factor 1 these rows' scores span up to 19 log2 units, so two keys carry most of the weight
-    and the K' rounding moves weight between them: a property of a bf16 cache on this layer,
-    not of the indexing under test. The seeds below clear the bar in the same replay."""
-    _small_stream(GEMMA_LOCAL_LAYER, 3, 1, 100, [130, 40], 2, 7105)
-    _small_stream(GEMMA_LOCAL_LAYER, 8, 2, 64, [150, 60], 2, 7108)
+    and 4 (two blocks per KV head). These are the first seeds the test was written with; with
+    dot-product factor 1 some rows' scores span ~19 log2 units, so two keys carry most of the
+    weight and the rounding of the score operands shows most on this layer."""
+    _small_stream(GEMMA_LOCAL_LAYER, 3, 1, 100, [130, 40], 2, 7103)
+    _small_stream(GEMMA_LOCAL_LAYER, 8, 2, 64, [150, 60], 2, 7104)
 
 
 def test_gemma_partly_filled_caches():
