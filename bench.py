@@ -55,10 +55,12 @@ class Timer:
         self.pairs.append((a, b))
         return a, b
 
-    def mean_ms(self):
+    def median_ms(self):
+        """Median of the recorded spans (robust to a stray slow launch)."""
         self.torch.cuda.synchronize()
-        v = [a.elapsed_time(b) for a, b in self.pairs]
-        return sum(v) / len(v)
+        v = sorted(a.elapsed_time(b) for a, b in self.pairs)
+        n = len(v)
+        return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
 
 def dev_bf16(torch, x):
@@ -117,10 +119,12 @@ def bench_prefill(torch, swg, wl, steps, warmup, norm_offset, fuse_q=False):
         step(ts.span(), ta.span())
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step, ms_attn = ts.mean_ms(), ta.mean_ms()
+    ms_attn = ta.median_ms()
+    # whole-step figure: the K steps back to back (first step's start to last step's end) / K
+    ms_step = ts.pairs[0][0].elapsed_time(ts.pairs[-1][1]) / steps
     flops = wl.flops()
     return dict(workload=wl.name, flops=flops, ms_per_step=ms_step, ms_attn=ms_attn,
-                step_tflops=flops / ms_step / 1e9, attn_tflops=flops / ms_attn / 1e9,
+                ms_step_median=ts.median_ms(), step_tflops=flops / ms_step / 1e9, attn_tflops=flops / ms_attn / 1e9,
                 wall_ms_per_step=wall / steps * 1e3)
 
 
@@ -160,7 +164,7 @@ def bench_chunked_prefill(torch, swg, wl, chunk, steps, warmup):
     ts = Timer(torch)
     for _ in range(steps):
         step(ts.span())
-    ms = ts.mean_ms()
+    ms = ts.median_ms()
     flops = wl.flops()
     return dict(workload=f"{wl.name}_chunks{chunk}", n_chunks=len(starts), ms_per_step=ms,
                 step_tflops=flops / ms / 1e9)
@@ -200,7 +204,7 @@ def bench_decode_batched(torch, swg, wl, layer_idx, steps, warmup, post_rope=Fal
         a.record()
         run()
         b.record()
-    ms = t.mean_ms()
+    ms = t.median_ms()
     nbytes = wl.kv_bytes(ly)
     del kc, vc
     torch.cuda.empty_cache()
@@ -242,7 +246,7 @@ def bench_decode_ragged(torch, swg, wl, layer_idx, steps, warmup):
         a.record()
         run()
         b.record()
-    ms = t.mean_ms()
+    ms = t.median_ms()
     keys = [int(p) + 1 if ly.window == 0 else min(int(p), ly.window - 1) + 1 for p in pos]
     nbytes = 2 * 2 * wl.Hkv * wl.d * sum(keys)
     del kc, vc
@@ -295,7 +299,7 @@ def bench_gemma_prefill(torch, swg, wl, steps, warmup):
     ts, ta = Timer(torch), Timer(torch)
     for _ in range(steps):
         step(ts.span(), ta.span())
-    ms_step, ms_attn = ts.mean_ms(), ta.mean_ms()
+    ms_step, ms_attn = ts.median_ms(), ta.median_ms()
     flops = wl.flops()
     return dict(workload=wl.name, flops=flops, ms_per_step=ms_step, ms_attn=ms_attn,
                 step_tflops=flops / ms_step / 1e9, attn_tflops=flops / ms_attn / 1e9,
@@ -332,7 +336,7 @@ def bench_gemma_decode(torch, swg, wl, steps, warmup):
         a.record()
         run()
         b.record()
-    ms = t.mean_ms()
+    ms = t.median_ms()
     nbytes = wl.kv_bytes()
     del kc, vc
     torch.cuda.empty_cache()
@@ -433,11 +437,7 @@ def cpu_baseline(wl, norm_offset, n_rows):
     import numpy as np
 
     from oracle import LayerKVCache, attention_layer_step
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        cores = len(os.sched_getaffinity(0))
+    cores = _cpu_cores()
     inp = wl.draw()
     rows = np.linspace(0, wl.T - 1, n_rows).astype(np.int64)
     t0 = time.perf_counter()
@@ -451,6 +451,107 @@ def cpu_baseline(wl, norm_offset, n_rows):
     return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{wl.name}: {n_rows} of {wl.T} query rows x {wl.Hq} heads (full norm, cache, "
                       f"RoPE of all {wl.T} keys; fp64 NumPy), {sec:.1f} s"}
+
+
+def _cpu_cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:  # noqa: BLE001
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_global_rows(wl, block=256):
+    """The oracle on the global prefill workload at a fixed row subset: the first, the last and
+    two middle blocks of `block` query rows, all heads (norm of every row, RoPE of every key,
+    attention of the subset). Reported as TFLOP/s of the subset's attended pairs; the full
+    run's time is extrapolated at that rate."""
+    import numpy as np
+
+    from oracle import LayerKVCache, attention_layer_step
+    inp = wl.draw()
+    T = wl.T
+    starts = [0, T // 2 - block, T // 2, T - block]
+    rows = np.concatenate([np.arange(s0, s0 + block) for s0 in starts])
+    t0 = time.perf_counter()
+    attention_layer_step(inp["q"][0], inp["k"][0], inp["v"][0], LayerKVCache(wl.Hkv, wl.d, 0),
+                         theta=wl.rope.theta, yarn_factor=wl.rope.yarn_factor, q_norm_w=inp["wq"],
+                         k_norm_w=inp["wk"], norm_offset=wl.norm_offset, scale=wl.scale, rows=rows)
+    sec = time.perf_counter() - t0
+    flops = 4.0 * wl.d * wl.Hq * float(np.sum(rows + 1))
+    rate = flops / sec
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": _cpu_cores(), "kind": "oracle",
+            "sample": f"{wl.name}: rows {starts} + 0..{block - 1} ({len(rows)} of {T}) x {wl.Hq} heads, "
+                      f"fp64 NumPy, {sec:.1f} s",
+            "full_run_s_extrapolated": wl.flops() / rate}
+
+
+def _prior_kv(n_keys, Hkv, d, gen_seed):
+    """Kept K/V of one sequence of a decode workload, drawn on the host with the device caches'
+    recipe (N(0, 1) rounded to bf16), as float32 [n_keys, Hkv, d]."""
+    import torch
+
+    from synthetic.workloads import device_normal_bf16
+    pk = device_normal_bf16((n_keys, Hkv, d), gen_seed, "cpu").to(torch.float32).numpy()
+    pv = device_normal_bf16((n_keys, Hkv, d), gen_seed + 1, "cpu").to(torch.float32).numpy()
+    return pk, pv
+
+
+def _oracle_decode_one(wl, layer_idx, step, b, pk, pv):
+    """Seconds of the oracle's decode step of sequence b (cache holding its kept tokens, norm
+    and RoPE of the new token, RoPE of every cached key, attention) at `step`; pk / pv hold at
+    least the kept tokens (the newest last)."""
+    from oracle import LayerKVCache, attention_layer_step
+    ly = wl.layers[layer_idx]
+    p = wl.pos_offset + step
+    kept = wl.keys_attended(ly, step) - 1
+    new = wl.draw_new_tokens(step, layer_idx)
+    t0 = time.perf_counter()
+    cache = LayerKVCache.with_prior(pk[pk.shape[0] - kept:], pv[pv.shape[0] - kept:], p, ly.window)
+    attention_layer_step(new["q"][b], new["k"][b], new["v"][b], cache, theta=ly.rope.theta,
+                         yarn_factor=ly.rope.yarn_factor, q_norm_w=new["wq"], k_norm_w=new["wk"],
+                         norm_offset=wl.norm_offset, scale=wl.scale)
+    return time.perf_counter() - t0
+
+
+def cpu_baselines_extra():
+    """The oracle on the other workloads: a fixed row subset of the global prefill, the whole
+    batched decode (both layers) and the 8-layer period decode at steps 0, 63 and 127."""
+    from synthetic.workloads import BATCHED_DECODE, GLOBAL_PREFILL, PERIOD_DECODE
+    out = {}
+    log("[bench] cpu oracle: global prefill row subset")
+    out["cpu_baseline_prefill_global"] = cpu_baseline_global_rows(GLOBAL_PREFILL)
+    log(f"[bench]   {out['cpu_baseline_prefill_global']}")
+    cores = _cpu_cores()
+    wl = BATCHED_DECODE
+    for li, ly in enumerate(wl.layers):
+        log(f"[bench] cpu oracle: batched decode layer {li}, all {wl.B} sequences")
+        kept = wl.keys_attended(ly) - 1
+        sec = 0.0
+        for b in range(wl.B):
+            pk, pv = _prior_kv(kept, wl.Hkv, wl.d, 7001 + 31 * b + li)
+            sec += _oracle_decode_one(wl, li, 0, b, pk, pv)
+        name = f"cpu_baseline_{wl.name}_{'global' if ly.window == 0 else 'local'}"
+        out[name] = {"value": wl.kv_bytes(ly) / sec / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+                     "sample": f"all {wl.B} sequences, {wl.keys_attended(ly)} keys each, fp64 NumPy, {sec:.1f} s"}
+        log(f"[bench]   {out[name]}")
+    wl = PERIOD_DECODE
+    steps = (0, 63, 127)
+    sec_step = {s_: 0.0 for s_ in steps}
+    log(f"[bench] cpu oracle: period decode steps {steps}, {wl.B} sequences x 8 layers")
+    for b in range(wl.B):
+        for li, ly in enumerate(wl.layers):
+            pk, pv = _prior_kv(wl.keys_attended(ly, steps[-1]) - 1, wl.Hkv, wl.d, 9001 + 31 * b + li)
+            for s_ in steps:
+                sec_step[s_] += _oracle_decode_one(wl, li, s_, b, pk, pv)
+    total_sec = sum(sec_step.values())
+    total_bytes = sum(wl.kv_bytes(ly, s_) for s_ in steps for ly in wl.layers)
+    out["cpu_baseline_period_decode"] = {
+        "value": total_bytes / total_sec / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "sample": f"{wl.name}: steps 0, 63, 127 x 8 layers x {wl.B} sequences, fp64 NumPy, {total_sec:.1f} s",
+        "s_per_step": {str(k): round(v, 3) for k, v in sec_step.items()}}
+    log(f"[bench]   {out['cpu_baseline_period_decode']}")
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -559,6 +660,7 @@ def main():
         log("[bench] cpu oracle baseline")
         cpu = cpu_baseline(LOCAL_PREFILL, LOCAL_PREFILL.norm_offset, args.cpu_rows)
         log(f"[bench]   {cpu}")
+        extra.update(cpu_baselines_extra())
     line = {
         "metric": METRIC,
         "value": round(local["step_tflops"], 3),
@@ -574,7 +676,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": LOCAL_PREFILL.name, "B": 1, "T": 8192, "Hq": 64, "Hkv": 8, "d": 128,
                    "window": 2048,
-                   "step": "kv_append + attn_prefill"},
+                   "step": "kv_append + attn_prefill",
+                   "cache_state": "inputs resident in HBM; the 256 MB last-level cache is not flushed "
+                                  "between steps, so the prefill finds much of the Q' the append has just "
+                                  "written there (as in an append -> prefill pipeline)",
+                   "timing": "ms_per_step = K whole steps / K; roofline from the median HIP-event duration "
+                             "of the attention launch"},
         "roofline": {"bound": "mfma", "achieved": round(local["attn_tflops"], 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(local["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
