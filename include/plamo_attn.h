@@ -41,7 +41,8 @@
  *   - Positions are 64-bit; one pos_offset serves every sequence of the batch
  *     (the *_ragged calls take one position per sequence).
  *   - Entry points hold no mutable global state and may be called from several
- *     host threads on different streams.
+ *     host threads on different streams (except plamo_attn_decode_noalloc, whose
+ *     per-GPU scratch is shared by all its calls on that GPU).
  */
 #ifndef PLAMO_ATTN_H
 #define PLAMO_ATTN_H
@@ -233,6 +234,29 @@ PLAMO_API int plamo_attn_decode(int dtype, const void* q_rot, const void* k_cach
                       const void* v_cache, long long cap, void* out, void* workspace,
                       size_t workspace_bytes, int B, int T, int Hq, int Hkv, int d,
                       int window, long long pos_offset, const void* rope_table,
+                      size_t rope_table_bytes, float softmax_scale, int cache_order,
+                      void* stream);
+
+/* ---------------------------------------------------------------------------
+ * plamo_attn_decode_noalloc -- plamo_attn_decode without a workspace argument
+ *
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). Same arguments, checks, kernels and
+ * results as plamo_attn_decode; the split-K partials go to the library's own scratch, a
+ * static device array of PLAMO_DECODE_SCRATCH_BYTES on each GPU, held until the process
+ * ends. Nothing is allocated or freed by the call. A call whose partials would need more
+ * (plamo_attn_decode_workspace_bytes(...) > PLAMO_DECODE_SCRATCH_BYTES) returns
+ * PLAMO_ERR_WORKSPACE and launches nothing. The scratch belongs to the GPU that is current
+ * on the calling thread (its address is looked up once per device); `stream` must be a
+ * stream of that GPU. Every call on a GPU shares its scratch: calls that overlap on one GPU
+ * (different streams, or host threads without ordering) race; order them on one stream.
+ * The scratch needs no clearing (each call writes every partial it reads).
+ * ------------------------------------------------------------------------- */
+#define PLAMO_DECODE_SCRATCH_BYTES (8u << 20)
+
+PLAMO_API int plamo_attn_decode_noalloc(int dtype, const void* q_rot, const void* k_cache,
+                      const void* v_cache, long long cap, void* out, int B, int T, int Hq,
+                      int Hkv, int d, int window, long long pos_offset, const void* rope_table,
                       size_t rope_table_bytes, float softmax_scale, int cache_order,
                       void* stream);
 

@@ -280,6 +280,30 @@ def plamo_attn_decode(q_rot, k_cache, v_cache, out, workspace, *, window: int, p
     _check(st, "plamo_attn_decode")
 
 
+PLAMO_DECODE_SCRATCH_BYTES = 8 << 20
+
+
+def plamo_attn_decode_noalloc(q_rot, k_cache, v_cache, out, *, window: int, pos_offset: int, rope_table,
+                              softmax_scale: float | None = None, cache_post_rope: bool = False,
+                              stream=None) -> None:
+    """plamo_attn_decode without a workspace: the split-K partials go to the library's own
+    per-GPU scratch (PLAMO_DECODE_SCRATCH_BYTES); calls that overlap on one GPU race."""
+    dt = out.dtype
+    B, T, Hq, d = q_rot.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, cap, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches must both be [B, Hkv, cap, d]")
+    if tuple(out.shape) != (B, T, Hq, d):
+        raise ValueError("out must match q_rot")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    st = _lib.load().plamo_attn_decode_noalloc(
+        _dtype_code(dt), _dev(q_rot, "q_rot", score_dtype(dt)), _dev(k_cache, "k_cache", dt),
+        _dev(v_cache, "v_cache", dt), int(cap), _dev(out, "out", dt), B, T, Hq, Hkv, d, int(window),
+        int(pos_offset), _dev(rope_table, "rope_table", torch.float32), _nbytes(rope_table), scale,
+        _order(cache_post_rope), _stream(stream))
+    _check(st, "plamo_attn_decode_noalloc")
+
+
 # ----------------------------------------------------------------------------
 # ragged batches: one position (and, for append / prefill, one token count) per sequence
 # ----------------------------------------------------------------------------

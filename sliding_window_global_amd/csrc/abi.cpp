@@ -276,7 +276,7 @@ int attn_decode_impl(int dtype, const void* q_rot, const void* k_cache, const vo
                      long long cap, void* out, void* workspace, size_t workspace_bytes, int B, int T,
                      int Hq, int Hkv, int d, int window, long long pos_offset, const long long* seq_pos,
                      const void* rope_table, size_t rope_table_bytes, float softmax_scale,
-                     int cache_order, void* stream) {
+                     int cache_order, void* stream, bool own_scratch = false) {
   if (dtype != PLAMO_BF16) return fail(dtype == PLAMO_F32 ? PLAMO_ERR_UNSUPPORTED : PLAMO_ERR_INVALID_ARG,
                                        "decode reads a bf16 cache");
   if (T != 1) return fail(T < 0 ? PLAMO_ERR_INVALID_ARG : PLAMO_ERR_UNSUPPORTED, "decode takes T = 1");
@@ -304,8 +304,20 @@ int attn_decode_impl(int dtype, const void* q_rot, const void* k_cache, const vo
   }
   const plamo::DecodePlan plan = plamo::plan_decode(B, Hkv, S, seq_pos != nullptr);
   const size_t need = plamo::decode_workspace_bytes(B, Hq, d, plan);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return fail(PLAMO_ERR_WORKSPACE, "workspace too small");
+  if (own_scratch) {
+    if (need > plamo::kDecodeScratchBytes)
+      return fail(PLAMO_ERR_WORKSPACE, "split-K partials of this call exceed the 8 MiB scratch of "
+                                       "plamo_attn_decode_noalloc; use plamo_attn_decode with a workspace");
+  } else if (need > 0 && (!workspace || workspace_bytes < need)) {
+    return fail(PLAMO_ERR_WORKSPACE, "workspace too small");
+  }
   if (static_cast<long long>(B) * Hq > 0x7fffffffLL) return fail(PLAMO_ERR_UNSUPPORTED, "grid too large");
+  if (own_scratch && need > 0) {
+    float* ptr = nullptr;
+    const hipError_t e = plamo::decode_scratch(&ptr);
+    if (e != hipSuccess) return fail(PLAMO_ERR_HIP, "no device address for the decode scratch");
+    workspace = ptr;
+  }
 
   plamo::DecodeArgs a{};
   a.q_rot = q_rot; a.k_cache = k_cache; a.v_cache = v_cache; a.cap = cap; a.out = out;
@@ -413,6 +425,17 @@ int plamo_attn_decode(int dtype, const void* q_rot, const void* k_cache, const v
   return attn_decode_impl(dtype, q_rot, k_cache, v_cache, cap, out, workspace, workspace_bytes, B, T, Hq,
                           Hkv, d, window, pos_offset, nullptr, rope_table, rope_table_bytes,
                           softmax_scale, cache_order, stream);
+}
+
+static_assert(plamo::kDecodeScratchBytes == PLAMO_DECODE_SCRATCH_BYTES, "scratch size as declared");
+
+int plamo_attn_decode_noalloc(int dtype, const void* q_rot, const void* k_cache, const void* v_cache,
+                              long long cap, void* out, int B, int T, int Hq, int Hkv, int d, int window,
+                              long long pos_offset, const void* rope_table, size_t rope_table_bytes,
+                              float softmax_scale, int cache_order, void* stream) {
+  return attn_decode_impl(dtype, q_rot, k_cache, v_cache, cap, out, nullptr, 0, B, T, Hq, Hkv, d, window,
+                          pos_offset, nullptr, rope_table, rope_table_bytes, softmax_scale, cache_order,
+                          stream, true);
 }
 
 int plamo_attn_decode_ragged(int dtype, const void* q_rot, const void* k_cache, const void* v_cache,

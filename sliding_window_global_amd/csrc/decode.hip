@@ -29,7 +29,34 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <mutex>
+
 namespace plamo {
+
+// Split-K partial results of plamo_attn_decode_noalloc, for callers that cannot allocate:
+// one array per GPU, held until the process ends. Every call on a GPU reuses that GPU's
+// array (calls that overlap on one GPU race). Host code never passes the array's name to a
+// kernel: it passes the device address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+hipError_t decode_scratch(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* per_device[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    per_device[dev] = static_cast<float*>(p);
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
+}
 
 namespace {
 

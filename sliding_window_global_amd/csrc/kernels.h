@@ -76,6 +76,10 @@ struct DecodePlan {
 };
 DecodePlan plan_decode(int B, int Hkv, long long S, bool ragged);
 size_t decode_workspace_bytes(int B, int Hq, int d, const DecodePlan& plan);
+// Size of the library's own split-K scratch (plamo_attn_decode_noalloc), and its device
+// address on the current GPU (looked up once per device).
+constexpr size_t kDecodeScratchBytes = size_t(8) << 20;
+hipError_t decode_scratch(float** ptr);
 
 struct DecodeArgs {
   const void* q_rot;    // [B, 1, Hq, d]

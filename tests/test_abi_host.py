@@ -303,3 +303,15 @@ def test_sublayer_entry_points_validate(lib):
     assert norm(x=MISALIGNED) == INVALID
     assert norm(y=None) == INVALID
     assert norm(rows=0) == OK
+
+
+def test_decode_noalloc_rejects_partials_beyond_its_scratch(lib):
+    """plamo_attn_decode_noalloc checks the split-K partials against its fixed scratch before
+    touching the GPU: d = 512, one KV head of 16 query heads and 65536 keys need 256 ranges of
+    16 x 514 floats, above the 8 MiB."""
+    assert lib.plamo_attn_decode_workspace_bytes(1, 16, 1, 512, 0, 65535) > 8 << 20
+    big = lib.plamo_attn_decode_noalloc(BF16, FAKE, FAKE, FAKE, 65536, FAKE, 1, 1, 16, 1, 512, 0, 65535,
+                                        None, 0, 1.0, 1, None)
+    assert big == -3
+    assert lib.plamo_attn_decode_noalloc(BF16, FAKE, FAKE, FAKE, 65536, FAKE, 0, 1, 16, 1, 512, 0, 65535,
+                                         None, 0, 1.0, 1, None) == 0  # B = 0: nothing to do
