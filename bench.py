@@ -390,9 +390,10 @@ def bench_mixer(torch, swg, wl, steps, warmup):
                 qkv_proj_tflops=qkv_flops / part[0] / 1e9, o_proj_tflops=o_flops / part[2] / 1e9)
 
 
-def bench_period(torch, swg, wl, n_steps):
+def bench_period(torch, swg, wl, n_steps, fused=False):
     """The 8-layer period (7 local W=2048 + 1 global), append + decode per layer per step,
-    at 131072+k global context, batch 8."""
+    at 131072+k global context, batch 8. fused: each layer's step is one launch
+    (plamo_decode_step) instead of the append, the decode and the merge of its key ranges."""
     from sliding_window_global_amd import layer
     from synthetic.workloads import device_normal_bf16
     caches, tabs, bufs, news = [], [], [], []
@@ -401,7 +402,7 @@ def bench_period(torch, swg, wl, n_steps):
         caches.append((device_normal_bf16((wl.B, wl.Hkv, cap, wl.d), wl.cache_seed(li), "cuda"),
                        device_normal_bf16((wl.B, wl.Hkv, cap, wl.d), wl.cache_seed(li) + 1, "cuda")))
         tabs.append(swg.make_rope_table(wl.pos_offset + wl.steps + 64, rope_params(swg, ly.rope)))
-        bufs.append(layer.DecodeBuffers(wl.B, wl.Hq, wl.Hkv, wl.d, ly.window, wl.pos_offset + wl.steps))
+        bufs.append(layer.DecodeBuffers(wl.B, wl.Hq, wl.Hkv, wl.d, ly.window, wl.pos_offset + wl.steps, fused=fused))
     for s in range(min(n_steps, 4)):  # a few distinct token sets, reused cyclically
         news.append([{k: (dev_bf16(torch, x) if x is not None else None) for k, x in wl.draw_new_tokens(s, li).items()}
                      for li in range(len(wl.layers))])
@@ -417,14 +418,14 @@ def bench_period(torch, swg, wl, n_steps):
             kc, vc = caches[li]
             layer.decode(nt["q"], nt["k"], nt["v"], kc, vc, window=ly.window, pos_offset=p,
                          rope_table=tabs[li], q_norm_w=nt["wq"], k_norm_w=nt["wk"],
-                         norm_offset=wl.norm_offset, bufs=bufs[li])
+                         norm_offset=wl.norm_offset, bufs=bufs[li], fused=fused)
             total_bytes += wl.kv_bytes(ly, s)
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1)
     del caches
     torch.cuda.empty_cache()
-    return dict(workload=wl.name, steps=n_steps, ms_total=ms, ms_per_step=ms / n_steps,
+    return dict(workload=wl.name + ("_one_launch" if fused else ""), steps=n_steps, ms_total=ms, ms_per_step=ms / n_steps,
                 kv_bytes_total=total_bytes, gbs=total_bytes / ms / 1e6,
                 frac_hbm=total_bytes / ms / 1e6 / PEAK_HBM_GBS)
 
@@ -642,6 +643,10 @@ def main():
         r = bench_period(torch, swg, PERIOD_DECODE, args.period_steps)
         log(f"[bench]   {r}")
         extra["period_decode"] = r
+        log("[bench] 8-layer period decode, one launch per layer step")
+        r = bench_period(torch, swg, PERIOD_DECODE, args.period_steps, fused=True)
+        log(f"[bench]   {r}")
+        extra["period_decode_one_launch"] = r
 
     if only == "copy_calibration":
         # a plain device-to-device copy of known size: the reference for HBM byte counters

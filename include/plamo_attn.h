@@ -238,6 +238,35 @@ PLAMO_API int plamo_attn_decode(int dtype, const void* q_rot, const void* k_cach
                       void* stream);
 
 /* ---------------------------------------------------------------------------
+ * plamo_decode_step -- one decode step of a layer in one launch: steps 1-4 for one new
+ * token per sequence [P3 §3.2, §4.3, §4.4, §4.5, §5.1, §6]
+ *
+ * The same result as plamo_kv_append(T = 1) followed by plamo_attn_decode at the same
+ * pos_offset p, without the Q' buffer and the separate merge: q [B, 1, Hq, d], k, v
+ * [B, 1, Hkv, d] are the projected new token (bf16); gains, offset, eps, caches, rope table,
+ * window and cache_order as for plamo_kv_append (V as given: no v_norm); out [B, 1, Hq, d]
+ * (bf16). The token's normalised K (rotated first with POST_ROPE) and V go into cache slot
+ * p (global) or p mod window (local); attention reads the kept tokens and the new one.
+ * d = 128 only (PLAMO_ERR_UNSUPPORTED otherwise); bf16; uniform batch.
+ *
+ * workspace: at least plamo_decode_step_workspace_bytes(...) bytes (NULL allowed when 0),
+ * dedicated to this call. Its first bytes hold one 32-bit counter per (sequence, KV head)
+ * that must be zero before the first call (allocate it zeroed once); every call leaves them
+ * at zero again. The key ranges' partial states follow. Calls sharing a workspace must be
+ * ordered (one stream).
+ * ------------------------------------------------------------------------- */
+PLAMO_API size_t plamo_decode_step_workspace_bytes(int B, int Hq, int Hkv, int d, int window,
+                                                   long long pos_offset);
+
+PLAMO_API int plamo_decode_step(int dtype, const void* q, const void* k, const void* v,
+                      const void* q_norm_w, const void* k_norm_w, float norm_offset,
+                      float norm_eps, void* k_cache, void* v_cache, long long cap, void* out,
+                      void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int d,
+                      int window, long long pos_offset, const void* rope_table,
+                      size_t rope_table_bytes, float softmax_scale, int cache_order,
+                      void* stream);
+
+/* ---------------------------------------------------------------------------
  * plamo_attn_decode_noalloc -- plamo_attn_decode without a workspace argument
  *
  * For callers that cannot allocate device memory (code under HIP graph capture, tight

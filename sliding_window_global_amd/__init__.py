@@ -280,6 +280,36 @@ def plamo_attn_decode(q_rot, k_cache, v_cache, out, workspace, *, window: int, p
     _check(st, "plamo_attn_decode")
 
 
+def plamo_decode_step_workspace_bytes(B: int, Hq: int, Hkv: int, window: int, pos_offset: int,
+                                      d: int = HEAD_DIM) -> int:
+    return int(_lib.load().plamo_decode_step_workspace_bytes(B, Hq, Hkv, d, int(window), int(pos_offset)))
+
+
+def plamo_decode_step(q, k, v, k_cache, v_cache, out, workspace, *, window: int, pos_offset: int, rope_table,
+                      q_norm_w=None, k_norm_w=None, norm_offset: float = 1.0, norm_eps: float = 1e-6,
+                      softmax_scale: float | None = None, cache_post_rope: bool = False, stream=None) -> None:
+    """One decode step of a layer in one launch (plamo_kv_append + plamo_attn_decode): q
+    [B,1,Hq,d], k/v [B,1,Hkv,d] (bf16) -> out [B,1,Hq,d]; the new token goes into the caches.
+    workspace: a zero-initialised tensor of plamo_decode_step_workspace_bytes (kept across calls)."""
+    dt = q.dtype
+    B, T, Hq, d = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    if T != 1 or tuple(k.shape) != (B, 1, Hkv, d) or tuple(v.shape) != (B, 1, Hkv, d):
+        raise ValueError("need q [B,1,Hq,d] and k, v [B,1,Hkv,d]")
+    if tuple(k_cache.shape) != (B, Hkv, cap, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches must both be [B, Hkv, cap, d]")
+    if tuple(out.shape) != (B, 1, Hq, d):
+        raise ValueError("out must match q")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    st = _lib.load().plamo_decode_step(
+        _dtype_code(dt), _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt), _dev(q_norm_w, "q_norm_w", dt),
+        _dev(k_norm_w, "k_norm_w", dt), float(norm_offset), float(norm_eps), _dev(k_cache, "k_cache", dt),
+        _dev(v_cache, "v_cache", dt), int(cap), _dev(out, "out", dt), _dev(workspace, "workspace"),
+        _nbytes(workspace), B, Hq, Hkv, d, int(window), int(pos_offset), _dev(rope_table, "rope_table", torch.float32),
+        _nbytes(rope_table), scale, _order(cache_post_rope), _stream(stream))
+    _check(st, "plamo_decode_step")
+
+
 PLAMO_DECODE_SCRATCH_BYTES = 8 << 20
 
 

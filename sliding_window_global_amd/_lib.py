@@ -38,6 +38,10 @@ SIGNATURES = {
     "plamo_attn_decode": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_ll, c_void_p, c_void_p, c_size, c_int,
                                   c_int, c_int, c_int, c_int, c_int, c_ll, c_void_p, c_size, c_float, c_int,
                                   c_void_p]),
+    "plamo_decode_step_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int, c_ll]),
+    "plamo_decode_step": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_float,
+                                  c_void_p, c_void_p, c_ll, c_void_p, c_void_p, c_size, c_int, c_int, c_int,
+                                  c_int, c_int, c_ll, c_void_p, c_size, c_float, c_int, c_void_p]),
     "plamo_attn_decode_noalloc": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_ll, c_void_p, c_int, c_int,
                                           c_int, c_int, c_int, c_int, c_ll, c_void_p, c_size, c_float, c_int,
                                           c_void_p]),

@@ -427,6 +427,65 @@ int plamo_attn_decode(int dtype, const void* q_rot, const void* k_cache, const v
                           softmax_scale, cache_order, stream);
 }
 
+size_t plamo_decode_step_workspace_bytes(int B, int Hq, int Hkv, int d, int window, long long pos_offset) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || window < 0 || pos_offset < 0 || d != kHeadDim) return 0;
+  const long long S = kept_tokens(window, pos_offset) + 1;
+  return plamo::decode_step_workspace_bytes(B, Hq, Hkv, d, plamo::plan_decode(B, Hkv, S, false, plamo::kStepMinChunk));
+}
+
+int plamo_decode_step(int dtype, const void* q, const void* k, const void* v, const void* q_norm_w,
+                      const void* k_norm_w, float norm_offset, float norm_eps, void* k_cache, void* v_cache,
+                      long long cap, void* out, void* workspace, size_t workspace_bytes, int B, int Hq,
+                      int Hkv, int d, int window, long long pos_offset, const void* rope_table,
+                      size_t rope_table_bytes, float softmax_scale, int cache_order, void* stream) {
+  if (dtype != PLAMO_BF16) return fail(dtype == PLAMO_F32 ? PLAMO_ERR_UNSUPPORTED : PLAMO_ERR_INVALID_ARG,
+                                       "the decode step reads and writes a bf16 cache");
+  if (int st = check_heads(B, 1, Hq, Hkv, d, window, pos_offset)) return st;
+  if (d != kHeadDim) return fail(PLAMO_ERR_UNSUPPORTED, "the one-launch decode step is for d = 128");
+  if (cache_order != PLAMO_CACHE_PRE_ROPE && cache_order != PLAMO_CACHE_POST_ROPE)
+    return fail(PLAMO_ERR_INVALID_ARG, "unknown cache_order");
+  if (B == 0) return ok();
+  if (!q || !k || !v || !k_cache || !v_cache || !out || !rope_table)
+    return fail(PLAMO_ERR_INVALID_ARG, "q, k, v, caches, out and rope_table must be non-NULL");
+  if ((q_norm_w == nullptr) != (k_norm_w == nullptr))
+    return fail(PLAMO_ERR_INVALID_ARG, "give both norm weights or neither");
+  const void* ptrs[] = {q, k, v, q_norm_w, k_norm_w, k_cache, v_cache, out, workspace, rope_table};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if (!(norm_eps >= 0.f) || !std::isfinite(norm_offset)) return fail(PLAMO_ERR_INVALID_ARG, "bad norm offset/eps");
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return fail(PLAMO_ERR_INVALID_ARG, "softmax_scale must be > 0");
+  if (window > 0 && cap < window) return fail(PLAMO_ERR_INVALID_ARG, "local cache needs cap >= window");
+  if (window == 0 && cap < pos_offset + 1) return fail(PLAMO_ERR_INVALID_ARG, "global cache needs cap >= pos_offset + 1");
+  const long long kept = kept_tokens(window, pos_offset);
+  const long long S = kept + 1;
+  const bool post = cache_order == PLAMO_CACHE_POST_ROPE;
+  const long long covered = table_positions(rope_table_bytes, d);
+  if (covered < 0) return fail(PLAMO_ERR_INVALID_ARG, "rope_table_bytes is not a whole number of rows");
+  if (covered < (post ? pos_offset + 1 : S)) return fail(PLAMO_ERR_WORKSPACE, "rope table does not cover the positions");
+  const plamo::DecodePlan plan = plamo::plan_decode(B, Hkv, S, false, plamo::kStepMinChunk);
+  const size_t need = plamo::decode_step_workspace_bytes(B, Hq, Hkv, d, plan);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return fail(PLAMO_ERR_WORKSPACE, "workspace too small");
+  if (static_cast<long long>(B) * Hq > 0x7fffffffLL) return fail(PLAMO_ERR_UNSUPPORTED, "grid too large");
+
+  plamo::DecodeArgs a{};
+  a.k_cache = k_cache; a.v_cache = v_cache; a.cap = cap; a.out = out;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.window = window;
+  a.S = S; a.base = pos_offset - kept; a.plan = plan;
+  a.pos_offset = pos_offset;
+  a.post_rope = post;
+  a.rope = static_cast<const float2*>(rope_table);
+  a.scale = softmax_scale;
+  a.d = d;
+  a.fused = true;
+  a.q_in = q; a.k_in = k; a.v_in = v; a.wq = q_norm_w; a.wk = k_norm_w;
+  a.norm_offset = norm_offset; a.eps = norm_eps;
+  if (need > 0) {
+    a.tickets = static_cast<unsigned*>(workspace);
+    a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + plamo::decode_step_tickets_bytes(B, Hkv));
+  }
+  return launched(plamo::launch_decode_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
 static_assert(plamo::kDecodeScratchBytes == PLAMO_DECODE_SCRATCH_BYTES, "scratch size as declared");
 
 int plamo_attn_decode_noalloc(int dtype, const void* q_rot, const void* k_cache, const void* v_cache,

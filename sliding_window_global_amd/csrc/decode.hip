@@ -67,7 +67,6 @@ constexpr int kSub = 16;                   // keys per wave per tile
 constexpr int kMaxGroup = 16;
 constexpr int kPartial = kHeadDim + 2;     // acc[128], m, l
 constexpr int kMaxSplit = 256;             // key ranges per (sequence, KV head)
-constexpr long long kMinChunk = 256;       // keys per range, at least
 constexpr int kVRow = kHeadDim + 16;       // padded V row in LDS (elements): 288 B
 constexpr int kVChunks = kSub * kVRow / 8; // 16-byte slots of one V sub-tile: 288
 constexpr int kVLoads = (kVChunks + 63) / 64;  // direct loads per V sub-tile: 5
@@ -89,7 +88,10 @@ enum CacheMode { kContiguous = 0, kRing = 1, kSmallRing = 2 };
 
 // kRotate: the cache holds K before RoPE (rotated here at renumbered positions); otherwise
 // it holds K already rotated at absolute positions and is used as stored.
-template <int kMode, bool kRotate>
+// kFused: the one-launch step (see DecodeArgs::fused): Q' is formed here from the projected
+// query, the block holding the newest key first writes that token's K and V into the cache,
+// and the key ranges of a (sequence, KV head) are merged by whichever of its blocks ends last.
+template <int kMode, bool kRotate, bool kFused>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a) {
   constexpr int kLoads = kLoadsPerIssue<kRotate>;
   // three ring slots, separate LDS objects so that reads of one slot never wait for the
@@ -105,8 +107,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m16 = lane & 15;  // MFMA row/col index within 16
   const int g = lane >> 4;    // lane group 0..3
-  // a ragged batch launches its key ranges range-major (see the launcher)
-  const bool range_major = a.seq_pos != nullptr;
+  // a ragged batch and the one-launch step launch their key ranges range-major (see the launcher)
+  const bool range_major = kFused || a.seq_pos != nullptr;
   const int split = range_major ? blockIdx.z : blockIdx.x;
   const int kvh = range_major ? blockIdx.x : blockIdx.y;
   const int b = range_major ? blockIdx.y : blockIdx.z;
@@ -128,24 +130,89 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   const bf16_t* __restrict__ vc =
       static_cast<const bf16_t*>(a.v_cache) + (static_cast<long long>(b) * a.Hkv + kvh) * a.cap * kHeadDim;
 
+  // ---- one-launch step: the new token's K and V into the cache -----------------------
+  // 「PLaMo 3アーキテクチャ徹底解析」 §3.2 / §4.3: k is normalised (gain c + w, eps) over its
+  // 128 components; §4.4: the cache stores it before RoPE (post-RoPE order: rotated at its
+  // absolute position first) and V as given, token p in slot p (global) or p mod W (local).
+  // Only the block whose range ends with the newest key (renumbered S - 1) reads that key,
+  // and in it only the wave that owns that key's place in its tile: that wave writes the row
+  // (two components per lane) and waits for the stores before it issues any load. (It is
+  // also the only wave that uses the row as the filler of keys past the range end: a wave
+  // before it has a full tile, a wave after it has no key there and skips the tile.)
+  __shared__ float2 zq[kHalf];  // (one-launch step) rotation factors of the query position
+  if (kFused && s_end == S) {  // block-uniform
+    if (wave == static_cast<int>(((S - 1 - s_begin) & (kTile - 1)) / kSub)) {
+      const long long p = a.pos_offset;
+      const long long slot = a.window == 0 ? p : p % a.window;
+      const long long row = (static_cast<long long>(b) * a.Hkv + kvh) * a.cap + slot;
+      const uint32_t* ksrc = static_cast<const uint32_t*>(a.k_in) + (static_cast<long long>(b) * a.Hkv + kvh) * kHalf;
+      const uint32_t* vsrc = static_cast<const uint32_t*>(a.v_in) + (static_cast<long long>(b) * a.Hkv + kvh) * kHalf;
+      const uint32_t kw2 = ksrc[lane], vw2 = vsrc[lane];
+      float x0 = lo_bf16(kw2), x1 = hi_bf16(kw2);  // components 2 lane, 2 lane + 1
+      if (a.wk) {
+        const float inv = rsqrtf(wave_sum(x0 * x0 + x1 * x1) * (1.f / kHeadDim) + a.eps);
+        const uint32_t gw = static_cast<const uint32_t*>(a.wk)[lane];
+        x0 *= inv * (a.norm_offset + lo_bf16(gw));
+        x1 *= inv * (a.norm_offset + hi_bf16(gw));
+      }
+      if (!kRotate) {  // post-RoPE cache: pair j = 2 (lane & 31) + u of components (j, j + 64)
+        const float y0 = __shfl_xor(x0, 32, 64), y1 = __shfl_xor(x1, 32, 64);
+        const float2 z0 = rope_factor(a.rope, p, 2 * (lane & 31)), z1 = rope_factor(a.rope, p, 2 * (lane & 31) + 1);
+        if (lane < 32) {
+          x0 = x0 * z0.x - y0 * z0.y;
+          x1 = x1 * z1.x - y1 * z1.y;
+        } else {
+          x0 = y0 * z0.y + x0 * z0.x;
+          x1 = y1 * z1.y + x1 * z1.x;
+        }
+      }
+      reinterpret_cast<uint32_t*>(static_cast<bf16_t*>(const_cast<void*>(a.k_cache)) + row * kHeadDim)[lane] = pack_bf16x2(x0, x1);
+      reinterpret_cast<uint32_t*>(static_cast<bf16_t*>(const_cast<void*>(a.v_cache)) + row * kHeadDim)[lane] = vw2;
+      __builtin_amdgcn_s_waitcnt(0);  // (gfx9: the stores count in vmcnt)
+    }
+  }
+
   // ---- Q' fragment (B operand of S^T): head m16, dims of the lane's 16 pairs --------
-  // slice 0: 16g+e, slice 1: 16g+8+e, slice 2: 64+16g+e, slice 3: 64+16g+8+e (e = 0..7)
-  // (loaded here, zeroed for the padding heads once the loads have landed, below)
+  // slice s: dims 32s + 8g + e (e = 0..7); slices s and s + 2 hold the rotation pairs
+  // j = 32s + 8g + e and j + 64. Each slice of a key row is 64 contiguous bytes.
+  // (loaded here, zeroed for the padding heads once the loads have landed, below; in the
+  // one-launch step the projected query and its gains are loaded here and Q' is formed below)
   const bool q_ok = m16 < G;
   u32x4 qw[4];
+  u32x4 gq[kFused ? 4 : 1];
+  float2 zf = {0.f, 0.f}, zc = {0.f, 0.f};  // (one-launch step, wave 0) fine / coarse factor of pair `lane`
   f16x8 qf[4];
-  {
-    const f16_t* src = static_cast<const f16_t*>(a.q_rot) +
-                       (static_cast<long long>(b) * a.Hq + kvh * G + (q_ok ? m16 : 0)) * kHeadDim;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qw[s] = *reinterpret_cast<const u32x4*>(src + (s >> 1) * kHalf + g * 16 + (s & 1) * 8);
+  for (int s = 0; s < (kFused ? 4 : 1); ++s) gq[s] = u32x4{0, 0, 0, 0};
+  {
+    if (kFused) {
+      const bf16_t* src = static_cast<const bf16_t*>(a.q_in) +
+                          (static_cast<long long>(b) * a.Hq + kvh * G + (q_ok ? m16 : 0)) * kHeadDim;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qw[s] = *reinterpret_cast<const u32x4*>(src + s * 32 + g * 8);
+      if (a.wq) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) gq[s] = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.wq) + s * 32 + g * 8);
+      }
+      if (wave == 0) {  // table rows of the query position (the product is formed below)
+        const long long rp = a.post_rope ? a.pos_offset : S - 1;
+        zf = a.rope[(rp & (kRopeFine - 1)) * kHalf + lane];
+        zc = a.rope[(kRopeFine + (rp >> 6)) * kHalf + lane];
+      }
+    } else {
+      const f16_t* src = static_cast<const f16_t*>(a.q_rot) +
+                         (static_cast<long long>(b) * a.Hq + kvh * G + (q_ok ? m16 : 0)) * kHeadDim;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qw[s] = *reinterpret_cast<const u32x4*>(src + s * 32 + g * 8);
+    }
   }
 
   // ---- fine rope factors of this lane's key (its position & 63 is fixed) -------------
   const int key_in_tile = wave * kSub + m16;
   float2 fine[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) fine[e] = kRotate ? a.rope[key_in_tile * kHalf + g * 16 + e] : float2{0.f, 0.f};
+  for (int e = 0; e < 16; ++e)
+    fine[e] = kRotate ? a.rope[key_in_tile * kHalf + (e >> 3) * 32 + g * 8 + (e & 7)] : float2{0.f, 0.f};
 
   // ---- per-lane pieces of the loads ---------------------------------------------------
   // V direct load i, lane l fills padded slot p = 64 i + l: row p / 18, chunk p % 18 (the
@@ -178,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
     {
       const bf16_t* row = kc + cache_row(key_in_tile) * kHeadDim;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) kw[s] = *reinterpret_cast<const u32x4*>(row + (s >> 1) * kHalf + g * 16 + (s & 1) * 8);
+      for (int s = 0; s < 4; ++s) kw[s] = *reinterpret_cast<const u32x4*>(row + s * 32 + g * 8);
     }
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) {
@@ -224,7 +291,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
       kf[s] = __builtin_bit_cast(f16x8, w);
     }
 #pragma unroll
-    for (int hs = 0; hs < 2 && kRotate; ++hs) {  // hs: slices (hs, hs+2) hold pairs 16g + 8hs + e
+    for (int hs = 0; hs < 2 && kRotate; ++hs) {  // hs: slices (hs, hs+2) hold pairs 32hs + 8g + e
       u32x4 lo_w, hi_w;
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
@@ -234,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
           const int e = e2 * 2 + u;
           const float x0 = u ? hi_bf16(kw[hs][e2]) : lo_bf16(kw[hs][e2]);
           const float x1 = u ? hi_bf16(kw[hs + 2][e2]) : lo_bf16(kw[hs + 2][e2]);
-          const float2 cr = cslot[g * 16 + hs * 8 + e];
+          const float2 cr = cslot[hs * 32 + g * 8 + e];
           const float2 f = fine[hs * 8 + e];
           const float zx = cr.x * f.x - cr.y * f.y;
           const float zy = cr.x * f.y + cr.y * f.x;
@@ -308,6 +375,52 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(qw[s]));
 #pragma unroll
   for (int e = 0; e < 16 && kRotate; ++e) asm volatile("" : "+v"(fine[e].x), "+v"(fine[e].y));
+  if constexpr (kFused) {
+    // §3.2 / §4.3: q (c + w) / sqrt(mean(q^2) + eps) over the head's 128 components (the
+    // lane holds 32, the other lane groups of head m16 the rest); §6.1: pair j = 32s + 8g + e
+    // (slices s and s + 2) turns by the factor of the query position; rounded once to half.
+#pragma unroll
+    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(gq[s]));
+    asm volatile("" : "+v"(zf.x), "+v"(zf.y), "+v"(zc.x), "+v"(zc.y));
+    if (wave == 0)  // rotation factor of the query position for pair `lane` (rope_factor's product)
+      zq[lane] = make_float2(zc.x * zf.x - zc.y * zf.y, zc.x * zf.y + zc.y * zf.x);
+    __syncthreads();  // zq written
+    float x[4][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[s][2 * i] = lo_bf16(qw[s][i]);
+        x[s][2 * i + 1] = hi_bf16(qw[s][i]);
+        ss += x[s][2 * i] * x[s][2 * i] + x[s][2 * i + 1] * x[s][2 * i + 1];
+      }
+    if (a.wq) {
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      const float inv = rsqrtf(ss * (1.f / kHeadDim) + a.eps);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[s][2 * i] *= inv * (a.norm_offset + lo_bf16(gq[s][i]));
+          x[s][2 * i + 1] *= inv * (a.norm_offset + hi_bf16(gq[s][i]));
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 z = zq[32 * s + 8 * g + e];
+        const float x0 = x[s][e], x1 = x[s + 2][e];
+        x[s][e] = x0 * z.x - x1 * z.y;
+        x[s + 2][e] = x0 * z.y + x1 * z.x;
+      }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qw[s][i] = pack_f16x2(x[s][2 * i], x[s][2 * i + 1]);
+  }
 #pragma unroll
   for (int s = 0; s < 4; ++s) qf[s] = __builtin_bit_cast(f16x8, q_ok ? qw[s] : u32x4{0, 0, 0, 0});
   // Before computing tile t, an explicit wait leaves the loads of the tiles issued after it
@@ -378,11 +491,69 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
       static_cast<bf16_t*>(a.out)[bh * kHeadDim + d] = f32_to_bf16(acc / l);
     } else {
       float* dst = a.ws + (bh * a.plan.n_split + split) * kPartial;
-      dst[d] = acc;
-      if (d == 0) {
-        dst[kHeadDim] = M;
-        dst[kHeadDim + 1] = l;
+      if (kFused) {  // written through to the device-coherent level (read by another block)
+        __hip_atomic_store(dst + d, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0) {
+          __hip_atomic_store(dst + kHeadDim, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(dst + kHeadDim + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      } else {
+        dst[d] = acc;
+        if (d == 0) {
+          dst[kHeadDim] = M;
+          dst[kHeadDim + 1] = l;
+        }
       }
+    }
+  }
+  if constexpr (kFused) {
+    // One-launch step: the last block of this (sequence, KV head) to get here merges the
+    // ranges' states in range order (deterministic) and writes the output. The ticket
+    // wraps back to 0 on the last arrival (atomicInc with limit n_split - 1).
+    // The states go out as device-coherent (write-through) stores and are read back as
+    // device-coherent loads, so no cache-wide writeback or invalidation is needed: each thread
+    // waits until its stores are acknowledged, the barrier then covers the whole block, and
+    // only after that does the block take its ticket; the block that takes the last ticket
+    // issues its loads after the ticket has returned.
+    if (single) return;  // block-uniform
+    __shared__ int is_last;
+    __builtin_amdgcn_s_waitcnt(0);  // (gfx9: stores count in vmcnt)
+    __syncthreads();
+    if (threadIdx.x == 0)
+      is_last = atomicInc(a.tickets + (static_cast<long long>(b) * a.Hkv + kvh),
+                          static_cast<unsigned>(a.plan.n_split - 1)) == static_cast<unsigned>(a.plan.n_split - 1);
+    __syncthreads();
+    if (!is_last) return;  // block-uniform
+    const int n_split = a.plan.n_split;
+    // this (sequence, KV head)'s states: [G heads][n_split][acc[128], m, l], read with
+    // device-coherent (sc1) buffer loads, all of them independent of each other
+    const float* base_p = a.ws + (static_cast<long long>(b) * a.Hq + kvh * G) * n_split * kPartial;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(base_p), 0, G * n_split * kPartial * static_cast<int>(sizeof(float)), 0x00020000);
+    constexpr int kCoherent = 16;  // sc1
+    auto ld = [&](int off) { return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off * 4, 0, kCoherent)); };
+    // m and l of every (head, range) into LDS (the V slots are free now)
+    float* sm = reinterpret_cast<float*>(&vs0[0][0]);
+    float* sl = reinterpret_cast<float*>(&vs1[0][0]);
+    static_assert(sizeof(vs0) >= kMaxGroup * kMaxSplit * sizeof(float), "merge buffer");
+    for (int t = threadIdx.x; t < G * n_split; t += kThreads) {
+      sm[t] = ld(t * kPartial + kHeadDim);
+      sl[t] = ld(t * kPartial + kHeadDim + 1);
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
+      const int h = idx / kHeadDim, d = idx % kHeadDim;
+      const long long bh = static_cast<long long>(b) * a.Hq + kvh * G + h;
+      float M = -INFINITY;
+      for (int i = 0; i < n_split; ++i) M = fmaxf(M, sm[h * n_split + i]);
+      float acc = 0.f, l = 0.f;
+#pragma unroll 8
+      for (int i = 0; i < n_split; ++i) {
+        const float w = fast_exp2(sm[h * n_split + i] - M);
+        acc += w * ld((h * n_split + i) * kPartial + d);
+        l += w * sl[h * n_split + i];
+      }
+      static_cast<bf16_t*>(a.out)[bh * kHeadDim + d] = f32_to_bf16(acc / l);
     }
   }
 }
@@ -432,15 +603,15 @@ __global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(DecodeArgs a) 
 
 }  // namespace
 
-DecodePlan plan_decode(int B, int Hkv, long long S, bool ragged) {
-  // Aim for ~512 blocks (2 per CU, one wave per SIMD each) with at least kMinChunk keys
+DecodePlan plan_decode(int B, int Hkv, long long S, bool ragged, long long min_chunk) {
+  // Aim for ~512 blocks (2 per CU, one wave per SIMD each) with at least min_chunk keys
   // each and at most kMaxSplit ranges per (sequence, KV head). A ragged batch only knows
   // its longest sequence here; its ranges are cut finer (~8 blocks per slot at the
   // longest length) so that short and long sequences even out over the CUs.
   const long long pairs = static_cast<long long>(B) * Hkv;
   const long long target_blocks = ragged ? 8 * 512 : 512;
   long long n = (target_blocks + pairs - 1) / pairs;
-  const long long by_min_chunk = (S + kMinChunk - 1) / kMinChunk;
+  const long long by_min_chunk = (S + min_chunk - 1) / min_chunk;
   if (n > by_min_chunk) n = by_min_chunk;
   if (n > kMaxSplit) n = kMaxSplit;
   if (n < 1) n = 1;
@@ -458,27 +629,50 @@ size_t decode_workspace_bytes(int B, int Hq, int d, const DecodePlan& plan) {
   return static_cast<size_t>(B) * Hq * plan.n_split * (d + 2) * sizeof(float);
 }
 
+size_t decode_step_tickets_bytes(int B, int Hkv) {
+  return (static_cast<size_t>(B) * Hkv * sizeof(unsigned) + 255) / 256 * 256;
+}
+
+size_t decode_step_workspace_bytes(int B, int Hq, int Hkv, int d, const DecodePlan& plan) {
+  // the tickets first (the same place whatever the plan), then the partial states
+  if (plan.n_split == 1) return 0;
+  return decode_step_tickets_bytes(B, Hkv) + decode_workspace_bytes(B, Hq, d, plan);
+}
+
+namespace {
+template <bool kFused>
+void launch_split(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
+  if (!a.post_rope) {
+    if (a.window == 0)
+      hipLaunchKernelGGL((decode_split_kernel<kContiguous, true, kFused>), grid, dim3(kThreads), 0, stream, a);
+    else if (a.window >= kTile)
+      hipLaunchKernelGGL((decode_split_kernel<kRing, true, kFused>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<kSmallRing, true, kFused>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    if (a.window == 0)
+      hipLaunchKernelGGL((decode_split_kernel<kContiguous, false, kFused>), grid, dim3(kThreads), 0, stream, a);
+    else if (a.window >= kTile)
+      hipLaunchKernelGGL((decode_split_kernel<kRing, false, kFused>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<kSmallRing, false, kFused>), grid, dim3(kThreads), 0, stream, a);
+  }
+}
+}  // namespace
+
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   // Blocks are dispatched in index order. A ragged batch puts the key range slowest: the
   // first ranges of every (sequence, KV head) start together, later ranges (only the longer
   // sequences have them) fill the slots as they free up, and the empty ranges of short
-  // sequences come last.
-  const dim3 grid = a.seq_pos ? dim3(a.Hkv, a.B, a.plan.n_split) : dim3(a.plan.n_split, a.Hkv, a.B);
-  if (!a.post_rope) {
-    if (a.window == 0)
-      hipLaunchKernelGGL((decode_split_kernel<kContiguous, true>), grid, dim3(kThreads), 0, stream, a);
-    else if (a.window >= kTile)
-      hipLaunchKernelGGL((decode_split_kernel<kRing, true>), grid, dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_split_kernel<kSmallRing, true>), grid, dim3(kThreads), 0, stream, a);
-  } else {
-    if (a.window == 0)
-      hipLaunchKernelGGL((decode_split_kernel<kContiguous, false>), grid, dim3(kThreads), 0, stream, a);
-    else if (a.window >= kTile)
-      hipLaunchKernelGGL((decode_split_kernel<kRing, false>), grid, dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_split_kernel<kSmallRing, false>), grid, dim3(kThreads), 0, stream, a);
+  // sequences come last. The one-launch step does the same, so that with B Hkv a multiple of
+  // 8 the ranges of one (sequence, KV head) go to one XCD (blocks are dealt to the 8 XCDs
+  // round robin) and its merge reads states from that XCD's L2.
+  if (a.fused) {
+    launch_split<true>(a, dim3(a.Hkv, a.B, a.plan.n_split), stream);
+    return hipGetLastError();
   }
+  const dim3 grid = a.seq_pos ? dim3(a.Hkv, a.B, a.plan.n_split) : dim3(a.plan.n_split, a.Hkv, a.B);
+  launch_split<false>(a, grid, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.plan.n_split == 1) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.Hq), dim3(kHeadDim), 0, stream, a);

@@ -4,6 +4,10 @@
 
 #include <hip/hip_runtime.h>
 
+#ifndef STEP_MIN_CHUNK
+#define STEP_MIN_CHUNK 256
+#endif
+
 namespace plamo {
 
 // n_rot: pairs j < n_rot turn; the others get frequency 0 (p-RoPE); n_rot = d/2 for all.
@@ -74,7 +78,10 @@ struct DecodePlan {
   int n_split;         // key ranges per (sequence, KV head)
   long long chunk;     // keys per range, a multiple of the key tile
 };
-DecodePlan plan_decode(int B, int Hkv, long long S, bool ragged);
+// min_chunk: keys per range, at least (a multiple of the 64-key tile)
+DecodePlan plan_decode(int B, int Hkv, long long S, bool ragged, long long min_chunk = 256);
+// the one-launch step's ranges (fewer, longer: each range's state goes through the merge)
+constexpr long long kStepMinChunk = STEP_MIN_CHUNK;
 size_t decode_workspace_bytes(int B, int Hq, int d, const DecodePlan& plan);
 // Size of the library's own split-K scratch (plamo_attn_decode_noalloc), and its device
 // address on the current GPU (looked up once per device).
@@ -98,8 +105,24 @@ struct DecodeArgs {
   const float2* rope;
   float scale;
   int d;                     // head dim: 128; 256 or 512 with a post-RoPE cache
+  // One-launch step (d = 128, uniform batch): the decode kernel also does what the append
+  // does for the new token (Q norm and rotation in every block; K norm, K and V into the
+  // cache in the block holding the newest key) and merges the key ranges itself (the last
+  // block of a (sequence, KV head) to finish, counted on `tickets`, which start and end at 0).
+  bool fused;
+  const void* q_in;          // [B, 1, Hq, d] projected (bf16)
+  const void* k_in;          // [B, 1, Hkv, d]
+  const void* v_in;
+  const void* wq;            // NULL = no Q/K norm
+  const void* wk;
+  float norm_offset, eps;
+  unsigned* tickets;         // [B * Hkv]
 };
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+// Workspace of the one-launch step: the tickets (a 256-byte multiple), then the partial
+// states (0 bytes in all when no merge).
+size_t decode_step_tickets_bytes(int B, int Hkv);
+size_t decode_step_workspace_bytes(int B, int Hq, int Hkv, int d, const DecodePlan& plan);
 // Head dims 256 and 512, post-RoPE cache.
 hipError_t launch_decode_wide_bf16(const DecodeArgs& a, hipStream_t stream);
 

@@ -155,9 +155,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   auto issue_k = [&](int step, bf16_t* buf) __attribute__((always_inline)) { issue(k_rsrc, step, buf); };
   auto issue_v = [&](int step, bf16_t* buf) __attribute__((always_inline)) { issue(v_rsrc, step, buf); };
 
-  // K'(0) is copied while the Q' fragments below are loaded (and, fused, formed): the two
-  // latencies overlap instead of adding up.
+  // K'(0), K'(1) and V^T(0) are copied while the Q' fragments below are loaded (and, fused,
+  // formed): the latencies overlap instead of adding up.
   issue_k(0, ks0);
+  if (n_tiles > 1) issue_k(1, ks1);
+  issue_v(0, vs0);
 
   // ---- Q' fragment (MFMA B operand): lane holds dims s*16 + hl*8 .. +7 of its row ----
   // Pre-multiplied by scale * log2(e), so that S comes out of the MFMA in exp2 units, and
@@ -270,6 +272,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   for (int e = 0; e < 16; ++e) neg_m[e] = 0.f;
   constexpr int kDepth = 4;  // MFMA operands read ahead from LDS
 
+  using T1 = std::integral_constant<bool, true>;
+  using T0 = std::integral_constant<bool, false>;
   // One pipeline step: S^T(step+1) = K'(step+1) Q'^T (if kQK) on the matrix cores while
   // the vector ALUs turn S^T(step) into P^T (if kPV); then O^T += V^T(step) P^T (if kPV)
   // while the row maxima of S^T(step+1) are taken. `s_cur` holds S^T(step) shifted and
@@ -319,15 +323,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     // (kQK: a next tile exists; the last step is run without the QK half)
     if (kQK && needs_mask(step + 1)) {
       // key k of the tile is visible to the row at position kept + qrow iff
-      // k <= kept + qrow - j0 and, on local layers, k > kept + qrow - j0 - window
+      // 0 <= kept + qrow - j0 - k (< window on local layers): one unsigned compare
       const int dq = kept + qrow - (kt_hi - step - 1) * BN - hl * 8;
+      const unsigned lim = kLocal ? static_cast<unsigned>(a.window) : 0x80000000u;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int ko = kb * 32 + (e >> 3) * 16 + (e & 7);
-          const bool ok = ko <= dq && (!kLocal || ko > dq - a.window);
-          if (!ok) s_next[kb][e] = -INFINITY;
+          if (!(static_cast<unsigned>(dq - ko) < lim)) s_next[kb][e] = -INFINITY;
         }
     }
 
@@ -366,11 +370,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
         // keeps -inf); later: it moves up by the gain, if any
         const float bump = first ? (mx == -INFINITY ? 0.f : mx) : fmaxf(mx, 0.f);
         const float alpha = first ? 0.f : fast_exp2(-bump);
-        l_run *= alpha;
+        // (while no row of the wave has seen a key, O and l are still zero: nothing to scale)
+        if (__builtin_amdgcn_ballot_w64(!first) != 0) {  // wave-uniform
+          l_run *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+          for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+            for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -382,8 +389,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
       }
     }
   };
-  using T1 = std::integral_constant<bool, true>;
-  using T0 = std::integral_constant<bool, false>;
   // `k_fill`, `v_fill` receive K'(step+2) and V^T(step+1); `kbuf` holds K'(step+1) and
   // `vbuf` V^T(step). The buffers refilled here were last read before the previous barrier.
   // QK: whether a next tile exists (the last step only multiplies P V).
@@ -398,15 +403,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     }
   };
 
-  // ---- K'(0) in LDS; S^T(0) while K'(1) and V^T(0) arrive; then steps 0 .. n_tiles-1 ----
+  // ---- K'(0), K'(1), V^T(0) in LDS; S^T(0); then steps 0 .. n_tiles-1 ----
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   f32x16 s_a[2], s_b[2];  // S^T of the current and of the next tile, roles alternating
-  if (n_tiles > 1) issue_k(1, ks1);
-  issue_v(0, vs0);
   step_body(T1{}, T0{}, -1, ks0, vs1, s_b, s_a);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
+  __syncthreads();  // every wave is done with K'(0) before step 0 refills its buffer
   int step = 0;
   for (; step + 2 < n_tiles; step += 2) {
     run_step(T1{}, step, ks1, vs0, ks0, vs1, s_a, s_b);

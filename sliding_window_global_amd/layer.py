@@ -14,6 +14,7 @@ import torch
 from dataclasses import dataclass
 
 from . import (plamo_attn_decode, plamo_attn_decode_ragged, plamo_attn_decode_ragged_workspace_bytes,
+               plamo_decode_step, plamo_decode_step_workspace_bytes,
                plamo_attn_decode_workspace_bytes, plamo_attn_prefill, plamo_attn_prefill_fused_q,
                plamo_attn_prefill_fused_q_ragged, plamo_attn_prefill_ragged, plamo_kv_append,
                plamo_kv_append_ragged, plamo_linear, plamo_qkv_projection, plamo_rms_norm,
@@ -68,22 +69,37 @@ class DecodeBuffers:
     """Q', output and split workspace of one decode step (ragged: sized for a ragged batch
     whose positions are at most pos_offset)."""
 
-    def __init__(self, B, Hq, Hkv, d, window, pos_offset, dtype=torch.bfloat16, device="cuda", ragged=False):
+    def __init__(self, B, Hq, Hkv, d, window, pos_offset, dtype=torch.bfloat16, device="cuda", ragged=False,
+                 fused=False):
         self.q_rot = torch.empty((B, 1, Hq, d), dtype=score_dtype(dtype), device=device)
         self.out = torch.empty((B, 1, Hq, d), dtype=dtype, device=device)
         size = plamo_attn_decode_ragged_workspace_bytes if ragged else plamo_attn_decode_workspace_bytes
         nbytes = size(B, Hq, Hkv, window, pos_offset, d)
         self.workspace = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device=device)
+        # the one-launch step's workspace: zeroed once (its counters stay zero between calls)
+        self.step_workspace = None
+        if fused:
+            nb = plamo_decode_step_workspace_bytes(B, Hq, Hkv, window, pos_offset, d)
+            self.step_workspace = torch.zeros(max(1, (nb + 3) // 4), dtype=torch.float32, device=device)
 
 
 def decode(q, k, v, k_cache, v_cache, *, window, pos_offset, rope_table, q_norm_w=None,
            k_norm_w=None, norm_offset=1.0, norm_eps=1e-6, bufs: DecodeBuffers | None = None,
-           softmax_scale=None, stream=None, cache_post_rope=False, v_norm=False) -> DecodeBuffers:
-    """One decode step at absolute position pos_offset: q [B,1,Hq,d], k/v [B,1,Hkv,d]."""
+           softmax_scale=None, stream=None, cache_post_rope=False, v_norm=False, fused=False) -> DecodeBuffers:
+    """One decode step at absolute position pos_offset: q [B,1,Hq,d], k/v [B,1,Hkv,d]. fused
+    (d = 128, no v_norm): one launch, plamo_decode_step, instead of the append and the decode."""
     B, _, Hq, d = q.shape
     Hkv = k.shape[2]
     if bufs is None:
-        bufs = DecodeBuffers(B, Hq, Hkv, d, window, pos_offset, q.dtype, q.device)
+        bufs = DecodeBuffers(B, Hq, Hkv, d, window, pos_offset, q.dtype, q.device, fused=fused)
+    if fused:
+        if v_norm:
+            raise ValueError("the one-launch step takes V as given")
+        plamo_decode_step(q, k, v, k_cache, v_cache, bufs.out, bufs.step_workspace, window=window,
+                          pos_offset=pos_offset, rope_table=rope_table, q_norm_w=q_norm_w, k_norm_w=k_norm_w,
+                          norm_offset=norm_offset, norm_eps=norm_eps, softmax_scale=softmax_scale,
+                          cache_post_rope=cache_post_rope, stream=stream)
+        return bufs
     plamo_kv_append(q, k, v, bufs.q_rot, window=window, pos_offset=pos_offset, rope_table=rope_table,
                     q_norm_w=q_norm_w, k_norm_w=k_norm_w, norm_offset=norm_offset, norm_eps=norm_eps,
                     k_cache=k_cache, v_cache=v_cache, cache_post_rope=cache_post_rope, v_norm=v_norm,

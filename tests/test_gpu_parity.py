@@ -279,7 +279,8 @@ def test_prefill_empty_is_noop():
 # decode
 # ----------------------------------------------------------------------------
 
-def _decode_case(B, Hq, Hkv, window, pos_offset, rope, seed, check_b, poison_future=True, post_rope=False):
+def _decode_case(B, Hq, Hkv, window, pos_offset, rope, seed, check_b, poison_future=True, post_rope=False,
+                 fused=False):
     d = 128
     cap = window if window else pos_offset + 1
     kc = device_normal_bf16((B, Hkv, cap, d), seed, "cuda")
@@ -299,9 +300,12 @@ def _decode_case(B, Hq, Hkv, window, pos_offset, rope, seed, check_b, poison_fut
     tab = rope_table(rope, max(pos_offset + 2, 64))
     bufs = layer.decode(dev(q), dev(k), dev(v), kc, vc, window=window, pos_offset=pos_offset,
                         rope_table=tab, q_norm_w=dev(wq), k_norm_w=dev(wk), norm_offset=1.0,
-                        cache_post_rope=post_rope)
+                        cache_post_rope=post_rope, fused=fused)
     torch.cuda.synchronize()
     out = host(bufs.out)
+    if fused:  # the counters of the merge are back at zero
+        tickets = swg.plamo_decode_step_workspace_bytes(B, Hq, Hkv, window, pos_offset) > 0
+        assert not tickets or torch.all(bufs.step_workspace.view(torch.int32)[:B * Hkv] == 0)
     for b in check_b:
         ref = oracle_decode_one(q[b], k[b], v[b], prior_k[b], prior_v[b], pos_offset, window=window,
                                 rope=rope, wq=wq, wk=wk, post_rope=post_rope)
@@ -318,6 +322,34 @@ def test_decode_small_batch(window, pos_offset):
     """Ring fill-up and wrap, contiguous growth, tile edges; dead slots hold NaN."""
     rope = Rope(1e4) if window else Rope(1e6, 64.0)
     _decode_case(3, 16, 2, window, pos_offset, rope, 100 + pos_offset + window, check_b=[0, 1, 2])
+
+
+@pytest.mark.parametrize("window,pos_offset,post_rope", [
+    (2048, 0, False), (2048, 100, False), (2048, 2047, False), (2048, 32767 + 1000, False), (0, 0, False),
+    (0, 63, False), (0, 64, False), (0, 5000, False), (16, 40, False), (1, 50, False), (2, 8, False),
+    (2048, 5000, True), (0, 5000, True), (16, 40, True)])
+def test_decode_step_one_launch(window, pos_offset, post_rope):
+    """plamo_decode_step (the append's work for the new token, attention and the merge of the
+    key ranges in one launch): ring fill-up and wrap, contiguous growth, tile edges, both
+    cache orders; dead slots hold NaN, also the slot the new token takes."""
+    rope = Rope(1e4) if window else Rope(1e6, 64.0)
+    _decode_case(3, 16, 2, window, pos_offset, rope, 500 + pos_offset + window, check_b=[0, 1, 2],
+                 post_rope=post_rope, fused=True)
+
+
+@pytest.mark.parametrize("layer_idx", [0, 1], ids=["local_ring2048", "global32768"])
+def test_decode_step_one_launch_full_size(layer_idx):
+    """The one-launch step at the batched-decode shape (B = 64) and at the period's (B = 8,
+    131071 kept global tokens: eight key ranges merged by ticket)."""
+    wl = BATCHED_DECODE
+    ly = wl.layers[layer_idx]
+    _decode_case(wl.B, wl.Hq, wl.Hkv, ly.window, wl.pos_offset, ly.rope, wl.cache_seed(layer_idx),
+                 check_b=[0, 31, 63], poison_future=False, fused=True)
+    wl = PERIOD_DECODE
+    li = 7 if layer_idx else 0
+    ly = wl.layers[li]
+    _decode_case(wl.B, wl.Hq, wl.Hkv, ly.window, wl.pos_offset, ly.rope, wl.cache_seed(li),
+                 check_b=[0, 7], poison_future=False, fused=True)
 
 
 @pytest.mark.parametrize("G", [1, 4, 16])
@@ -361,8 +393,9 @@ def test_decode_period_long_context_step():
                      check_b=[0, 7], poison_future=False)
 
 
-@pytest.mark.parametrize("li", [0, 7], ids=["local_ring2048", "global131072"])
-def test_decode_period_128_steps(li):
+@pytest.mark.parametrize("li,fused", [(0, False), (7, False), (0, True), (7, True)],
+                         ids=["local_ring2048", "global131072", "local_ring2048_one_launch", "global131072_one_launch"])
+def test_decode_period_128_steps(li, fused):
     """The 8-layer period's 128 consecutive decode steps (append + decode per step) on one
     local and the global layer at B = 8 from 131071 kept tokens; steps 0, 63 and 127 of two
     sequences against the oracle run on the same token stream (its cache takes every step's
@@ -381,10 +414,12 @@ def test_decode_period_128_steps(li):
     tab = rope_table(ly.rope, p0 + steps + 64)
     omega_kw = dict(theta=ly.rope.theta, yarn_factor=ly.rope.yarn_factor, orig_ctx=ly.rope.orig_ctx,
                     beta_fast=ly.rope.beta_fast, beta_slow=ly.rope.beta_slow)
+    # one set of buffers for all steps (the one-launch step's counters must stay consistent)
+    bufs = layer.DecodeBuffers(B, Hq, Hkv, d, W, p0 + steps, fused=fused)
     for k in range(steps):
         x = wl.draw_new_tokens(k, li)
         db = layer.decode(dev(x["q"]), dev(x["k"]), dev(x["v"]), kc, vc, window=W, pos_offset=p0 + k, rope_table=tab,
-                          q_norm_w=dev(x["wq"]), k_norm_w=dev(x["wk"]), norm_offset=c)
+                          q_norm_w=dev(x["wq"]), k_norm_w=dev(x["wk"]), norm_offset=c, fused=fused, bufs=bufs)
         if k in check_k:
             torch.cuda.synchronize()
             out = host(db.out)
