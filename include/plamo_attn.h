@@ -172,6 +172,24 @@ PLAMO_API int plamo_kv_append(int dtype, const void* q, const void* k, const voi
                     void* stream);
 
 /* ---------------------------------------------------------------------------
+ * plamo_prefill_pack -- caller-held keys and values into the prefill operand layouts
+ * [P3 §4.1, §4.5]
+ *
+ * For callers that hold the attended keys already rotated (an engine's post-RoPE cache, or
+ * their own norm and RoPE) and want plamo_attn_prefill without plamo_kv_append: writes the
+ * k_rot and v_t operands that plamo_attn_prefill reads, exactly in the layouts documented
+ * for plamo_kv_append's k_rot_out and v_t_out, for the S keys (S = kept + T of that call;
+ * Tp = plamo_prefill_padded_len(S) rows each, rows S .. Tp-1 zero).
+ * k_rot [B, S, Hkv, d]  rotated K' of the keys in renumbered (or absolute, post-RoPE) order
+ * v     [B, S, Hkv, d]  V of the same keys
+ * dtype PLAMO_BF16: inputs bf16 (d = 128, 256 or 512), K' written as fp16 (exact for values
+ * in the half range, |x| <= 65504); PLAMO_F32: inputs fp32, d = 128. The query operand
+ * q_rot for plamo_attn_prefill is [B, T, Hq, d] (fp16 for PLAMO_BF16), the caller's Q'.
+ * ------------------------------------------------------------------------- */
+PLAMO_API int plamo_prefill_pack(int dtype, const void* k_rot, const void* v, void* k_rot_out,
+                       void* v_t_out, int B, long long S, int Hkv, int d, void* stream);
+
+/* ---------------------------------------------------------------------------
  * plamo_attn_prefill -- step 4 for a prefill of T tokens [P3 §4.5, §5.1]
  *
  * q_rot [B, T, Hq, d] (fp16 for PLAMO_BF16); k_rot and v_t in the dtype's layout written by

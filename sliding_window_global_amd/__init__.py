@@ -210,6 +210,22 @@ def plamo_kv_append(q, k, v, q_out, *, window: int, pos_offset: int, rope_table,
     _check(st, "plamo_kv_append")
 
 
+def plamo_prefill_pack(k_rot_in, v_in, k_rot_out, v_t_out, *, stream=None) -> None:
+    """Caller-held K' and V [B, S, Hkv, d] into the prefill operand layouts (shapes from
+    prefill_operand_shapes with T = S, pos_offset = 0; K' output in score_dtype)."""
+    dt = v_in.dtype
+    B, S, Hkv, d = v_in.shape
+    if tuple(k_rot_in.shape) != (B, S, Hkv, d):
+        raise ValueError("k_rot_in and v_in must both be [B, S, Hkv, d]")
+    k_shape, v_shape = prefill_operand_shapes(B, S, Hkv, d, dt)
+    if tuple(k_rot_out.shape) != k_shape or tuple(v_t_out.shape) != v_shape:
+        raise ValueError(f"k_rot_out must be {list(k_shape)} and v_t_out {list(v_shape)}")
+    st = _lib.load().plamo_prefill_pack(
+        _dtype_code(dt), _dev(k_rot_in, "k_rot_in", dt), _dev(v_in, "v_in", dt),
+        _dev(k_rot_out, "k_rot_out", score_dtype(dt)), _dev(v_t_out, "v_t_out", dt), B, S, Hkv, d, _stream(stream))
+    _check(st, "plamo_prefill_pack")
+
+
 def plamo_attn_prefill(q_rot, k_rot, v_t, out, *, window: int, pos_offset: int = 0,
                        softmax_scale: float | None = None, stream=None) -> None:
     """q_rot [B,T,Hq,d], k_rot / v_t as prefill_operand_shapes -> out [B,T,Hq,d] (q_rot and

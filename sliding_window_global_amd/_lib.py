@@ -25,6 +25,8 @@ SIGNATURES = {
     "plamo_kv_append": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_float,
                                 c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_ll, c_int, c_int, c_int,
                                 c_int, c_int, c_int, c_ll, c_void_p, c_size, c_int, c_void_p]),
+    "plamo_prefill_pack": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_ll, c_int, c_int,
+                                   c_void_p]),
     "plamo_attn_prefill": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                    c_int, c_int, c_ll, c_float, c_void_p]),
     "plamo_attn_prefill_fused_q": (c_int, [c_int, c_void_p, c_void_p, c_float, c_float, c_void_p, c_void_p,

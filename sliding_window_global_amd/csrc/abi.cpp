@@ -486,6 +486,26 @@ int plamo_decode_step(int dtype, const void* q, const void* k, const void* v, co
   return launched(plamo::launch_decode_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
+int plamo_prefill_pack(int dtype, const void* k_rot, const void* v, void* k_rot_out, void* v_t_out, int B,
+                       long long S, int Hkv, int d, void* stream) {
+  if (dtype != PLAMO_F32 && dtype != PLAMO_BF16) return fail(PLAMO_ERR_INVALID_ARG, "unknown dtype");
+  if (B < 0 || S < 0 || Hkv < 1) return fail(PLAMO_ERR_INVALID_ARG, "need B >= 0, S >= 0, Hkv >= 1");
+  if (!known_head_dim(d)) return fail(PLAMO_ERR_UNSUPPORTED, "head dim must be 128, 256 or 512");
+  if (d != kHeadDim && dtype != PLAMO_BF16) return fail(PLAMO_ERR_UNSUPPORTED, "head dims 256 and 512 are bf16 only");
+  if (B == 0 || S == 0) return ok();
+  if (!k_rot || !v || !k_rot_out || !v_t_out) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be non-NULL");
+  const void* ptrs[] = {k_rot, v, k_rot_out, v_t_out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  const long long Tp = plamo_prefill_padded_len(S);
+  if (Tp / 64 > 0x7fffffffLL || static_cast<long long>(B) * Hkv > 65535LL * 65535LL || B > 65535 || Hkv > 65535)
+    return fail(PLAMO_ERR_UNSUPPORTED, "grid too large");
+  plamo::PackArgs a{};
+  a.k = k_rot; a.v = v; a.k_rot_out = k_rot_out; a.v_t_out = v_t_out;
+  a.B = B; a.Hkv = Hkv; a.d = d; a.S = S; a.Tp = Tp;
+  return launched(plamo::launch_prefill_pack(a, dtype == PLAMO_BF16, static_cast<hipStream_t>(stream)));
+}
+
 static_assert(plamo::kDecodeScratchBytes == PLAMO_DECODE_SCRATCH_BYTES, "scratch size as declared");
 
 int plamo_attn_decode_noalloc(int dtype, const void* q_rot, const void* k_cache, const void* v_cache,

@@ -615,6 +615,63 @@ __global__ __launch_bounds__(kThreads) void prefill_operands_kernel(AppendArgs a
   }
 }
 
+// Caller-held rotated keys K' and values V [B, S, Hkv, D] into the prefill operand layouts
+// (the ones the append kernels write). One block = one 64-key tile of one (sequence, KV
+// head); rows S .. Tp-1 are zero. bf16: K' tile [D/8][64][8] as IEEE halves (exact for
+// bf16 inputs in the half range), V^T tile [8][D][8]; fp32: [Tp][D] and [D][Tp].
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void prefill_pack_kernel(PackArgs a) {
+  constexpr int kVec = 16 / sizeof(E);
+  constexpr int kChunks = D / kVec;  // 16-byte chunks per row
+  const long long R0 = static_cast<long long>(blockIdx.x) * kTokBlock;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const long long bh = static_cast<long long>(b) * a.Hkv + kvh;
+  const E* __restrict__ k = static_cast<const E*>(a.k);
+  const E* __restrict__ v = static_cast<const E*>(a.v);
+  E* __restrict__ k_out = static_cast<E*>(a.k_rot_out);
+  E* __restrict__ v_out = static_cast<E*>(a.v_t_out);
+  auto row_of = [&](const E* base, long long R) { return base + ((static_cast<long long>(b) * a.S + R) * a.Hkv + kvh) * D; };
+  for (int i = threadIdx.x; i < kTokBlock * kChunks; i += kThreads) {
+    const int r = i / kChunks, c = i % kChunks;
+    const long long R = R0 + r;
+    u32x4 w = R < a.S ? reinterpret_cast<const u32x4*>(row_of(k, R))[c] : u32x4{0, 0, 0, 0};
+    if constexpr (sizeof(E) == 2) {
+      w = u32x4{bf16x2_to_f16x2(w[0]), bf16x2_to_f16x2(w[1]), bf16x2_to_f16x2(w[2]), bf16x2_to_f16x2(w[3])};
+      *reinterpret_cast<u32x4*>(k_out + (bh * a.Tp + R0) * D + (c * kTokBlock + r) * kVec) = w;
+    } else {
+      *reinterpret_cast<u32x4*>(k_out + (bh * a.Tp + R) * D + c * kVec) = w;
+    }
+  }
+  if constexpr (sizeof(E) == 2) {
+    for (int i = threadIdx.x; i < 8 * kChunks; i += kThreads) {  // key chunk kc x dim chunk cidx
+      const int kc = i / kChunks, cidx = i % kChunks;
+      u32x4 w[8], o[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const long long R = R0 + kc * 8 + r;
+        w[r] = R < a.S ? reinterpret_cast<const u32x4*>(row_of(v, R))[cidx] : u32x4{0, 0, 0, 0};
+      }
+      transpose8x8_bf16(w, o);
+      u32x4* dst = reinterpret_cast<u32x4*>(v_out + (bh * a.Tp + R0) * D) + kc * D + cidx * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[e] = o[e];
+    }
+  } else {
+    for (int i = threadIdx.x; i < kTokBlock * D; i += kThreads) {  // dim dd, key r (keys fastest)
+      const int dd = i / kTokBlock, r = i % kTokBlock;
+      const long long R = R0 + r;
+      v_out[(bh * D + dd) * a.Tp + R] = R < a.S ? row_of(v, R)[dd] : E(0);
+    }
+  }
+}
+
+template <typename E, int D>
+hipError_t launch_pack(const PackArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((prefill_pack_kernel<E, D>), dim3(static_cast<unsigned>(a.Tp / kTokBlock), a.Hkv, a.B),
+                     dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <typename E, int D>
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   const bool operands = a.k_rot_out || a.v_t_out;
@@ -651,6 +708,15 @@ hipError_t launch_kv_append_bf16(const AppendArgs& a, hipStream_t stream) {
 }
 hipError_t launch_kv_append_f32(const AppendArgs& a, hipStream_t stream) {
   return launch_append<float, kHeadDim>(a, stream);
+}
+
+hipError_t launch_prefill_pack(const PackArgs& a, bool bf16, hipStream_t stream) {
+  if (!bf16) return launch_pack<float, kHeadDim>(a, stream);
+  switch (a.d) {
+    case 256: return launch_pack<bf16_t, 256>(a, stream);
+    case 512: return launch_pack<bf16_t, 512>(a, stream);
+    default: return launch_pack<bf16_t, kHeadDim>(a, stream);
+  }
 }
 
 }  // namespace plamo

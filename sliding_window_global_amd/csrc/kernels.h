@@ -48,6 +48,17 @@ struct AppendArgs {
 hipError_t launch_kv_append_bf16(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_kv_append_f32(const AppendArgs& a, hipStream_t stream);
 
+// Caller-held K' and V [B, S, Hkv, d] into the prefill operand layouts (Tp rows each).
+struct PackArgs {
+  const void* k;
+  const void* v;
+  void* k_rot_out;
+  void* v_t_out;
+  int B, Hkv, d;
+  long long S, Tp;
+};
+hipError_t launch_prefill_pack(const PackArgs& a, bool bf16, hipStream_t stream);
+
 struct PrefillArgs {
   const void* q_rot;  // [B, T, Hq, d]
   const void* k_rot;  // [B, Hkv, Tp, d]

@@ -315,3 +315,14 @@ def test_decode_noalloc_rejects_partials_beyond_its_scratch(lib):
     assert big == -3
     assert lib.plamo_attn_decode_noalloc(BF16, FAKE, FAKE, FAKE, 65536, FAKE, 0, 1, 16, 1, 512, 0, 65535,
                                          None, 0, 1.0, 1, None) == 0  # B = 0: nothing to do
+
+
+def test_prefill_pack_checks(lib):
+    """plamo_prefill_pack validates before launching: dtype, head dim, sizes, pointers."""
+    assert lib.plamo_prefill_pack(7, FAKE, FAKE, FAKE, FAKE, 1, 10, 2, 128, None) == INVALID
+    assert lib.plamo_prefill_pack(BF16, FAKE, FAKE, FAKE, FAKE, 1, 10, 2, 64, None) == -2
+    assert lib.plamo_prefill_pack(F32, FAKE, FAKE, FAKE, FAKE, 1, 10, 2, 256, None) == -2
+    assert lib.plamo_prefill_pack(BF16, FAKE, FAKE, FAKE, FAKE, -1, 10, 2, 128, None) == INVALID
+    assert lib.plamo_prefill_pack(BF16, None, FAKE, FAKE, FAKE, 1, 10, 2, 128, None) == INVALID
+    assert lib.plamo_prefill_pack(BF16, ctypes.c_void_p(0x7F0000000008), FAKE, FAKE, FAKE, 1, 10, 2, 128, None) == INVALID
+    assert lib.plamo_prefill_pack(BF16, None, None, None, None, 1, 0, 2, 128, None) == 0  # nothing to pack

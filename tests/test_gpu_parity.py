@@ -258,6 +258,42 @@ def test_prefill_global_full_size_pages_setting():
         del out
 
 
+@pytest.mark.parametrize("window,pos_offset,T,d", [(0, 0, 300, 128), (0, 100, 200, 128), (64, 500, 130, 128),
+                                                   (2048, 0, 777, 128), (100, 40, 150, 256)])
+def test_prefill_pack_caller_operands(window, pos_offset, T, d):
+    """plamo_prefill_pack + plamo_attn_prefill on keys and queries the caller rotated itself
+    (here: the oracle's normalised and rotated K' and Q' of every attended key and query,
+    rounded to bf16 / fp16): step 4 alone against the oracle's attention on those operands,
+    and the packed layouts against a host re-tiling."""
+    from oracle import gqa_attention
+    B, Hq, Hkv = 2, 8, 2
+    kept = pos_offset if window == 0 else min(pos_offset, window - 1)
+    S = kept + T
+    dr = Draw(8800 + S + window + d, True)
+    k_rot = dr.normal((B, S, Hkv, d))            # caller's K' (bf16-exact values)
+    v = dr.normal((B, S, Hkv, d))
+    q_rot = dr.normal((B, T, Hq, d)).astype(np.float16).astype(np.float32)  # caller's Q' (fp16)
+    scale = 1.0 / math.sqrt(d)
+    k_shape, v_shape = swg.prefill_operand_shapes(B, T, Hkv, d, torch.bfloat16, window, pos_offset)
+    k_out = torch.full(k_shape, float("nan"), dtype=torch.float16, device="cuda")
+    v_out = torch.full(v_shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    swg.plamo_prefill_pack(dev(k_rot), dev(v), k_out, v_out)
+    out = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device="cuda")
+    swg.plamo_attn_prefill(torch.from_numpy(q_rot).to(torch.float16).cuda(), k_out, v_out, out, window=window,
+                           pos_offset=pos_offset, softmax_scale=scale)
+    torch.cuda.synchronize()
+    Sp = k_shape[2] * 64
+    kr = untile_k_rot(host(k_out))
+    k_half = k_rot.astype(np.float16).astype(np.float64)  # bf16 -> half: exact except below 2^-14
+    assert np.array_equal(kr[:, :, :S].transpose(0, 2, 1, 3), k_half) and np.all(kr[:, :, S:] == 0)
+    vt = untile_v_t(host(v_out))
+    assert np.array_equal(vt[..., :S].transpose(0, 3, 1, 2), v) and np.all(vt[..., S:] == 0) and vt.shape[-1] == Sp
+    got = host(out)
+    for b in range(B):
+        ref = gqa_attention(q_rot[b], k_half[b], v[b], np.arange(kept, S), np.arange(S), window, scale)
+        assert_parity(got[b], ref, TOL_BF16, f"pack + prefill b={b} W={window} p={pos_offset} T={T} d={d}")
+
+
 def test_prefill_deterministic():
     wl = LOCAL_PREFILL
     inp = wl.draw()
