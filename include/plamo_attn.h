@@ -111,7 +111,8 @@ PLAMO_API int plamo_rope_table_init(void* table, size_t table_bytes, long long m
                           const plamo_rope* rope, void* stream);
 
 /* Padded key count used by the prefill operand layouts: S rounded up to 128, where a
- * chunk of T tokens after `kept` cached ones (below) attends S = kept + T keys. */
+ * chunk of T tokens after `kept` cached ones (below) attends S = kept + T keys. Returns 0
+ * for S <= 0 and for S > 2^40 (beyond any position the rope table covers). */
 PLAMO_API long long plamo_prefill_padded_len(long long S);
 
 /* ---------------------------------------------------------------------------

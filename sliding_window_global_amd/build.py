@@ -20,7 +20,7 @@ LIB_NAME = "libplamo_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["rope_table.hip", "append.hip", "prefill_bf16.hip", "prefill_wide.hip", "prefill_f32.hip", "decode.hip",
+SOURCES = ["rope_table.hip", "append.hip", "prefill_bf16.hip", "prefill_wide.hip", "prefill_f32.hip", "decode.hip", "plan.cpp",
            "decode_wide.hip", "norm.hip", "gemm.hip", "abi.cpp"]
 LINK_LIBS: list[str] = []
 # The bf16 prefill's softmax only ever sees finite or -inf scores: without NaN semantics

@@ -87,9 +87,9 @@ const char* plamo_status_str(int status) {
 
 const char* plamo_last_error(void) { return g_last_error; }
 
-long long plamo_prefill_padded_len(long long T) {
-  if (T <= 0) return 0;
-  return (T + kPad - 1) / kPad * kPad;
+long long plamo_prefill_padded_len(long long S) {
+  if (S <= 0 || S > (1LL << 40)) return 0;
+  return (S + kPad - 1) / kPad * kPad;
 }
 
 size_t plamo_rope_table_bytes(long long max_pos, int d) {
@@ -492,6 +492,7 @@ int plamo_prefill_pack(int dtype, const void* k_rot, const void* v, void* k_rot_
   if (B < 0 || S < 0 || Hkv < 1) return fail(PLAMO_ERR_INVALID_ARG, "need B >= 0, S >= 0, Hkv >= 1");
   if (!known_head_dim(d)) return fail(PLAMO_ERR_UNSUPPORTED, "head dim must be 128, 256 or 512");
   if (d != kHeadDim && dtype != PLAMO_BF16) return fail(PLAMO_ERR_UNSUPPORTED, "head dims 256 and 512 are bf16 only");
+  if (S > (1LL << 40)) return fail(PLAMO_ERR_UNSUPPORTED, "S must be <= 2^40");
   if (B == 0 || S == 0) return ok();
   if (!k_rot || !v || !k_rot_out || !v_t_out) return fail(PLAMO_ERR_INVALID_ARG, "tensors must be non-NULL");
   const void* ptrs[] = {k_rot, v, k_rot_out, v_t_out};
@@ -552,7 +553,7 @@ int plamo_qkv_projection(const void* u, const void* w_qkv, void* q, void* k, voi
                          int Hq, int Hkv, int d, void* stream) {
   if (M < 0 || D < 1 || Hq < 1 || Hkv < 1 || d < 1) return fail(PLAMO_ERR_INVALID_ARG, "bad sizes");
   if (D % 64 || d % 8) return fail(PLAMO_ERR_UNSUPPORTED, "need D % 64 == 0 and d % 8 == 0");
-  const long long N = static_cast<long long>(Hq + 2 * Hkv) * d;
+  const long long N = (static_cast<long long>(Hq) + 2LL * Hkv) * d;
   if (M > 65535LL * 256 || N > (1LL << 30) || static_cast<long long>(D) * 256 * 2 > 0x7fffffffLL)
     return fail(PLAMO_ERR_UNSUPPORTED, "sizes too large");
   if (M == 0) return ok();
@@ -564,7 +565,7 @@ int plamo_qkv_projection(const void* u, const void* w_qkv, void* q, void* k, voi
   a.x = u; a.w = w_qkv; a.M = M; a.N = N; a.K = D;
   a.y[0] = q; a.y[1] = k; a.y[2] = v;
   a.part_end[0] = static_cast<long long>(Hq) * d;
-  a.part_end[1] = static_cast<long long>(Hq + Hkv) * d;
+  a.part_end[1] = (static_cast<long long>(Hq) + Hkv) * d;
   a.part_end[2] = N;
   return launched(plamo::launch_gemm_bf16(a, static_cast<hipStream_t>(stream)));
 }
