@@ -11,9 +11,10 @@
 // range of renumbered keys, a multiple of 64 long, cut into 64-key tiles. Wave w owns
 // keys 16w .. 16w+15 of every tile and streams them on its own, without block barriers:
 //   K rows   global -> registers, already in the MFMA operand layout (4 x 16 B per lane),
-//   V rows   global -> LDS by direct loads (rows padded to 288 B, so that the transposing
-//            operand reads below, four rows of 32 B per lane group, are free of bank
-//            conflicts),
+//   V rows   global -> LDS by direct loads, four rows per load; the 16-byte chunks of a row
+//            are stored XOR-swizzled by the row index (each lane loads the chunk its LDS
+//            slot should hold), so that the transposing operand reads below, 32 B of eight
+//            rows at a time, are free of bank conflicts without padding,
 //   rope     the tile's coarse factor row global -> LDS by one direct load,
 // three sub-tiles per wave in flight or in use (a ring unrolled by three).
 //   S^T[16 keys][16 heads] = K'[16][128] Q'^T  (v_mfma_f32_16x16x32_f16: Q' arrives as IEEE
@@ -67,10 +68,10 @@ constexpr int kSub = 16;                   // keys per wave per tile
 constexpr int kMaxGroup = 16;
 constexpr int kPartial = kHeadDim + 2;     // acc[128], m, l
 constexpr int kMaxSplit = 256;             // key ranges per (sequence, KV head)
-constexpr int kVRow = kHeadDim + 16;       // padded V row in LDS (elements): 288 B
-constexpr int kVChunks = kSub * kVRow / 8; // 16-byte slots of one V sub-tile: 288
-constexpr int kVLoads = (kVChunks + 63) / 64;  // direct loads per V sub-tile: 5
-constexpr int kVSlot = kVLoads * 64 * 8;   // elements reserved per V sub-tile
+constexpr int kVLoads = kSub * kHeadDim / 8 / 64;  // direct loads per V sub-tile (16 B a lane): 4
+constexpr int kVSlot = kSub * kHeadDim;    // elements of one V sub-tile in LDS
+// 16-byte chunk c of V row r of a sub-tile sits at chunk c ^ v_swizzle(r) of that row
+__device__ __forceinline__ int v_swizzle(int r) { return 2 * (r & 7); }
 constexpr float kRescaleLog2 = 8.f;        // lazy-rescale threshold (log2 units)
 // loads per tile issue: K rows, V rows and (when K is rotated here) the coarse rope row
 template <bool kRotate>
@@ -215,14 +216,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
     fine[e] = kRotate ? a.rope[key_in_tile * kHalf + (e >> 3) * 32 + g * 8 + (e & 7)] : float2{0.f, 0.f};
 
   // ---- per-lane pieces of the loads ---------------------------------------------------
-  // V direct load i, lane l fills padded slot p = 64 i + l: row p / 18, chunk p % 18 (the
-  // pad chunks 16, 17 and the slots past 16 rows copy a chunk of the last row, never read).
+  // V direct load i, lane l fills chunk slot l & 15 of row 4 i + l / 16: it loads the
+  // row's chunk (l & 15) ^ v_swizzle(row).
   int v_row[kVLoads], v_col[kVLoads];
 #pragma unroll
   for (int i = 0; i < kVLoads; ++i) {
-    const int p = 64 * i + lane;
-    v_row[i] = min(p / (kVRow / 8), kSub - 1);
-    v_col[i] = min(p % (kVRow / 8), 15);
+    v_row[i] = 4 * i + (lane >> 4);
+    v_col[i] = (lane & 15) ^ v_swizzle(v_row[i]);
   }
   // Issue the loads of this wave's keys of the next tile into a K register set, a V slot
   // and a coarse-row slot. Tiles are issued in order 0, 1, 2, ...; past the end the last
@@ -344,13 +344,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
     const s16x4 pb = __builtin_bit_cast(s16x4, pw);
 
     // V^T fragments: d = 16dt + m16, keys 4g + i of the sub-tile, one transposing LDS read
-    // each: lane 4r + q of lane group g addresses key 4g + r, dims 16dt + 4q .. +3, and the
+    // each: lane 4r + q of lane group g addresses key 4g + r, dims 16dt + 4q .. +3 (half
+    // q & 1 of chunk 2dt + q / 2, stored at chunk (2dt + q / 2) ^ v_swizzle(4g + r)), and the
     // read hands lane m16 of the group dim 16dt + m16 of the four keys (key 4g + i in i).
-    const bf16_t* vrow = vslot + (4 * g + (m16 >> 2)) * kVRow + (m16 & 3) * 4;
+    const int vr = 4 * g + (m16 >> 2);
+    const bf16_t* vrow = vslot + vr * kHeadDim + (m16 & 3) * 4;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const s16x4 va = __builtin_bit_cast(s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                     (lds_v4i16_t*)(vrow + dt * 16)));
+                                                     (lds_v4i16_t*)(vrow + 8 * ((2 * dt) ^ v_swizzle(vr)))));
       oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[dt], 0, 0, 0);
     }
   };
