@@ -155,12 +155,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   auto issue_k = [&](int step, bf16_t* buf) __attribute__((always_inline)) { issue(k_rsrc, step, buf); };
   auto issue_v = [&](int step, bf16_t* buf) __attribute__((always_inline)) { issue(v_rsrc, step, buf); };
 
-  // K'(0), K'(1) and V^T(0) are copied while the Q' fragments below are loaded (and, fused,
-  // formed): the latencies overlap instead of adding up.
-  issue_k(0, ks0);
-  if (n_tiles > 1) issue_k(1, ks1);
-  issue_v(0, vs0);
-
   // ---- Q' fragment (MFMA B operand): lane holds dims s*16 + hl*8 .. +7 of its row ----
   // Pre-multiplied by scale * log2(e), so that S comes out of the MFMA in exp2 units, and
   // rounded to IEEE half (Q' arrives as halves from the append, or is formed here in fp32).
@@ -173,10 +167,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     const bool ok = qrow < n_rows;
     const bf16_t* src = q + (static_cast<long long>(b) * a.T + (ok ? qrow : 0)) * a.Hq * kHeadDim +
                         static_cast<long long>(hq) * kHeadDim + hl * 8;
+    // The rows' Q (or Q') go out first, since they gate the first MFMA; K'(0), K'(1) and
+    // V^T(0) are copied while they arrive (and, fused, while Q' is formed).
+    // (src is row 0 for rows past n_rows: the loads are unconditional and the values are
+    // zeroed afterwards; a load under a branch made the compiler wait for every load in
+    // flight, the tile copies included, in the middle of these)
+    u32x4 qraw[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qraw[s] = *reinterpret_cast<const u32x4*>(src + s * 16);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_k(0, ks0);
+    if (n_tiles > 1) issue_k(1, ks1);
+    issue_v(0, vs0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qraw[s][i] = ok ? qraw[s][i] : 0u;
     if (!kFuseQ) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        u32x4 w = ok ? *reinterpret_cast<const u32x4*>(src + s * 16) : u32x4{0, 0, 0, 0};
+        u32x4 w = qraw[s];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           w[i] = pack_f16x2(lo_f16(w[i]) * c, hi_f16(w[i]) * c);
@@ -191,7 +202,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
       float ss = 0.f;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const u32x4 w = ok ? *reinterpret_cast<const u32x4*>(src + s * 16) : u32x4{0, 0, 0, 0};
+        const u32x4 w = qraw[s];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           x[s][2 * i] = lo_bf16(w[i]);
@@ -421,24 +432,39 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     run_step(T0{}, step, ks1, vs0, ks0, vs1, s_a, s_b);
   }
 
-  // ---- normalise and store: lane writes d = dt*32 + i*8 + hl*4 + 0..3 of its row ----
+  // ---- normalise, then store whole rows through LDS ----------------------------------
+  // The lane holds d = dt*32 + i*8 + hl*4 + 0..3 of its row: stored as they are, every store
+  // would write 16 B into each of 32 rows. Instead each wave stages its 32 rows (8 KiB, in
+  // a K' buffer: the last step reads none) with the 16-byte chunk c of row n at chunk
+  // c ^ (n mod 16), which keeps both the staging writes and the row reads free of bank
+  // conflicts, and then writes four whole 256-byte rows per store.
   const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
   const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
-  if (qrow < n_rows) {
-    const float inv = 1.f / l_tot;
-    bf16_t* dst = static_cast<bf16_t*>(a.out) +
-                  (static_cast<long long>(b) * a.T + qrow) * a.Hq * kHeadDim +
-                  static_cast<long long>(hq) * kHeadDim;
+  const float inv = 1.f / l_tot;  // (rows past n_rows: never stored)
+  bf16_t* const stage = (wave < 2 ? ks0 : ks1) + (wave & 1) * 32 * kHeadDim;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d0 = dt * 32 + i * 8 + hl * 4;
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[dt][i * 4 + 0] * inv, oacc[dt][i * 4 + 1] * inv);
-        w[1] = pack_bf16x2(oacc[dt][i * 4 + 2] * inv, oacc[dt][i * 4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(dst + d0) = w;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int chunk = dt * 4 + i;
+      u32x2 w;
+      w[0] = pack_bf16x2(oacc[dt][i * 4 + 0] * inv, oacc[dt][i * 4 + 1] * inv);
+      w[1] = pack_bf16x2(oacc[dt][i * 4 + 2] * inv, oacc[dt][i * 4 + 3] * inv);
+      *reinterpret_cast<u32x2*>(stage + n * kHeadDim + (chunk ^ (n & 15)) * 8 + hl * 4) = w;
+    }
+  // the wave's own staging writes are done before its reads (no other wave touches them)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  bf16_t* const out_base = static_cast<bf16_t*>(a.out) + static_cast<long long>(hq) * kHeadDim;
+  const int c16 = lane & 15;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = j * 4 + (lane >> 4);  // row of the wave, chunk c16 of it
+    const u32x4 w = *reinterpret_cast<const u32x4*>(stage + r * kHeadDim + (c16 ^ (r & 15)) * 8);
+    if (r0 + r < n_rows)  // (not read again by this kernel: streamed past the caches)
+      __builtin_nontemporal_store(
+          w, reinterpret_cast<u32x4*>(out_base + (static_cast<long long>(b) * a.T + r0 + r) * a.Hq * kHeadDim +
+                                      c16 * 8));
   }
 }
 
