@@ -63,6 +63,24 @@ class Timer:
         return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
 
+SETTLE_S = 0.25  # seconds of untimed load before each workload's warmup steps
+
+
+def settle(torch, fn, seconds=SETTLE_S):
+    """Run fn (one step of the workload about to be timed) until `seconds` of wall time have
+    passed, untimed. The GPU's clocks are still rising during the first tens of milliseconds of
+    load: measured on MI355X, the local prefill kernel timed 0.52 ms after 5 warmup steps and
+    0.46 ms after 100 or 400. The warmup steps follow this phase."""
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+        n += 4
+    return n
+
+
 def dev_bf16(torch, x):
     import numpy as np
     return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda()
@@ -109,6 +127,7 @@ def bench_prefill(torch, swg, wl, steps, warmup, norm_offset, fuse_q=False):
         if t_step:
             t_step[1].record()
 
+    settle(torch, step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -159,6 +178,7 @@ def bench_chunked_prefill(torch, swg, wl, chunk, steps, warmup):
         if t_step:
             t_step[1].record()
 
+    settle(torch, step)
     for _ in range(warmup):
         step()
     ts = Timer(torch)
@@ -196,6 +216,7 @@ def bench_decode_batched(torch, swg, wl, layer_idx, steps, warmup, post_rope=Fal
         swg.plamo_attn_decode(bufs.q_rot, kc, vc, bufs.out, bufs.workspace, window=ly.window,
                               pos_offset=p, rope_table=tab, cache_post_rope=post_rope)
 
+    settle(torch, run)
     for _ in range(warmup):
         run()
     t = Timer(torch)
@@ -238,6 +259,7 @@ def bench_decode_ragged(torch, swg, wl, layer_idx, steps, warmup):
         swg.plamo_attn_decode_ragged(bufs.q_rot, kc, vc, bufs.out, bufs.workspace, window=ly.window,
                                      seq_pos_offsets=sp, max_pos_offset=maxp, rope_table=tab)
 
+    settle(torch, run)
     for _ in range(warmup):
         run()
     t = Timer(torch)
@@ -294,6 +316,7 @@ def bench_gemma_prefill(torch, swg, wl, steps, warmup):
         t_attn[1].record() if t_attn else None
         t_step[1].record() if t_step else None
 
+    settle(torch, step)
     for _ in range(warmup):
         step()
     ts, ta = Timer(torch), Timer(torch)
@@ -328,6 +351,7 @@ def bench_gemma_decode(torch, swg, wl, steps, warmup):
         swg.plamo_attn_decode(bufs.q_rot, kc, vc, bufs.out, bufs.workspace, window=L.window, pos_offset=p,
                               rope_table=None, softmax_scale=L.scale, cache_post_rope=True)
 
+    settle(torch, run)
     for _ in range(warmup):
         run()
     t = Timer(torch)
@@ -371,6 +395,7 @@ def bench_mixer(torch, swg, wl, steps, warmup):
         if ev:
             ev[3].record()
 
+    settle(torch, step)
     for _ in range(warmup):
         step()
     evs = []
@@ -406,6 +431,15 @@ def bench_period(torch, swg, wl, n_steps, fused=False):
     for s in range(min(n_steps, 4)):  # a few distinct token sets, reused cyclically
         news.append([{k: (dev_bf16(torch, x) if x is not None else None) for k, x in wl.draw_new_tokens(s, li).items()}
                      for li in range(len(wl.layers))])
+    def step0():  # step 0 again writes the same token into the same cache slot: no state change
+        for li, ly in enumerate(wl.layers):
+            nt = news[0][li]
+            kc, vc = caches[li]
+            layer.decode(nt["q"], nt["k"], nt["v"], kc, vc, window=ly.window, pos_offset=wl.pos_offset,
+                         rope_table=tabs[li], q_norm_w=nt["wq"], k_norm_w=nt["wk"],
+                         norm_offset=wl.norm_offset, bufs=bufs[li], fused=fused)
+
+    settle(torch, step0)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -685,7 +719,8 @@ def main():
                    "cache_state": "inputs resident in HBM; the 256 MB last-level cache is not flushed "
                                   "between steps, so the prefill finds much of the Q' the append has just "
                                   "written there (as in an append -> prefill pipeline)",
-                   "timing": "ms_per_step = K whole steps / K; roofline from the median HIP-event duration "
+                   "timing": f"{SETTLE_S} s of untimed steps (clocks settle), then W warmup steps, then "
+                             "ms_per_step = K whole steps / K; roofline from the median HIP-event duration "
                              "of the attention launch"},
         "roofline": {"bound": "mfma", "achieved": round(local["attn_tflops"], 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
