@@ -80,6 +80,10 @@ constexpr int kLoadsPerIssue = 4 + kVLoads + (kRotate ? 1 : 0);
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
+// Cache policy of the K/V row loads: non-temporal (every row is read once). Measured on a
+// plain 4 GiB streaming read: ~7.0 TB/s with it, ~6.1-6.2 TB/s without, whatever the grid.
+constexpr int kNonTemporal = 2;
+
 // s_waitcnt vmcnt(n), expcnt / lgkmcnt left alone (gfx9 encoding: vmcnt bits 3:0, 15:14)
 constexpr unsigned wait_vmcnt(int n) { return 0x0F70u | (n & 15) | ((n >> 4) << 14); }
 
@@ -245,14 +249,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
     {
       const bf16_t* row = kc + cache_row(key_in_tile) * kHeadDim;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) kw[s] = *reinterpret_cast<const u32x4*>(row + s * 32 + g * 8);
+      for (int s = 0; s < 4; ++s) kw[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + s * 32 + g * 8));
     }
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) {
       // (the address goes through a named pointer: passing the lambda call straight into
       // the builtin drops this kernel's host-side launch stub)
       const bf16_t* src = vc + cache_row(wave * kSub + v_row[i]) * kHeadDim + v_col[i] * 8;
-      __builtin_amdgcn_global_load_lds(src, vslot + i * 512, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, vslot + i * 512, 16, 0, kNonTemporal);
     }
     if (kRotate) {  // coarse row of the tile (64 pairs, 512 B), copied twice over the 64 lanes
       const float2* crow = a.rope + (kRopeFine + (tb_issue >> 6)) * kHalf + (lane & 31) * 2;
