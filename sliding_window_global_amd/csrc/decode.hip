@@ -80,8 +80,11 @@ constexpr int kLoadsPerIssue = 4 + kVLoads + (kRotate ? 1 : 0);
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-// Cache policy of the K/V row loads: non-temporal (every row is read once). Measured on a
-// plain 4 GiB streaming read: ~7.0 TB/s with it, ~6.1-6.2 TB/s without, whatever the grid.
+// Cache policy of the V row loads: non-temporal (every row is read once, whole rows per
+// load). Measured on a plain 4 GiB streaming read: ~7.0 TB/s with it, ~6.1-6.2 TB/s without,
+// whatever the grid. The K row loads stay cached: each 128-byte line of a K row is fetched
+// by two loads (64 B of 16 rows each), and non-temporal K loads fetched some lines twice
+// from HBM (period local layer 80 MB per launch against 74 MB cached, 67 MB of rows).
 constexpr int kNonTemporal = 2;
 
 // s_waitcnt vmcnt(n), expcnt / lgkmcnt left alone (gfx9 encoding: vmcnt bits 3:0, 15:14)
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
     {
       const bf16_t* row = kc + cache_row(key_in_tile) * kHeadDim;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) kw[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + s * 32 + g * 8));
+      for (int s = 0; s < 4; ++s) kw[s] = *reinterpret_cast<const u32x4*>(row + s * 32 + g * 8);
     }
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) {
