@@ -34,10 +34,11 @@ constexpr int kSub = 16;       // keys per wave per tile
 constexpr int kMaxGroup = 16;
 constexpr float kRescaleLog2 = 8.f;
 
-// Cache policy of the K/V row loads: non-temporal for d = 256 (every row is read once; a
-// plain streaming read measured ~7.0 TB/s with it, ~6.1-6.2 TB/s without, and this decode
-// 6.13 against 5.92-5.95 TB/s), cached for d = 512 (measured 6.09-6.10 non-temporal against
-// 6.19 cached).
+// Cache policy of the V row loads: non-temporal (every row is read once, in whole 16-byte
+// chunks of consecutive rows; a plain streaming read measured ~7.0 TB/s with it, ~6.1-6.2
+// TB/s without). K rows stay cached: each of their 128-byte lines is fetched by two loads,
+// and non-temporal K loads made the decode slower (d = 512: 6.09 against 6.19 TB/s with
+// both non-temporal; 6.88 with cached K and non-temporal V).
 constexpr int kNonTemporal = 2;
 
 constexpr unsigned wait_vmcnt(int n) { return 0x0F70u | (n & 15) | ((n >> 4) << 14); }
@@ -136,16 +137,14 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 2 : 1) void decode_wide_kernel
     {
       const bf16_t* row = kc + cache_row(key_in_tile) * D + g * 8;
 #pragma unroll
-      for (int s = 0; s < W::kKC; ++s)
-        kw[s] = D == 256 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + s * 32))
-                         : *reinterpret_cast<const u32x4*>(row + s * 32);
+      for (int s = 0; s < W::kKC; ++s) kw[s] = *reinterpret_cast<const u32x4*>(row + s * 32);
     }
 #pragma unroll
     for (int i = 0; i < W::kVLoads; ++i) {
       const int p = 64 * i + lane;
       const int v_row = min(p / W::kRC, kSub - 1), v_col = min(p % W::kRC, D / 8 - 1);
       const bf16_t* src = vc + cache_row(wave * kSub + v_row) * D + v_col * 8;
-      __builtin_amdgcn_global_load_lds(src, vslot + i * 512, 16, 0, D == 256 ? kNonTemporal : 0);
+      __builtin_amdgcn_global_load_lds(src, vslot + i * 512, 16, 0, kNonTemporal);
     }
     if (t_issue + 1 < n_tiles) {
       ++t_issue;
