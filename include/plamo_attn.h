@@ -242,7 +242,10 @@ PLAMO_API int plamo_attn_prefill_fused_q(int dtype, const void* q, const void* q
  * the score product.
  * workspace: device scratch of at least plamo_attn_decode_workspace_bytes(...)
  * bytes (split-K partial results); contents on entry do not matter. When that
- * size is 0 (one key range per sequence and KV head) workspace may be NULL.
+ * size is 0 (one key range per sequence and KV head) workspace may be NULL. The
+ * size never decreases as pos_offset grows (the same holds for the ragged and the
+ * one-launch step sizes below), so a workspace sized for the largest position a
+ * caller will pass serves every smaller one.
  * dtype must be PLAMO_BF16; T must be 1. cache_order as given to plamo_kv_append
  * (POST_ROPE: rope_table may be NULL and is not read).
  * ------------------------------------------------------------------------- */

@@ -88,6 +88,9 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 struct DecodePlan {
   int n_split;         // key ranges per (sequence, KV head)
   long long chunk;     // keys per range, a multiple of the key tile
+  int max_split;       // n_split <= max_split, and max_split never decreases as S grows: the
+                       // workspace is sized by it, so a workspace sized for a position serves
+                       // every smaller one
 };
 // min_chunk: keys per range, at least (a multiple of the 64-key tile)
 DecodePlan plan_decode(int B, int Hkv, long long S, bool ragged, long long min_chunk = 256);

@@ -28,14 +28,18 @@ DecodePlan plan_decode(int B, int Hkv, long long S, bool ragged, long long min_c
   chunk = (chunk + kTile - 1) / kTile * kTile;
   DecodePlan p;
   p.chunk = chunk;
-  p.n_split = static_cast<int>((S + chunk - 1) / chunk);
+  p.n_split = static_cast<int>((S + chunk - 1) / chunk);  // <= n (chunk >= S / n)
+  // n never decreases as S grows; n_split can (the chunk is rounded up to whole tiles), so the
+  // workspace is sized by n
+  p.max_split = static_cast<int>(n);
   return p;
 }
 
 size_t decode_workspace_bytes(int B, int Hq, int d, const DecodePlan& plan) {
-  // one split writes the output directly; a split's partial state is acc[d], m, l
-  if (plan.n_split == 1) return 0;
-  return static_cast<size_t>(B) * Hq * plan.n_split * (d + 2) * sizeof(float);
+  // one split writes the output directly; a split's partial state is acc[d], m, l (sized
+  // for max_split ranges, at least n_split)
+  if (plan.max_split == 1) return 0;
+  return static_cast<size_t>(B) * Hq * plan.max_split * (d + 2) * sizeof(float);
 }
 
 size_t decode_step_tickets_bytes(int B, int Hkv) {
@@ -44,7 +48,7 @@ size_t decode_step_tickets_bytes(int B, int Hkv) {
 
 size_t decode_step_workspace_bytes(int B, int Hq, int Hkv, int d, const DecodePlan& plan) {
   // the tickets first (the same place whatever the plan), then the partial states
-  if (plan.n_split == 1) return 0;
+  if (plan.max_split == 1) return 0;
   return decode_step_tickets_bytes(B, Hkv) + decode_workspace_bytes(B, Hq, d, plan);
 }
 

@@ -139,6 +139,14 @@ int main() {
                              nullptr), -3, "attn_decode workspace - 1");
     want(plamo_attn_decode(1, A, A, A, cd - 1, A, A, ws, B, 1, Hq, Hkv, d, window, pos, A, tbd, 0.088f, order,
                            nullptr), -1, "attn_decode cap - 1");
+    // a workspace sized for a later position serves this one
+    const size_t ws_later = plamo_attn_decode_workspace_bytes(B, Hq, Hkv, d, window, pos + 1 + static_cast<long long>(next() % 5000));
+    if (ws_later < ws) {
+      std::fprintf(stderr, "decode workspace shrinks with the position (pos %lld)\n", pos);
+      ++g_bad;
+    }
+    want(plamo_attn_decode(1, A, A, A, window ? cd : cd + 5000, A, ws_later ? A : nullptr, ws_later, B, 1, Hq, Hkv, d,
+                           window, pos, A, tbd, 0.088f, order, nullptr), 0, "attn_decode, later workspace");
     want(plamo_attn_decode_noalloc(1, A, A, A, cd, A, B, 1, Hq, Hkv, d, window, pos, A, tbd, 0.088f, order, nullptr),
          ws > PLAMO_DECODE_SCRATCH_BYTES ? -3 : 0, "attn_decode_noalloc");
     const size_t wss = plamo_decode_step_workspace_bytes(B, Hq, Hkv, d, window, pos);

@@ -83,6 +83,24 @@ def test_decode_workspace_sizes(lib):
     assert n > 0 and n % (514 * 4 * 8 * 32) == 0 and n // (514 * 4 * 8 * 32) > 1
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,d,window", [(8, 64, 8, 128, 0), (8, 64, 8, 128, 2048), (1, 8, 2, 128, 0),
+                                                 (64, 64, 8, 128, 0), (3, 32, 4, 512, 0), (5, 32, 16, 256, 1024)])
+def test_decode_workspace_sizes_never_shrink(lib, B, Hq, Hkv, d, window):
+    """A workspace sized for a position serves every smaller one: the three size queries are
+    non-decreasing in the position (the key-range count can fall when a range is rounded up to
+    whole tiles; the workspace is sized by the count before that rounding)."""
+    queries = [lib.plamo_attn_decode_workspace_bytes, lib.plamo_attn_decode_ragged_workspace_bytes]
+    if d == 128:
+        queries.append(lib.plamo_decode_step_workspace_bytes)
+    positions = list(range(0, 9000)) + list(range(9000, 300000, 97))
+    for f in queries:
+        prev = 0
+        for p in positions:
+            n = f(B, Hq, Hkv, d, window, p)
+            assert n >= prev, (f.__name__, p, prev, n)
+            prev = n
+
+
 def _append(lib, **over):
     a = dict(dtype=BF16, q=FAKE, k=FAKE, v=FAKE, wq=None, wk=None, c=1.0, eps=1e-6, v_norm=0, q_out=FAKE,
              k_rot=None, v_t=None, kc=None, vc=None, cap=0, B=1, T=4, Hq=8, Hkv=2, d=128, window=16,
