@@ -108,20 +108,26 @@ def bench_prefill(torch, swg, wl, steps, warmup, norm_offset, fuse_q=False):
     vc = torch.empty_like(kc)
     bufs = layer.PrefillBuffers(wl.B, wl.T, wl.Hq, wl.Hkv, wl.d, torch.bfloat16)
 
-    def step(t_step=None, t_attn=None):
-        if t_step:
-            t_step[0].record()
+    def append():
         swg.plamo_kv_append(q if not fuse_q else None, k, v, bufs.q_rot if not fuse_q else None,
                             window=wl.window, pos_offset=0, rope_table=tab, q_norm_w=wq, k_norm_w=wk,
                             norm_offset=norm_offset, k_rot_out=bufs.k_rot, v_t_out=bufs.v_t, k_cache=kc,
                             v_cache=vc)
-        if t_attn:
-            t_attn[0].record()
+
+    def attention():
         if fuse_q:
             swg.plamo_attn_prefill_fused_q(q, bufs.k_rot, bufs.v_t, bufs.out, window=wl.window, rope_table=tab,
                                            q_norm_w=wq, norm_offset=norm_offset)
         else:
             swg.plamo_attn_prefill(bufs.q_rot, bufs.k_rot, bufs.v_t, bufs.out, window=wl.window)
+
+    def step(t_step=None, t_attn=None):
+        if t_step:
+            t_step[0].record()
+        append()
+        if t_attn:
+            t_attn[0].record()
+        attention()
         if t_attn:
             t_attn[1].record()
         if t_step:
@@ -142,9 +148,36 @@ def bench_prefill(torch, swg, wl, steps, warmup, norm_offset, fuse_q=False):
     # whole-step figure: the K steps back to back (first step's start to last step's end) / K
     ms_step = ts.pairs[0][0].elapsed_time(ts.pairs[-1][1]) / steps
     flops = wl.flops()
-    return dict(workload=wl.name, flops=flops, ms_per_step=ms_step, ms_attn=ms_attn,
-                ms_step_median=ts.median_ms(), step_tflops=flops / ms_step / 1e9, attn_tflops=flops / ms_attn / 1e9,
-                wall_ms_per_step=wall / steps * 1e3)
+    out = dict(workload=wl.name, flops=flops, ms_per_step=ms_step, ms_attn=ms_attn,
+               ms_step_median=ts.median_ms(), step_tflops=flops / ms_step / 1e9, attn_tflops=flops / ms_attn / 1e9,
+               wall_ms_per_step=wall / steps * 1e3)
+    out.update(cold_cache(torch, append, attention, steps))
+    return out
+
+
+def cold_summary(r):
+    """The cold-cache figures of a bench_prefill result, with their TFLOP/s."""
+    return {"cold_ms_append": r["cold_ms_append"], "cold_ms_attn": r["cold_ms_attn"],
+            "cold_ms_step": r["cold_ms_step"], "cold_attn_tflops": r["flops"] / r["cold_ms_attn"] / 1e9,
+            "cold_step_tflops": r["flops"] / r["cold_ms_step"] / 1e9}
+
+
+def cold_cache(torch, append, attention, steps):
+    """The step with the caches cold: a 512 MiB buffer (twice the 256 MB last-level cache) is
+    rewritten before the append and again before the attention, so that each kernel reads its
+    inputs from HBM; medians over `steps` repetitions of each kernel's own HIP-event time."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    t_app, t_att = Timer(torch), Timer(torch)
+    for _ in range(steps):
+        for fn, timer in ((append, t_app), (attention, t_att)):
+            flush.zero_()
+            a, b = timer.span()
+            a.record()
+            fn()
+            b.record()
+    ms_app, ms_att = t_app.median_ms(), t_att.median_ms()
+    del flush
+    return dict(cold_ms_append=ms_app, cold_ms_attn=ms_att, cold_ms_step=ms_app + ms_att)
 
 
 def bench_chunked_prefill(torch, swg, wl, chunk, steps, warmup):
@@ -623,12 +656,14 @@ def main():
         log("[bench] local prefill T=8192 W=2048")
         local = bench_prefill(torch, swg, LOCAL_PREFILL, args.steps, args.warmup, LOCAL_PREFILL.norm_offset)
         log(f"[bench]   {local}")
+        extra["prefill_local_cold_cache"] = cold_summary(local)
         log("[bench] local prefill, Q normalised and rotated inside the attention kernel")
         u = bench_prefill(torch, swg, LOCAL_PREFILL, args.steps, args.warmup, LOCAL_PREFILL.norm_offset,
                           fuse_q=True)
         log(f"[bench]   {u}")
         extra["prefill_local_fused_q"] = {k: u[k] for k in ("workload", "ms_per_step", "ms_attn", "step_tflops",
                                                              "attn_tflops")}
+        extra["prefill_local_fused_q"].update(cold_summary(u))
     if only in ("", "prefill_global"):
         log("[bench] global prefill T=32768 YaRN")
         g = bench_prefill(torch, swg, GLOBAL_PREFILL, max(3, args.steps // 4), max(1, args.warmup // 2),
@@ -636,6 +671,7 @@ def main():
         log(f"[bench]   {g}")
         extra["prefill_global"] = {k: g[k] for k in ("workload", "ms_per_step", "ms_attn", "step_tflops", "attn_tflops")}
         extra["prefill_global"]["frac_mfma"] = g["attn_tflops"] / PEAK_BF16_TFLOPS
+        extra["prefill_global"].update(cold_summary(g))
     if only in ("", "prefill_chunked"):
         for wl, chunk, n in ((LOCAL_PREFILL, 2048, args.steps), (GLOBAL_PREFILL, 8192, max(3, args.steps // 4))):
             log(f"[bench] chunked prefill {wl.name} chunk={chunk}")
@@ -718,7 +754,8 @@ def main():
                    "step": "kv_append + attn_prefill",
                    "cache_state": "inputs resident in HBM; the 256 MB last-level cache is not flushed "
                                   "between steps, so the prefill finds much of the Q' the append has just "
-                                  "written there (as in an append -> prefill pipeline)",
+                                  "written there (as in an append -> prefill pipeline); extra."
+                                  "prefill_local_cold_cache has each kernel after a 512 MiB flush",
                    "timing": f"{SETTLE_S} s of untimed steps (clocks settle), then W warmup steps, then "
                              "ms_per_step = K whole steps / K; roofline from the median HIP-event duration "
                              "of the attention launch"},
