@@ -293,23 +293,50 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void prefill_wide_kernel(Prefill
     if (step + 1 < n_steps) run_step(step + 1, ks1, vs1, ks0, vs0);
   }
 
-  // ---- normalise and store: lane writes dims 16 dt + 4 g .. +3 of its row -------------
+  // ---- normalise, then store whole rows through LDS ----------------------------------
+  // The lane holds dims 16 dt + 4 g .. +3 of its row: stored as they are, every store would
+  // write 32 B into each of 16 rows. Instead each wave stages one 16-row block at a time in
+  // its share of the four operand buffers (with 8 waves one eighth of them: 16 whole rows at
+  // d = 256 and at d = 512), 16-byte chunk c of row n at chunk c ^ n (conflict-free writes and
+  // row reads), and writes whole rows with 16-byte stores.
+  block_barrier();  // every wave is past its last operand read
+  constexpr int kPerBuf = kWaves / 4;  // waves sharing one operand buffer
+  static_assert(kWaves % 4 == 0 && 16 * D <= kSub / kPerBuf, "a wave stages 16 whole rows in its share");
+  const int bi = wave / kPerBuf;
+  bf16_t* const stage = (bi == 0 ? ks0 : bi == 1 ? ks1 : bi == 2 ? vs0 : vs1) + (wave % kPerBuf) * (kSub / kPerBuf);
+  constexpr int kRowChunks = D / 8;             // 16-byte chunks per row
+  constexpr int kRowsPerRead = 64 / kRowChunks;  // rows one 64-lane read covers
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     float l = l_run[nb];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    const int row = r0 + nb * 16 + n;
-    if (row < n_rows) {
-      const float inv = 1.f / l;
-      bf16_t* dst = static_cast<bf16_t*>(a.out) + ((static_cast<long long>(b) * a.T + row) * a.Hq + hq) * D + 4 * g;
+    const float inv = 1.f / l;  // (rows past n_rows: never stored)
 #pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) {
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[nb][dt][0] * inv, oacc[nb][dt][1] * inv);
-        w[1] = pack_bf16x2(oacc[nb][dt][2] * inv, oacc[nb][dt][3] * inv);
-        *reinterpret_cast<u32x2*>(dst + dt * 16) = w;
-      }
+    for (int dt = 0; dt < kDT; ++dt) {
+      u32x2 w;
+      w[0] = pack_bf16x2(oacc[nb][dt][0] * inv, oacc[nb][dt][1] * inv);
+      w[1] = pack_bf16x2(oacc[nb][dt][2] * inv, oacc[nb][dt][3] * inv);
+      const int c = 2 * dt + (g >> 1);
+      *reinterpret_cast<u32x2*>(stage + n * D + (c ^ n) * 8 + (g & 1) * 4) = w;
+    }
+    // the wave's own staging writes are done before its reads (no other wave touches them)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    bf16_t* const out_base = static_cast<bf16_t*>(a.out) + static_cast<long long>(hq) * D;
+    const int c = lane % kRowChunks;
+#pragma unroll
+    for (int j = 0; j < 16 / kRowsPerRead; ++j) {
+      const int r = j * kRowsPerRead + lane / kRowChunks;  // row of the block, chunk c of it
+      const u32x4 w = *reinterpret_cast<const u32x4*>(stage + r * D + (c ^ r) * 8);
+      const int row = r0 + nb * 16 + r;
+      if (row < n_rows)  // (not read again by this kernel: streamed past the caches)
+        __builtin_nontemporal_store(
+            w, reinterpret_cast<u32x4*>(out_base + (static_cast<long long>(b) * a.T + row) * a.Hq * D + c * 8));
+    }
+    if (nb + 1 < NB) {  // the reads are done before the next block's writes
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
