@@ -7,7 +7,8 @@
 // block  = 256 rows of x (m) x 256 rows of W (n), 8 waves in a 4 (m) x 2 (n) grid, each wave
 //          64 m x 128 n = 2 x 4 blocks of v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators).
 //          W fragments are the MFMA A operand (32 n x 16 k), x fragments the B operand, so a
-//          lane's accumulators hold one m and runs of 4 consecutive n: 8-byte stores.
+//          lane's accumulators hold one m and runs of 4 consecutive n; the output goes out
+//          through LDS as whole 256-byte row segments.
 // tiles  = 64 k per step: W and x tiles 256 x 64 (32 KiB each), double buffered (128 KiB,
 //          one block per CU), copied global -> LDS by buffer loads with the LDS bit (a
 //          resource per operand block bounds every read; rows past M or N read 0). LDS rows
@@ -144,27 +145,46 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     }
   }
 
-  // store: accumulator (i, j) register e holds m = m0 + wm*64 + j*32 + lane % 32 and
-  // n = n0 + wn*128 + i*32 + (e/4)*8 + (lane/32)*4 + e%4; column n belongs to output part p
-  // (parts are multiples of 8 wide, so a run of 4 never straddles two parts)
+  // store through LDS: accumulator (i, j) register e holds m = wm*64 + j*32 + lane % 32 and
+  // n = wn*128 + i*32 + (e/4)*8 + (lane/32)*4 + e%4 of the block tile. Stored as they are,
+  // every store would write 16 B into each of 32 rows; instead each wave stages its 64 x 128
+  // tile (16 KiB, one eighth of the operand buffers, which the last barrier freed), 16-byte
+  // chunk c of row r at chunk c ^ (r mod 16), and writes 256-byte row segments, 16 bytes per
+  // lane. Column n belongs to output part p (parts are multiples of 8 wide, so a 16-byte
+  // chunk never straddles two parts).
+  bf16_t* const stage = (wave < 2 ? as0 : wave < 4 ? as1 : wave < 6 ? bs0 : bs1) + (wave & 1) * (64 * 128);
+  static_assert(BN * BK / 2 == 64 * 128 && BM * BK / 2 == 64 * 128, "a wave stages 64 x 128 in half a buffer");
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const long long m = m0 + wm * 64 + j * 32 + (lane & 31);
-    if (m >= a.M) continue;
+    const int r = j * 32 + (lane & 31);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const long long n = n0 + wn * 128 + i * 32 + q * 8 + (lane >> 5) * 4;
-        if (n >= N) continue;
-        const int p = n < a.part_end[0] ? 0 : (n < a.part_end[1] ? 1 : 2);
-        const long long first = p == 0 ? 0 : a.part_end[p - 1];
-        const long long width = a.part_end[p] - first;
         u32x2 w;
         w[0] = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
         w[1] = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-        *reinterpret_cast<u32x2*>(static_cast<bf16_t*>(a.y[p]) + m * width + (n - first)) = w;
+        const int c = i * 4 + q;
+        *reinterpret_cast<u32x2*>(stage + r * 128 + (c ^ (r & 15)) * 8 + (lane >> 5) * 4) = w;
       }
+  }
+  // the wave's own staging writes are done before its reads (no other wave touches them)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  const int c = lane & 15;
+  const long long n = n0 + wn * 128 + c * 8;
+  if (n < N) {
+    const int p = n < a.part_end[0] ? 0 : (n < a.part_end[1] ? 1 : 2);
+    const long long first = p == 0 ? 0 : a.part_end[p - 1];
+    const long long width = a.part_end[p] - first;
+    bf16_t* const dst = static_cast<bf16_t*>(a.y[p]) + (n - first);
+#pragma unroll
+    for (int k4 = 0; k4 < 16; ++k4) {
+      const int r = k4 * 4 + (lane >> 4);  // row of the wave's tile, chunk c of it
+      const long long m = m0 + wm * 64 + r;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(stage + r * 128 + (c ^ (r & 15)) * 8);
+      if (m < a.M) *reinterpret_cast<u32x4*>(dst + m * width) = w;
+    }
   }
 }
 
