@@ -62,6 +62,37 @@ def gpu_kw(L: GemmaLayer, wq, wk):
                 softmax_scale=L.scale, cache_post_rope=True, v_norm=True)
 
 
+@pytest.mark.parametrize("L,Hq,Hkv,window", [(GEMMA_LOCAL_LAYER, 4, 2, 128), (GEMMA_GLOBAL_LAYER, 4, 1, 0)],
+                         ids=["d256", "d512_p025"])
+def test_wide_prefill_writes_exactly_its_output(L, Hq, Hkv, window):
+    """The wide prefill's output sits at the front of a NaN-filled buffer 1024 elements longer:
+    every element written (ragged last block: T = 300), nothing past it (each wave stages its
+    16-row blocks in LDS and stores whole rows), every row of both sequences against the oracle."""
+    import dataclasses
+    L = dataclasses.replace(L, Hq=Hq, Hkv=Hkv, window=window)
+    B, T, d = 2, 300, L.d
+    dr = Draw(9090 + d, True)
+    q, k, v = L.draw_tokens(dr, B, T)
+    wq, wk = L.draw_gains(dr)
+    cap = window if window else T
+    kc = torch.full((B, Hkv, cap, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    bufs = layer.PrefillBuffers(B, T, Hq, Hkv, d, torch.bfloat16, "cuda", window, 0)
+    n = B * T * Hq * d
+    canary = torch.full((n + 1024,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    bufs.out = canary[:n].view(B, T, Hq, d)
+    kd = dev(k)
+    layer.prefill(dev(q), kd, kd if L.kv_shared else dev(v), window=window, rope_table=table_for(L, T + 64),
+                  k_cache=kc, v_cache=vc, bufs=bufs, **gpu_kw(L, wq, wk))
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(canary[n:]).all()), "write past the output"
+    assert not bool(torch.isnan(bufs.out).any()), "output element left unwritten"
+    for b in range(B):
+        cache = LayerKVCache(Hkv, d, window, post_rope=True)
+        ref = oracle_step(L, q[b], k[b], v[b], cache, wq, wk)
+        assert_parity(host(bufs.out[b]), ref, TOL_BF16, f"d={d} sequence {b}")
+
+
 @pytest.mark.parametrize("L", [GEMMA_LOCAL_LAYER, GEMMA_GLOBAL_LAYER], ids=["d256", "d512_p025"])
 def test_wide_rope_table(L):
     """Coarse x fine product equals exp(i p w_j) from the oracle's frequencies; with p-RoPE the

@@ -49,6 +49,49 @@ def test_linear_matches_fp64_matmul(M, N, K):
     assert_parity(host(y)[rows], ref, TOL_BF16, f"linear {M}x{N}x{K}")
 
 
+def _canaried(n, shape):
+    """A view of the first n elements of a NaN-filled buffer 1024 elements longer, and the buffer."""
+    buf = torch.full((n + 1024,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    return buf[:n].view(*shape), buf
+
+
+@pytest.mark.parametrize("M,N,K", [(77, 264, 128), (300, 1536, 256), (1, 1024, 5120), (513, 520, 64)])
+def test_linear_writes_exactly_its_output(M, N, K):
+    """Every output element is written and nothing past the output: y sits at the front of a
+    NaN-filled buffer, whose tail must stay NaN, with ragged row and column tiles (the epilogue
+    stages each wave's tile in LDS and writes 16-byte chunks of whole rows); every row checked."""
+    g = torch.Generator(device="cuda").manual_seed(7 * M + N)
+    x = torch.randn((M, K), generator=g, device="cuda").bfloat16()
+    w = (torch.randn((N, K), generator=g, device="cuda") / math.sqrt(K)).bfloat16()
+    y, buf = _canaried(M * N, (M, N))
+    swg.plamo_linear(x, w, y)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(buf[M * N:]).all()), "write past the output"
+    assert not bool(torch.isnan(y).any()), "output element left unwritten"
+    assert_parity(host(y), host(x) @ host(w).T, TOL_BF16, f"linear {M}x{N}x{K}, all rows")
+
+
+def test_qkv_projection_writes_exactly_its_outputs():
+    """The Q | K | V split of the fused projection at a ragged shape: each part written whole,
+    nothing past any of them, every row checked."""
+    M, D, Hq, Hkv, d = 301, 256, 8, 2, 128
+    g = torch.Generator(device="cuda").manual_seed(4711)
+    u = torch.randn((M, D), generator=g, device="cuda").bfloat16()
+    w = (torch.randn(((Hq + 2 * Hkv) * d, D), generator=g, device="cuda") / math.sqrt(D)).bfloat16()
+    q, qb = _canaried(M * Hq * d, (M, Hq, d))
+    k, kb = _canaried(M * Hkv * d, (M, Hkv, d))
+    v, vb = _canaried(M * Hkv * d, (M, Hkv, d))
+    swg.plamo_qkv_projection(u, w, q, k, v)
+    torch.cuda.synchronize()
+    for name, t, buf in (("Q", q, qb), ("K", k, kb), ("V", v, vb)):
+        assert bool(torch.isnan(buf[t.numel():]).all()), f"write past the {name} part"
+        assert not bool(torch.isnan(t).any()), f"{name} element left unwritten"
+    full = host(u) @ host(w).T
+    assert_parity(host(q).reshape(M, -1), full[:, :Hq * d], TOL_BF16, "Q part, all rows")
+    assert_parity(host(k).reshape(M, -1), full[:, Hq * d:(Hq + Hkv) * d], TOL_BF16, "K part, all rows")
+    assert_parity(host(v).reshape(M, -1), full[:, (Hq + Hkv) * d:], TOL_BF16, "V part, all rows")
+
+
 @pytest.mark.parametrize("M,D,Hq,Hkv", [(8192, 5120, 64, 8), (301, 256, 8, 2), (3, 5120, 64, 8)])
 def test_qkv_projection_matches_fp64(M, D, Hq, Hkv):
     """One GEMM against the fused weight, its output columns split into Q | K | V at Hq d and

@@ -181,6 +181,30 @@ def test_prefill_bf16_small(B, T, Hq, Hkv, W):
     assert_parity(host(bufs.out), ref, TOL_BF16, f"B{B} T{T} Hq{Hq} Hkv{Hkv} W{W}")
 
 
+@pytest.mark.parametrize("fuse_q", [False, True], ids=["unfused", "fused_q"])
+def test_prefill_writes_exactly_its_output(fuse_q):
+    """The output sits at the front of a NaN-filled buffer 1024 elements longer: every element
+    of it written (ragged last 128-row block: T = 300), nothing past it (the epilogue stages
+    each wave's rows in LDS and stores whole rows), every row against the oracle."""
+    B, T, Hq, Hkv, W, d = 2, 300, 8, 2, 128, 128
+    dr = Draw(31337, True)
+    inp = dict(q=dr.normal((B, T, Hq, d)), k=dr.normal((B, T, Hkv, d)), v=dr.normal((B, T, Hkv, d)),
+               wq=dr.normal((d,), 0.02), wk=dr.normal((d,), 0.02))
+    rope = Rope(1e4)
+    bufs = layer.PrefillBuffers(B, T, Hq, Hkv, d, torch.bfloat16, "cuda", W, 0)
+    n = B * T * Hq * d
+    canary = torch.full((n + 1024,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    bufs.out = canary[:n].view(B, T, Hq, d)
+    layer.prefill(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), window=W, rope_table=rope_table(rope, T + 64),
+                  q_norm_w=dev(inp["wq"]), k_norm_w=dev(inp["wk"]), norm_offset=1.0, bufs=bufs, fuse_q=fuse_q)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(canary[n:]).all()), "write past the output"
+    assert not bool(torch.isnan(bufs.out).any()), "output element left unwritten"
+    ref = oracle_prefill(inp["q"], inp["k"], inp["v"], window=W, rope=rope, wq=inp["wq"], wk=inp["wk"],
+                         norm_offset=1.0)
+    assert_parity(host(bufs.out), ref, TOL_BF16, f"canaried output fuse_q={fuse_q}")
+
+
 def _sample_rows(T, n_mid, seed):
     rng = np.random.default_rng(seed)
     fixed = [0, 1, 63, 64, 127, 128, 2047, 2048, 2049, T // 2, T - 129, T - 128, T - 2, T - 1]
