@@ -4,21 +4,24 @@
 // output columns are split into Q | K | V; the epilogue writes each part to its own tensor.
 // §4.5: the output projection (K = Hq d, N = hidden).
 //
-// block  = 256 rows of x (m) x 256 rows of W (n), 8 waves in a 4 (m) x 2 (n) grid, each wave
-//          64 m x 128 n = 2 x 4 blocks of v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators).
-//          W fragments are the MFMA A operand (32 n x 16 k), x fragments the B operand, so a
-//          lane's accumulators hold one m and runs of 4 consecutive n; the output goes out
-//          through LDS as whole 256-byte row segments.
-// tiles  = 64 k per step: W and x tiles 256 x 64 (32 KiB each), double buffered (128 KiB,
-//          one block per CU), copied global -> LDS by buffer loads with the LDS bit (a
-//          resource per operand block bounds every read; rows past M or N read 0). LDS rows
-//          are 128 B; the 16-byte chunk c of row r sits at position c ^ ((r >> 1) & 7), so
-//          that the eight lanes of a row read one contiguous 128 B of global memory and the
-//          16 rows of a quarter-wave's fragment read fall into distinct banks. The next
+// block  = 256 rows of x (m) x BN rows of W (n), BN = 256 or 320, 8 waves in a 4 (m) x 2 (n)
+//          grid, each wave 64 m x BN/2 n = 2 x BN/64 blocks of v_mfma_f32_32x32x16_bf16 (128 or
+//          160 fp32 accumulators). W fragments are the MFMA A operand (32 n x 16 k), x fragments
+//          the B operand, so a lane's accumulators hold one m and runs of 4 consecutive n; the
+//          output goes out through LDS as whole row segments. The launch takes the column tile
+//          with the fewer rounds of one block per CU, weighted by its width (a 5120-wide output:
+//          16 tiles of 320 instead of 20 of 256, 2 rounds instead of 2.5 at M = 8192).
+// tiles  = 64 k per step: W tiles BN x 64 (32 or 40 KiB) and x tiles 256 x 64 (32 KiB), double
+//          buffered (128 or 144 KiB, one block per CU), copied global -> LDS by buffer loads with
+//          the LDS bit (a resource per operand block bounds every read; rows past M or N read
+//          0). LDS rows are 128 B; the 16-byte chunk c of row r sits at position c ^ ((r >> 1) &
+//          7), so that the eight lanes of a row read one contiguous 128 B of global memory and
+//          the 16 rows of a quarter-wave's fragment read fall into distinct banks. The next
 //          sub-step's fragments are read while the current sub-step's MFMAs run.
-// Measured on the sublayer shapes: ~1.0-1.1 PFLOP/s; the same kernel without the tile copies
-// (timing only) runs ~1.5-1.8, a 4-stage copy ring and an XCD-grouped tile order changed
-// nothing, so the LDS traffic of the copies plus the operand reads is what limits it.
+// Measured on the sublayer shapes: ~1.2-1.26 PFLOP/s; the same kernel without the tile copies
+// (timing only) ran ~1.5-1.8 before the output went through LDS, a 4-stage copy ring and an
+// XCD-grouped tile order changed nothing, so the LDS traffic of the copies plus the operand
+// reads is what limits it.
 // Requirements (checked by the caller): K % 64 == 0, every output part's width % 8 == 0.
 #include "common.h"
 #include "kernels.h"
@@ -28,7 +31,6 @@ namespace plamo {
 namespace {
 
 constexpr int BM = 256;  // rows of x per block
-constexpr int BN = 256;  // rows of W per block
 constexpr int BK = 64;   // k per step (8 chunks of 8)
 constexpr int kChunks = BK / 8;
 constexpr int kThreads = 512;
@@ -43,7 +45,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
+// BN: rows of W per block, 256 or 320; a wave covers 64 m x BN/2 n, NI = BN/64 MFMA blocks
+// of 32 n (320 = 2 x 5 x 32: a 5120-wide output in 16 column tiles instead of 20)
+template <int BN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr int NI = BN / 64;   // 32-wide n blocks per wave
+  constexpr int WN = BN / 2;    // n per wave
   __shared__ __attribute__((aligned(1024))) bf16_t as0[BN * BK];
   __shared__ __attribute__((aligned(1024))) bf16_t as1[BN * BK];
   __shared__ __attribute__((aligned(1024))) bf16_t bs0[BM * BK];
@@ -87,9 +94,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     issue(x_rsrc, BM / kWaves, step, bbuf);
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[NI][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -104,16 +111,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     return *reinterpret_cast<const bf16x8*>(buf + (r * kChunks + (c ^ swz(r))) * 8);
   };
   auto compute = [&](const bf16_t* abuf, const bf16_t* bbuf) __attribute__((always_inline)) {
-    bf16x8 af[2][4], bfr[2][2];
+    bf16x8 af[2][NI], bfr[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[0][i] = frag(abuf, wn * 128 + i * 32, 0);
+    for (int i = 0; i < NI; ++i) af[0][i] = frag(abuf, wn * WN + i * 32, 0);
 #pragma unroll
     for (int j = 0; j < 2; ++j) bfr[0][j] = frag(bbuf, wm * 64 + j * 32, 0);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
       if (s + 1 < BK / 16) {  // next sub-step's fragments go out before this one's MFMAs
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[(s + 1) & 1][i] = frag(abuf, wn * 128 + i * 32, s + 1);
+        for (int i = 0; i < NI; ++i) af[(s + 1) & 1][i] = frag(abuf, wn * WN + i * 32, s + 1);
 #pragma unroll
         for (int j = 0; j < 2; ++j) bfr[(s + 1) & 1][j] = frag(bbuf, wm * 64 + j * 32, s + 1);
       }
@@ -121,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
       // group waits for its own fragments)
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bfr[s & 1][j], acc[i][j], 0, 0, 0);
@@ -146,44 +153,57 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   }
 
   // store through LDS: accumulator (i, j) register e holds m = wm*64 + j*32 + lane % 32 and
-  // n = wn*128 + i*32 + (e/4)*8 + (lane/32)*4 + e%4 of the block tile. Stored as they are,
-  // every store would write 16 B into each of 32 rows; instead each wave stages its 64 x 128
-  // tile (16 KiB, one eighth of the operand buffers, which the last barrier freed), 16-byte
-  // chunk c of row r at chunk c ^ (r mod 16), and writes 256-byte row segments, 16 bytes per
-  // lane. Column n belongs to output part p (parts are multiples of 8 wide, so a 16-byte
-  // chunk never straddles two parts).
-  bf16_t* const stage = (wave < 2 ? as0 : wave < 4 ? as1 : wave < 6 ? bs0 : bs1) + (wave & 1) * (64 * 128);
-  static_assert(BN * BK / 2 == 64 * 128 && BM * BK / 2 == 64 * 128, "a wave stages 64 x 128 in half a buffer");
+  // n = wn*WN + i*32 + (e/4)*8 + (lane/32)*4 + e%4 of the block tile. Stored as they are,
+  // every store would write 16 B into each of 32 rows; instead each wave stages 32 rows x WN
+  // at a time (8 KiB at BN = 256, 10 KiB at 320: a quarter of one W buffer, free after the
+  // last barrier) and writes whole row segments of WN columns, 16 bytes per lane (at BN = 256
+  // the 16-byte chunk c of row r sits at c ^ (r mod 16), which keeps the staging writes free
+  // of bank conflicts). Column n belongs to output part p (parts are multiples of 8 wide, so
+  // a 16-byte chunk never straddles two parts).
+  constexpr int CW = WN / 8;            // 16-byte chunks per staged row
+  constexpr int kRowsPerRead = 64 / CW;  // rows one 64-lane read covers (16 or 20 lanes each)
+  static_assert(4 * 32 * WN == BN * BK, "four waves stage 32 rows x WN in one W buffer");
+  auto phys = [](int r, int c) __attribute__((always_inline)) { return CW == 16 ? (c ^ (r & 15)) : c; };
+  bf16_t* const stage = (wave < 4 ? as0 : as1) + (wave & 3) * (32 * WN);
+  const int c = lane % CW;
+  const int r_lane = lane / CW;  // row of the read within its group (lanes past the last group idle)
+  const long long n = n0 + wn * WN + c * 8;
+  const bool col_ok = r_lane < kRowsPerRead && n < N;
+  int p = 0;
+  long long first = 0, width = 0;
+  if (col_ok) {
+    p = n < a.part_end[0] ? 0 : (n < a.part_end[1] ? 1 : 2);
+    first = p == 0 ? 0 : a.part_end[p - 1];
+    width = a.part_end[p] - first;
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int r = j * 32 + (lane & 31);
+    const int r = lane & 31;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         u32x2 w;
         w[0] = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
         w[1] = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-        const int c = i * 4 + q;
-        *reinterpret_cast<u32x2*>(stage + r * 128 + (c ^ (r & 15)) * 8 + (lane >> 5) * 4) = w;
+        *reinterpret_cast<u32x2*>(stage + r * WN + phys(r, i * 4 + q) * 8 + (lane >> 5) * 4) = w;
       }
-  }
-  // the wave's own staging writes are done before its reads (no other wave touches them)
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-  const int c = lane & 15;
-  const long long n = n0 + wn * 128 + c * 8;
-  if (n < N) {
-    const int p = n < a.part_end[0] ? 0 : (n < a.part_end[1] ? 1 : 2);
-    const long long first = p == 0 ? 0 : a.part_end[p - 1];
-    const long long width = a.part_end[p] - first;
-    bf16_t* const dst = static_cast<bf16_t*>(a.y[p]) + (n - first);
+    // the wave's own staging writes are done before its reads (no other wave touches them)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    if (col_ok) {
+      bf16_t* const dst = static_cast<bf16_t*>(a.y[p]) + (n - first);
 #pragma unroll
-    for (int k4 = 0; k4 < 16; ++k4) {
-      const int r = k4 * 4 + (lane >> 4);  // row of the wave's tile, chunk c of it
-      const long long m = m0 + wm * 64 + r;
-      const u32x4 w = *reinterpret_cast<const u32x4*>(stage + r * 128 + (c ^ (r & 15)) * 8);
-      if (m < a.M) *reinterpret_cast<u32x4*>(dst + m * width) = w;
+      for (int k = 0; k < (32 + kRowsPerRead - 1) / kRowsPerRead; ++k) {
+        const int rr = k * kRowsPerRead + r_lane;  // staged row, chunk c of it
+        const long long m = m0 + wm * 64 + j * 32 + rr;
+        if (rr < 32 && m < a.M)
+          *reinterpret_cast<u32x4*>(dst + m * width) = *reinterpret_cast<const u32x4*>(stage + rr * WN + phys(rr, c) * 8);
+      }
+    }
+    if (j == 0) {  // the reads are done before the next half's writes
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
@@ -191,8 +211,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>((a.N + BN - 1) / BN), static_cast<unsigned>((a.M + BM - 1) / BM));
-  hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(kThreads), 0, stream, a);
+  // Column tiles of 256 or 320: the one whose rounds of one block per CU times its width is
+  // smaller (e.g. N = 5120, M = 8192: 640 blocks of 256 are 2.5 rounds, 512 blocks of 320 are 2;
+  // a tie goes to 320, which reads fewer operand bytes per FLOP).
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const long long mb = (a.M + BM - 1) / BM;
+  auto cost = [&](long long bn) { return ((a.N + bn - 1) / bn * mb + cus - 1) / cus * bn; };
+  if (cost(320) <= cost(256)) {
+    const dim3 grid(static_cast<unsigned>((a.N + 319) / 320), static_cast<unsigned>(mb));
+    hipLaunchKernelGGL(gemm_bf16_kernel<320>, grid, dim3(kThreads), 0, stream, a);
+  } else {
+    const dim3 grid(static_cast<unsigned>((a.N + 255) / 256), static_cast<unsigned>(mb));
+    hipLaunchKernelGGL(gemm_bf16_kernel<256>, grid, dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -55,11 +55,13 @@ def _canaried(n, shape):
     return buf[:n].view(*shape), buf
 
 
-@pytest.mark.parametrize("M,N,K", [(77, 264, 128), (300, 1536, 256), (1, 1024, 5120), (513, 520, 64)])
+@pytest.mark.parametrize("M,N,K", [(77, 264, 128), (300, 1536, 256), (1, 1024, 5120), (513, 520, 64),
+                                   (8000, 5112, 64)])
 def test_linear_writes_exactly_its_output(M, N, K):
     """Every output element is written and nothing past the output: y sits at the front of a
     NaN-filled buffer, whose tail must stay NaN, with ragged row and column tiles (the epilogue
-    stages each wave's tile in LDS and writes 16-byte chunks of whole rows); every row checked."""
+    stages each wave's tile in LDS and writes 16-byte chunks of whole rows); every row checked.
+    8000 x 5112 takes the 320-wide column tiles (512 blocks of 320 against 640 of 256)."""
     g = torch.Generator(device="cuda").manual_seed(7 * M + N)
     x = torch.randn((M, K), generator=g, device="cuda").bfloat16()
     w = (torch.randn((N, K), generator=g, device="cuda") / math.sqrt(K)).bfloat16()
