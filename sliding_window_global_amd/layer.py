@@ -212,15 +212,19 @@ def _mixer_out(x, attn_out, wts, bufs, stream):
 
 def mixer_prefill(x, wts: MixerWeights, *, window, rope_table, k_cache=None, v_cache=None,
                   pos_offset=0, bufs: MixerBuffers | None = None, attn_bufs: PrefillBuffers | None = None,
-                  stream=None):
+                  stream=None, fuse_q: bool | None = None):
     """The attention sublayer over a chunk x [B, T, D] at pos_offset; returns (bufs, attn_bufs),
-    the new residual stream in bufs.out."""
+    the new residual stream in bufs.out. fuse_q (default: wherever the fused-Q prefill applies,
+    bf16 at d = 128): the attention kernel normalises and rotates the projected queries itself,
+    so Q' never goes through HBM."""
     B, T, D = x.shape
     bufs = bufs or MixerBuffers(B, T, D, wts, x.device)
     _mixer_in(x, wts, bufs, stream)
+    if fuse_q is None:
+        fuse_q = bufs.q.dtype == torch.bfloat16 and bufs.q.shape[-1] == 128
     attn_bufs = prefill(bufs.q, bufs.k, bufs.v, window=window, rope_table=rope_table, q_norm_w=wts.wq,
                         k_norm_w=wts.wk, norm_offset=wts.qk_offset, k_cache=k_cache, v_cache=v_cache,
-                        bufs=attn_bufs, stream=stream, pos_offset=pos_offset)
+                        bufs=attn_bufs, stream=stream, pos_offset=pos_offset, fuse_q=fuse_q)
     _mixer_out(x, attn_bufs.out, wts, bufs, stream)
     return bufs, attn_bufs
 

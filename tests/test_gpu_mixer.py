@@ -131,10 +131,12 @@ def _weights_host(w):
     return {k: host(v) for k, v in w.items()}
 
 
+@pytest.mark.parametrize("fuse_q", [True, False], ids=["fused_q", "unfused"])
 @pytest.mark.parametrize("window", [128, 0], ids=["local128", "global"])
-def test_mixer_small_matches_oracle(window):
+def test_mixer_small_matches_oracle(window, fuse_q):
     """Chunks [200, 100] then two decode steps of the sublayer at a small hidden width
-    (D = 256, Hq = 8, Hkv = 2, d = 128), B = 2."""
+    (D = 256, Hq = 8, Hkv = 2, d = 128), B = 2; the attention with Q normalised and rotated
+    inside the prefill kernel (the sublayer's default at d = 128) and through the append."""
     wl = MixerWorkload(name="mixer_small", B=2, T=302, D=256, Hq=8, Hkv=2, d=128, window=window,
                        rope=Rope(1e4) if window else Rope(1e6, 64.0), seed=4321 + window)
     x, wdev = wl.draw_device("cuda")
@@ -146,7 +148,7 @@ def test_mixer_small_matches_oracle(window):
     got, p = [], 0
     for T in (200, 100):
         mb, _ = layer.mixer_prefill(x[:, p:p + T].contiguous(), wts, window=window, rope_table=tab,
-                                    k_cache=kc, v_cache=vc, pos_offset=p)
+                                    k_cache=kc, v_cache=vc, pos_offset=p, fuse_q=fuse_q)
         torch.cuda.synchronize()
         got.append(host(mb.out))
         p += T
