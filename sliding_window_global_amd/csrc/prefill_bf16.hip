@@ -302,7 +302,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     // part A: 16 QK MFMAs; P^T words: pair j = keys 2j, 2j+1 of the lane's 32 (flat index
     // f = kb*16 + e), word j of the B operand for k-step j/4
     u32x4 pw[4];
-    float psum[4] = {0.f, 0.f, 0.f, 0.f};
     float* sc = reinterpret_cast<float*>(s_cur);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -315,15 +314,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
         sc[2 * i] = fast_exp2(sc[2 * i]);
         sc[2 * i + 1] = fast_exp2(sc[2 * i + 1]);
         if (i >= 1) pw[(i - 1) >> 2][(i - 1) & 3] = pack_bf16x2(sc[2 * i - 2], sc[2 * i - 1]);
-        if (i >= 2) psum[(i - 2) & 3] = add_bf16x2(pw[(i - 2) >> 2][(i - 2) & 3], psum[(i - 2) & 3]);
+        // row sum: one dot product per P word, chained straight into l (one link per
+        // MFMA slot, so the chain's latency stays hidden; no partial sums to clear or add)
+        if (i >= 2) l_run = add_bf16x2(pw[(i - 2) >> 2][(i - 2) & 3], l_run);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (kPV) {
       pw[3][3] = pack_bf16x2(sc[30], sc[31]);
-      psum[2] = add_bf16x2(pw[3][2], psum[2]);
-      psum[3] = add_bf16x2(pw[3][3], psum[3]);
-      l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+      l_run = add_bf16x2(pw[3][3], add_bf16x2(pw[3][2], l_run));
       // keep the P^T words computed here, under the QK MFMAs, rather than sunk past the
       // mask branch below
 #pragma unroll
@@ -362,8 +361,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
         for (int u = 0; u < cnt; u += 2) {
           const float x = s_next[(f + u) >> 4][(f + u) & 15], y = s_next[(f + u + 1) >> 4][(f + u + 1) & 15];
-          if (((f + u) >> 1) & 1) mx1 = fmaxf(mx1, fmaxf(x, y));
-          else mx0 = fmaxf(mx0, fmaxf(x, y));
+          // max(max(m, x), y): one v_max3 per two scores
+          if (((f + u) >> 1) & 1) mx1 = fmaxf(fmaxf(mx1, x), y);
+          else mx0 = fmaxf(fmaxf(mx0, x), y);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
