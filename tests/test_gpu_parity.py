@@ -427,6 +427,26 @@ def test_decode_batched_full_size(layer_idx):
                  check_b=[0, 31, 63], poison_future=False)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["split", "one_launch"])
+def test_decode_global_full_size_pages_setting(fused):
+    """The global decode at its batched shape (B = 64, 32767 kept + 1 keys) with the settings of
+    「PLaMo 3アーキテクチャ徹底解析」 (§3.2 table: q/k-norm offset 1; §6.3: YaRN s = 256 over
+    L0 = 4096; §6.2: base 1e6), where the YaRN amplitude squared (2.42) makes the scores the
+    sharpest: sampled sequences, through plamo_attn_decode and through the one-launch step."""
+    wl = BATCHED_DECODE
+    ly = wl.layers[1]
+    _decode_case(wl.B, wl.Hq, wl.Hkv, ly.window, wl.pos_offset, Rope(1e6, 256.0), wl.cache_seed(1),
+                 check_b=[0, 31, 63], poison_future=False, fused=fused)
+
+
+@pytest.mark.parametrize("pos_offset", [0, 63, 64, 5000])
+def test_decode_small_batch_yarn256(pos_offset):
+    """Global decode at YaRN s = 256 and norm offset 1 on contiguous growth and tile edges
+    (dead slots NaN), split path and one-launch step."""
+    for fused in (False, True):
+        _decode_case(3, 16, 2, 0, pos_offset, Rope(1e6, 256.0), 700 + pos_offset, check_b=[0, 1, 2], fused=fused)
+
+
 def test_decode_batched_full_size_post_rope():
     """The global batched-decode shape with a post-RoPE cache (the prior cache read as already
     rotated K, the new token rotated at its absolute position): sampled sequences."""
