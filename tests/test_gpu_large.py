@@ -108,3 +108,43 @@ def test_gemma_local_prefill_half_million_tokens():
                                    theta=L.theta, partial=1.0, q_norm_w=wq, k_norm_w=wk, norm_offset=L.norm_offset,
                                    eps=L.eps, scale=L.scale, v_norm=True, rows=np.array([r - s0]))
         assert_parity(got[0, i:i + 1], ref, TOL_BF16, f"row {r}")
+
+
+def test_decode_caches_beyond_2_32_elements():
+    """Batched global decode at 131072 keys and B = 64 (「PLaMo 3アーキテクチャ徹底解析」 §4.4,
+    §4.5; §2.3: the KV bytes a decode step reads): each cache holds 64 x 8 x 131072 x 128 ≈
+    8.6e9 elements (17 GiB), so the later sequences start past 2^32 elements. Through
+    plamo_attn_decode and through the one-launch step; the first and the last sequence
+    against the oracle."""
+    from helpers import oracle_decode_one
+    from synthetic.workloads import device_normal_bf16
+
+    B, Hq, Hkv, d, pos = 64, 64, 8, 128, 131071
+    rope = Rope(1e6, 64.0)
+    cap = pos + 1
+    print(f"\n[large] decode B={B} keys={cap} cache elements={B * Hkv * cap * d}", flush=True)
+    kc = device_normal_bf16((B, Hkv, cap, d), 9510, "cuda")
+    vc = device_normal_bf16((B, Hkv, cap, d), 9511, "cuda")
+    torch.cuda.empty_cache()
+    assert kc.numel() > 2 ** 32
+    check_b = [0, B - 1]
+    dr = Draw(9512, True)
+    q, k, v = dr.normal((B, 1, Hq, d)), dr.normal((B, 1, Hkv, d)), dr.normal((B, 1, Hkv, d))
+    wq, wk = dr.normal((d,), 0.02), dr.normal((d,), 0.02)
+    refs = {}
+    for b in check_b:
+        pk = host(kc[b, :, :pos]).transpose(1, 0, 2)
+        pv = host(vc[b, :, :pos]).transpose(1, 0, 2)
+        refs[b] = oracle_decode_one(q[b], k[b], v[b], pk, pv, pos, window=0, rope=rope, wq=wq, wk=wk)
+        del pk, pv
+    tab = swg.make_rope_table(cap + 64, swg.RopeParams(rope.theta, rope.yarn_factor, rope.orig_ctx,
+                                                       rope.beta_fast, rope.beta_slow))
+    for fused in (False, True):
+        # (both calls write the same new token into slot pos; the oracle's prior is slots < pos)
+        bufs = layer.decode(dev(q), dev(k), dev(v), kc, vc, window=0, pos_offset=pos, rope_table=tab,
+                            q_norm_w=dev(wq), k_norm_w=dev(wk), norm_offset=1.0, fused=fused)
+        torch.cuda.synchronize()
+        out = host(bufs.out)
+        for b in check_b:
+            assert_parity(out[b], refs[b], TOL_BF16, f"decode b={b} fused={fused}")
+        del bufs
