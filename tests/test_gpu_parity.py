@@ -542,6 +542,44 @@ def test_prefill_then_decode_matches_oracle(window):
     assert_parity(got[:, rows], ref, TOL_BF16, f"prefill+decode W={window}")
 
 
+@pytest.mark.parametrize("window,pos_offset,rope", [(2048, 100000, Rope(1e4)), (0, 100000, Rope(1e6, 256.0))],
+                         ids=["ring2048", "global_yarn256"])
+def test_prefill_chunk_after_long_context(window, pos_offset, rope):
+    """A 300-token chunk after 100000 tokens (「PLaMo 3アーキテクチャ徹底解析」 §4.4: the chunk
+    attends the kept keys the cache returns, renumbered from 0, then appends itself): the
+    cache holds the kept tokens drawn directly (normalised pre-RoPE K, raw V) at their slots
+    (the ring wrapped many times; the global cache 100000 deep, at the pages' s = 256 and norm
+    offset 1), every other slot NaN; sampled rows of both sequences against the oracle."""
+    B, Hq, Hkv, d, T = 2, 8, 2, 128, 300
+    cap = window if window else pos_offset + T
+    kc = device_normal_bf16((B, Hkv, cap, d), 4100 + window, "cuda")
+    vc = device_normal_bf16((B, Hkv, cap, d), 4101 + window, "cuda")
+    slots = kept_slots(pos_offset, window)
+    live = np.zeros(cap, dtype=bool)
+    live[slots] = True
+    dead = torch.from_numpy(np.nonzero(~live)[0]).cuda()
+    kc[:, :, dead] = float("nan")
+    vc[:, :, dead] = float("nan")
+    sel = torch.from_numpy(slots).cuda()
+    prior_k = [host(kc[b][:, sel]).transpose(1, 0, 2) for b in range(B)]
+    prior_v = [host(vc[b][:, sel]).transpose(1, 0, 2) for b in range(B)]
+    dr = Draw(4102 + window, True)
+    q, k, v = dr.normal((B, T, Hq, d)), dr.normal((B, T, Hkv, d)), dr.normal((B, T, Hkv, d))
+    wq, wk = dr.normal((d,), 0.02), dr.normal((d,), 0.02)
+    tab = rope_table(rope, pos_offset + T + 64)
+    bufs = layer.prefill(dev(q), dev(k), dev(v), window=window, rope_table=tab, k_cache=kc, v_cache=vc,
+                         pos_offset=pos_offset, q_norm_w=dev(wq), k_norm_w=dev(wk), norm_offset=1.0)
+    torch.cuda.synchronize()
+    out = host(bufs.out)
+    rows = np.array([0, 1, 63, 64, 150, T - 2, T - 1])
+    for b in range(B):
+        cache = LayerKVCache.with_prior(prior_k[b], prior_v[b], pos_offset, window)
+        ref = attention_layer_step(q[b], k[b], v[b], cache, theta=rope.theta, yarn_factor=rope.yarn_factor,
+                                   orig_ctx=rope.orig_ctx, beta_fast=rope.beta_fast, beta_slow=rope.beta_slow,
+                                   q_norm_w=wq, k_norm_w=wk, norm_offset=1.0, scale=1.0 / math.sqrt(d), rows=rows)
+        assert_parity(out[b][rows], ref, TOL_BF16, f"chunk after {pos_offset} W={window} b={b}")
+
+
 @pytest.mark.parametrize("window,chunks,bf16", [(0, [100, 37, 300], True), (16, [5, 20, 3, 40], True),
                                                 (2048, [1500, 700, 900, 64], True),
                                                 (128, [200, 1, 311], False)],
